@@ -1,0 +1,166 @@
+"""ORACLE -- test infrastructure only.
+
+A plain, slow CPU model of the decode-step hot path (slot-buffer matching,
+reservation under lifetime or bucketed-LRU eviction, miss-only row transfer,
+and attention over the selected entries).  Only the tests, the smoke check
+and the CPU leg of the benchmark may import it; the product library never
+does, and shares no code with it.
+
+  avsg_oracle.c   the state machine of one step per unit (plain C, qsort and
+                  a two-pointer merge), compiled with gcc on first use
+  attention.py    float64 attention over the selected rows (numpy)
+
+Parity pins: the state machine is checked against a separate brute-force
+replay, hand-worked traces, closed forms and invariants; attention against
+torch's scaled_dot_product_attention with a boolean mask and closed forms.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+from . import attention  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "avsg_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+_lock = threading.Lock()
+
+OK, ERR_UNSORTED, ERR_RANGE, ERR_CAPACITY, ERR_STATE = 0, 16, 17, 18, 19
+LIFETIME, LRU = 0, 1
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc: -O2, no intrinsics, OpenMP over units."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", _SRC,
+                               "-o", tmp])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_slots", "n_entries", "n_tokens", "k", "policy", "lifetime_L", "n_buckets")]
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            p = ctypes.c_void_p
+            lib.oracle_unit_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64] + [p] * 8
+            lib.oracle_unit_step.restype = ctypes.c_int
+            lib.oracle_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, ctypes.c_int64] + [p] * 9
+            lib.oracle_step.restype = None
+            _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags.c_contiguous
+    return a.ctypes.data
+
+
+class OracleBuffer:
+    """Per-unit slot state and (optionally) the device buffer contents,
+    advanced one decode step at a time.
+
+    slot_tok [units][S] int32 (-1 = empty), life [units][S] int32 (lifetime,
+    or last-selected step with -1 = never for the LRU policy), buf
+    [units][S][row_elems] uint16 when `track_buf`.
+    """
+
+    def __init__(self, n_slots, n_entries, n_tokens, k, policy, lifetime_L, n_buckets, units,
+                 row_elems=0, track_buf=False):
+        self.cfg = _Cfg(n_slots, n_entries, n_tokens, k,
+                        LRU if policy in ("lru", LRU) else LIFETIME, lifetime_L, n_buckets)
+        self.units = units
+        self.row_elems = row_elems
+        self.track_buf = track_buf
+        self.reset()
+
+    @classmethod
+    def for_workload(cls, w, track_buf=False, units=None):
+        return cls(w.n_slots, w.n_entries, w.n_q_tokens, w.k, w.policy, w.lifetime_L, w.n_buckets,
+                   w.units if units is None else units, w.row_elems, track_buf)
+
+    def reset(self):
+        S = self.cfg.n_slots
+        self.t = 0
+        self.slot_tok = np.full((self.units, S), -1, dtype=np.int32)
+        self.life = np.full((self.units, S), -1 if self.cfg.policy == LRU else 0, dtype=np.int32)
+        self.buf = (np.zeros((self.units, S, self.row_elems), dtype=np.uint16)
+                    if self.track_buf else None)
+
+    def step(self, sel: np.ndarray, host_kv: np.ndarray | None = None) -> dict:
+        """Advance one step with selections sel [units][T][k].  When the buffer
+        is tracked, reserved slots receive host_kv[u][id] byte for byte."""
+        c = self.cfg
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        assert sel.shape == (self.units, c.n_tokens, c.k)
+        tk = c.n_tokens * c.k
+        res = dict(
+            hit_flag=np.zeros((self.units, c.n_tokens, c.k), dtype=np.uint8),
+            sel_slot=np.zeros((self.units, c.n_tokens, c.k), dtype=np.int32),
+            fill_slot=np.zeros((self.units, c.n_slots), dtype=np.int32),
+            fill_id=np.zeros((self.units, c.n_slots), dtype=np.int32),
+            counts=np.zeros((self.units, 4), dtype=np.int32),
+            status=np.zeros(self.units, dtype=np.int32),
+        )
+        assert tk > 0
+        _load().oracle_step(ctypes.byref(c), self.units, self.t, _p(sel), _p(self.slot_tok),
+                            _p(self.life), _p(res["hit_flag"]), _p(res["sel_slot"]),
+                            _p(res["fill_slot"]), _p(res["fill_id"]), _p(res["counts"]),
+                            _p(res["status"]))
+        res["n_hit"] = res["counts"][:, 0].copy()
+        res["n_miss"] = res["counts"][:, 1].copy()
+        res["n_evict"] = res["counts"][:, 2].copy()
+        res["n_union"] = res["counts"][:, 3].copy()
+        if self.track_buf:
+            assert host_kv is not None
+            for u in range(self.units):
+                m = res["n_miss"][u]
+                if m:
+                    self.buf[u, res["fill_slot"][u, :m]] = host_kv[u, res["fill_id"][u, :m]]
+        self.t += 1
+        return res
+
+    def snapshot(self):
+        return (self.t, self.slot_tok.copy(), self.life.copy(),
+                None if self.buf is None else self.buf.copy())
+
+    def restore(self, snap):
+        self.t, st, lf, bf = snap
+        self.slot_tok, self.life = st.copy(), lf.copy()
+        self.buf = None if bf is None else bf.copy()
+
+
+def unit_step(n_slots, n_entries, k, policy, lifetime_L, n_buckets, t, sel, slot_tok, life):
+    """Single-unit call for small hand-built cases: returns (status, result
+    dict) and updates slot_tok / life (int32 arrays) in place."""
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    if sel.ndim == 1:
+        sel = sel[None, :]
+    T = sel.shape[0]
+    cfg = _Cfg(n_slots, n_entries, T, k, LRU if policy in ("lru", LRU) else LIFETIME, lifetime_L,
+               n_buckets)
+    assert slot_tok.dtype == np.int32 and life.dtype == np.int32
+    hit = np.zeros((T, k), np.uint8)
+    ss = np.zeros((T, k), np.int32)
+    fs = np.zeros(n_slots, np.int32)
+    fi = np.zeros(n_slots, np.int32)
+    cnt = np.zeros(4, np.int32)
+    st = _load().oracle_unit_step(ctypes.byref(cfg), t, _p(sel), _p(slot_tok), _p(life), _p(hit),
+                                  _p(ss), _p(fs), _p(fi), _p(cnt))
+    m = int(cnt[1])
+    return st, dict(hit_flag=hit, sel_slot=ss, fill_slot=fs[:m].copy(), fill_id=fi[:m].copy(),
+                    n_hit=int(cnt[0]), n_miss=m, n_evict=int(cnt[2]), n_union=int(cnt[3]))

@@ -1,0 +1,77 @@
+"""ORACLE -- test infrastructure only (tests, smoke check, CPU benchmark leg).
+
+Decode attention restricted to the selected entries, in float64, written as
+its definition.  The AVSG abstract (arxivdaily 2609.37538, abstract) states
+that the operator preserves the exact token selections of dynamic sparse
+attention, so the output of a step is plain softmax attention of each query
+head over exactly the selected K/V rows; it never depends on which rows
+happened to be resident.  This model therefore reads the rows straight from
+the host KV, not from any buffer.
+
+Readings where the pages are silent:
+  - query head h uses KV head h // (Hq / Hkv) (consecutive groups);
+  - a selected page contributes all of its tokens (no intra-page mask);
+  - a latent row serves as the key (all head_dim_qk values) and its first
+    head_dim_v values serve as the value;
+  - a unit whose step failed validation produces zeros.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def unit_kv(w, host_kv_unit: np.ndarray, ids: np.ndarray):
+    """K [n][dqk] and V [n][dv] (float64) of the selected entries of one unit;
+    n = len(ids) * tokens_per_entry, tokens of a page in order."""
+    rows = bf16_to_f64(host_kv_unit[np.asarray(ids)])          # [k][row_elems]
+    if w.latent:
+        return rows[:, :w.head_dim_qk], rows[:, :w.head_dim_v]
+    tpe = w.tokens_per_entry
+    K = rows[:, :tpe * w.head_dim_qk].reshape(-1, w.head_dim_qk)
+    V = rows[:, tpe * w.head_dim_qk:].reshape(-1, w.head_dim_v)
+    return K, V
+
+
+def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """o[h] = sum_i softmax_i(scale * <q[h], K[i]>) V[i], for q [G][d]."""
+    s = scale * (q @ K.T)                                        # [G][n]
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ V                                                 # [G][dv]
+
+
+def attend_unit(w, q_bits: np.ndarray, host_kv_unit: np.ndarray, sel_unit: np.ndarray, unit: int,
+                token: int, heads=None) -> np.ndarray:
+    """Output rows [G'][dv] of unit `unit`, query token `token`, for the query
+    heads `heads` (default: all heads mapped to this unit's KV head)."""
+    G = w.n_q_heads // w.n_kv_heads
+    b, g = divmod(unit, w.n_kv_heads)
+    if heads is None:
+        heads = range(g * G, (g + 1) * G)
+    heads = list(heads)
+    q = bf16_to_f64(q_bits[b, token, heads, :])                  # [G'][dqk]
+    K, V = unit_kv(w, host_kv_unit, sel_unit[token])
+    return softmax_attention(q, K, V, w.softmax_scale)
+
+
+def attend(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=None,
+           units=None) -> np.ndarray:
+    """float64 out [B][T][Hq][dv] for one step.  host_kv is [units][N][row]
+    (uint16 bf16 bits), sel is [units][T][k].  Units not in `units` are NaN;
+    units with a nonzero status are zero."""
+    out = np.full((w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_v), np.nan)
+    G = w.n_q_heads // w.n_kv_heads
+    for u in (range(w.units) if units is None else units):
+        b, g = divmod(u, w.n_kv_heads)
+        for j in range(w.n_q_tokens):
+            if status is not None and status[u] != 0:
+                out[b, j, g * G:(g + 1) * G] = 0.0
+            else:
+                out[b, j, g * G:(g + 1) * G] = attend_unit(w, q_bits, host_kv[u], sel[u], u, j)
+    return out

@@ -1,0 +1,69 @@
+"""The seeded input generator: determinism, recipe properties, known values.
+CPU only."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import tracegen as tg
+
+
+def test_splitmix64_reference_values():
+    """splitmix64 seeded with 0 yields this published sequence (the
+    generator's first outputs appear in Vigna's reference implementation and
+    many test suites)."""
+    # rnd(key, i) = mix(key + (i+1)*golden): with key 0 these are the first
+    # three outputs of splitmix64 started from state 0.
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    assert [tg.splitmix_output(0, i) for i in range(3)] == want
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_selection_recipe(cid):
+    w = tg.WORKLOADS[cid]
+    steps = 6
+    sel = tg.selections(w, steps=steps)
+    assert sel.shape == (steps, w.units, w.n_q_tokens, w.k)
+    assert ((sel >= 0) & (sel < w.n_entries)).all()
+    assert (np.diff(sel, axis=-1) > 0).all()
+    keep = int(np.floor(w.overlap * w.k + 0.5))
+    keep_sh = int(np.floor(w.overlap_shared * w.k + 0.5))
+    for u in (0, w.units - 1):
+        for t in range(1, steps):
+            assert np.intersect1d(sel[t, u, 0], sel[t - 1, u, 0]).size == keep
+        for j in range(1, w.n_q_tokens):
+            assert np.intersect1d(sel[2, u, 0], sel[2, u, j]).size == keep_sh
+    assert np.array_equal(sel, tg.selections(w, steps=steps))
+
+
+def test_allhit_and_allmiss_modes():
+    w = tg.WORKLOADS[2]
+    h = tg.selections(w, steps=4, mode="allhit")
+    assert all(np.array_equal(h[0], h[t]) for t in range(4))
+    m = tg.selections(w, steps=8, mode="allmiss")
+    seen = set()
+    for t in range(8):
+        s = set(m[t, 3, 0].tolist())
+        assert not (s & seen)
+        seen |= s
+
+
+def test_kv_rows_and_queries():
+    w = tg.WORKLOADS[2]
+    kv = tg.fill_kv(w, units=2)
+    assert np.array_equal(tg.fill_kv_rows(w, 1, 333, 5), kv[1, 333:338])
+    x = tg.bf16_to_f64(kv)
+    assert abs(x.mean()) < 5e-3 and abs(x.std() - 1) < 5e-3
+    q0, q1 = tg.queries(w, 0), tg.queries(w, 1)
+    assert q0.shape == (8, 1, 32, 128) and not np.array_equal(q0, q1)
+    assert np.array_equal(q0, tg.queries(w, 0))
+
+
+def test_zipf_head_is_hot():
+    """Rank-1 of Zipf(1.1) over 32768 positions carries about 14% of the mass;
+    its position (permutation[0]) should be in nearly every step-0 selection
+    of size 2048 (test of the sampler, not of the method)."""
+    w = tg.WORKLOADS[2]
+    sel = tg.selections(w, steps=1)
+    hits = sum(int(tg.permutation(w, u)[0] in set(sel[0, u, 0].tolist())) for u in range(16))
+    assert hits == 16
