@@ -1,0 +1,385 @@
+// Host side of the libavsg C ABI: configuration checks, workspace layout,
+// stream-ordered launches of the step kernels, error words and pinned memory.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "avsg_internal.h"
+
+struct avsg_ctx {
+  avsg_config cfg;
+  avsg::WsLayout ws;
+  avsg::Derived d;
+  hipStream_t stream;
+  int device;
+  int num_cus;
+  int gather_grid;
+  char* workspace;
+  int64_t t;
+  const void* pinned_checked;    // last host_kv pointer found pinned
+  const void* pinned_device;     // its device-visible address
+};
+
+namespace avsg {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int32_t next_pow2(int64_t x) {
+  int32_t c = 64;
+  while (c < x) c <<= 1;
+  return c;
+}
+
+bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
+  d->units = c.batch * c.n_kv_heads;
+  d->G = c.n_q_heads / c.n_kv_heads;
+  d->row_elems = c.kv_layout == AVSG_KV_LATENT
+                     ? c.head_dim_qk
+                     : c.tokens_per_entry * (c.head_dim_qk + c.head_dim_v);
+  d->nbins = c.policy == AVSG_POLICY_BUCKET_LRU ? c.n_buckets + 1 : c.lifetime_L + 2;
+  const int64_t tk = (int64_t)c.n_q_tokens * c.k;
+  ws->ucap = (int32_t)(tk < c.n_slots ? tk : c.n_slots);
+  ws->table_cap = next_pow2(2 * (int64_t)ws->ucap);
+  d->log_table_cap = 0;
+  while ((1 << d->log_table_cap) < ws->table_cap) ++d->log_table_cap;
+  const int64_t rows = (int64_t)c.k * c.tokens_per_entry;
+  if (c.kv_layout == AVSG_KV_LATENT) {
+    ws->split_rows = 256;
+  } else {
+    ws->split_rows = 128;
+  }
+  ws->nsplit = (int32_t)((rows + ws->split_rows - 1) / ws->split_rows);
+  const int64_t T = c.n_q_tokens;
+  size_t off = 0;
+  ws->unit_status = off; off = align256(off + 4 * (size_t)d->units);
+  ws->miss_count = off;  off = align256(off + 4 * (size_t)d->units);
+  ws->misses = off;      off = align256(off + 8 * (size_t)d->units * ws->ucap);
+  ws->err_word = off;    off = align256(off + 8);
+  ws->counters = off;    off = align256(off + 4 * (size_t)d->units * T);
+  ws->partials = off;
+  off = align256(off + 4 * (size_t)d->units * T * ws->nsplit * (size_t)(c.n_q_heads / c.n_kv_heads) *
+                           (size_t)(c.head_dim_v + 2));
+  ws->total = off;
+  const int64_t lds_ints = 2 * (int64_t)ws->ucap + ws->table_cap + 2 * 16 * (int64_t)d->nbins +
+                           d->nbins + 64 + (c.n_q_tokens > 1 ? tk : ws->ucap) +
+                           (c.n_q_tokens > 1 ? tk + c.k + 1 : 0);
+  d->mr_lds = 4 * (size_t)lds_ints;
+  return true;
+}
+
+}  // namespace avsg
+
+using namespace avsg;
+
+static avsg_status check_config_impl(const avsg_config* c) {
+  if (!c) return AVSG_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_tokens < 1 ||
+      c->head_dim_qk < 1 || c->head_dim_v < 1 || c->n_entries < 1 || c->tokens_per_entry < 1 ||
+      c->k < 1 || c->n_slots < 1)
+    return AVSG_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads != 0) return AVSG_ERR_INVALID_ARG;
+  if (c->k > c->n_slots || c->k > c->n_entries) return AVSG_ERR_INVALID_ARG;
+  if (c->policy != AVSG_POLICY_LIFETIME && c->policy != AVSG_POLICY_BUCKET_LRU)
+    return AVSG_ERR_INVALID_ARG;
+  if (c->policy == AVSG_POLICY_LIFETIME && (c->lifetime_L < 1 || c->lifetime_L > 1022))
+    return AVSG_ERR_INVALID_ARG;
+  if (c->policy == AVSG_POLICY_BUCKET_LRU && (c->n_buckets < 1 || c->n_buckets > 1023))
+    return AVSG_ERR_INVALID_ARG;
+  if (c->kv_layout != AVSG_KV_SPLIT && c->kv_layout != AVSG_KV_LATENT) return AVSG_ERR_INVALID_ARG;
+  if (!(c->softmax_scale > 0.f)) return AVSG_ERR_INVALID_ARG;
+  if ((int64_t)c->batch * c->n_kv_heads > (1 << 20)) return AVSG_ERR_UNSUPPORTED;
+  if (c->n_q_tokens > 2) return AVSG_ERR_UNSUPPORTED;
+  if (c->n_slots > kMRThreads * kMaxSlotsPerLane) return AVSG_ERR_UNSUPPORTED;
+  if (c->n_slots >= kMissFlag || c->n_entries >= (1 << 30)) return AVSG_ERR_UNSUPPORTED;
+  if (c->kv_layout == AVSG_KV_SPLIT) {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (c->head_dim_qk != 128 || c->head_dim_v != 128) return AVSG_ERR_UNSUPPORTED;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return AVSG_ERR_UNSUPPORTED;
+  } else {
+    if (c->tokens_per_entry != 1 || c->n_kv_heads != 1) return AVSG_ERR_INVALID_ARG;
+    if (c->head_dim_qk != 576 || c->head_dim_v != 512) return AVSG_ERR_UNSUPPORTED;
+    if (c->n_q_heads % 64 != 0) return AVSG_ERR_UNSUPPORTED;
+    return AVSG_ERR_UNSUPPORTED;  // latent attention kernel not built yet
+  }
+  WsLayout ws;
+  Derived d;
+  layout_for(*c, &ws, &d);
+  if (d.mr_lds > 160 * 1024) return AVSG_ERR_UNSUPPORTED;
+  // gather addresses rows with 32-bit piece indices
+  const int64_t row16 = (int64_t)d.row_elems * 2 / 16;
+  if ((int64_t)d.row_elems * 2 % 16 != 0) return AVSG_ERR_UNSUPPORTED;
+  if ((int64_t)d.units * ws.ucap * row16 >= ((int64_t)1 << 32)) return AVSG_ERR_UNSUPPORTED;
+  return AVSG_OK;
+}
+
+extern "C" {
+
+avsg_status avsg_check_config(const avsg_config* cfg) { return check_config_impl(cfg); }
+
+size_t avsg_workspace_bytes(const avsg_config* cfg) {
+  if (check_config_impl(cfg) != AVSG_OK) return 0;
+  WsLayout ws;
+  Derived d;
+  layout_for(*cfg, &ws, &d);
+  return ws.total;
+}
+
+const char* avsg_status_string(avsg_status s) {
+  switch (s) {
+    case AVSG_OK: return "ok";
+    case AVSG_ERR_INVALID_ARG: return "invalid argument";
+    case AVSG_ERR_NOT_PINNED: return "host_kv is not pinned device-mapped host memory";
+    case AVSG_ERR_HIP: return "HIP runtime error";
+    case AVSG_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case AVSG_ERR_UNSORTED: return "selection not strictly ascending";
+    case AVSG_ERR_RANGE: return "selected id out of range";
+    case AVSG_ERR_CAPACITY: return "selection union exceeds buffer slots";
+    case AVSG_ERR_STATE: return "invalid buffer state";
+  }
+  return "unknown status";
+}
+
+avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, size_t ws_bytes,
+                        avsg_ctx** out) {
+  if (!out) return AVSG_ERR_INVALID_ARG;
+  *out = nullptr;
+  avsg_status st = check_config_impl(cfg);
+  if (st != AVSG_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255)) return AVSG_ERR_INVALID_ARG;
+  avsg_ctx* c = new (std::nothrow) avsg_ctx();
+  if (!c) return AVSG_ERR_INVALID_ARG;
+  c->cfg = *cfg;
+  layout_for(*cfg, &c->ws, &c->d);
+  if (ws_bytes < c->ws.total) { delete c; return AVSG_ERR_INVALID_ARG; }
+  if (hipGetDevice(&c->device) != hipSuccess) { delete c; return AVSG_ERR_HIP; }
+  int lds_max = 0;
+  if (hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) !=
+          hipSuccess) {
+    delete c;
+    return AVSG_ERR_HIP;
+  }
+  if ((int64_t)c->d.mr_lds > lds_max) { delete c; return AVSG_ERR_UNSUPPORTED; }
+  if (c->d.mr_lds > 64 * 1024 && match_reserve_set_lds(c->d.mr_lds) != hipSuccess) {
+    delete c;
+    return AVSG_ERR_HIP;
+  }
+  c->gather_grid = c->num_cus * 2;
+  c->stream = (hipStream_t)stream;
+  c->workspace = (char*)workspace;
+  c->t = 0;
+  c->pinned_checked = nullptr;
+  c->pinned_device = nullptr;
+  // zero the library-owned workspace words (status, counts, error, counters)
+  if (launch_fill_i32((int32_t*)c->workspace, 0, c->ws.partials / 4, c->stream) != hipSuccess) {
+    delete c;
+    return AVSG_ERR_HIP;
+  }
+  *out = c;
+  return AVSG_OK;
+}
+
+avsg_status avsg_set_stream(avsg_ctx* ctx, void* stream) {
+  if (!ctx) return AVSG_ERR_INVALID_ARG;
+  ctx->stream = (hipStream_t)stream;
+  return AVSG_OK;
+}
+
+avsg_status avsg_destroy(avsg_ctx* ctx) {
+  delete ctx;
+  return AVSG_OK;
+}
+
+int64_t avsg_get_step(const avsg_ctx* ctx) { return ctx ? ctx->t : -1; }
+
+avsg_status avsg_set_step(avsg_ctx* ctx, int64_t t) {
+  if (!ctx || t < 0 || t > INT32_MAX) return AVSG_ERR_INVALID_ARG;
+  ctx->t = t;
+  return AVSG_OK;
+}
+
+int32_t avsg_attn_splits(const avsg_ctx* ctx) { return ctx ? ctx->ws.nsplit : 0; }
+
+avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes) {
+  if (!ctx || !slot_table || !lifetimes) return AVSG_ERR_INVALID_ARG;
+  const size_t n = (size_t)ctx->d.units * ctx->cfg.n_slots;
+  const int32_t life0 = ctx->cfg.policy == AVSG_POLICY_BUCKET_LRU ? -1 : 0;
+  if (launch_fill_i32(slot_table, -1, n, ctx->stream) != hipSuccess ||
+      launch_fill_i32(lifetimes, life0, n, ctx->stream) != hipSuccess ||
+      launch_fill_i32((int32_t*)(ctx->workspace + ctx->ws.err_word), 0, 2, ctx->stream) != hipSuccess)
+    return AVSG_ERR_HIP;
+  ctx->t = 0;
+  return AVSG_OK;
+}
+
+static avsg_status device_view_of_pinned(avsg_ctx* ctx, const void* host, const void** dev) {
+  if (host == ctx->pinned_checked) { *dev = ctx->pinned_device; return AVSG_OK; }
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();
+    return AVSG_ERR_NOT_PINNED;
+  }
+  if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) return AVSG_ERR_NOT_PINNED;
+  ctx->pinned_checked = host;
+  ctx->pinned_device = attr.devicePointer;
+  *dev = attr.devicePointer;
+  return AVSG_OK;
+}
+
+avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
+                      const uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
+                      int32_t* lifetimes, float* out, const avsg_hit_stats* hs) {
+  if (!ctx || !sel_idx || !q || !host_kv || !buf_kv || !slot_table || !lifetimes || !out || !hs ||
+      !hs->hit_flag || !hs->sel_slot || !hs->n_hit || !hs->n_miss || !hs->n_evict)
+    return AVSG_ERR_INVALID_ARG;
+  const void* host_dev = nullptr;
+  avsg_status st = device_view_of_pinned(ctx, host_kv, &host_dev);
+  if (st != AVSG_OK) return st;
+  const avsg_config& c = ctx->cfg;
+  char* ws = ctx->workspace;
+  int32_t* unit_status = (int32_t*)(ws + ctx->ws.unit_status);
+  int32_t* miss_count = (int32_t*)(ws + ctx->ws.miss_count);
+  int2* misses = (int2*)(ws + ctx->ws.misses);
+
+  MatchReserveParams mp;
+  mp.sel = sel_idx;
+  mp.slot_table = slot_table;
+  mp.lifetimes = lifetimes;
+  mp.hit_flag = hs->hit_flag;
+  mp.sel_slot = hs->sel_slot;
+  mp.n_hit = hs->n_hit;
+  mp.n_miss = hs->n_miss;
+  mp.n_evict = hs->n_evict;
+  mp.user_status = hs->unit_status;
+  mp.unit_status = unit_status;
+  mp.miss_count = miss_count;
+  mp.misses = misses;
+  mp.err_word = (uint32_t*)(ws + ctx->ws.err_word);
+  mp.t = ctx->t;
+  mp.S = c.n_slots;
+  mp.N = c.n_entries;
+  mp.T = c.n_q_tokens;
+  mp.k = c.k;
+  mp.ucap = ctx->ws.ucap;
+  mp.table_cap = ctx->ws.table_cap;
+  mp.log_table_cap = ctx->d.log_table_cap;
+  mp.policy = c.policy;
+  mp.L = c.lifetime_L;
+  mp.B = c.n_buckets;
+  mp.nbins = ctx->d.nbins;
+  if (launch_match_reserve(mp, ctx->d.units, ctx->d.mr_lds, ctx->stream) != hipSuccess)
+    return AVSG_ERR_HIP;
+
+  GatherParams gp;
+  gp.misses = misses;
+  gp.miss_count = miss_count;
+  gp.host_kv = (const uint4*)host_dev;
+  gp.buf_kv = (uint4*)buf_kv;
+  gp.N = c.n_entries;
+  gp.S = c.n_slots;
+  gp.units = ctx->d.units;
+  gp.ucap = ctx->ws.ucap;
+  gp.row16 = ctx->d.row_elems * 2 / 16;
+  if (launch_gather(gp, ctx->gather_grid, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
+
+  AttnParams ap;
+  ap.sel_slot = hs->sel_slot;
+  ap.unit_status = unit_status;
+  ap.q = q;
+  ap.buf_kv = buf_kv;
+  ap.out = out;
+  ap.partials = (float*)(ws + ctx->ws.partials);
+  ap.counters = (uint32_t*)(ws + ctx->ws.counters);
+  ap.S = c.n_slots;
+  ap.units = ctx->d.units;
+  ap.Hkv = c.n_kv_heads;
+  ap.Hq = c.n_q_heads;
+  ap.T = c.n_q_tokens;
+  ap.k = c.k;
+  ap.tpe = c.tokens_per_entry;
+  ap.row_elems = ctx->d.row_elems;
+  ap.nsplit = ctx->ws.nsplit;
+  ap.split_rows = ctx->ws.split_rows;
+  ap.scale_log2e = c.softmax_scale * 1.4426950408889634f;
+  hipError_t e = c.kv_layout == AVSG_KV_LATENT
+                     ? launch_attn_latent(ap, c.head_dim_qk, c.head_dim_v, ctx->stream)
+                     : launch_attn_split(ap, ctx->d.G, ctx->stream);
+  if (e != hipSuccess) return AVSG_ERR_HIP;
+  ctx->t += 1;
+  return AVSG_OK;
+}
+
+static avsg_status status_from_bits(uint32_t bits) {
+  if (bits & (1u << (AVSG_ERR_RANGE - 16))) return AVSG_ERR_RANGE;
+  if (bits & (1u << (AVSG_ERR_UNSORTED - 16))) return AVSG_ERR_UNSORTED;
+  if (bits & (1u << (AVSG_ERR_CAPACITY - 16))) return AVSG_ERR_CAPACITY;
+  if (bits & (1u << (AVSG_ERR_STATE - 16))) return AVSG_ERR_STATE;
+  return AVSG_OK;
+}
+
+avsg_status avsg_last_error(avsg_ctx* ctx) {
+  if (!ctx) return AVSG_ERR_INVALID_ARG;
+  uint32_t bits = 0;
+  uint32_t* dev = (uint32_t*)(ctx->workspace + ctx->ws.err_word);
+  if (hipMemcpyAsync(&bits, dev, 4, hipMemcpyDeviceToHost, ctx->stream) != hipSuccess ||
+      hipStreamSynchronize(ctx->stream) != hipSuccess)
+    return AVSG_ERR_HIP;
+  if (launch_fill_i32((int32_t*)dev, 0, 1, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
+  return status_from_bits(bits);
+}
+
+avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const int32_t* lifetimes) {
+  if (!ctx || !slot_table || !lifetimes) return AVSG_ERR_INVALID_ARG;
+  uint32_t* word = (uint32_t*)(ctx->workspace + ctx->ws.err_word) + 1;
+  if (launch_fill_i32((int32_t*)word, 0, 1, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
+  const avsg_config& c = ctx->cfg;
+  if (launch_validate(slot_table, lifetimes, ctx->d.units, c.n_slots, c.n_entries, c.policy,
+                      c.lifetime_L, ctx->t, word, ctx->stream) != hipSuccess)
+    return AVSG_ERR_HIP;
+  uint32_t bits = 0;
+  if (hipMemcpyAsync(&bits, word, 4, hipMemcpyDeviceToHost, ctx->stream) != hipSuccess ||
+      hipStreamSynchronize(ctx->stream) != hipSuccess)
+    return AVSG_ERR_HIP;
+  return bits ? AVSG_ERR_STATE : AVSG_OK;
+}
+
+avsg_status avsg_host_alloc(size_t bytes, unsigned flags, void** host_ptr) {
+  if (!host_ptr || bytes == 0) return AVSG_ERR_INVALID_ARG;
+  *host_ptr = nullptr;
+  unsigned f = hipHostMallocMapped | hipHostMallocPortable |
+               ((flags & AVSG_HOST_COHERENT) ? hipHostMallocCoherent : hipHostMallocNonCoherent);
+  if (hipHostMalloc(host_ptr, bytes, f) != hipSuccess) {
+    (void)hipGetLastError();
+    *host_ptr = nullptr;
+    return AVSG_ERR_HIP;
+  }
+  return AVSG_OK;
+}
+
+avsg_status avsg_host_free(void* host_ptr) {
+  if (!host_ptr) return AVSG_ERR_INVALID_ARG;
+  return hipHostFree(host_ptr) == hipSuccess ? AVSG_OK : AVSG_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace avsg {
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace avsg

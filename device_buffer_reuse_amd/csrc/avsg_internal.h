@@ -1,0 +1,83 @@
+// Internal declarations shared by the libavsg translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/avsg.h"
+
+namespace avsg {
+
+constexpr int kMRThreads = 1024;      // match_reserve: one workgroup per unit
+constexpr int kMRWaves = kMRThreads / 64;
+constexpr int kMaxSlotsPerLane = 16;  // => n_slots <= 16384
+constexpr int kMissFlag = 1 << 30;    // marks a union entry that was a miss
+constexpr int kAttnThreads = 256;
+constexpr int kGatherThreads = 256;
+
+// Layout of the caller's workspace (byte offsets, each 256-aligned).
+struct WsLayout {
+  size_t unit_status, miss_count, misses, err_word, counters, partials, total;
+  int32_t ucap;       // union capacity per unit = min(T*k, S)
+  int32_t table_cap;  // hash table cells, power of two >= 2*ucap
+  int32_t nsplit;     // attention splits per (unit, token)
+  int32_t split_rows; // token rows per split
+};
+
+struct Derived {
+  int32_t units, G, row_elems, nbins, log_table_cap;
+  size_t mr_lds;  // dynamic LDS bytes of match_reserve
+};
+
+bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d);
+
+struct MatchReserveParams {
+  const int32_t* sel;     // [units][T][k]
+  int32_t* slot_table;    // [units][S]
+  int32_t* lifetimes;     // [units][S]
+  uint8_t* hit_flag;      // [units][T][k]
+  int32_t* sel_slot;      // [units][T][k]
+  int32_t* n_hit;
+  int32_t* n_miss;
+  int32_t* n_evict;
+  int32_t* user_status;   // may be null
+  int32_t* unit_status;   // workspace [units]
+  int32_t* miss_count;    // workspace [units]
+  int2* misses;           // workspace [units][ucap]: (slot, id) in miss order
+  uint32_t* err_word;
+  int64_t t;
+  int32_t S, N, T, k, ucap, table_cap, log_table_cap, policy, L, B, nbins;
+};
+
+struct GatherParams {
+  const int2* misses;
+  const int32_t* miss_count;
+  const uint4* host_kv;   // device-visible address of the pinned host rows
+  uint4* buf_kv;
+  int64_t N, S;
+  int32_t units, ucap, row16;
+};
+
+struct AttnParams {
+  const int32_t* sel_slot;    // [units][T][k]
+  const int32_t* unit_status; // [units]
+  const uint16_t* q;          // [B][T][Hq][dqk]
+  const uint16_t* buf_kv;     // [units][S][row]
+  float* out;                 // [B][T][Hq][dv]
+  float* partials;            // [units*T][nsplit][G][dv + 2]
+  uint32_t* counters;         // [units*T]
+  int64_t S;
+  int32_t units, Hkv, Hq, T, k, tpe, row_elems, nsplit, split_rows;
+  float scale_log2e;
+};
+
+hipError_t launch_match_reserve(const MatchReserveParams& p, int units, size_t lds, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, int grid, hipStream_t s);
+hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s);
+hipError_t launch_attn_latent(const AttnParams& p, int dqk, int dv, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
+hipError_t launch_validate(const int32_t* slot_table, const int32_t* lifetimes, int units, int S,
+                           int N, int policy, int L, int64_t t, uint32_t* err, hipStream_t s);
+hipError_t match_reserve_set_lds(size_t lds);
+
+}  // namespace avsg

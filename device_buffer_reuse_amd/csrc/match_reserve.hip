@@ -1,0 +1,457 @@
+// K1: match the selected entries of a unit against its slot buffer, update
+// lifetimes / recency stamps, choose victims without a sort, reserve slots for
+// the misses and list the misses for the gather.  One workgroup (16 waves)
+// per (request, KV head) unit.
+//
+// Method (AVSG abstract, arxivdaily 2609.37538): a vectorised hash match finds
+// reusable buffer slots and reserves slots for entries needing a transfer;
+// lifetime-based management keeps frequently selected entries resident; one
+// reservation is shared by all query tokens of an MTP iteration.  Bucketed LRU
+// (Spin summary, gist.science 2604.26837, section 2B) groups slots by recency
+// bucket so that eviction needs no global sort and runs in parallel.
+//
+// gfx950 mapping:
+//  * The union U of the iteration's sorted selections is built in LDS (for
+//    two tokens by a rank formula: each element's position in U is found by
+//    binary search in the other list minus the duplicates before it).
+//  * U is hashed into an LDS open-addressing table (linear probing, load
+//    factor <= 0.5, multiplicative hash); every slot of the buffer then probes
+//    its resident id, one slot per lane, 64 lanes at a time.  Hashing U rather
+//    than the slots keeps the table at 2|U| cells and turns "is this slot a
+//    candidate" into the same probe.
+//  * Victim selection is a stable counting selection: each candidate slot gets
+//    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first); ranks
+//    inside a bin follow slot order via ballot/mbcnt per wave plus per-(wave,
+//    bin) prefix sums; the m first candidates in (bin, slot) order are the
+//    victims.  No comparison sort, no order-dependent atomics: the result is
+//    deterministic.
+//  * The r-th miss in ascending id order takes the r-th victim, its row is
+//    listed as (slot, id) for the gather kernel.
+#include "avsg_internal.h"
+
+namespace avsg {
+namespace {
+
+constexpr int kInvalid = -2;  // slot beyond S in this lane's range
+
+__device__ __forceinline__ uint32_t hash_id(int32_t id, int log_cap) {
+  return ((uint32_t)id * 0x9E3779B1u) >> (32 - log_cap);
+}
+
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Exclusive scan over the whole workgroup in thread order; sWs holds 16 ints.
+__device__ __forceinline__ int block_excl_scan(int v, int* sWs, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = wave_incl_scan(v, lane);
+  if (lane == 63) sWs[w] = inc;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kMRWaves; ++i) {
+    int x = sWs[i];
+    pre += (i < w) ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return pre + inc - v;
+}
+
+// number of elements of the sorted array a[0..n) that are < x
+__device__ __forceinline__ int lower_bound_lds(const int32_t* a, int n, int32_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int hash_lookup(const int32_t* sHash, const int32_t* sU, int cap_mask,
+                                           int log_cap, int32_t x) {
+  uint32_t h = hash_id(x, log_cap);
+  while (true) {
+    int c = sHash[h];
+    if (c < 0) return -1;
+    if (sU[c] == x) return c;
+    h = (h + 1) & cap_mask;
+  }
+}
+
+enum { kFlagRange = 1, kFlagUnsorted = 2, kFlagCapacity = 4, kFlagState = 8 };
+
+__device__ __forceinline__ int flags_to_status(int f) {
+  if (f & kFlagRange) return AVSG_ERR_RANGE;
+  if (f & kFlagUnsorted) return AVSG_ERR_UNSORTED;
+  if (f & kFlagCapacity) return AVSG_ERR_CAPACITY;
+  return AVSG_ERR_STATE;
+}
+
+template <int MAXP>
+__global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveParams p) {
+  extern __shared__ int32_t lds[];
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int S = p.S, N = p.N, T = p.T, k = p.k, ucap = p.ucap, C = p.table_cap;
+  const int nbins = p.nbins, tk = T * k;
+  const bool lru = p.policy == AVSG_POLICY_BUCKET_LRU;
+
+  int32_t* sU = lds;                         // [ucap] union, ascending
+  int32_t* sUslot = sU + ucap;               // [ucap] slot of each union entry (+ miss flag)
+  int32_t* sHash = sUslot + ucap;            // [C] union index or -1
+  int32_t* sCnt = sHash + C;                 // [16][nbins]
+  int32_t* sOff = sCnt + kMRWaves * nbins;   // [16][nbins]
+  int32_t* sTot = sOff + kMRWaves * nbins;   // [nbins] -> exclusive bin starts
+  int32_t* sMisc = sTot + nbins;             // [64]: 0 flags, 1 evictions, 16.. scan scratch
+  int32_t* sMiss = sMisc + 64;               // [max(ucap, T*k)]; T=2: first holds both lists
+  int32_t* sMap = sMiss + (T > 1 ? tk : ucap);  // T=2: [T*k] union index per (token, entry)
+  int32_t* sDup = sMap + (T > 1 ? tk : 0);      // T=2: [k+1] duplicates before each A index
+  int32_t* sWs = sMisc + 16;
+
+  const int32_t* sel = p.sel + (size_t)u * tk;
+  int32_t* slot_table = p.slot_table + (size_t)u * S;
+  int32_t* lifetimes = p.lifetimes + (size_t)u * S;
+
+  if (tid < 64) sMisc[tid] = 0;
+  for (int i = tid; i < C; i += kMRThreads) sHash[i] = -1;
+  for (int i = tid; i < ucap; i += kMRThreads) sUslot[i] = -1;
+  __syncthreads();
+
+  // ---- 1. validate each token's list: ids in range, strictly ascending
+  {
+    int bad = 0;
+    for (int i = tid; i < tk; i += kMRThreads) {
+      int32_t x = sel[i];
+      int pos = i % k;
+      if (x < 0 || x >= N) bad |= kFlagRange;
+      if (pos > 0 && x <= sel[i - 1]) bad |= kFlagUnsorted;
+      if (T > 1) sMiss[i] = x;  // stage both lists for the union
+    }
+    if (bad) atomicOr(&sMisc[0], bad);
+  }
+  __syncthreads();
+
+  // ---- 2. union U of the T lists (T = 1: the list itself)
+  int nu = k;
+  if (sMisc[0] == 0) {
+    if (T == 1) {
+      for (int i = tid; i < k; i += kMRThreads) sU[i] = sel[i];
+    } else {
+      const int32_t* A = sMiss;
+      const int32_t* Bl = sMiss + k;
+      int run = 0;
+      for (int c0 = 0; c0 < k; c0 += kMRThreads) {
+        int i = c0 + tid;
+        int dup = 0;
+        if (i < k) {
+          int lb = lower_bound_lds(Bl, k, A[i]);
+          dup = (lb < k && Bl[lb] == A[i]) ? 1 : 0;
+        }
+        int tot;
+        int pre = block_excl_scan(dup, sWs, &tot);
+        if (i < k) sDup[i] = run + pre;
+        run += tot;
+      }
+      if (tid == 0) sDup[k] = run;
+      __syncthreads();
+      nu = 2 * k - sDup[k];
+      if (nu > S) {
+        if (tid == 0) sMisc[0] = kFlagCapacity;
+      } else {
+        for (int i = tid; i < k; i += kMRThreads) {
+          int32_t a = A[i];
+          int pos = i + lower_bound_lds(Bl, k, a) - sDup[i];
+          sU[pos] = a;
+          sMap[i] = pos;
+        }
+        for (int j = tid; j < k; j += kMRThreads) {
+          int32_t b = Bl[j];
+          int la = lower_bound_lds(A, k, b);
+          int pos = la + j - sDup[la];
+          sU[pos] = b;  // a duplicate writes the same value at the same position
+          sMap[k + j] = pos;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. hash U into the LDS table
+  const int log_cap = p.log_table_cap, cap_mask = C - 1;
+  if (sMisc[0] == 0) {
+    for (int i = tid; i < nu; i += kMRThreads) {
+      uint32_t h = hash_id(sU[i], log_cap);
+      while (atomicCAS(&sHash[h], -1, i) != -1) h = (h + 1) & cap_mask;
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. every slot probes its resident id; state checks
+  const int R = ((S + kMRThreads - 1) / kMRThreads) * 64;  // slots per wave, multiple of 64
+  const int s0 = w * R, s1 = min(s0 + R, S);
+  int tok[MAXP], lf[MAXP], bin[MAXP], rank[MAXP];
+  bool changed[MAXP];
+  if (sMisc[0] == 0) {
+    int bad = 0;
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      const int s = s0 + q * 64 + lane;
+      tok[q] = kInvalid;
+      lf[q] = 0;
+      bin[q] = kInvalid;
+      changed[q] = false;
+      if (q * 64 < R && s < s1) {
+        int32_t x = slot_table[s];
+        int32_t l = lifetimes[s];
+        tok[q] = x;
+        lf[q] = l;
+        bin[q] = 0;
+        if (x < -1 || x >= N) {
+          bad = 1;
+        } else if (x >= 0) {
+          if (!lru && (l < 0 || l > p.L)) bad = 1;
+          if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
+          int i = hash_lookup(sHash, sU, cap_mask, log_cap, x);
+          if (i >= 0) {
+            if (atomicCAS(&sUslot[i], -1, s) != -1) bad = 1;  // id of U held by two slots
+            bin[q] = -1;                                       // hit
+          }
+        }
+      }
+    }
+    if (bad) atomicOr(&sMisc[0], kFlagState);
+  }
+  __syncthreads();
+
+  const int flags = sMisc[0];
+  if (flags) {
+    const int code = flags_to_status(flags);
+    for (int i = tid; i < tk; i += kMRThreads) {
+      p.sel_slot[(size_t)u * tk + i] = -1;
+      p.hit_flag[(size_t)u * tk + i] = 0;
+    }
+    if (tid == 0) {
+      p.n_hit[u] = 0;
+      p.n_miss[u] = 0;
+      p.n_evict[u] = 0;
+      p.unit_status[u] = code;
+      p.miss_count[u] = 0;
+      if (p.user_status) p.user_status[u] = code;
+      atomicOr(p.err_word, 1u << (code - 16));
+    }
+    return;
+  }
+
+  // ---- 5. policy update and eviction bins (registers)
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    if (tok[q] == kInvalid) continue;
+    if (bin[q] == -1) {
+      lf[q] = lru ? (int32_t)p.t : p.L;
+    } else if (tok[q] >= 0) {
+      if (!lru) {
+        lf[q] = lf[q] > 0 ? lf[q] - 1 : 0;
+        bin[q] = 1 + lf[q];
+      } else {
+        int64_t bucket = p.t - (int64_t)lf[q] - 1;
+        if (bucket > p.B - 1) bucket = p.B - 1;
+        bin[q] = 1 + (p.B - 1 - (int)bucket);
+      }
+    } else {
+      bin[q] = 0;
+    }
+  }
+
+  // ---- 6. misses of U in ascending id order
+  int m = 0;
+  for (int c0 = 0; c0 < nu; c0 += kMRThreads) {
+    int i = c0 + tid;
+    int miss = (i < nu && sUslot[i] < 0) ? 1 : 0;
+    int tot;
+    int pre = block_excl_scan(miss, sWs, &tot);
+    if (miss) sMiss[m + pre] = i;
+    m += tot;
+  }
+
+  // ---- 7. victims: the m first candidates in (bin, slot) order
+  if (m > 0) {
+    for (int b = lane; b < nbins; b += 64) sCnt[w * nbins + b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      bool act = bin[q] >= 0;
+      rank[q] = 0;
+      uint64_t pend = __ballot(act);
+      while (pend) {
+        const int lead = __builtin_ctzll(pend);
+        const int b = __builtin_amdgcn_readlane(bin[q], lead);
+        const bool mine = act && bin[q] == b;
+        const uint64_t grp = __ballot(mine);
+        const int base = sCnt[w * nbins + b];
+        if (mine) rank[q] = base + mbcnt64(grp);
+        if (lane == 0) sCnt[w * nbins + b] = base + __popcll(grp);
+        pend &= ~grp;
+        act = act && !mine;
+      }
+    }
+    __syncthreads();
+    for (int b = tid; b < nbins; b += kMRThreads) {
+      int tot = 0;
+      for (int v = 0; v < kMRWaves; ++v) tot += sCnt[v * nbins + b];
+      sTot[b] = tot;
+    }
+    __syncthreads();
+    {
+      int run = 0;
+      for (int c0 = 0; c0 < nbins; c0 += kMRThreads) {
+        int b = c0 + tid;
+        int v = b < nbins ? sTot[b] : 0;
+        int tot;
+        int pre = block_excl_scan(v, sWs, &tot);
+        if (b < nbins) sTot[b] = run + pre;
+        run += tot;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kMRWaves * nbins; idx += kMRThreads) {
+      const int v = idx / nbins, b = idx - v * nbins;
+      int off = sTot[b];
+      for (int x = 0; x < v; ++x) off += sCnt[x * nbins + b];
+      sOff[idx] = off;
+    }
+    __syncthreads();
+    int ev = 0;
+    int2* misses = p.misses + (size_t)u * ucap;
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      if (bin[q] < 0) continue;
+      const int r = sOff[w * nbins + bin[q]] + rank[q];
+      if (r < m) {
+        const int s = s0 + q * 64 + lane;
+        const int i = sMiss[r];
+        const int32_t id = sU[i];
+        if (tok[q] >= 0) ++ev;
+        tok[q] = id;
+        lf[q] = lru ? (int32_t)p.t : p.L;
+        changed[q] = true;
+        sUslot[i] = s | kMissFlag;
+        misses[r] = make_int2(s, id);
+      }
+    }
+    if (ev) atomicAdd(&sMisc[1], ev);
+  }
+
+  // ---- 8. write the new slot state back
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    if (tok[q] == kInvalid) continue;
+    const int s = s0 + q * 64 + lane;
+    lifetimes[s] = lf[q];
+    if (changed[q]) slot_table[s] = tok[q];
+  }
+  __syncthreads();
+
+  // ---- 9. per-(token, entry) outputs read off the union
+  for (int i = tid; i < tk; i += kMRThreads) {
+    const int ui = (T == 1) ? i : sMap[i];
+    const int v = sUslot[ui];
+    p.sel_slot[(size_t)u * tk + i] = v & ~kMissFlag;
+    p.hit_flag[(size_t)u * tk + i] = (v & kMissFlag) ? 0 : 1;
+  }
+  if (tid == 0) {
+    p.n_hit[u] = nu - m;
+    p.n_miss[u] = m;
+    p.n_evict[u] = sMisc[1];
+    p.unit_status[u] = 0;
+    p.miss_count[u] = m;
+    if (p.user_status) p.user_status[u] = 0;
+  }
+}
+
+template <int MAXP>
+hipError_t launch_mr(const MatchReserveParams& p, int units, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL(match_reserve_kernel<MAXP>, dim3(units), dim3(kMRThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int MAXP>
+hipError_t set_lds(size_t lds) {
+  return hipFuncSetAttribute((const void*)match_reserve_kernel<MAXP>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+// ---- full state validation: ranges and duplicate ids over all slots
+__global__ __launch_bounds__(kMRThreads) void validate_kernel(const int32_t* slot_table,
+                                                              const int32_t* lifetimes, int S,
+                                                              int N, int policy, int L, int64_t t,
+                                                              int log_cap, uint32_t* err) {
+  extern __shared__ int32_t tab[];
+  const int u = blockIdx.x;
+  const int C = 1 << log_cap;
+  for (int i = threadIdx.x; i < C; i += kMRThreads) tab[i] = -1;
+  __syncthreads();
+  int bad = 0;
+  for (int s = threadIdx.x; s < S; s += kMRThreads) {
+    const int32_t x = slot_table[(size_t)u * S + s];
+    const int32_t l = lifetimes[(size_t)u * S + s];
+    if (x < -1 || x >= N) { bad = 1; continue; }
+    if (x < 0) continue;
+    if (policy == AVSG_POLICY_LIFETIME && (l < 0 || l > L)) bad = 1;
+    if (policy == AVSG_POLICY_BUCKET_LRU && (l < 0 || (int64_t)l >= t)) bad = 1;
+    uint32_t h = hash_id(x, log_cap);
+    while (true) {
+      int prev = atomicCAS(&tab[h], -1, x);
+      if (prev == -1) break;
+      if (prev == x) { bad = 1; break; }
+      h = (h + 1) & (C - 1);
+    }
+  }
+  if (bad) atomicOr(err, 1u);
+}
+
+}  // namespace
+
+hipError_t launch_match_reserve(const MatchReserveParams& p, int units, size_t lds, hipStream_t s) {
+  const int per_lane = (p.S + kMRThreads - 1) / kMRThreads;
+  if (per_lane <= 1) return launch_mr<1>(p, units, lds, s);
+  if (per_lane <= 2) return launch_mr<2>(p, units, lds, s);
+  if (per_lane <= 4) return launch_mr<4>(p, units, lds, s);
+  if (per_lane <= 8) return launch_mr<8>(p, units, lds, s);
+  return launch_mr<16>(p, units, lds, s);
+}
+
+hipError_t match_reserve_set_lds(size_t lds) {
+  hipError_t e;
+  if ((e = set_lds<1>(lds)) != hipSuccess) return e;
+  if ((e = set_lds<2>(lds)) != hipSuccess) return e;
+  if ((e = set_lds<4>(lds)) != hipSuccess) return e;
+  if ((e = set_lds<8>(lds)) != hipSuccess) return e;
+  return set_lds<16>(lds);
+}
+
+hipError_t launch_validate(const int32_t* slot_table, const int32_t* lifetimes, int units, int S,
+                           int N, int policy, int L, int64_t t, uint32_t* err, hipStream_t s) {
+  int log_cap = 6;
+  while ((1 << log_cap) < 2 * S) ++log_cap;
+  const size_t lds = sizeof(int32_t) << log_cap;
+  hipError_t e = hipFuncSetAttribute((const void*)validate_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(validate_kernel, dim3(units), dim3(kMRThreads), lds, s, slot_table, lifetimes,
+                     S, N, policy, L, t, log_cap, err);
+  return hipGetLastError();
+}
+
+}  // namespace avsg

@@ -1,0 +1,189 @@
+/*
+ * avsg.h -- C ABI of libavsg: an HBM slot buffer for dynamic sparse attention
+ * decode over a host-offloaded KV cache, on one MI355X (gfx950).
+ *
+ * What one decode step computes (avsg_step) follows the AVSG abstract
+ * (arxivdaily 2609.37538, abstract): the selected KV entries of each
+ * (request, KV head) unit are matched against the entries already resident in
+ * a device buffer by a vectorised hash match, slots are reserved for the
+ * entries that need a host-to-device transfer, only those are transferred,
+ * with the transfer split evenly over the GPU's compute units, lifetime-based
+ * management keeps frequently selected entries resident across steps, and one
+ * reservation serves every query token of a multi-token-prediction iteration.
+ * The bucketed-LRU alternative and head-wise pages follow the Spin summary
+ * (gist.science 2604.26837, section 2B).  Attention then runs over the
+ * buffer's slots; because selections are exact, its result equals attention
+ * over the selected entries read from host memory.
+ *
+ * Conventions
+ *  - A unit is one (request, KV head): unit u = b * n_kv_heads + g.
+ *  - An entry is one token (tokens_per_entry = 1) or one page of
+ *    tokens_per_entry tokens.  Entries are identified by their position id in
+ *    [0, n_entries) within their unit.
+ *  - bf16 values are passed as their uint16_t bit patterns.
+ *  - Every pointer documented as "device" must be device memory of the GPU the
+ *    context was created on (hipMalloc / torch CUDA tensors); "host, pinned"
+ *    means memory from avsg_host_alloc or hipHostMalloc.
+ *  - The caller owns all memory.  The library owns only the context struct;
+ *    the workspace belongs to the caller but its contents to the library, and
+ *    it must stay allocated and untouched across steps.
+ *  - All calls that enqueue GPU work are asynchronous and ordered on the
+ *    context's stream; none waits for the GPU unless documented ("syncs").
+ *  - Errors in the data (selections, buffer state) are found on the GPU:
+ *    the affected unit keeps its state, its outputs are zero / -1, and the
+ *    error is reported by avsg_last_error.  Nothing is dropped silently.
+ *  - One context per stream; calls on one context are not thread-safe.
+ */
+#ifndef AVSG_H
+#define AVSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum avsg_status {
+  AVSG_OK = 0,
+  AVSG_ERR_INVALID_ARG = 1,  /* null pointer, bad config, workspace too small */
+  AVSG_ERR_NOT_PINNED = 2,   /* host_kv is not pinned, device-mapped host memory */
+  AVSG_ERR_HIP = 3,          /* a HIP runtime call failed */
+  AVSG_ERR_UNSUPPORTED = 4,  /* config valid but outside this build's kernels */
+  /* data errors, found on the GPU and reported by avsg_last_error */
+  AVSG_ERR_UNSORTED = 16,    /* a token's selection is not strictly ascending */
+  AVSG_ERR_RANGE = 17,       /* a selected id is outside [0, n_entries) */
+  AVSG_ERR_CAPACITY = 18,    /* the union of an iteration's selections exceeds n_slots */
+  AVSG_ERR_STATE = 19        /* slot_table / lifetimes are not a valid buffer state */
+} avsg_status;
+
+typedef enum avsg_kv_layout {
+  /* row of an entry = K[tokens_per_entry][head_dim_qk] then V[tokens_per_entry][head_dim_v] */
+  AVSG_KV_SPLIT = 0,
+  /* row of an entry = one latent vector of head_dim_qk values (one token);
+   * the key is the whole row, the value its first head_dim_v values */
+  AVSG_KV_LATENT = 1
+} avsg_kv_layout;
+
+typedef enum avsg_policy {
+  /* Lifetime-based management (AVSG abstract).  A slot whose entry is selected
+   * gets lifetime L; every other occupied slot loses one per step, floored at
+   * 0; a slot at 0 stays resident and can still hit. */
+  AVSG_POLICY_LIFETIME = 0,
+  /* Bucketed LRU (Spin summary, section 2B): lifetimes[] holds the step of
+   * last selection; the bucket of a slot is min(t - stamp - 1, n_buckets - 1)
+   * and older buckets are evicted first. */
+  AVSG_POLICY_BUCKET_LRU = 1
+} avsg_policy;
+
+typedef struct avsg_config {
+  int32_t batch;             /* requests */
+  int32_t n_kv_heads;        /* KV heads per request (1 for the latent layout) */
+  int32_t n_q_heads;         /* query heads per request; head h reads KV head h / (n_q_heads / n_kv_heads) */
+  int32_t n_q_tokens;        /* T: query tokens per iteration sharing one reservation (1 or 2) */
+  int32_t head_dim_qk;       /* split layout: 128; latent layout: 576 */
+  int32_t head_dim_v;        /* split layout: 128; latent layout: 512 */
+  int32_t kv_layout;         /* avsg_kv_layout */
+  int32_t n_entries;         /* N: entries per unit in host memory */
+  int32_t tokens_per_entry;  /* 1 (token entries) or 16 (pages); latent layout: 1 */
+  int32_t k;                 /* entries selected per query token */
+  int32_t n_slots;           /* S: buffer slots per unit */
+  int32_t policy;            /* avsg_policy */
+  int32_t lifetime_L;        /* L >= 1 (lifetime policy) */
+  int32_t n_buckets;         /* B >= 1 (bucketed LRU) */
+  float softmax_scale;       /* multiplies q.k before the softmax */
+} avsg_config;
+
+/* Per-step outputs besides the attention result; all device pointers. */
+typedef struct avsg_hit_stats {
+  uint8_t* hit_flag;     /* [units][T][k]: 1 if the entry was resident before this step */
+  int32_t* sel_slot;     /* [units][T][k]: slot holding the entry after this step (-1 on error) */
+  int32_t* n_hit;        /* [units]: entries of the union that were resident */
+  int32_t* n_miss;       /* [units]: entries of the union transferred from host memory */
+  int32_t* n_evict;      /* [units]: reserved slots that held another entry */
+  int32_t* unit_status;  /* [units]: 0 or the avsg_status of that unit's data error; may be NULL */
+} avsg_hit_stats;
+
+typedef struct avsg_ctx avsg_ctx;
+
+/* Checks a configuration on the host only (no GPU needed).  Returns AVSG_OK,
+ * AVSG_ERR_INVALID_ARG (inconsistent values) or AVSG_ERR_UNSUPPORTED (a shape
+ * the kernels of this build do not handle). */
+avsg_status avsg_check_config(const avsg_config* cfg);
+
+/* Bytes of device workspace a context for cfg needs (0 if cfg is invalid).
+ * Host only. */
+size_t avsg_workspace_bytes(const avsg_config* cfg);
+
+/* Creates a context on the current HIP device.  `stream` is a hipStream_t
+ * (NULL = the null stream).  `workspace` is device memory of at least
+ * avsg_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the caller and
+ * kept alive and untouched until avsg_destroy.  Initialising it is enqueued
+ * on the stream.  The step counter starts at 0. */
+avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, size_t ws_bytes,
+                        avsg_ctx** out);
+
+/* Changes the stream later calls enqueue on. */
+avsg_status avsg_set_stream(avsg_ctx* ctx, void* stream);
+
+/* Frees the context struct (not the caller's memory). Does not sync. */
+avsg_status avsg_destroy(avsg_ctx* ctx);
+
+/* Empties the buffer: slot_table[units][S] = -1, lifetimes[units][S] = 0
+ * (lifetime policy) or -1 (LRU), step counter = 0, pending errors cleared.
+ * Device pointers; enqueued on the stream. */
+avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes);
+
+/* One decode step t (the context's counter; it then advances by one).
+ *   sel_idx    device, int32 [batch][n_kv_heads][T][k]: each token's selected
+ *              entry ids, strictly ascending, in [0, N).          read only
+ *   q          device, bf16 [batch][T][n_q_heads][head_dim_qk]     read only
+ *   host_kv    host, pinned, bf16 [units][N][row]: the full KV cache, row as
+ *              given by kv_layout.                                  read only
+ *   buf_kv     device, bf16 [units][S][row]: the slot buffer.       in/out
+ *   slot_table device, int32 [units][S]: id held by each slot, -1 = empty.
+ *                                                                   in/out
+ *   lifetimes  device, int32 [units][S]: lifetime, or stamp (LRU).   in/out
+ *   out        device, fp32 [batch][T][n_q_heads][head_dim_v]: attention of
+ *              each query head over its token's selected entries; 0 for a
+ *              unit with a data error.                              written
+ *   hit_stats  host struct of device pointers (see avsg_hit_stats). written
+ * Returns AVSG_ERR_INVALID_ARG for null pointers, AVSG_ERR_NOT_PINNED if
+ * host_kv is not device-accessible pinned host memory, AVSG_ERR_HIP if a
+ * launch fails; data errors are reported later by avsg_last_error.  Never
+ * waits for the GPU. */
+avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
+                      const uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
+                      int32_t* lifetimes, float* out, const avsg_hit_stats* hit_stats);
+
+/* Syncs the stream and returns the highest-precedence data error raised by
+ * the steps since the last call (RANGE, then UNSORTED, CAPACITY, STATE), or
+ * AVSG_OK; then clears it. */
+avsg_status avsg_last_error(avsg_ctx* ctx);
+
+/* Full check of a buffer state (syncs): every id in [-1, N), no id held by
+ * two slots, lifetimes in [0, L] (or stamps in [0, t)) for occupied slots.
+ * Returns AVSG_OK or AVSG_ERR_STATE. */
+avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const int32_t* lifetimes);
+
+/* Step counter (decode step of the next avsg_step), for checkpoint/resume. */
+int64_t avsg_get_step(const avsg_ctx* ctx);
+avsg_status avsg_set_step(avsg_ctx* ctx, int64_t t);
+
+/* Pinned host memory the GPU can read directly.  flags: 0 = default (non-
+ * coherent, cacheable by the GPU), AVSG_HOST_COHERENT = fine-grained. */
+#define AVSG_HOST_COHERENT 1u
+avsg_status avsg_host_alloc(size_t bytes, unsigned flags, void** host_ptr);
+avsg_status avsg_host_free(void* host_ptr);
+
+/* Static string naming a status. */
+const char* avsg_status_string(avsg_status s);
+
+/* Number of split-k partitions the attention of one (unit, token) uses. */
+int32_t avsg_attn_splits(const avsg_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AVSG_H */

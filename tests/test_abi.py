@@ -1,0 +1,74 @@
+"""The C ABI library loads and exports every function include/avsg.h
+declares; host-only calls (config checks, workspace sizing, status strings)
+work without a GPU.  CPU only."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tracegen as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "avsg.h")
+
+
+def _lib():
+    from device_buffer_reuse_amd import avsg, build as hipbuild
+    if hipbuild.needs_build():
+        hipbuild.build()
+    return avsg
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(avsg_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    avsg = _lib()
+    lib = ctypes.CDLL(avsg.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(avsg.EXPORTED) == names
+
+
+def test_config_checks_host_only():
+    avsg = _lib()
+    for cid in (1, 2, 3, 4):
+        c = avsg.config_from_workload(tg.WORKLOADS[cid])
+        assert avsg.avsg_check_config(c) == avsg.OK
+        assert avsg.avsg_workspace_bytes(c) > 0
+    bad = avsg.config_from_workload(tg.WORKLOADS[2])
+    bad.n_q_heads = 30
+    assert avsg.avsg_check_config(bad) == avsg.ERR_INVALID_ARG
+    assert avsg.avsg_workspace_bytes(bad) == 0
+    big = avsg.config_from_workload(tg.WORKLOADS[2])
+    big.n_q_tokens = 3
+    assert avsg.avsg_check_config(big) == avsg.ERR_UNSUPPORTED
+    ks = avsg.config_from_workload(tg.WORKLOADS[2])
+    ks.k = ks.n_slots + 1
+    assert avsg.avsg_check_config(ks) == avsg.ERR_INVALID_ARG
+
+
+def test_status_strings():
+    avsg = _lib()
+    for s in (0, 1, 2, 3, 4, 16, 17, 18, 19):
+        assert avsg.status_string(s) and "unknown" not in avsg.status_string(s)
+
+
+def test_workspace_sizes_match_layout():
+    """Workspace holds per-unit miss lists (8 B per union capacity), split
+    partials and a few words; its size follows the config."""
+    avsg = _lib()
+    w = tg.WORKLOADS[2]
+    c = avsg.config_from_workload(w)
+    ws = avsg.avsg_workspace_bytes(c)
+    misses = 8 * w.units * min(w.k * w.n_q_tokens, w.n_slots)
+    partials = 4 * w.units * 16 * 4 * 130
+    assert misses + partials <= ws <= misses + partials + 8 * 1024

@@ -1,0 +1,88 @@
+"""HIP path vs oracle, element by element, through the C ABI.
+
+State (slot tables, lifetimes / stamps, hit flags, slots, counts, buffer
+bytes) must match bit for bit; attention within 2e-2 max abs and 1e-3
+relative L1 per step."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import tracegen as tg
+from gpu_harness import Runner, say
+
+pytestmark = pytest.mark.gpu
+
+# Reduced shapes that span several tiles and end in ragged tails (k, S, N not
+# multiples of 64/128/1024), plus the tiny workload at full size.
+SMALL = {
+    "tiny": tg.WORKLOADS[1],
+    "batch_ragged": tg.WORKLOADS[2].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003,
+                                            k=300, n_slots=1000, steps=14),
+    "mtp_ragged": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003,
+                                          k=300, n_slots=700, steps=12),
+    "long_ragged": tg.WORKLOADS[4].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001,
+                                           k=37, n_slots=100, steps=40),
+    "lru_small_b": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=4, n_entries=700,
+                                           tokens_per_entry=1, k=50, n_slots=90, n_buckets=3,
+                                           steps=30),
+    "gqa8_L1": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=16, n_entries=3000,
+                                       k=129, n_slots=300, lifetime_L=1, steps=10),
+    "gqa1_k1": tg.WORKLOADS[2].replace(batch=3, n_kv_heads=1, n_q_heads=1, n_entries=64, k=1,
+                                       n_slots=2, steps=10, overlap=0.0),
+    "slots_16k": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=40000,
+                                         k=4000, n_slots=16384, steps=6),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name):
+    w = SMALL[name]
+    say("[parity] %s units=%d k=%d S=%d T=%d" % (name, w.units, w.k, w.n_slots, w.n_q_tokens))
+    sel = tg.selections(w)
+    run = Runner(w)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("mode", ["allhit", "allmiss"])
+def test_parity_trace_modes(mode):
+    w = SMALL["batch_ragged"].replace(n_entries=6000, steps=8)
+    say("[parity] modes %s" % mode)
+    sel = tg.selections(w, mode=mode)
+    run = Runner(w)
+    try:
+        for t in range(w.steps):
+            r, _ = run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+            if mode == "allmiss":
+                assert (r["n_hit"] == 0).all()
+            elif t > 0:
+                assert (r["n_miss"] == 0).all()
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_parity_full_size(cid):
+    """Full workload shapes, every step: all state bit-exact, attention of a
+    sample of units against the oracle, buffer bytes at the end."""
+    w = tg.WORKLOADS[cid]
+    steps = w.steps if cid != 4 else 64
+    say("[parity-full] %s units=%d steps=%d" % (w.name, w.units, steps))
+    sel = tg.selections(w, steps=steps)
+    rng = np.random.default_rng(cid)
+    sample = sorted(rng.choice(w.units, size=min(6, w.units), replace=False).tolist())
+    run = Runner(w, attn_units=sample)
+    try:
+        for t in range(steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=(t % 4 == 0 or t == steps - 1))
+        got = run.st.buf_kv.cpu().numpy().view(np.uint16)
+        occ = run.ob.slot_tok >= 0
+        assert np.array_equal(got[occ], run.ob.buf[occ])
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
