@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the HBM slot buffer on one MI355X.
+
+One step = one avsg_step over all units of the workload: match + reserve,
+miss-only gather from pinned host memory, split-k attention.  The default
+workload is the batch one (8 requests x 8 KV heads x 32 query heads,
+head_dim 128, context 32768, k = 2048, 8192 slots per unit, lifetime L = 16)
+on its natural trace (90% overlap + Zipf(1.1) tail), with `--warmup` untimed
+steps, then exactly `--steps` timed steps.  Inputs (selections, queries) are
+resident in HBM before the timed region; the KV cache is in pinned host
+memory, which is the method's premise.
+
+Prints one JSON line (rank 0).  Extra fields: per-kernel event times, hit
+rate and host bytes per step, the all-hit and all-miss traces, and the CPU
+oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+HOST_LINK_GBS = 64.0        # PCIe 5.0 x16, one direction
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (tracegen.WORKLOADS)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-extra", action="store_true", help="skip all-hit / all-miss passes")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+class Bench:
+    def __init__(self, w, total_steps):
+        import torch
+        import tracegen as tg
+        from device_buffer_reuse_amd import avsg, build as hipbuild
+        if not os.path.exists(avsg.LIB_PATH):
+            hipbuild.build()
+        self.torch, self.tg, self.avsg, self.w = torch, tg, avsg, w
+        self.cfg = avsg.config_from_workload(w)
+        self.ctx = avsg.Context(self.cfg)
+        self.st = avsg.State(self.cfg)
+        self.host = avsg.HostBuffer((w.units, w.n_entries, w.row_elems))
+        tg.fill_kv(w, out=self.host.array)
+        self.total = total_steps
+        q = np.stack([tg.queries(w, t) for t in range(total_steps)])
+        self.q_dev = torch.from_numpy(q.view(np.int16)).cuda()
+        self.hs = self.st.stats.struct()
+        self.lib = avsg.load()
+
+    def load_trace(self, mode, steps):
+        sel = self.tg.selections(self.w, steps=steps, mode=mode)
+        self.sel_np = sel
+        self.sel_dev = self.torch.from_numpy(sel).cuda()
+
+    def reset(self):
+        self.ctx.reset(self.st.slot_table, self.st.lifetimes)
+
+    def run(self, t0, t1, stats=None):
+        lib, h, s = self.lib, self.ctx.handle, self.st
+        import ctypes
+        hsp = ctypes.byref(self.hs)
+        sel0, selb = self.sel_dev.data_ptr(), self.sel_dev[0].numel() * 4
+        q0, qb = self.q_dev.data_ptr(), self.q_dev[0].numel() * 2
+        args = (self.host.ptr, s.buf_kv.data_ptr(), s.slot_table.data_ptr(), s.lifetimes.data_ptr(),
+                s.out.data_ptr())
+        for t in range(t0, t1):
+            rc = lib.avsg_step(h, sel0 + t * selb, q0 + (t % self.total) * qb, *args, hsp)
+            if rc != 0:
+                raise self.avsg.AvsgError(rc, "avsg_step")
+            if stats is not None:
+                stats[0] += s.stats.n_hit
+                stats[1] += s.stats.n_miss
+
+    def timed(self, t0, t1, profile=False):
+        torch = self.torch
+        if profile:
+            self.ctx.profile_begin(t1 - t0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.run(t0, t1)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        kern = None
+        if profile:
+            kern, n = self.ctx.profile_end()
+            assert n == t1 - t0
+        return ms, kern
+
+
+def attn_bytes(w):
+    """Algorithmic bytes of one attention launch: the selected K/V rows, the
+    slot list, the queries and the fp32 outputs."""
+    kv = w.units * w.n_q_tokens * w.k * w.tokens_per_entry * (w.head_dim_qk +
+                                                               (0 if w.latent else w.head_dim_v)) * 2
+    return kv + w.units * w.n_q_tokens * w.k * 4 + w.batch * w.n_q_tokens * w.n_q_heads * (
+        w.head_dim_qk * 2 + w.head_dim_v * 4)
+
+
+def attn_flops(w):
+    return 2 * w.batch * w.n_q_tokens * w.n_q_heads * w.k * w.tokens_per_entry * (w.head_dim_qk +
+                                                                                  w.head_dim_v)
+
+
+def match_bytes(w, misses_per_step):
+    """Algorithmic bytes of one match_reserve launch: selections, the slot
+    table read, lifetimes read and written, hit flags and slots written, the
+    reserved slots' ids and the miss list."""
+    tk = w.units * w.n_q_tokens * w.k
+    return tk * 4 + w.units * w.n_slots * 4 * 3 + tk * 5 + misses_per_step * (4 + 8)
+
+
+def cpu_baseline(w, t_start, seconds):
+    """The oracle (state machine + float64 attention) on the same workload,
+    from step t_start on, until `seconds` have elapsed."""
+    import tracegen as tg
+    import oracle
+    from oracle import attention as oatt
+    from threadpoolctl import threadpool_limits
+    lim = threadpool_limits(1)
+    oracle.set_threads(1)
+    steps_needed = t_start + 64
+    sel = tg.selections(w, steps=steps_needed)
+    host = tg.fill_kv(w)
+    ob = oracle.OracleBuffer.for_workload(w)
+    for t in range(t_start):
+        ob.step(sel[t])
+    done, t0 = 0, time.perf_counter()
+    t = t_start
+    while time.perf_counter() - t0 < seconds and t < steps_needed:
+        r = ob.step(sel[t])
+        oatt.attend(w, tg.queries(w, t), host, sel[t], r["status"])
+        done += 1
+        t += 1
+    el = time.perf_counter() - t0
+    del lim
+    return {"value": done * w.entries_per_step / el, "unit": "entries/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d decode steps (t=%d..%d) of the same workload, all %d units: C state "
+                      "machine + float64 numpy attention, one thread" % (done, t_start,
+                                                                         t_start + done - 1,
+                                                                         w.units)}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: the slot buffer's units are independent and this build "
+              "runs on a single MI355X; --gpus %d is not supported" % max(a.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tracegen as tg
+    w = tg.WORKLOADS[a.workload]
+    W, K = a.warmup, a.steps
+    total = W + K
+    b = Bench(w, total)
+    entries = w.entries_per_step
+    row_bytes = w.row_bytes
+
+    # ---- natural trace: value
+    b.load_trace("natural", total)
+    b.reset()
+    b.run(0, W)
+    ms, _ = b.timed(W, W + K)
+    assert b.ctx.last_error() == 0
+
+    # ---- same steps again with per-kernel events, plus hit statistics
+    b.reset()
+    b.run(0, W)
+    _, kern = b.timed(W, W + K, profile=True)
+    b.reset()
+    b.run(0, W)
+    acc = [torch.zeros(w.units, dtype=torch.int64, device="cuda") for _ in range(2)]
+    b.run(W, W + K, stats=acc)
+    n_hit, n_miss = int(acc[0].sum()), int(acc[1].sum())
+    miss_per_step = n_miss / K
+    union_per_step = (n_hit + n_miss) / K
+
+    per = {"match_reserve": kern[0] / K, "gather": kern[1] / K, "attention": kern[2] / K}
+    ab = attn_bytes(w)
+    att_gbs = ab / (per["attention"] * 1e-3) / 1e9
+    gat_gbs = miss_per_step * row_bytes / (per["gather"] * 1e-3) / 1e9
+    mr_gbs = match_bytes(w, miss_per_step) / (per["match_reserve"] * 1e-3) / 1e9
+    dominant = max(per, key=per.get)
+    if dominant == "gather":
+        roof = {"bound": "host-link", "achieved": round(gat_gbs, 2), "peak": HOST_LINK_GBS,
+                "unit": "GB/s", "frac": round(gat_gbs / HOST_LINK_GBS, 4), "traffic": None,
+                "kernel": "gather", "bytes_per_launch": int(miss_per_step * row_bytes)}
+    elif dominant == "attention":
+        roof = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "attention", "bytes_per_launch": ab}
+    else:
+        roof = {"bound": "hbm", "achieved": round(mr_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(mr_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "match_reserve", "bytes_per_launch": int(match_bytes(w, miss_per_step))}
+
+    kernels = {
+        "match_reserve": {"us": round(per["match_reserve"] * 1e3, 2), "GB/s": round(mr_gbs, 1)},
+        "gather": {"us": round(per["gather"] * 1e3, 2), "host_GB/s": round(gat_gbs, 2),
+                   "host_link_frac": round(gat_gbs / HOST_LINK_GBS, 4)},
+        "attention": {"us": round(per["attention"] * 1e3, 2), "GB/s": round(att_gbs, 1),
+                      "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4),
+                      "TFLOP/s": round(attn_flops(w) / (per["attention"] * 1e-3) / 1e12, 2)},
+    }
+
+    extra = {}
+    if not a.no_extra:
+        # all-hit: step 0 fills the buffer, later steps reuse every entry
+        nh = min(K, 64)
+        b.load_trace("allhit", nh + 1)
+        b.reset()
+        b.run(0, 1)
+        ms_h, kh = b.timed(1, nh + 1, profile=True)
+        step_bytes = ab + match_bytes(w, 0)
+        extra["all_hit"] = {
+            "steps": nh, "ms_per_step": round(ms_h / nh, 4),
+            "step_hbm_GB/s": round(step_bytes / (ms_h / nh * 1e-3) / 1e9, 1),
+            "step_hbm_frac": round(step_bytes / (ms_h / nh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "attention_us": round(kh[2] / nh * 1e3, 2),
+            "attention_hbm_frac": round(ab / (kh[2] / nh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "match_reserve_us": round(kh[0] / nh * 1e3, 2)}
+        # all-miss: disjoint windows, every entry crosses the host link
+        nm = min(K, 32)
+        b.load_trace("allmiss", nm + 4)
+        b.reset()
+        b.run(0, 4)
+        ms_m, km = b.timed(4, nm + 4, profile=True)
+        mb = w.units * w.n_q_tokens * w.k * row_bytes
+        extra["all_miss"] = {
+            "steps": nm, "ms_per_step": round(ms_m / nm, 4),
+            "host_bytes_per_step": mb,
+            "step_host_GB/s": round(mb / (ms_m / nm * 1e-3) / 1e9, 2),
+            "gather_us": round(km[1] / nm * 1e3, 2),
+            "gather_host_GB/s": round(mb / (km[1] / nm * 1e-3) / 1e9, 2),
+            "gather_host_link_frac": round(mb / (km[1] / nm * 1e-3) / 1e9 / HOST_LINK_GBS, 4)}
+        assert b.ctx.last_error() == 0
+        # pinned hipMemcpy host->device peak, for context
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8).pin_memory()
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(4):
+            dst.copy_(src, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        extra["pinned_memcpy_h2d_GB/s"] = round(4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
+    if a.calibrate_copy:
+        x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = {"read": x.numel() * 4, "write": y.numel() * 4}
+
+    value = K * entries / (ms * 1e-3)
+    line = {
+        "metric": "decode steps/s & selected KV entries/s; % HBM and host-link roofline",
+        "value": round(value, 1), "unit": "entries/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms / K, 5),
+        "steps_per_s": round(K / (ms * 1e-3), 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.batch, "kv_heads": w.n_kv_heads,
+                   "q_heads": w.n_q_heads, "q_tokens": w.n_q_tokens, "head_dim_qk": w.head_dim_qk,
+                   "head_dim_v": w.head_dim_v, "context_entries": w.n_entries,
+                   "tokens_per_entry": w.tokens_per_entry, "k": w.k, "slots": w.n_slots,
+                   "policy": w.policy, "lifetime_L": w.lifetime_L, "buckets": w.n_buckets,
+                   "trace": "natural: %.0f%% overlap + Zipf(%.1f) tail" % (100 * w.overlap, w.zipf_s),
+                   "entries_per_step": entries},
+        "hit_rate": round(n_hit / max(n_hit + n_miss, 1), 5),
+        "miss_rows_per_step": round(miss_per_step, 1),
+        "host_bytes_per_step": int(miss_per_step * row_bytes),
+        "union_per_step": round(union_per_step, 1),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    line.update(extra)
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    b.ctx.close()
+    b.host.free()
+
+
+if __name__ == "__main__":
+    main()

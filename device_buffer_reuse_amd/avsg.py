@@ -27,7 +27,7 @@ HOST_COHERENT = 1
 EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_set_stream",
             "avsg_destroy", "avsg_reset", "avsg_step", "avsg_last_error", "avsg_validate_state",
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
-            "avsg_status_string", "avsg_attn_splits"]
+            "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end"]
 
 
 class AvsgError(RuntimeError):
@@ -81,6 +81,8 @@ def load():
         "avsg_host_free": ([p], i32),
         "avsg_status_string": ([i32], ctypes.c_char_p),
         "avsg_attn_splits": ([p], ctypes.c_int32),
+        "avsg_profile_begin": ([p, ctypes.c_int32], i32),
+        "avsg_profile_end": ([p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -146,6 +148,18 @@ def avsg_set_step(ctx: int, t: int) -> int:
 
 def avsg_attn_splits(ctx: int) -> int:
     return int(load().avsg_attn_splits(ctx))
+
+
+def avsg_profile_begin(ctx: int, max_steps: int) -> int:
+    return load().avsg_profile_begin(ctx, max_steps)
+
+
+def avsg_profile_end(ctx: int):
+    """Returns (status, [ms of match_reserve, gather, attention], steps)."""
+    ms = (ctypes.c_double * 3)()
+    n = ctypes.c_int32()
+    st = load().avsg_profile_end(ctx, ms, ctypes.byref(n))
+    return st, [ms[0], ms[1], ms[2]], n.value
 
 
 def avsg_host_alloc(nbytes: int, flags: int = 0):
@@ -287,6 +301,18 @@ class Context:
         st = avsg_set_step(self.handle, value)
         if st != OK:
             raise AvsgError(st, "avsg_set_step")
+
+    def profile_begin(self, max_steps: int):
+        st = avsg_profile_begin(self.handle, max_steps)
+        if st != OK:
+            raise AvsgError(st, "avsg_profile_begin")
+
+    def profile_end(self):
+        """(per-kernel summed ms [match_reserve, gather, attention], steps)"""
+        st, ms, n = avsg_profile_end(self.handle)
+        if st != OK:
+            raise AvsgError(st, "avsg_profile_end")
+        return ms, n
 
     @property
     def attn_splits(self) -> int:

@@ -19,6 +19,8 @@ struct avsg_ctx {
   int64_t t;
   const void* pinned_checked;    // last host_kv pointer found pinned
   const void* pinned_device;     // its device-visible address
+  hipEvent_t* prof_events;       // 4 per profiled step, or null
+  int32_t prof_max, prof_used;
 };
 
 namespace avsg {
@@ -43,11 +45,13 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->table_cap = next_pow2(2 * (int64_t)ws->ucap);
   d->log_table_cap = 0;
   while ((1 << d->log_table_cap) < ws->table_cap) ++d->log_table_cap;
+  d->ubits = 1;
+  while ((1 << d->ubits) < ws->ucap) ++d->ubits;
   const int64_t rows = (int64_t)c.k * c.tokens_per_entry;
   if (c.kv_layout == AVSG_KV_LATENT) {
     ws->split_rows = 256;
   } else {
-    ws->split_rows = 128;
+    ws->split_rows = 128;  // one workgroup of the split-layout attention
   }
   ws->nsplit = (int32_t)((rows + ws->split_rows - 1) / ws->split_rows);
   const int64_t T = c.n_q_tokens;
@@ -82,10 +86,10 @@ static avsg_status check_config_impl(const avsg_config* c) {
   if (c->k > c->n_slots || c->k > c->n_entries) return AVSG_ERR_INVALID_ARG;
   if (c->policy != AVSG_POLICY_LIFETIME && c->policy != AVSG_POLICY_BUCKET_LRU)
     return AVSG_ERR_INVALID_ARG;
-  if (c->policy == AVSG_POLICY_LIFETIME && (c->lifetime_L < 1 || c->lifetime_L > 1022))
-    return AVSG_ERR_INVALID_ARG;
-  if (c->policy == AVSG_POLICY_BUCKET_LRU && (c->n_buckets < 1 || c->n_buckets > 1023))
-    return AVSG_ERR_INVALID_ARG;
+  if (c->lifetime_L < 1 || c->n_buckets < 1) return AVSG_ERR_INVALID_ARG;
+  // eviction bins (empty + lifetimes 0..L, or empty + buckets) must fit 128
+  if (c->policy == AVSG_POLICY_LIFETIME && c->lifetime_L > 126) return AVSG_ERR_UNSUPPORTED;
+  if (c->policy == AVSG_POLICY_BUCKET_LRU && c->n_buckets > 127) return AVSG_ERR_UNSUPPORTED;
   if (c->kv_layout != AVSG_KV_SPLIT && c->kv_layout != AVSG_KV_LATENT) return AVSG_ERR_INVALID_ARG;
   if (!(c->softmax_scale > 0.f)) return AVSG_ERR_INVALID_ARG;
   if ((int64_t)c->batch * c->n_kv_heads > (1 << 20)) return AVSG_ERR_UNSUPPORTED;
@@ -106,6 +110,8 @@ static avsg_status check_config_impl(const avsg_config* c) {
   Derived d;
   layout_for(*c, &ws, &d);
   if (d.mr_lds > 160 * 1024) return AVSG_ERR_UNSUPPORTED;
+  // a hash cell packs (id << ubits | union index) with the top bit clear
+  if ((int64_t)c->n_entries > ((int64_t)1 << (31 - d.ubits))) return AVSG_ERR_UNSUPPORTED;
   // gather addresses rows with 32-bit piece indices
   const int64_t row16 = (int64_t)d.row_elems * 2 / 16;
   if ((int64_t)d.row_elems * 2 % 16 != 0) return AVSG_ERR_UNSUPPORTED;
@@ -172,6 +178,8 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->t = 0;
   c->pinned_checked = nullptr;
   c->pinned_device = nullptr;
+  c->prof_events = nullptr;
+  c->prof_max = c->prof_used = 0;
   // zero the library-owned workspace words (status, counts, error, counters)
   if (launch_fill_i32((int32_t*)c->workspace, 0, c->ws.partials / 4, c->stream) != hipSuccess) {
     delete c;
@@ -187,7 +195,56 @@ avsg_status avsg_set_stream(avsg_ctx* ctx, void* stream) {
   return AVSG_OK;
 }
 
+static void destroy_prof_events(avsg_ctx* ctx) {
+  if (!ctx->prof_events) return;
+  for (int32_t i = 0; i < 4 * ctx->prof_max; ++i)
+    if (ctx->prof_events[i]) (void)hipEventDestroy(ctx->prof_events[i]);
+  free(ctx->prof_events);
+  ctx->prof_events = nullptr;
+  ctx->prof_max = ctx->prof_used = 0;
+}
+
+avsg_status avsg_profile_begin(avsg_ctx* ctx, int32_t max_steps) {
+  if (!ctx || max_steps < 1 || ctx->prof_events) return AVSG_ERR_INVALID_ARG;
+  ctx->prof_events = (hipEvent_t*)calloc(4 * (size_t)max_steps, sizeof(hipEvent_t));
+  if (!ctx->prof_events) return AVSG_ERR_INVALID_ARG;
+  ctx->prof_max = max_steps;
+  ctx->prof_used = 0;
+  for (int32_t i = 0; i < 4 * max_steps; ++i)
+    if (hipEventCreate(&ctx->prof_events[i]) != hipSuccess) {
+      destroy_prof_events(ctx);
+      return AVSG_ERR_HIP;
+    }
+  return AVSG_OK;
+}
+
+avsg_status avsg_profile_end(avsg_ctx* ctx, double* ms, int32_t* steps) {
+  if (!ctx || !ms || !steps || !ctx->prof_events) return AVSG_ERR_INVALID_ARG;
+  avsg_status st = AVSG_OK;
+  ms[0] = ms[1] = ms[2] = 0.0;
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess) st = AVSG_ERR_HIP;
+  for (int32_t i = 0; st == AVSG_OK && i < ctx->prof_used; ++i)
+    for (int k = 0; k < 3; ++k) {
+      float x = 0.f;
+      if (hipEventElapsedTime(&x, ctx->prof_events[4 * i + k], ctx->prof_events[4 * i + k + 1]) !=
+          hipSuccess) {
+        st = AVSG_ERR_HIP;
+        break;
+      }
+      ms[k] += x;
+    }
+  *steps = ctx->prof_used;
+  destroy_prof_events(ctx);
+  return st;
+}
+
+static inline void prof_mark(avsg_ctx* ctx, int k) {
+  if (ctx->prof_events && ctx->prof_used < ctx->prof_max)
+    (void)hipEventRecord(ctx->prof_events[4 * ctx->prof_used + k], ctx->stream);
+}
+
 avsg_status avsg_destroy(avsg_ctx* ctx) {
+  if (ctx) destroy_prof_events(ctx);
   delete ctx;
   return AVSG_OK;
 }
@@ -266,12 +323,15 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   mp.ucap = ctx->ws.ucap;
   mp.table_cap = ctx->ws.table_cap;
   mp.log_table_cap = ctx->d.log_table_cap;
+  mp.ubits = ctx->d.ubits;
   mp.policy = c.policy;
   mp.L = c.lifetime_L;
   mp.B = c.n_buckets;
   mp.nbins = ctx->d.nbins;
+  prof_mark(ctx, 0);
   if (launch_match_reserve(mp, ctx->d.units, ctx->d.mr_lds, ctx->stream) != hipSuccess)
     return AVSG_ERR_HIP;
+  prof_mark(ctx, 1);
 
   GatherParams gp;
   gp.misses = misses;
@@ -284,6 +344,7 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   gp.ucap = ctx->ws.ucap;
   gp.row16 = ctx->d.row_elems * 2 / 16;
   if (launch_gather(gp, ctx->gather_grid, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
+  prof_mark(ctx, 2);
 
   AttnParams ap;
   ap.sel_slot = hs->sel_slot;
@@ -308,6 +369,8 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
                      ? launch_attn_latent(ap, c.head_dim_qk, c.head_dim_v, ctx->stream)
                      : launch_attn_split(ap, ctx->d.G, ctx->stream);
   if (e != hipSuccess) return AVSG_ERR_HIP;
+  prof_mark(ctx, 3);
+  if (ctx->prof_events && ctx->prof_used < ctx->prof_max) ctx->prof_used += 1;
   ctx->t += 1;
   return AVSG_OK;
 }

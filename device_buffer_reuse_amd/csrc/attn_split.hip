@@ -1,6 +1,6 @@
 // K3 + K4: split-k decode attention over the buffer slots of the selected
-// entries (K/V split layout, grouped-query heads), with the split merge fused
-// into the last workgroup of each (unit, token).
+// entries (K/V split layout, grouped-query heads), then the merge of the
+// splits.
 //
 // What it computes: for each unit, query token and query head of the unit,
 // softmax(scale * q K^T) V over exactly the selected entries (all tokens of a
@@ -9,26 +9,28 @@
 // exact, so this equals attention over the same rows read from host memory.
 //
 // gfx950 mapping (HBM-bound, VALU):
-//  * A workgroup (4 waves) owns `split_rows` token rows of one (unit, token).
-//    16 lanes cover one 256-byte K or V row of a token (16 bytes each), so a
-//    wave reads 4 rows (1 KiB) per load instruction and a workgroup 16; the
-//    8 iterations of a 128-row split are issued before any use.
+//  * A workgroup (4 waves) owns 128 token rows of one (unit, token).  16 lanes
+//    cover one 256-byte K or V half-row of a token (16 bytes each), so a wave
+//    reads 4 half-rows (1 KiB) per load instruction; each lane issues the K
+//    and V loads of its 8 rows before any use, so a workgroup has its whole
+//    64 KiB in flight at once and every selected byte is read exactly once.
 //  * q.k uses v_dot2_f32_bf16 on bf16 pairs (products exact, fp32 sums); the
 //    16 partial sums of a row are added by four DPP steps inside the row.
 //  * Scores go to LDS; one wave per head takes the split's maximum and the
-//    exp2 weights; the V pass reads the other half of each row (each byte of
-//    a selected row is read once) and accumulates p * v in fp32.
-//  * Split partials (max, sum, o) go to the workspace; the last workgroup of a
-//    (unit, token), found with an agent-scope counter, merges them in split
-//    order, so the result does not depend on workgroup timing.
+//    exp2 weights; p * v accumulates in fp32 from the V halves in registers.
+//  * Split partials (max, sum, o) go to the workspace and a second small
+//    kernel merges them in split order, so the result does not depend on
+//    workgroup timing.  (Merging inside the last workgroup of each (unit,
+//    token) needs an agent-scope release in every workgroup, which writes
+//    back the XCD's L2 each time and cost more than the extra launch.)
 #include "avsg_internal.h"
 
 namespace avsg {
 namespace {
 
 constexpr int kD = 128;           // head dim of the split layout
-constexpr int kMaxSplitRows = 256;
-constexpr int kUnr = 8;           // row batches in flight per lane
+constexpr int kUnr = 8;           // rows in flight per lane group
+constexpr int kSplitRows = 16 * kUnr;  // token rows per workgroup
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
@@ -67,11 +69,10 @@ __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 
 
 template <int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) {
-  __shared__ float sScore[G][kMaxSplitRows];
-  __shared__ int32_t sSlot[kMaxSplitRows];
+  __shared__ float sScore[G][kSplitRows];
+  __shared__ int32_t sSlot[kSplitRows];
   __shared__ float sO[4][G][kD];
   __shared__ float sM[G], sL[G];
-  __shared__ int sLast;
 
   const int nsplit = p.nsplit;
   const int uj = blockIdx.x / nsplit;
@@ -83,175 +84,198 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
   const int tpe = p.tpe;
   const bool bad = p.unit_status[u] != 0;
   const int n_rows = p.k * tpe;
-  const int r0 = sp * p.split_rows, r1 = min(r0 + p.split_rows, n_rows);
+  const int r0 = sp * kSplitRows, r1 = min(r0 + kSplitRows, n_rows);
   const int nr = r1 - r0;
-  const size_t part_stride = (size_t)G * (kD + 2);
-  float* part = p.partials + ((size_t)uj * nsplit + sp) * part_stride;
+  float* orow = p.out + (((size_t)b * p.T + j) * p.Hq + g * G) * kD;
+  if (bad) {
+    if (nsplit == 1)
+      for (int idx = tid; idx < G * kD; idx += kAttnThreads) orow[idx] = 0.f;
+    return;
+  }
 
-  if (!bad) {
-    const int e0 = r0 / tpe, e1 = (r1 - 1) / tpe + 1;
-    for (int i = tid; i < e1 - e0; i += kAttnThreads) sSlot[i] = p.sel_slot[(size_t)uj * p.k + e0 + i];
+  const int e0 = r0 / tpe, e1 = (r1 - 1) / tpe + 1;
+  for (int i = tid; i < e1 - e0; i += kAttnThreads) sSlot[i] = p.sel_slot[(size_t)uj * p.k + e0 + i];
 
-    uint32_t qf[G][4];
+  uint32_t qf[G][4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4 qq = *reinterpret_cast<const uint4*>(
-          p.q + (((size_t)b * p.T + j) * p.Hq + g * G + h) * kD + c * 8);
-      qf[h][0] = qq.x; qf[h][1] = qq.y; qf[h][2] = qq.z; qf[h][3] = qq.w;
+  for (int h = 0; h < G; ++h) {
+    const uint4 qq = *reinterpret_cast<const uint4*>(
+        p.q + (((size_t)b * p.T + j) * p.Hq + g * G + h) * kD + c * 8);
+    qf[h][0] = qq.x; qf[h][1] = qq.y; qf[h][2] = qq.z; qf[h][3] = qq.w;
+  }
+  __syncthreads();
+
+  const uint16_t* ubase = p.buf_kv + (size_t)u * p.S * p.row_elems;
+  const int v_off = tpe * kD;
+  float o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[h][x] = 0.f;
+
+  // K and V halves of this lane group's rows, all in flight together
+  uint4 kr[kUnr], vr[kUnr];
+#pragma unroll
+  for (int e = 0; e < kUnr; ++e) {
+    const int rr = e * 16 + w * 4 + rg;
+    if (rr < nr) {
+      const int row = r0 + rr;
+      const int ent = row / tpe, sub = row - ent * tpe;
+      const uint16_t* base = ubase + (size_t)sSlot[ent - e0] * p.row_elems + sub * kD + c * 8;
+      kr[e] = *reinterpret_cast<const uint4*>(base);
+      vr[e] = *reinterpret_cast<const uint4*>(base + v_off);
     }
-    __syncthreads();
-
-    const uint16_t* ubase = p.buf_kv + (size_t)u * p.S * p.row_elems;
-    const int v_off = tpe * kD;
-
-    // pass 1: scores
-    for (int rb = 0; rb < nr; rb += 16 * kUnr) {
-      uint4 kr[kUnr];
+  }
 #pragma unroll
-      for (int e = 0; e < kUnr; ++e) {
-        const int rr = rb + e * 16 + w * 4 + rg;
-        if (rr < nr) {
-          const int row = r0 + rr;
-          const int ent = row / tpe, sub = row - ent * tpe;
-          const int slot = sSlot[ent - e0];
-          kr[e] = *reinterpret_cast<const uint4*>(ubase + (size_t)slot * p.row_elems + sub * kD + c * 8);
-        }
-      }
+  for (int e = 0; e < kUnr; ++e) {
+    const int rr = e * 16 + w * 4 + rg;
+    if (rr < nr) {
 #pragma unroll
-      for (int e = 0; e < kUnr; ++e) {
-        const int rr = rb + e * 16 + w * 4 + rg;
-        if (rr < nr) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float acc = dot2(qf[h][0], kr[e].x, 0.f);
-            acc = dot2(qf[h][1], kr[e].y, acc);
-            acc = dot2(qf[h][2], kr[e].z, acc);
-            acc = dot2(qf[h][3], kr[e].w, acc);
-            acc = row_sum16(acc);
-            if (c == h) sScore[h][rr] = acc * p.scale_log2e;
-          }
-        }
+      for (int h = 0; h < G; ++h) {
+        float acc = dot2(qf[h][0], kr[e].x, 0.f);
+        acc = dot2(qf[h][1], kr[e].y, acc);
+        acc = dot2(qf[h][2], kr[e].z, acc);
+        acc = dot2(qf[h][3], kr[e].w, acc);
+        acc = row_sum16(acc);
+        if (c == h) sScore[h][rr] = acc * p.scale_log2e;
       }
     }
-    __syncthreads();
-
-    // split maximum and exp2 weights, one wave per head
-    for (int h = w; h < G; h += 4) {
-      float mx = -INFINITY;
-      for (int i = lane; i < nr; i += 64) mx = fmaxf(mx, sScore[h][i]);
-      mx = wave_max(mx);
-      float sum = 0.f;
-      for (int i = lane; i < nr; i += 64) {
-        const float e = __builtin_amdgcn_exp2f(sScore[h][i] - mx);
-        sScore[h][i] = e;
-        sum += e;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) { sM[h] = mx; sL[h] = sum; }
+  }
+  __syncthreads();
+  // split maximum and exp2 weights, one wave per head
+  for (int h = w; h < G; h += 4) {
+    float mx = -INFINITY;
+    for (int i = lane; i < nr; i += 64) mx = fmaxf(mx, sScore[h][i]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int i = lane; i < nr; i += 64) {
+      const float e = __builtin_amdgcn_exp2f(sScore[h][i] - mx);
+      sScore[h][i] = e;
+      sum += e;
     }
-    __syncthreads();
-
-    // pass 2: o = sum p v
-    float o[G][8];
+    sum = wave_sum(sum);
+    if (lane == 0) { sM[h] = mx; sL[h] = sum; }
+  }
+  __syncthreads();
+  // o += p v
+#pragma unroll
+  for (int e = 0; e < kUnr; ++e) {
+    const int rr = e * 16 + w * 4 + rg;
+    if (rr < nr) {
+      float vf[8] = {bf_lo(vr[e].x), bf_hi(vr[e].x), bf_lo(vr[e].y), bf_hi(vr[e].y),
+                     bf_lo(vr[e].z), bf_hi(vr[e].z), bf_lo(vr[e].w), bf_hi(vr[e].w)};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pw = sScore[h][rr];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) o[h][x] = fmaf(pw, vf[x], o[h][x]);
+      }
+    }
+  }
+  // reduce over the 4 row groups of the wave, then over the 4 waves
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      o[h][x] += __shfl_xor(o[h][x], 16, 64);
+      o[h][x] += __shfl_xor(o[h][x], 32, 64);
+    }
+  if (rg == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int x = 0; x < 8; ++x) o[h][x] = 0.f;
-    for (int rb = 0; rb < nr; rb += 16 * kUnr) {
-      uint4 vr[kUnr];
-#pragma unroll
-      for (int e = 0; e < kUnr; ++e) {
-        const int rr = rb + e * 16 + w * 4 + rg;
-        if (rr < nr) {
-          const int row = r0 + rr;
-          const int ent = row / tpe, sub = row - ent * tpe;
-          const int slot = sSlot[ent - e0];
-          vr[e] = *reinterpret_cast<const uint4*>(ubase + (size_t)slot * p.row_elems + v_off + sub * kD + c * 8);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < kUnr; ++e) {
-        const int rr = rb + e * 16 + w * 4 + rg;
-        if (rr < nr) {
-          float vf[8] = {bf_lo(vr[e].x), bf_hi(vr[e].x), bf_lo(vr[e].y), bf_hi(vr[e].y),
-                         bf_lo(vr[e].z), bf_hi(vr[e].z), bf_lo(vr[e].w), bf_hi(vr[e].w)};
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float pw = sScore[h][rr];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) o[h][x] = fmaf(pw, vf[x], o[h][x]);
-          }
-        }
-      }
-    }
-    // reduce over the 4 row groups of the wave, then over the 4 waves
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        o[h][x] += __shfl_xor(o[h][x], 16, 64);
-        o[h][x] += __shfl_xor(o[h][x], 32, 64);
-      }
-    if (rg == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int x = 0; x < 8; ++x) sO[w][h][c * 8 + x] = o[h][x];
-    }
-    __syncthreads();
+      for (int x = 0; x < 8; ++x) sO[w][h][c * 8 + x] = o[h][x];
+  }
+  __syncthreads();
+  if (nsplit == 1) {
     for (int idx = tid; idx < G * kD; idx += kAttnThreads) {
       const int h = idx / kD, d = idx - h * kD;
-      part[h * kD + d] = (sO[0][h][d] + sO[1][h][d]) + (sO[2][h][d] + sO[3][h][d]);
+      orow[idx] = ((sO[0][h][d] + sO[1][h][d]) + (sO[2][h][d] + sO[3][h][d])) / sL[h];
     }
-    if (tid < G) {
-      part[G * kD + tid] = sM[tid];
-      part[G * kD + G + tid] = sL[tid];
-    }
+    return;
   }
-
-  // merge of the splits by the last workgroup of this (unit, token)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&p.counters[uj], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    sLast = (prev == (unsigned)(nsplit - 1));
-  }
-  __syncthreads();
-  if (!sLast) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  const float* pbase = p.partials + (size_t)uj * nsplit * part_stride;
-  float* orow = p.out + (((size_t)b * p.T + j) * p.Hq + g * G) * kD;
+  const size_t part_stride = (size_t)G * (kD + 2);
+  float* part = p.partials + ((size_t)uj * nsplit + sp) * part_stride;
   for (int idx = tid; idx < G * kD; idx += kAttnThreads) {
     const int h = idx / kD, d = idx - h * kD;
-    if (bad) { orow[idx] = 0.f; continue; }
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pbase[s * part_stride + G * kD + h]);
-    float acc = 0.f, lsum = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ps = pbase + s * part_stride;
-      const float wgt = __builtin_amdgcn_exp2f(ps[G * kD + h] - mx);
-      lsum = fmaf(ps[G * kD + G + h], wgt, lsum);
-      acc = fmaf(ps[h * kD + d], wgt, acc);
-    }
-    orow[idx] = acc / lsum;
+    part[idx] = (sO[0][h][d] + sO[1][h][d]) + (sO[2][h][d] + sO[3][h][d]);
   }
-  if (tid == 0) p.counters[uj] = 0u;
+  if (tid < G) {
+    part[G * kD + tid] = sM[tid];
+    part[G * kD + G + tid] = sL[tid];
+  }
+}
+
+// Merge of the split partials of each (unit, token) in split order:
+// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
+template <int G>
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnParams p) {
+  extern __shared__ float sWt[];  // [nsplit][G] weights 2^(m_s - M) / L
+  __shared__ float sML[2][G];
+  const int uj = blockIdx.x;
+  const int u = uj / p.T, j = uj - u * p.T;
+  const int b = u / p.Hkv, g = u - b * p.Hkv;
+  const int nsplit = p.nsplit, tid = threadIdx.x;
+  const size_t part_stride = (size_t)G * (kD + 2);
+  const float* pbase = p.partials + (size_t)uj * nsplit * part_stride;
+  float* orow = p.out + (((size_t)b * p.T + j) * p.Hq + g * G) * kD;
+  if (p.unit_status[u] != 0) {
+    for (int idx = tid; idx < G * kD; idx += kAttnThreads) orow[idx] = 0.f;
+    return;
+  }
+  for (int i = tid; i < nsplit * G; i += kAttnThreads) {
+    const int s = i / G, h = i - s * G;
+    sWt[i] = pbase[s * part_stride + G * kD + h];
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mx = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, sWt[s * G + tid]);
+    float lsum = 0.f;
+    for (int s = 0; s < nsplit; ++s)
+      lsum = fmaf(pbase[s * part_stride + G * kD + G + tid],
+                  __builtin_amdgcn_exp2f(sWt[s * G + tid] - mx), lsum);
+    sML[0][tid] = mx;
+    sML[1][tid] = 1.f / lsum;
+  }
+  __syncthreads();
+  for (int i = tid; i < nsplit * G; i += kAttnThreads) {
+    const int h = i % G;
+    sWt[i] = __builtin_amdgcn_exp2f(sWt[i] - sML[0][h]) * sML[1][h];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kD; idx += kAttnThreads) {
+    const int h = idx / kD;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) acc = fmaf(pbase[s * part_stride + idx], sWt[s * G + h], acc);
+    orow[idx] = acc;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s) {
+template <int G>
+static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.units * p.T * p.nsplit));
+  hipLaunchKernelGGL(attn_split_kernel<G>, grid, dim3(kAttnThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  const size_t lds = sizeof(float) * (size_t)p.nsplit * G;
+  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3((unsigned)(p.units * p.T)), dim3(kAttnThreads),
+                     lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s) {
+  if (p.split_rows != kSplitRows) return hipErrorInvalidValue;
   switch (G) {
-    case 1: hipLaunchKernelGGL(attn_split_kernel<1>, grid, dim3(kAttnThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(attn_split_kernel<2>, grid, dim3(kAttnThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(attn_split_kernel<4>, grid, dim3(kAttnThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(attn_split_kernel<8>, grid, dim3(kAttnThreads), 0, s, p); break;
+    case 1: return launch_g<1>(p, s);
+    case 2: return launch_g<2>(p, s);
+    case 4: return launch_g<4>(p, s);
+    case 8: return launch_g<8>(p, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace avsg

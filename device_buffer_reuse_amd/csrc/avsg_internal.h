@@ -25,7 +25,7 @@ struct WsLayout {
 };
 
 struct Derived {
-  int32_t units, G, row_elems, nbins, log_table_cap;
+  int32_t units, G, row_elems, nbins, log_table_cap, ubits;
   size_t mr_lds;  // dynamic LDS bytes of match_reserve
 };
 
@@ -46,7 +46,7 @@ struct MatchReserveParams {
   int2* misses;           // workspace [units][ucap]: (slot, id) in miss order
   uint32_t* err_word;
   int64_t t;
-  int32_t S, N, T, k, ucap, table_cap, log_table_cap, policy, L, B, nbins;
+  int32_t S, N, T, k, ucap, table_cap, log_table_cap, ubits, policy, L, B, nbins;
 };
 
 struct GatherParams {

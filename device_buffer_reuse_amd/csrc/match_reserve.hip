@@ -14,17 +14,21 @@
 //  * The union U of the iteration's sorted selections is built in LDS (for
 //    two tokens by a rank formula: each element's position in U is found by
 //    binary search in the other list minus the duplicates before it).
-//  * U is hashed into an LDS open-addressing table (linear probing, load
-//    factor <= 0.5, multiplicative hash); every slot of the buffer then probes
-//    its resident id, one slot per lane, 64 lanes at a time.  Hashing U rather
-//    than the slots keeps the table at 2|U| cells and turns "is this slot a
-//    candidate" into the same probe.
+//  * U is hashed into an LDS open-addressing table (load factor <= 0.5,
+//    multiplicative hash).  A cell packs (id << ubits | union index) in 32 bits
+//    and cells are probed four at a time: one 16-byte LDS read fetches a whole
+//    aligned bucket, so a probe rarely needs a second read and never a
+//    dependent one.  Every slot of the buffer then probes its resident id, one
+//    slot per lane, 64 lanes at a time.  Hashing U rather than the slots keeps
+//    the table at 2|U| cells and turns "is this slot a candidate" into the
+//    same probe.
 //  * Victim selection is a stable counting selection: each candidate slot gets
-//    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first); ranks
-//    inside a bin follow slot order via ballot/mbcnt per wave plus per-(wave,
-//    bin) prefix sums; the m first candidates in (bin, slot) order are the
-//    victims.  No comparison sort, no order-dependent atomics: the result is
-//    deterministic.
+//    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first).  A
+//    histogram of the bins gives the threshold bin b* that holds the m-th
+//    candidate; only candidates in bins <= b* are ranked, inside their bin in
+//    slot order via ballot/mbcnt per wave plus per-(wave, bin) prefix sums; the
+//    m first candidates in (bin, slot) order are the victims.  No comparison
+//    sort, no order-dependent atomics: the result is deterministic.
 //  * The r-th miss in ascending id order takes the r-th victim, its row is
 //    listed as (slot, id) for the gather kernel.
 #include "avsg_internal.h"
@@ -79,15 +83,33 @@ __device__ __forceinline__ int lower_bound_lds(const int32_t* a, int n, int32_t 
   return lo;
 }
 
-__device__ __forceinline__ int hash_lookup(const int32_t* sHash, const int32_t* sU, int cap_mask,
-                                           int log_cap, int32_t x) {
-  uint32_t h = hash_id(x, log_cap);
+constexpr int32_t kEmpty = -1;  // a filled cell has its top bit clear
+
+// Union index of id x, or -1.  Buckets of 4 cells are scanned in order from
+// x's home bucket; insertion fills the first empty cell from the start of the
+// home bucket, so an empty cell in a scanned bucket ends the search.
+__device__ __forceinline__ int hash_find(const int32_t* sHash, int log_cap, int ubits,
+                                         int32_t x) {
+  const int bmask = ((1 << log_cap) >> 2) - 1;
+  uint32_t hb = hash_id(x, log_cap) >> 2;
+  const uint32_t umask = (1u << ubits) - 1;
   while (true) {
-    int c = sHash[h];
-    if (c < 0) return -1;
-    if (sU[c] == x) return c;
-    h = (h + 1) & cap_mask;
+    const int4 c = reinterpret_cast<const int4*>(sHash)[hb];
+    if (c.x != kEmpty && (c.x >> ubits) == x) return c.x & umask;
+    if (c.y != kEmpty && (c.y >> ubits) == x) return c.y & umask;
+    if (c.z != kEmpty && (c.z >> ubits) == x) return c.z & umask;
+    if (c.w != kEmpty && (c.w >> ubits) == x) return c.w & umask;
+    if ((c.x == kEmpty) | (c.y == kEmpty) | (c.z == kEmpty) | (c.w == kEmpty)) return -1;
+    hb = (hb + 1) & bmask;
   }
+}
+
+__device__ __forceinline__ void hash_insert(int32_t* sHash, int log_cap, int ubits, int32_t x,
+                                            int32_t i) {
+  const int cmask = (1 << log_cap) - 1;
+  uint32_t cell = (hash_id(x, log_cap) >> 2) << 2;
+  const int32_t v = (x << ubits) | i;
+  while (atomicCAS(&sHash[cell], kEmpty, v) != kEmpty) cell = (cell + 1) & cmask;
 }
 
 enum { kFlagRange = 1, kFlagUnsorted = 2, kFlagCapacity = 4, kFlagState = 8 };
@@ -99,6 +121,24 @@ __device__ __forceinline__ int flags_to_status(int f) {
   return AVSG_ERR_STATE;
 }
 
+// Exclusive scan of a 0/1 flag over the workgroup in thread order.
+__device__ __forceinline__ int block_excl_scan_bit(bool v, int* sWs, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t m = __ballot(v);
+  if (lane == 0) sWs[w] = __popcll(m);
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kMRWaves; ++i) {
+    int x = sWs[i];
+    pre += (i < w) ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return pre + mbcnt64(m);
+}
+
 template <int MAXP>
 __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveParams p) {
   extern __shared__ int32_t lds[];
@@ -108,11 +148,11 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const int nbins = p.nbins, tk = T * k;
   const bool lru = p.policy == AVSG_POLICY_BUCKET_LRU;
 
-  int32_t* sU = lds;                         // [ucap] union, ascending
+  int32_t* sHash = lds;                      // [C] packed (id, union index) or -1
+  int32_t* sU = sHash + C;                   // [ucap] union, ascending
   int32_t* sUslot = sU + ucap;               // [ucap] slot of each union entry (+ miss flag)
-  int32_t* sHash = sUslot + ucap;            // [C] union index or -1
-  int32_t* sCnt = sHash + C;                 // [16][nbins]
-  int32_t* sOff = sCnt + kMRWaves * nbins;   // [16][nbins]
+  int32_t* sCnt = sUslot + ucap;             // [16][nbins] per-wave candidates per bin
+  int32_t* sOff = sCnt + kMRWaves * nbins;   // [16][nbins] first rank of (wave, bin)
   int32_t* sTot = sOff + kMRWaves * nbins;   // [nbins] -> exclusive bin starts
   int32_t* sMisc = sTot + nbins;             // [64]: 0 flags, 1 evictions, 16.. scan scratch
   int32_t* sMiss = sMisc + 64;               // [max(ucap, T*k)]; T=2: first holds both lists
@@ -124,6 +164,23 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   int32_t* slot_table = p.slot_table + (size_t)u * S;
   int32_t* lifetimes = p.lifetimes + (size_t)u * S;
 
+  // ---- 0. issue the loads of this lane's slots first; they complete while
+  //         the selection is validated, merged and hashed
+  const int R = ((S + kMRThreads - 1) / kMRThreads) * 64;  // slots per wave, multiple of 64
+  const int s0 = w * R, s1 = min(s0 + R, S);
+  int tok[MAXP], lf[MAXP], bin[MAXP], rank[MAXP];
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    const int s = s0 + q * 64 + lane;
+    tok[q] = kInvalid;
+    lf[q] = 0;
+    if (q * 64 < R && s < s1) {
+      tok[q] = slot_table[s];
+      lf[q] = lifetimes[s];
+    }
+  }
+  int32_t* stage = (T > 1) ? sMiss : sU;  // T = 1: the list is U itself
+  for (int i = tid; i < tk; i += kMRThreads) stage[i] = sel[i];
   if (tid < 64) sMisc[tid] = 0;
   for (int i = tid; i < C; i += kMRThreads) sHash[i] = -1;
   for (int i = tid; i < ucap; i += kMRThreads) sUslot[i] = -1;
@@ -133,101 +190,83 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   {
     int bad = 0;
     for (int i = tid; i < tk; i += kMRThreads) {
-      int32_t x = sel[i];
-      int pos = i % k;
+      const int32_t x = stage[i];
       if (x < 0 || x >= N) bad |= kFlagRange;
-      if (pos > 0 && x <= sel[i - 1]) bad |= kFlagUnsorted;
-      if (T > 1) sMiss[i] = x;  // stage both lists for the union
+      if (i % k != 0 && x <= stage[i - 1]) bad |= kFlagUnsorted;
     }
     if (bad) atomicOr(&sMisc[0], bad);
   }
   __syncthreads();
 
-  // ---- 2. union U of the T lists (T = 1: the list itself)
+  // ---- 2. union U of the two lists (T = 2): position of each element =
+  //         elements below it in both lists minus duplicates below it
   int nu = k;
-  if (sMisc[0] == 0) {
-    if (T == 1) {
-      for (int i = tid; i < k; i += kMRThreads) sU[i] = sel[i];
-    } else {
-      const int32_t* A = sMiss;
-      const int32_t* Bl = sMiss + k;
-      int run = 0;
-      for (int c0 = 0; c0 < k; c0 += kMRThreads) {
-        int i = c0 + tid;
-        int dup = 0;
-        if (i < k) {
-          int lb = lower_bound_lds(Bl, k, A[i]);
-          dup = (lb < k && Bl[lb] == A[i]) ? 1 : 0;
-        }
-        int tot;
-        int pre = block_excl_scan(dup, sWs, &tot);
-        if (i < k) sDup[i] = run + pre;
-        run += tot;
+  if (T > 1 && sMisc[0] == 0) {
+    const int32_t* A = sMiss;
+    const int32_t* Bl = sMiss + k;
+    int run = 0;
+    for (int c0 = 0; c0 < k; c0 += kMRThreads) {
+      const int i = c0 + tid;
+      bool dup = false;
+      if (i < k) {
+        const int lb = lower_bound_lds(Bl, k, A[i]);
+        dup = lb < k && Bl[lb] == A[i];
       }
-      if (tid == 0) sDup[k] = run;
-      __syncthreads();
-      nu = 2 * k - sDup[k];
-      if (nu > S) {
-        if (tid == 0) sMisc[0] = kFlagCapacity;
-      } else {
-        for (int i = tid; i < k; i += kMRThreads) {
-          int32_t a = A[i];
-          int pos = i + lower_bound_lds(Bl, k, a) - sDup[i];
-          sU[pos] = a;
-          sMap[i] = pos;
-        }
-        for (int j = tid; j < k; j += kMRThreads) {
-          int32_t b = Bl[j];
-          int la = lower_bound_lds(A, k, b);
-          int pos = la + j - sDup[la];
-          sU[pos] = b;  // a duplicate writes the same value at the same position
-          sMap[k + j] = pos;
-        }
+      int tot;
+      const int pre = block_excl_scan_bit(dup, sWs, &tot);
+      if (i < k) sDup[i] = run + pre;
+      run += tot;
+    }
+    if (tid == 0) sDup[k] = run;
+    __syncthreads();
+    nu = 2 * k - sDup[k];
+    if (nu > S) {
+      if (tid == 0) sMisc[0] = kFlagCapacity;
+    } else {
+      for (int i = tid; i < k; i += kMRThreads) {
+        const int32_t a = A[i];
+        const int pos = i + lower_bound_lds(Bl, k, a) - sDup[i];
+        sU[pos] = a;
+        sMap[i] = pos;
+      }
+      for (int j = tid; j < k; j += kMRThreads) {
+        const int32_t b = Bl[j];
+        const int la = lower_bound_lds(A, k, b);
+        const int pos = la + j - sDup[la];
+        sU[pos] = b;  // a duplicate writes the same value at the same position
+        sMap[k + j] = pos;
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 3. hash U into the LDS table
-  const int log_cap = p.log_table_cap, cap_mask = C - 1;
+  const int log_cap = p.log_table_cap, ubits = p.ubits;
   if (sMisc[0] == 0) {
-    for (int i = tid; i < nu; i += kMRThreads) {
-      uint32_t h = hash_id(sU[i], log_cap);
-      while (atomicCAS(&sHash[h], -1, i) != -1) h = (h + 1) & cap_mask;
-    }
+    for (int i = tid; i < nu; i += kMRThreads) hash_insert(sHash, log_cap, ubits, sU[i], i);
   }
   __syncthreads();
 
   // ---- 4. every slot probes its resident id; state checks
-  const int R = ((S + kMRThreads - 1) / kMRThreads) * 64;  // slots per wave, multiple of 64
-  const int s0 = w * R, s1 = min(s0 + R, S);
-  int tok[MAXP], lf[MAXP], bin[MAXP], rank[MAXP];
-  bool changed[MAXP];
   if (sMisc[0] == 0) {
     int bad = 0;
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) {
       const int s = s0 + q * 64 + lane;
-      tok[q] = kInvalid;
-      lf[q] = 0;
+      const int32_t x = tok[q];
       bin[q] = kInvalid;
-      changed[q] = false;
-      if (q * 64 < R && s < s1) {
-        int32_t x = slot_table[s];
-        int32_t l = lifetimes[s];
-        tok[q] = x;
-        lf[q] = l;
-        bin[q] = 0;
-        if (x < -1 || x >= N) {
-          bad = 1;
-        } else if (x >= 0) {
-          if (!lru && (l < 0 || l > p.L)) bad = 1;
-          if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
-          int i = hash_lookup(sHash, sU, cap_mask, log_cap, x);
-          if (i >= 0) {
-            if (atomicCAS(&sUslot[i], -1, s) != -1) bad = 1;  // id of U held by two slots
-            bin[q] = -1;                                       // hit
-          }
+      if (x == kInvalid) continue;
+      bin[q] = 0;
+      if (x < -1 || x >= N) {
+        bad = 1;
+      } else if (x >= 0) {
+        const int32_t l = lf[q];
+        if (!lru && (l < 0 || l > p.L)) bad = 1;
+        if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
+        const int i = hash_find(sHash, log_cap, ubits, x);
+        if (i >= 0) {
+          if (atomicCAS(&sUslot[i], -1, s) != -1) bad = 1;  // id of U held by two slots
+          bin[q] = -1;                                       // hit
         }
       }
     }
@@ -277,21 +316,55 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // ---- 6. misses of U in ascending id order
   int m = 0;
   for (int c0 = 0; c0 < nu; c0 += kMRThreads) {
-    int i = c0 + tid;
-    int miss = (i < nu && sUslot[i] < 0) ? 1 : 0;
+    const int i = c0 + tid;
+    const bool miss = i < nu && sUslot[i] < 0;
     int tot;
-    int pre = block_excl_scan(miss, sWs, &tot);
+    const int pre = block_excl_scan_bit(miss, sWs, &tot);
     if (miss) sMiss[m + pre] = i;
     m += tot;
   }
 
   // ---- 7. victims: the m first candidates in (bin, slot) order
+  int ev = 0;
+  bool changed[MAXP];
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) changed[q] = false;
   if (m > 0) {
+    // per-wave histogram of the candidates' bins
     for (int b = lane; b < nbins; b += 64) sCnt[w * nbins + b] = 0;
     __syncthreads();
 #pragma unroll
+    for (int q = 0; q < MAXP; ++q)
+      if (bin[q] >= 0) atomicAdd(&sCnt[w * nbins + bin[q]], 1);
+    __syncthreads();
+    // bin totals, their exclusive starts, and the threshold bin b* holding
+    // the m-th candidate (nbins <= 128 <= threads)
+    {
+      int tot = 0;
+      if (tid < nbins)
+        for (int v = 0; v < kMRWaves; ++v) tot += sCnt[v * nbins + tid];
+      int all;
+      const int pre = block_excl_scan(tot, sWs, &all);
+      if (tid < nbins) {
+        sTot[tid] = pre;
+        if (pre < m && pre + tot >= m) sMisc[2] = tid;
+      }
+    }
+    __syncthreads();
+    const int bstar = sMisc[2];
+    for (int idx = tid; idx < kMRWaves * (bstar + 1); idx += kMRThreads) {
+      const int v = idx / (bstar + 1), b = idx - v * (bstar + 1);
+      int off = sTot[b];
+      for (int x = 0; x < v; ++x) off += sCnt[x * nbins + b];
+      sOff[v * nbins + b] = off;
+    }
+    // rank of each candidate in bins <= b* among the wave's candidates of the
+    // same bin, in slot order; the running count of bin b lives in lane b
+    // (b < 64) or lane b - 64 (64 <= b < 128) of cntA / cntB
+    int cntA = 0, cntB = 0;
+#pragma unroll
     for (int q = 0; q < MAXP; ++q) {
-      bool act = bin[q] >= 0;
+      const bool act = bin[q] >= 0 && bin[q] <= bstar;
       rank[q] = 0;
       uint64_t pend = __ballot(act);
       while (pend) {
@@ -299,44 +372,20 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         const int b = __builtin_amdgcn_readlane(bin[q], lead);
         const bool mine = act && bin[q] == b;
         const uint64_t grp = __ballot(mine);
-        const int base = sCnt[w * nbins + b];
+        const int base = b < 64 ? __builtin_amdgcn_readlane(cntA, b)
+                                : __builtin_amdgcn_readlane(cntB, b - 64);
         if (mine) rank[q] = base + mbcnt64(grp);
-        if (lane == 0) sCnt[w * nbins + b] = base + __popcll(grp);
+        const int add = __popcll(grp);
+        if (b < 64) cntA += (lane == b) ? add : 0;
+        else cntB += (lane == b - 64) ? add : 0;
         pend &= ~grp;
-        act = act && !mine;
       }
     }
     __syncthreads();
-    for (int b = tid; b < nbins; b += kMRThreads) {
-      int tot = 0;
-      for (int v = 0; v < kMRWaves; ++v) tot += sCnt[v * nbins + b];
-      sTot[b] = tot;
-    }
-    __syncthreads();
-    {
-      int run = 0;
-      for (int c0 = 0; c0 < nbins; c0 += kMRThreads) {
-        int b = c0 + tid;
-        int v = b < nbins ? sTot[b] : 0;
-        int tot;
-        int pre = block_excl_scan(v, sWs, &tot);
-        if (b < nbins) sTot[b] = run + pre;
-        run += tot;
-      }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < kMRWaves * nbins; idx += kMRThreads) {
-      const int v = idx / nbins, b = idx - v * nbins;
-      int off = sTot[b];
-      for (int x = 0; x < v; ++x) off += sCnt[x * nbins + b];
-      sOff[idx] = off;
-    }
-    __syncthreads();
-    int ev = 0;
     int2* misses = p.misses + (size_t)u * ucap;
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) {
-      if (bin[q] < 0) continue;
+      if (bin[q] < 0 || bin[q] > bstar) continue;
       const int r = sOff[w * nbins + bin[q]] + rank[q];
       if (r < m) {
         const int s = s0 + q * 64 + lane;

@@ -61,6 +61,8 @@ def _load():
             lib.oracle_unit_step.restype = ctypes.c_int
             lib.oracle_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, ctypes.c_int64] + [p] * 9
             lib.oracle_step.restype = None
+            lib.oracle_set_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_threads.restype = None
             _lib = lib
     return _lib
 
@@ -68,6 +70,11 @@ def _load():
 def _p(a: np.ndarray) -> int:
     assert a.flags.c_contiguous
     return a.ctypes.data
+
+
+def set_threads(n: int) -> None:
+    """Threads of the state machine's OpenMP loop over units."""
+    _load().oracle_set_threads(int(n))
 
 
 class OracleBuffer:

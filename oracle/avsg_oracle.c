@@ -32,6 +32,7 @@
  * Each step is written out in that order, with a library sort (qsort) where
  * the reading asks for an order and a two-pointer merge for the match.
  */
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -237,3 +238,6 @@ void oracle_step(const oracle_cfg* c, int64_t units, int64_t t, const int32_t* s
                                  hit_flag + u * tk, sel_slot + u * tk, fill_slot + u * S,
                                  fill_id + u * S, counts + u * 4);
 }
+
+/* Threads used by oracle_step's loop over units. */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
