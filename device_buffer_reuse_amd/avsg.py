@@ -23,11 +23,13 @@ ERR_UNSORTED, ERR_RANGE, ERR_CAPACITY, ERR_STATE = 16, 17, 18, 19
 KV_SPLIT, KV_LATENT = 0, 1
 POLICY_LIFETIME, POLICY_BUCKET_LRU = 0, 1
 HOST_COHERENT = 1
+TRANSFER_FUSED, TRANSFER_BALANCED, TRANSFER_PER_UNIT = 0, 1, 2
 
 EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_set_stream",
             "avsg_destroy", "avsg_reset", "avsg_step", "avsg_last_error", "avsg_validate_state",
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
-            "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end"]
+            "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
+            "avsg_set_transfer_mode"]
 
 
 class AvsgError(RuntimeError):
@@ -82,6 +84,7 @@ def load():
         "avsg_status_string": ([i32], ctypes.c_char_p),
         "avsg_attn_splits": ([p], ctypes.c_int32),
         "avsg_profile_begin": ([p, ctypes.c_int32], i32),
+        "avsg_set_transfer_mode": ([p, ctypes.c_int32], i32),
         "avsg_profile_end": ([p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)], i32),
     }
     for name, (args, res) in sig.items():
@@ -148,6 +151,10 @@ def avsg_set_step(ctx: int, t: int) -> int:
 
 def avsg_attn_splits(ctx: int) -> int:
     return int(load().avsg_attn_splits(ctx))
+
+
+def avsg_set_transfer_mode(ctx: int, mode: int) -> int:
+    return load().avsg_set_transfer_mode(ctx, mode)
 
 
 def avsg_profile_begin(ctx: int, max_steps: int) -> int:
@@ -301,6 +308,11 @@ class Context:
         st = avsg_set_step(self.handle, value)
         if st != OK:
             raise AvsgError(st, "avsg_set_step")
+
+    def set_transfer_mode(self, mode: int):
+        st = avsg_set_transfer_mode(self.handle, mode)
+        if st != OK:
+            raise AvsgError(st, "avsg_set_transfer_mode")
 
     def profile_begin(self, max_steps: int):
         st = avsg_profile_begin(self.handle, max_steps)

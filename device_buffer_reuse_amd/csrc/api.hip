@@ -19,6 +19,7 @@ struct avsg_ctx {
   int64_t t;
   const void* pinned_checked;    // last host_kv pointer found pinned
   const void* pinned_device;     // its device-visible address
+  int32_t transfer_mode;         // avsg_transfer_mode
   hipEvent_t* prof_events;       // 4 per profiled step, or null
   int32_t prof_max, prof_used;
 };
@@ -59,6 +60,7 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->unit_status = off; off = align256(off + 4 * (size_t)d->units);
   ws->miss_count = off;  off = align256(off + 4 * (size_t)d->units);
   ws->misses = off;      off = align256(off + 8 * (size_t)d->units * ws->ucap);
+  ws->fetch = off;       off = align256(off + (size_t)d->units * tk);
   ws->err_word = off;    off = align256(off + 8);
   ws->counters = off;    off = align256(off + 4 * (size_t)d->units * T);
   ws->partials = off;
@@ -180,12 +182,19 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->pinned_device = nullptr;
   c->prof_events = nullptr;
   c->prof_max = c->prof_used = 0;
+  c->transfer_mode = AVSG_TRANSFER_FUSED;
   // zero the library-owned workspace words (status, counts, error, counters)
   if (launch_fill_i32((int32_t*)c->workspace, 0, c->ws.partials / 4, c->stream) != hipSuccess) {
     delete c;
     return AVSG_ERR_HIP;
   }
   *out = c;
+  return AVSG_OK;
+}
+
+avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode) {
+  if (!ctx || mode < AVSG_TRANSFER_FUSED || mode > AVSG_TRANSFER_PER_UNIT) return AVSG_ERR_INVALID_ARG;
+  ctx->transfer_mode = mode;
   return AVSG_OK;
 }
 
@@ -314,6 +323,7 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   mp.unit_status = unit_status;
   mp.miss_count = miss_count;
   mp.misses = misses;
+  mp.fetch = (uint8_t*)(ws + ctx->ws.fetch);
   mp.err_word = (uint32_t*)(ws + ctx->ws.err_word);
   mp.t = ctx->t;
   mp.S = c.n_slots;
@@ -343,11 +353,19 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   gp.units = ctx->d.units;
   gp.ucap = ctx->ws.ucap;
   gp.row16 = ctx->d.row_elems * 2 / 16;
-  if (launch_gather(gp, ctx->gather_grid, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
+  gp.per_unit = ctx->transfer_mode == AVSG_TRANSFER_PER_UNIT;
+  if (ctx->transfer_mode != AVSG_TRANSFER_FUSED &&
+      launch_gather(gp, gp.per_unit ? ctx->d.units : ctx->gather_grid, ctx->stream) != hipSuccess)
+    return AVSG_ERR_HIP;
   prof_mark(ctx, 2);
 
   AttnParams ap;
   ap.sel_slot = hs->sel_slot;
+  ap.sel = sel_idx;
+  ap.fetch = ctx->transfer_mode == AVSG_TRANSFER_FUSED ? (const uint8_t*)(ws + ctx->ws.fetch) : nullptr;
+  ap.host_kv = (const uint16_t*)host_dev;
+  ap.N = c.n_entries;
+  ap.token = 0;
   ap.unit_status = unit_status;
   ap.q = q;
   ap.buf_kv = buf_kv;

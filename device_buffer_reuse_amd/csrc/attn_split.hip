@@ -33,6 +33,7 @@ constexpr int kUnr = 8;           // rows in flight per lane group
 constexpr int kSplitRows = 16 * kUnr;  // token rows per workgroup
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -71,13 +72,15 @@ template <int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) {
   __shared__ float sScore[G][kSplitRows];
   __shared__ int32_t sSlot[kSplitRows];
+  __shared__ int32_t sSrc[kSplitRows];  // host row of a fetched entry, else -1
   __shared__ float sO[4][G][kD];
   __shared__ float sM[G], sL[G];
 
   const int nsplit = p.nsplit;
-  const int uj = blockIdx.x / nsplit;
-  const int sp = blockIdx.x - uj * nsplit;
-  const int u = uj / p.T, j = uj - u * p.T;
+  const int u = blockIdx.x / nsplit;
+  const int sp = blockIdx.x - u * nsplit;
+  const int j = p.token;
+  const int uj = u * p.T + j;
   const int b = u / p.Hkv, g = u - b * p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rg = lane >> 4, c = lane & 15;
@@ -94,7 +97,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
   }
 
   const int e0 = r0 / tpe, e1 = (r1 - 1) / tpe + 1;
-  for (int i = tid; i < e1 - e0; i += kAttnThreads) sSlot[i] = p.sel_slot[(size_t)uj * p.k + e0 + i];
+  for (int i = tid; i < e1 - e0; i += kAttnThreads) {
+    const size_t at = (size_t)uj * p.k + e0 + i;
+    sSlot[i] = p.sel_slot[at];
+    sSrc[i] = (p.fetch && p.fetch[at]) ? p.sel[at] : -1;
+  }
 
   uint32_t qf[G][4];
 #pragma unroll
@@ -105,7 +112,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
   }
   __syncthreads();
 
-  const uint16_t* ubase = p.buf_kv + (size_t)u * p.S * p.row_elems;
+  uint16_t* ubase = p.buf_kv + (size_t)u * p.S * p.row_elems;
+  const uint16_t* hbase = p.host_kv + (size_t)u * p.N * p.row_elems;
   const int v_off = tpe * kD;
   float o[G][8];
 #pragma unroll
@@ -113,17 +121,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
 #pragma unroll
     for (int x = 0; x < 8; ++x) o[h][x] = 0.f;
 
-  // K and V halves of this lane group's rows, all in flight together
+  // K and V halves of this lane group's rows, all in flight together: rows
+  // that missed come from pinned host memory (and are stored into their slot
+  // below), the others from the buffer in HBM
   uint4 kr[kUnr], vr[kUnr];
+  uint16_t* dst[kUnr];
 #pragma unroll
   for (int e = 0; e < kUnr; ++e) {
     const int rr = e * 16 + w * 4 + rg;
+    dst[e] = nullptr;
     if (rr < nr) {
       const int row = r0 + rr;
       const int ent = row / tpe, sub = row - ent * tpe;
-      const uint16_t* base = ubase + (size_t)sSlot[ent - e0] * p.row_elems + sub * kD + c * 8;
-      kr[e] = *reinterpret_cast<const uint4*>(base);
-      vr[e] = *reinterpret_cast<const uint4*>(base + v_off);
+      const int off = sub * kD + c * 8;
+      uint16_t* slot_row = ubase + (size_t)sSlot[ent - e0] * p.row_elems + off;
+      const int src = sSrc[ent - e0];
+      if (src >= 0) {
+        const u32x4* h = reinterpret_cast<const u32x4*>(hbase + (size_t)src * p.row_elems + off);
+        const u32x4 a = __builtin_nontemporal_load(h);
+        const u32x4 bb = __builtin_nontemporal_load(h + v_off / 8);
+        kr[e] = make_uint4(a.x, a.y, a.z, a.w);
+        vr[e] = make_uint4(bb.x, bb.y, bb.z, bb.w);
+        dst[e] = slot_row;
+      } else {
+        kr[e] = *reinterpret_cast<const uint4*>(slot_row);
+        vr[e] = *reinterpret_cast<const uint4*>(slot_row + v_off);
+      }
     }
   }
 #pragma unroll
@@ -141,6 +164,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
       }
     }
   }
+#pragma unroll
+  for (int e = 0; e < kUnr; ++e)
+    if (dst[e]) {
+      *reinterpret_cast<uint4*>(dst[e]) = kr[e];
+      *reinterpret_cast<uint4*>(dst[e] + v_off) = vr[e];
+    }
   __syncthreads();
   // split maximum and exp2 weights, one wave per head
   for (int h = w; h < G; h += 4) {
@@ -256,11 +285,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnParams p
 }  // namespace
 
 template <int G>
-static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.units * p.T * p.nsplit));
-  hipLaunchKernelGGL(attn_split_kernel<G>, grid, dim3(kAttnThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit == 1) return e;
+static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
+  // one launch per query token: a row that several tokens select is fetched
+  // by the first of them, and later tokens read it from the buffer
+  const dim3 grid((unsigned)(p0.units * p0.nsplit));
+  AttnParams p = p0;
+  for (int j = 0; j < p0.T; ++j) {
+    p.token = j;
+    hipLaunchKernelGGL(attn_split_kernel<G>, grid, dim3(kAttnThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.nsplit == 1) return hipSuccess;
   const size_t lds = sizeof(float) * (size_t)p.nsplit * G;
   hipLaunchKernelGGL(attn_combine_kernel<G>, dim3((unsigned)(p.units * p.T)), dim3(kAttnThreads),
                      lds, s, p);

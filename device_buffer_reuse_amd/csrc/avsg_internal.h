@@ -17,7 +17,7 @@ constexpr int kGatherThreads = 256;
 
 // Layout of the caller's workspace (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t unit_status, miss_count, misses, err_word, counters, partials, total;
+  size_t unit_status, miss_count, misses, fetch, err_word, counters, partials, total;
   int32_t ucap;       // union capacity per unit = min(T*k, S)
   int32_t table_cap;  // hash table cells, power of two >= 2*ucap
   int32_t nsplit;     // attention splits per (unit, token)
@@ -44,6 +44,7 @@ struct MatchReserveParams {
   int32_t* unit_status;   // workspace [units]
   int32_t* miss_count;    // workspace [units]
   int2* misses;           // workspace [units][ucap]: (slot, id) in miss order
+  uint8_t* fetch;         // workspace [units][T][k]: row to transfer with this token
   uint32_t* err_word;
   int64_t t;
   int32_t S, N, T, k, ucap, table_cap, log_table_cap, ubits, policy, L, B, nbins;
@@ -56,18 +57,24 @@ struct GatherParams {
   uint4* buf_kv;
   int64_t N, S;
   int32_t units, ucap, row16;
+  int32_t per_unit;       // 1: workgroup u copies unit u's rows (request-level)
 };
 
 struct AttnParams {
   const int32_t* sel_slot;    // [units][T][k]
+  const int32_t* sel;         // [units][T][k] selected ids
+  const uint8_t* fetch;       // [units][T][k] or null: rows to read from host and store
+  const uint16_t* host_kv;    // device-visible address of the pinned host rows
+  int64_t N;
   const int32_t* unit_status; // [units]
   const uint16_t* q;          // [B][T][Hq][dqk]
-  const uint16_t* buf_kv;     // [units][S][row]
+  uint16_t* buf_kv;           // [units][S][row]
   float* out;                 // [B][T][Hq][dv]
   float* partials;            // [units*T][nsplit][G][dv + 2]
   uint32_t* counters;         // [units*T]
   int64_t S;
   int32_t units, Hkv, Hq, T, k, tpe, row_elems, nsplit, split_rows;
+  int32_t token;              // query token of this launch
   float scale_log2e;
 };
 

@@ -10,7 +10,8 @@
 //
 // gfx950 mapping: every workgroup reads the per-unit miss counts written by
 // match_reserve (no host round trip), forms their prefix sum in LDS, and
-// takes an equal share of the global list of 16-byte pieces of missed rows.
+// takes an equal share of the global list of 16-byte pieces of missed rows
+// (or, in the request-level mode kept for comparison, one unit's rows).
 // Each lane issues several 16-byte loads from host memory before storing
 // them, so thousands of PCIe reads are in flight across the chip; a wave
 // reads 1 KiB of consecutive row bytes per instruction.
@@ -57,8 +58,16 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherParams p) 
   const uint32_t rows = (uint32_t)sPre[units];
   const uint32_t row16 = (uint32_t)p.row16;
   const uint64_t pieces = (uint64_t)rows * row16;
-  const uint32_t c0 = (uint32_t)(pieces * blockIdx.x / gridDim.x);
-  const uint32_t c1 = (uint32_t)(pieces * (blockIdx.x + 1) / gridDim.x);
+  uint32_t c0, c1;
+  if (p.per_unit) {
+    // request-level assignment: workgroup u copies exactly unit u's rows
+    c0 = (uint32_t)sPre[blockIdx.x] * row16;
+    c1 = (uint32_t)sPre[blockIdx.x + 1] * row16;
+  } else {
+    // equal shares of the global list of row pieces
+    c0 = (uint32_t)(pieces * blockIdx.x / gridDim.x);
+    c1 = (uint32_t)(pieces * (blockIdx.x + 1) / gridDim.x);
+  }
 
   int cur_unit = 0;
   for (uint32_t c = c0 + tid; c < c1; c += kGatherThreads * kUnroll) {

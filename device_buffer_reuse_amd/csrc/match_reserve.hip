@@ -37,6 +37,7 @@ namespace avsg {
 namespace {
 
 constexpr int kInvalid = -2;  // slot beyond S in this lane's range
+constexpr int kDupFlag = 1 << 30;  // token-1 entry also selected by token 0
 
 __device__ __forceinline__ uint32_t hash_id(int32_t id, int log_cap) {
   return ((uint32_t)id * 0x9E3779B1u) >> (32 - log_cap);
@@ -92,16 +93,20 @@ __device__ __forceinline__ int hash_find(const int32_t* sHash, int log_cap, int 
                                          int32_t x) {
   const int bmask = ((1 << log_cap) >> 2) - 1;
   uint32_t hb = hash_id(x, log_cap) >> 2;
-  const uint32_t umask = (1u << ubits) - 1;
+  const int umask = (1 << ubits) - 1;
+  int found = -1;
   while (true) {
+    // an empty cell (-1) shifts to -1, which never equals an id
     const int4 c = reinterpret_cast<const int4*>(sHash)[hb];
-    if (c.x != kEmpty && (c.x >> ubits) == x) return c.x & umask;
-    if (c.y != kEmpty && (c.y >> ubits) == x) return c.y & umask;
-    if (c.z != kEmpty && (c.z >> ubits) == x) return c.z & umask;
-    if (c.w != kEmpty && (c.w >> ubits) == x) return c.w & umask;
-    if ((c.x == kEmpty) | (c.y == kEmpty) | (c.z == kEmpty) | (c.w == kEmpty)) return -1;
+    found = ((c.x >> ubits) == x) ? (c.x & umask) : found;
+    found = ((c.y >> ubits) == x) ? (c.y & umask) : found;
+    found = ((c.z >> ubits) == x) ? (c.z & umask) : found;
+    found = ((c.w >> ubits) == x) ? (c.w & umask) : found;
+    const bool any_empty = (c.x == kEmpty) | (c.y == kEmpty) | (c.z == kEmpty) | (c.w == kEmpty);
+    if (found >= 0 || any_empty) break;
     hb = (hb + 1) & bmask;
   }
+  return found;
 }
 
 __device__ __forceinline__ void hash_insert(int32_t* sHash, int log_cap, int ubits, int32_t x,
@@ -233,8 +238,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         const int32_t b = Bl[j];
         const int la = lower_bound_lds(A, k, b);
         const int pos = la + j - sDup[la];
+        const bool dup = la < k && A[la] == b;
         sU[pos] = b;  // a duplicate writes the same value at the same position
-        sMap[k + j] = pos;
+        sMap[k + j] = pos | (dup ? kDupFlag : 0);
       }
     }
     __syncthreads();
@@ -248,6 +254,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   __syncthreads();
 
   // ---- 4. every slot probes its resident id; state checks
+  int hit_i[MAXP];
   if (sMisc[0] == 0) {
     int bad = 0;
 #pragma unroll
@@ -255,6 +262,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       const int s = s0 + q * 64 + lane;
       const int32_t x = tok[q];
       bin[q] = kInvalid;
+      hit_i[q] = -1;
       if (x == kInvalid) continue;
       bin[q] = 0;
       if (x < -1 || x >= N) {
@@ -265,11 +273,17 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
         const int i = hash_find(sHash, log_cap, ubits, x);
         if (i >= 0) {
-          if (atomicCAS(&sUslot[i], -1, s) != -1) bad = 1;  // id of U held by two slots
-          bin[q] = -1;                                       // hit
+          sUslot[i] = s;
+          hit_i[q] = i;
+          bin[q] = -1;  // hit
         }
       }
     }
+    __syncthreads();
+    // an id of U held by two slots: only one of the two stores survived
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q)
+      if (hit_i[q] >= 0 && sUslot[hit_i[q]] != s0 + q * 64 + lane) bad = 1;
     if (bad) atomicOr(&sMisc[0], kFlagState);
   }
   __syncthreads();
@@ -280,6 +294,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     for (int i = tid; i < tk; i += kMRThreads) {
       p.sel_slot[(size_t)u * tk + i] = -1;
       p.hit_flag[(size_t)u * tk + i] = 0;
+      p.fetch[(size_t)u * tk + i] = 0;
     }
     if (tid == 0) {
       p.n_hit[u] = 0;
@@ -414,10 +429,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 
   // ---- 9. per-(token, entry) outputs read off the union
   for (int i = tid; i < tk; i += kMRThreads) {
-    const int ui = (T == 1) ? i : sMap[i];
-    const int v = sUslot[ui];
+    const int mi = (T == 1) ? i : sMap[i];
+    const int v = sUslot[mi & ~kDupFlag];
+    const bool miss = (v & kMissFlag) != 0;
     p.sel_slot[(size_t)u * tk + i] = v & ~kMissFlag;
-    p.hit_flag[(size_t)u * tk + i] = (v & kMissFlag) ? 0 : 1;
+    p.hit_flag[(size_t)u * tk + i] = miss ? 0 : 1;
+    // the row is transferred by the first token that selects it
+    p.fetch[(size_t)u * tk + i] = (miss && !(mi & kDupFlag)) ? 1 : 0;
   }
   if (tid == 0) {
     p.n_hit[u] = nu - m;

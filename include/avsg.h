@@ -179,6 +179,23 @@ avsg_status avsg_host_free(void* host_ptr);
 /* Static string naming a status. */
 const char* avsg_status_string(avsg_status s);
 
+/* How missed rows reach the buffer.
+ *  AVSG_TRANSFER_FUSED (default): the attention workgroup that consumes a
+ *    missed row reads it from pinned host memory and stores it into its slot,
+ *    so host transfers overlap the HBM reads of the hits; the rows are spread
+ *    over all workgroups in selection order.
+ *  AVSG_TRANSFER_BALANCED: a separate kernel copies the global list of missed
+ *    rows, split into equal shares over all workgroups, before attention.
+ *  AVSG_TRANSFER_PER_UNIT: like BALANCED, but each unit's rows are copied by
+ *    one workgroup (request-level assignment; kept for comparison).
+ * Results are identical in every mode. */
+typedef enum avsg_transfer_mode {
+  AVSG_TRANSFER_FUSED = 0,
+  AVSG_TRANSFER_BALANCED = 1,
+  AVSG_TRANSFER_PER_UNIT = 2
+} avsg_transfer_mode;
+avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode);
+
 /* Number of split-k partitions the attention of one (unit, token) uses. */
 int32_t avsg_attn_splits(const avsg_ctx* ctx);
 

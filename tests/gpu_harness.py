@@ -42,7 +42,7 @@ def check_attention(got, ref, what=""):
 class Runner:
     """GPU state + oracle state for one workload."""
 
-    def __init__(self, w, host=None, track_buf=True, attn_units=None):
+    def __init__(self, w, host=None, track_buf=True, attn_units=None, mode=None):
         import torch
         self.torch = torch
         avsg = ensure_lib()
@@ -50,6 +50,8 @@ class Runner:
         self.w = w
         self.cfg = avsg.config_from_workload(w)
         self.ctx = avsg.Context(self.cfg)
+        if mode is not None:
+            self.ctx.set_transfer_mode(mode)
         self.st = avsg.State(self.cfg)
         self.ctx.reset(self.st.slot_table, self.st.lifetimes)
         if host is None:

@@ -63,12 +63,14 @@ def test_status_strings():
 
 
 def test_workspace_sizes_match_layout():
-    """Workspace holds per-unit miss lists (8 B per union capacity), split
-    partials and a few words; its size follows the config."""
+    """Workspace holds per-unit miss lists (8 B per union capacity), a fetch
+    flag per selected entry, split partials and a few words; its size follows
+    the config."""
     avsg = _lib()
     w = tg.WORKLOADS[2]
     c = avsg.config_from_workload(w)
     ws = avsg.avsg_workspace_bytes(c)
     misses = 8 * w.units * min(w.k * w.n_q_tokens, w.n_slots)
     partials = 4 * w.units * 16 * 4 * 130
-    assert misses + partials <= ws <= misses + partials + 8 * 1024
+    fetch = w.units * w.n_q_tokens * w.k
+    assert misses + partials + fetch <= ws <= misses + partials + fetch + 8 * 1024

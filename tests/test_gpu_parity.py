@@ -49,6 +49,22 @@ def test_parity_small(name):
         run.close()
 
 
+@pytest.mark.parametrize("name", ["batch_ragged", "mtp_ragged", "long_ragged"])
+@pytest.mark.parametrize("transfer", [1, 2])
+def test_parity_transfer_modes(name, transfer):
+    """The separate gather kernel (balanced shares, or one workgroup per unit)
+    gives the same state, buffer bytes and outputs as the fused default."""
+    w = SMALL[name].replace(steps=6)
+    say("[parity] %s transfer mode %d" % (name, transfer))
+    sel = tg.selections(w)
+    run = Runner(w, mode=transfer)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("mode", ["allhit", "allmiss"])
 def test_parity_trace_modes(mode):
     w = SMALL["batch_ragged"].replace(n_entries=6000, steps=8)
