@@ -50,7 +50,7 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   while ((1 << d->ubits) < ws->ucap) ++d->ubits;
   const int64_t rows = (int64_t)c.k * c.tokens_per_entry;
   if (c.kv_layout == AVSG_KV_LATENT) {
-    ws->split_rows = 256;
+    ws->split_rows = 512;  // one 8-wave workgroup per CU for 64 requests
   } else {
     ws->split_rows = 128;  // one workgroup of the split-layout attention
   }
@@ -105,8 +105,7 @@ static avsg_status check_config_impl(const avsg_config* c) {
   } else {
     if (c->tokens_per_entry != 1 || c->n_kv_heads != 1) return AVSG_ERR_INVALID_ARG;
     if (c->head_dim_qk != 576 || c->head_dim_v != 512) return AVSG_ERR_UNSUPPORTED;
-    if (c->n_q_heads % 64 != 0) return AVSG_ERR_UNSUPPORTED;
-    return AVSG_ERR_UNSUPPORTED;  // latent attention kernel not built yet
+    if (c->n_q_heads != 64 && c->n_q_heads != 128) return AVSG_ERR_UNSUPPORTED;
   }
   WsLayout ws;
   Derived d;
@@ -171,6 +170,10 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   }
   if ((int64_t)c->d.mr_lds > lds_max) { delete c; return AVSG_ERR_UNSUPPORTED; }
   if (c->d.mr_lds > 64 * 1024 && match_reserve_set_lds(c->d.mr_lds) != hipSuccess) {
+    delete c;
+    return AVSG_ERR_HIP;
+  }
+  if (cfg->kv_layout == AVSG_KV_LATENT && attn_latent_set_lds() != hipSuccess) {
     delete c;
     return AVSG_ERR_HIP;
   }

@@ -18,9 +18,9 @@
 //    16 partial sums of a row are added by four DPP steps inside the row.
 //  * Scores go to LDS; one wave per head takes the split's maximum and the
 //    exp2 weights; p * v accumulates in fp32 from the V halves in registers.
-//  * Split partials (max, sum, o) go to the workspace and a second small
-//    kernel merges them in split order, so the result does not depend on
-//    workgroup timing.  (Merging inside the last workgroup of each (unit,
+//  * Split partials (max, sum, o) go to the workspace and the combine kernel
+//    merges them in split order, so the result does not depend on workgroup
+//    timing.  (Merging inside the last workgroup of each (unit,
 //    token) needs an agent-scope release in every workgroup, which writes
 //    back the XCD's L2 each time and cost more than the extra launch.)
 #include "avsg_internal.h"
@@ -235,53 +235,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
   }
 }
 
-// Merge of the split partials of each (unit, token) in split order:
-// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
-template <int G>
-__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnParams p) {
-  extern __shared__ float sWt[];  // [nsplit][G] weights 2^(m_s - M) / L
-  __shared__ float sML[2][G];
-  const int uj = blockIdx.x;
-  const int u = uj / p.T, j = uj - u * p.T;
-  const int b = u / p.Hkv, g = u - b * p.Hkv;
-  const int nsplit = p.nsplit, tid = threadIdx.x;
-  const size_t part_stride = (size_t)G * (kD + 2);
-  const float* pbase = p.partials + (size_t)uj * nsplit * part_stride;
-  float* orow = p.out + (((size_t)b * p.T + j) * p.Hq + g * G) * kD;
-  if (p.unit_status[u] != 0) {
-    for (int idx = tid; idx < G * kD; idx += kAttnThreads) orow[idx] = 0.f;
-    return;
-  }
-  for (int i = tid; i < nsplit * G; i += kAttnThreads) {
-    const int s = i / G, h = i - s * G;
-    sWt[i] = pbase[s * part_stride + G * kD + h];
-  }
-  __syncthreads();
-  if (tid < G) {
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, sWt[s * G + tid]);
-    float lsum = 0.f;
-    for (int s = 0; s < nsplit; ++s)
-      lsum = fmaf(pbase[s * part_stride + G * kD + G + tid],
-                  __builtin_amdgcn_exp2f(sWt[s * G + tid] - mx), lsum);
-    sML[0][tid] = mx;
-    sML[1][tid] = 1.f / lsum;
-  }
-  __syncthreads();
-  for (int i = tid; i < nsplit * G; i += kAttnThreads) {
-    const int h = i % G;
-    sWt[i] = __builtin_amdgcn_exp2f(sWt[i] - sML[0][h]) * sML[1][h];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += kAttnThreads) {
-    const int h = idx / kD;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) acc = fmaf(pbase[s * part_stride + idx], sWt[s * G + h], acc);
-    orow[idx] = acc;
-  }
-}
-
 }  // namespace
 
 template <int G>
@@ -297,10 +250,7 @@ static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (p.nsplit == 1) return hipSuccess;
-  const size_t lds = sizeof(float) * (size_t)p.nsplit * G;
-  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3((unsigned)(p.units * p.T)), dim3(kAttnThreads),
-                     lds, s, p);
-  return hipGetLastError();
+  return launch_attn_combine(p0, G, kD, s);
 }
 
 hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s) {

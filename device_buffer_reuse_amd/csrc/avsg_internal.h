@@ -82,6 +82,8 @@ hipError_t launch_match_reserve(const MatchReserveParams& p, int units, size_t l
 hipError_t launch_gather(const GatherParams& p, int grid, hipStream_t s);
 hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s);
 hipError_t launch_attn_latent(const AttnParams& p, int dqk, int dv, hipStream_t s);
+hipError_t launch_attn_combine(const AttnParams& p, int G, int D, hipStream_t s);
+hipError_t attn_latent_set_lds();
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_validate(const int32_t* slot_table, const int32_t* lifetimes, int units, int S,
                            int N, int policy, int L, int64_t t, uint32_t* err, hipStream_t s);

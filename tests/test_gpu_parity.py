@@ -32,6 +32,11 @@ SMALL = {
                                        n_slots=2, steps=10, overlap=0.0),
     "slots_16k": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=40000,
                                          k=4000, n_slots=16384, steps=6),
+    "mla_ragged": tg.WORKLOADS[5].replace(batch=3, n_entries=5003, k=700, n_slots=1500, steps=8),
+    "mla_h64_short": tg.WORKLOADS[5].replace(batch=2, n_q_heads=64, n_entries=3000, k=45,
+                                             n_slots=200, steps=8),
+    "mla_mtp": tg.WORKLOADS[5].replace(batch=2, n_q_tokens=2, overlap_shared=0.5, n_entries=5003,
+                                       k=600, n_slots=1300, steps=6),
 }
 
 
@@ -49,7 +54,7 @@ def test_parity_small(name):
         run.close()
 
 
-@pytest.mark.parametrize("name", ["batch_ragged", "mtp_ragged", "long_ragged"])
+@pytest.mark.parametrize("name", ["batch_ragged", "mtp_ragged", "long_ragged", "mla_ragged"])
 @pytest.mark.parametrize("transfer", [1, 2])
 def test_parity_transfer_modes(name, transfer):
     """The separate gather kernel (balanced shares, or one workgroup per unit)
@@ -82,7 +87,7 @@ def test_parity_trace_modes(mode):
         run.close()
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
 def test_parity_full_size(cid):
     """Full workload shapes, every step: all state bit-exact, attention of a
     sample of units against the oracle, buffer bytes at the end."""
