@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 HOST_LINK_GBS = 64.0        # PCIe 5.0 x16, one direction
+MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix cores
+FP32_VALU_TFLOPS = 157.3    # fp32 vector ALU
 
 
 def parse():
@@ -41,6 +43,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extra", action="store_true", help="skip all-hit / all-miss passes")
+    ap.add_argument("--trace", default="natural", choices=["natural", "allhit", "allmiss"],
+                    help="selection trace of the timed steps (default natural)")
+    ap.add_argument("--transfer", type=int, default=0,
+                    help="0 fused (default), 1 balanced gather kernel, 2 per-unit gather kernel")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
     return ap.parse_args()
@@ -129,6 +135,39 @@ def match_bytes(w, misses_per_step):
     return tk * 4 + w.units * w.n_slots * 4 * 3 + tk * 5 + misses_per_step * (4 + 8)
 
 
+KERNEL_SOURCES = {"attention": ("attn_split_kernel<4>", ["attn_split.hip", "avsg_internal.h"]),
+                  "match_reserve": ("match_reserve_kernel<8>", ["match_reserve.hip", "avsg_internal.h"])}
+
+
+def counter_traffic(kernel, trace):
+    """HBM bytes per launch (reads + writes) of `kernel` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the batch workload, scaled by
+    the plain-copy calibration; None if the summary lacks that trace or the
+    kernel's source changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "counters_batch.md")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    name, files = KERNEL_SOURCES[kernel]
+    k = data["kernels"].get(name)
+    if not k:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "device_buffer_reuse_amd", "csrc", f), "rb").read())
+    if h.hexdigest()[:16] != k["source_sha256_16"]:
+        return None
+    r, wr = k.get("read_bytes_" + trace), k.get("write_bytes_" + trace)
+    if r is None or wr is None:
+        return None
+    return int(r + wr)
+
+
 def cpu_baseline(w, t_start, seconds):
     """The oracle (state machine + float64 attention) on the same workload,
     from step t_start on, until `seconds` have elapsed."""
@@ -178,8 +217,9 @@ def main():
     entries = w.entries_per_step
     row_bytes = w.row_bytes
 
-    # ---- natural trace: value
-    b.load_trace("natural", total)
+    b.ctx.set_transfer_mode(a.transfer)
+    # ---- the timed trace (natural by default): value
+    b.load_trace(a.trace, total)
     b.reset()
     b.run(0, W)
     ms, _ = b.timed(W, W + K)
@@ -198,32 +238,41 @@ def main():
     union_per_step = (n_hit + n_miss) / K
 
     per = {"match_reserve": kern[0] / K, "gather": kern[1] / K, "attention": kern[2] / K}
+    fused = a.transfer == 0
+    host_b = miss_per_step * row_bytes          # bytes over the host link per step
     ab = attn_bytes(w)
-    att_gbs = ab / (per["attention"] * 1e-3) / 1e9
-    gat_gbs = miss_per_step * row_bytes / (per["gather"] * 1e-3) / 1e9
-    mr_gbs = match_bytes(w, miss_per_step) / (per["match_reserve"] * 1e-3) / 1e9
-    dominant = max(per, key=per.get)
-    if dominant == "gather":
-        roof = {"bound": "host-link", "achieved": round(gat_gbs, 2), "peak": HOST_LINK_GBS,
-                "unit": "GB/s", "frac": round(gat_gbs / HOST_LINK_GBS, 4), "traffic": None,
-                "kernel": "gather", "bytes_per_launch": int(miss_per_step * row_bytes)}
-    elif dominant == "attention":
-        roof = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "attention", "bytes_per_launch": ab}
-    else:
-        roof = {"bound": "hbm", "achieved": round(mr_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(mr_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "match_reserve", "bytes_per_launch": int(match_bytes(w, miss_per_step))}
-
-    kernels = {
-        "match_reserve": {"us": round(per["match_reserve"] * 1e3, 2), "GB/s": round(mr_gbs, 1)},
-        "gather": {"us": round(per["gather"] * 1e3, 2), "host_GB/s": round(gat_gbs, 2),
-                   "host_link_frac": round(gat_gbs / HOST_LINK_GBS, 4)},
-        "attention": {"us": round(per["attention"] * 1e3, 2), "GB/s": round(att_gbs, 1),
-                      "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4),
-                      "TFLOP/s": round(attn_flops(w) / (per["attention"] * 1e-3) / 1e12, 2)},
+    # per kernel: algorithmic bytes (HBM / host link) and flops of one launch
+    use = {
+        "match_reserve": {"hbm": match_bytes(w, miss_per_step), "host": 0.0, "flop": 0.0},
+        "gather": {"hbm": 0.0 if fused else host_b, "host": 0.0 if fused else host_b, "flop": 0.0},
+        "attention": {"hbm": ab + (host_b if fused else 0.0), "host": host_b if fused else 0.0,
+                      "flop": float(attn_flops(w))},
     }
+    peaks = {"hbm": (HBM_PEAK_GBS, "GB/s", 1e9), "host": (HOST_LINK_GBS, "GB/s", 1e9),
+             "flop": (MFMA_BF16_TFLOPS if w.latent else FP32_VALU_TFLOPS, "TFLOP/s", 1e12)}
+    kernels = {}
+    for name, u in use.items():
+        t = per[name] * 1e-3
+        d = {"us": round(per[name] * 1e3, 2)}
+        for res, (pk, unit, scale) in peaks.items():
+            if u[res] > 0 and t > 0:
+                ach = u[res] / t / scale
+                d[res + "_" + unit] = round(ach, 2)
+                d[res + "_frac"] = round(ach / pk, 4)
+        kernels[name] = d
+    dominant = max(per, key=per.get)
+    du = use[dominant]
+    best = max((r for r in ("hbm", "host", "flop") if du[r] > 0),
+               key=lambda r: du[r] / (per[dominant] * 1e-3) / peaks[r][2] / peaks[r][0])
+    pk, unit, scale = peaks[best]
+    ach = du[best] / (per[dominant] * 1e-3) / scale
+    roof = {"bound": {"hbm": "hbm", "host": "host-link",
+                      "flop": "mfma" if w.latent else "alu"}[best],
+            "achieved": round(ach, 2), "peak": pk, "unit": unit, "frac": round(ach / pk, 4),
+            "traffic": (counter_traffic(dominant, a.trace)
+                        if w.name == "batch" and a.transfer == 0 else None),
+            "kernel": dominant,
+            "per_launch": int(du[best]) if best != "flop" else du[best]}
 
     extra = {}
     if not a.no_extra:
@@ -248,13 +297,16 @@ def main():
         b.run(0, 4)
         ms_m, km = b.timed(4, nm + 4, profile=True)
         mb = w.units * w.n_q_tokens * w.k * row_bytes
+        kt = km[2] if fused else km[1]   # kernel that carries the host transfer
         extra["all_miss"] = {
             "steps": nm, "ms_per_step": round(ms_m / nm, 4),
             "host_bytes_per_step": mb,
             "step_host_GB/s": round(mb / (ms_m / nm * 1e-3) / 1e9, 2),
-            "gather_us": round(km[1] / nm * 1e3, 2),
-            "gather_host_GB/s": round(mb / (km[1] / nm * 1e-3) / 1e9, 2),
-            "gather_host_link_frac": round(mb / (km[1] / nm * 1e-3) / 1e9 / HOST_LINK_GBS, 4)}
+            "step_host_link_frac": round(mb / (ms_m / nm * 1e-3) / 1e9 / HOST_LINK_GBS, 4),
+            "transfer_kernel": "attention" if fused else "gather",
+            "transfer_kernel_us": round(kt / nm * 1e3, 2),
+            "transfer_kernel_host_GB/s": round(mb / (kt / nm * 1e-3) / 1e9, 2),
+            "transfer_kernel_host_link_frac": round(mb / (kt / nm * 1e-3) / 1e9 / HOST_LINK_GBS, 4)}
         assert b.ctx.last_error() == 0
         # pinned hipMemcpy host->device peak, for context
         n = 256 << 20
@@ -290,7 +342,9 @@ def main():
                    "head_dim_v": w.head_dim_v, "context_entries": w.n_entries,
                    "tokens_per_entry": w.tokens_per_entry, "k": w.k, "slots": w.n_slots,
                    "policy": w.policy, "lifetime_L": w.lifetime_L, "buckets": w.n_buckets,
-                   "trace": "natural: %.0f%% overlap + Zipf(%.1f) tail" % (100 * w.overlap, w.zipf_s),
+                   "trace": ("natural: %.0f%% overlap + Zipf(%.1f) tail" % (100 * w.overlap, w.zipf_s)
+                             if a.trace == "natural" else a.trace),
+                   "transfer": ["fused", "balanced", "per-unit"][a.transfer],
                    "entries_per_step": entries},
         "hit_rate": round(n_hit / max(n_hit + n_miss, 1), 5),
         "miss_rows_per_step": round(miss_per_step, 1),
