@@ -50,7 +50,7 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   while ((1 << d->ubits) < ws->ucap) ++d->ubits;
   const int64_t rows = (int64_t)c.k * c.tokens_per_entry;
   if (c.kv_layout == AVSG_KV_LATENT) {
-    ws->split_rows = 512;  // one 8-wave workgroup per CU for 64 requests
+    ws->split_rows = 512;  // 4 splits: one 8-wave workgroup per CU for 64 requests
   } else {
     ws->split_rows = 128;  // one workgroup of the split-layout attention
   }

@@ -176,7 +176,12 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 1; i < 8; ++i) cm = fmaxf(cm, sv[i]);
     cm = xor_max(xor_max(cm, 16), 32);
-    const float m_new = fmaxf(m_run, cm);
+    // lazy rescaling: the reference maximum only moves when the chunk's
+    // maximum exceeds it by more than 8 (log2 units), so the weights stay
+    // below 2^8 and the accumulators are rescaled rarely; the result does not
+    // depend on which reference is used
+    const bool move = cm > m_run + 8.f;
+    const float m_new = move ? cm : m_run;
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
     float ps = 0.f;
     bf16x8 phi, plo;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
     ps += __shfl_xor(ps, 32, 64);
     l_run = l_run * corr + ps;
     m_run = m_new;
-    if (__ballot(corr != 1.f)) {
+    if (__ballot(move)) {
 #pragma unroll
       for (int t = 0; t < kMTiles; ++t) acc[t] *= corr;
     }

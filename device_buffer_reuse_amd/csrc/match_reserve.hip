@@ -109,6 +109,19 @@ __device__ __forceinline__ int hash_find(const int32_t* sHash, int log_cap, int 
   return found;
 }
 
+// Looks for x in one fetched bucket: returns the union index, -1 if the
+// bucket has an empty cell (x is absent), or -2 if the search must go on.
+__device__ __forceinline__ int bucket_check(const int4 c, int ubits, int32_t x) {
+  const int umask = (1 << ubits) - 1;
+  int found = -1;
+  found = ((c.x >> ubits) == x) ? (c.x & umask) : found;
+  found = ((c.y >> ubits) == x) ? (c.y & umask) : found;
+  found = ((c.z >> ubits) == x) ? (c.z & umask) : found;
+  found = ((c.w >> ubits) == x) ? (c.w & umask) : found;
+  const int lo = min(min(c.x, c.y), min(c.z, c.w));  // -1 iff a cell is empty
+  return (found >= 0 || lo < 0) ? found : -2;
+}
+
 __device__ __forceinline__ void hash_insert(int32_t* sHash, int log_cap, int ubits, int32_t x,
                                             int32_t i) {
   const int cmask = (1 << log_cap) - 1;
@@ -257,23 +270,44 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   int hit_i[MAXP];
   if (sMisc[0] == 0) {
     int bad = 0;
+    const int bmask = (C >> 2) - 1;
+    // state checks, and the first bucket of every probe of a group of 4
+    // slots read together so their LDS latencies overlap
 #pragma unroll
-    for (int q = 0; q < MAXP; ++q) {
-      const int s = s0 + q * 64 + lane;
-      const int32_t x = tok[q];
-      bin[q] = kInvalid;
-      hit_i[q] = -1;
-      if (x == kInvalid) continue;
-      bin[q] = 0;
-      if (x < -1 || x >= N) {
-        bad = 1;
-      } else if (x >= 0) {
-        const int32_t l = lf[q];
-        if (!lru && (l < 0 || l > p.L)) bad = 1;
-        if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
-        const int i = hash_find(sHash, log_cap, ubits, x);
+    for (int q0 = 0; q0 < MAXP; q0 += 4) {
+      int4 cb[4];
+      bool probe[4];
+#pragma unroll
+      for (int qq = 0; qq < 4 && q0 + qq < MAXP; ++qq) {
+        const int q = q0 + qq;
+        const int32_t x = tok[q];
+        bin[q] = kInvalid;
+        hit_i[q] = -1;
+        probe[qq] = false;
+        if (x == kInvalid) continue;
+        bin[q] = 0;
+        if (x < -1 || x >= N) {
+          bad = 1;
+        } else if (x >= 0) {
+          const int32_t l = lf[q];
+          if (!lru && (l < 0 || l > p.L)) bad = 1;
+          if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
+          probe[qq] = true;
+          cb[qq] = reinterpret_cast<const int4*>(sHash)[hash_id(x, log_cap) >> 2];
+        }
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4 && q0 + qq < MAXP; ++qq) {
+        const int q = q0 + qq;
+        if (!probe[qq]) continue;
+        int i = bucket_check(cb[qq], ubits, tok[q]);
+        if (i == -2) {  // full first bucket: continue in the following ones
+          uint32_t hb = ((hash_id(tok[q], log_cap) >> 2) + 1) & bmask;
+          while ((i = bucket_check(reinterpret_cast<const int4*>(sHash)[hb], ubits, tok[q])) == -2)
+            hb = (hb + 1) & bmask;
+        }
         if (i >= 0) {
-          sUslot[i] = s;
+          sUslot[i] = s0 + q * 64 + lane;
           hit_i[q] = i;
           bin[q] = -1;  // hit
         }
@@ -345,12 +379,14 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) changed[q] = false;
   if (m > 0) {
-    // per-wave histogram of the candidates' bins
-    for (int b = lane; b < nbins; b += 64) sCnt[w * nbins + b] = 0;
-    __syncthreads();
+    // per-wave histogram of the candidates' bins: one ballot per (bin, slot
+    // group), counted on the scalar unit; no LDS atomics
+    for (int b = 0; b < nbins; ++b) {
+      int cnt = 0;
 #pragma unroll
-    for (int q = 0; q < MAXP; ++q)
-      if (bin[q] >= 0) atomicAdd(&sCnt[w * nbins + bin[q]], 1);
+      for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
+      if (lane == 0) sCnt[w * nbins + b] = cnt;
+    }
     __syncthreads();
     // bin totals, their exclusive starts, and the threshold bin b* holding
     // the m-th candidate (nbins <= 128 <= threads)
@@ -373,27 +409,17 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       for (int x = 0; x < v; ++x) off += sCnt[x * nbins + b];
       sOff[v * nbins + b] = off;
     }
-    // rank of each candidate in bins <= b* among the wave's candidates of the
-    // same bin, in slot order; the running count of bin b lives in lane b
-    // (b < 64) or lane b - 64 (64 <= b < 128) of cntA / cntB
-    int cntA = 0, cntB = 0;
+    // rank of each candidate in bins <= b* among the wave's candidates of
+    // the same bin, in slot order (slot groups in order, lanes in order)
 #pragma unroll
-    for (int q = 0; q < MAXP; ++q) {
-      const bool act = bin[q] >= 0 && bin[q] <= bstar;
-      rank[q] = 0;
-      uint64_t pend = __ballot(act);
-      while (pend) {
-        const int lead = __builtin_ctzll(pend);
-        const int b = __builtin_amdgcn_readlane(bin[q], lead);
-        const bool mine = act && bin[q] == b;
-        const uint64_t grp = __ballot(mine);
-        const int base = b < 64 ? __builtin_amdgcn_readlane(cntA, b)
-                                : __builtin_amdgcn_readlane(cntB, b - 64);
-        if (mine) rank[q] = base + mbcnt64(grp);
-        const int add = __popcll(grp);
-        if (b < 64) cntA += (lane == b) ? add : 0;
-        else cntB += (lane == b - 64) ? add : 0;
-        pend &= ~grp;
+    for (int q = 0; q < MAXP; ++q) rank[q] = 0;
+    for (int b = 0; b <= bstar; ++b) {
+      int run = 0;
+#pragma unroll
+      for (int q = 0; q < MAXP; ++q) {
+        const uint64_t grp = __ballot(bin[q] == b);
+        if (bin[q] == b) rank[q] = run + mbcnt64(grp);
+        run += __popcll(grp);
       }
     }
     __syncthreads();
