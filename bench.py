@@ -43,10 +43,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extra", action="store_true", help="skip all-hit / all-miss passes")
-    ap.add_argument("--trace", default="natural", choices=["natural", "allhit", "allmiss"],
+    ap.add_argument("--trace", default="natural", choices=["natural", "allhit", "allmiss", "skewed"],
                     help="selection trace of the timed steps (default natural)")
     ap.add_argument("--transfer", type=int, default=0,
                     help="0 fused (default), 1 balanced gather kernel, 2 per-unit gather kernel")
+    ap.add_argument("--ablations", action="store_true",
+                    help="also compare transfer modes on a skewed-miss trace and hash vs "
+                         "dual-pointer matching")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
     return ap.parse_args()
@@ -166,6 +169,45 @@ def counter_traffic(kernel, trace):
     if r is None or wr is None:
         return None
     return int(r + wr)
+
+
+def ablations(b, w, n):
+    """Comparisons the AVSG abstract reports, reproduced in kind on this GPU:
+    (1) transfers spread over all workgroups vs assigned per unit, on a trace
+    where every 8th unit misses everything and the others hit everything;
+    (2) vectorised hash matching vs the scalar dual-pointer baseline (kernel
+    time of match_reserve on the natural trace)."""
+    out = {}
+    skew = {}
+    b.load_trace("skewed", n + 2)
+    for mode, name in ((0, "fused"), (1, "balanced"), (2, "per-unit")):
+        b.ctx.set_transfer_mode(mode)
+        b.reset()
+        b.run(0, 2)
+        ms, kern = b.timed(2, n + 2, profile=True)
+        units_missing = (w.units + 7) // 8
+        host_b = units_missing * w.n_q_tokens * w.k * w.row_bytes
+        kt = kern[2] if mode == 0 else kern[1]
+        skew[name] = {"ms_per_step": round(ms / n, 4),
+                      "transfer_kernel_us": round(kt / n * 1e3, 2),
+                      "effective_host_GB/s": round(host_b / (kt / n * 1e-3) / 1e9, 2)}
+    b.ctx.set_transfer_mode(0)
+    out["skewed_transfer"] = skew
+    match = {}
+    b.load_trace("natural", n + 16)
+    for mode, name in ((0, "hash"), (1, "dual_pointer")):
+        b.ctx.set_match_mode(mode)
+        b.reset()
+        b.run(0, 16)
+        ms, kern = b.timed(16, n + 16, profile=True)
+        match[name] = {"match_reserve_us": round(kern[0] / n * 1e3, 2),
+                       "ms_per_step": round(ms / n, 4)}
+    b.ctx.set_match_mode(0)
+    match["speedup"] = round(match["dual_pointer"]["match_reserve_us"] /
+                             match["hash"]["match_reserve_us"], 2)
+    out["matching"] = match
+    assert b.ctx.last_error() == 0
+    return out
 
 
 def cpu_baseline(w, t_start, seconds):
@@ -321,6 +363,8 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         extra["pinned_memcpy_h2d_GB/s"] = round(4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
+    if a.ablations:
+        extra["ablations"] = ablations(b, w, min(K, 32))
     if a.calibrate_copy:
         x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         y = torch.empty_like(x)

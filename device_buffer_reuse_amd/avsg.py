@@ -24,12 +24,13 @@ KV_SPLIT, KV_LATENT = 0, 1
 POLICY_LIFETIME, POLICY_BUCKET_LRU = 0, 1
 HOST_COHERENT = 1
 TRANSFER_FUSED, TRANSFER_BALANCED, TRANSFER_PER_UNIT = 0, 1, 2
+MATCH_HASH, MATCH_MERGE = 0, 1
 
 EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_set_stream",
             "avsg_destroy", "avsg_reset", "avsg_step", "avsg_last_error", "avsg_validate_state",
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
-            "avsg_set_transfer_mode"]
+            "avsg_set_transfer_mode", "avsg_set_match_mode"]
 
 
 class AvsgError(RuntimeError):
@@ -85,6 +86,7 @@ def load():
         "avsg_attn_splits": ([p], ctypes.c_int32),
         "avsg_profile_begin": ([p, ctypes.c_int32], i32),
         "avsg_set_transfer_mode": ([p, ctypes.c_int32], i32),
+        "avsg_set_match_mode": ([p, ctypes.c_int32], i32),
         "avsg_profile_end": ([p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)], i32),
     }
     for name, (args, res) in sig.items():
@@ -155,6 +157,10 @@ def avsg_attn_splits(ctx: int) -> int:
 
 def avsg_set_transfer_mode(ctx: int, mode: int) -> int:
     return load().avsg_set_transfer_mode(ctx, mode)
+
+
+def avsg_set_match_mode(ctx: int, mode: int) -> int:
+    return load().avsg_set_match_mode(ctx, mode)
 
 
 def avsg_profile_begin(ctx: int, max_steps: int) -> int:
@@ -313,6 +319,11 @@ class Context:
         st = avsg_set_transfer_mode(self.handle, mode)
         if st != OK:
             raise AvsgError(st, "avsg_set_transfer_mode")
+
+    def set_match_mode(self, mode: int):
+        st = avsg_set_match_mode(self.handle, mode)
+        if st != OK:
+            raise AvsgError(st, "avsg_set_match_mode")
 
     def profile_begin(self, max_steps: int):
         st = avsg_profile_begin(self.handle, max_steps)

@@ -20,6 +20,8 @@ struct avsg_ctx {
   const void* pinned_checked;    // last host_kv pointer found pinned
   const void* pinned_device;     // its device-visible address
   int32_t transfer_mode;         // avsg_transfer_mode
+  int32_t match_mode;            // avsg_match_mode
+  int lds_max;
   hipEvent_t* prof_events;       // 4 per profiled step, or null
   int32_t prof_max, prof_used;
 };
@@ -71,6 +73,10 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
                            d->nbins + 64 + (c.n_q_tokens > 1 ? tk : ws->ucap) +
                            (c.n_q_tokens > 1 ? tk + c.k + 1 : 0);
   d->mr_lds = 4 * (size_t)lds_ints;
+  d->merge_pow2 = 64;
+  while (d->merge_pow2 < c.n_slots) d->merge_pow2 <<= 1;
+  // merge baseline: one spare word, sorted (id, slot) pairs, slot -> union index
+  d->mr_lds_merge = d->mr_lds + 4 + 8 * (size_t)d->merge_pow2 + 4 * (size_t)c.n_slots;
   return true;
 }
 
@@ -186,6 +192,8 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->prof_events = nullptr;
   c->prof_max = c->prof_used = 0;
   c->transfer_mode = AVSG_TRANSFER_FUSED;
+  c->match_mode = AVSG_MATCH_HASH;
+  c->lds_max = lds_max;
   // zero the library-owned workspace words (status, counts, error, counters)
   if (launch_fill_i32((int32_t*)c->workspace, 0, c->ws.partials / 4, c->stream) != hipSuccess) {
     delete c;
@@ -198,6 +206,16 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
 avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode) {
   if (!ctx || mode < AVSG_TRANSFER_FUSED || mode > AVSG_TRANSFER_PER_UNIT) return AVSG_ERR_INVALID_ARG;
   ctx->transfer_mode = mode;
+  return AVSG_OK;
+}
+
+avsg_status avsg_set_match_mode(avsg_ctx* ctx, int32_t mode) {
+  if (!ctx || (mode != AVSG_MATCH_HASH && mode != AVSG_MATCH_MERGE)) return AVSG_ERR_INVALID_ARG;
+  if (mode == AVSG_MATCH_MERGE) {
+    if ((int64_t)ctx->d.mr_lds_merge > ctx->lds_max) return AVSG_ERR_UNSUPPORTED;
+    if (match_reserve_set_lds(ctx->d.mr_lds_merge) != hipSuccess) return AVSG_ERR_HIP;
+  }
+  ctx->match_mode = mode;
   return AVSG_OK;
 }
 
@@ -341,8 +359,11 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   mp.L = c.lifetime_L;
   mp.B = c.n_buckets;
   mp.nbins = ctx->d.nbins;
+  mp.match_mode = ctx->match_mode;
+  mp.merge_pow2 = ctx->d.merge_pow2;
   prof_mark(ctx, 0);
-  if (launch_match_reserve(mp, ctx->d.units, ctx->d.mr_lds, ctx->stream) != hipSuccess)
+  const size_t mr_lds = ctx->match_mode == AVSG_MATCH_MERGE ? ctx->d.mr_lds_merge : ctx->d.mr_lds;
+  if (launch_match_reserve(mp, ctx->d.units, mr_lds, ctx->stream) != hipSuccess)
     return AVSG_ERR_HIP;
   prof_mark(ctx, 1);
 

@@ -26,7 +26,9 @@ struct WsLayout {
 
 struct Derived {
   int32_t units, G, row_elems, nbins, log_table_cap, ubits;
-  size_t mr_lds;  // dynamic LDS bytes of match_reserve
+  size_t mr_lds;        // dynamic LDS bytes of match_reserve
+  size_t mr_lds_merge;  // the same with the merge baseline's sort buffers
+  int32_t merge_pow2;
 };
 
 bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d);
@@ -48,6 +50,8 @@ struct MatchReserveParams {
   uint32_t* err_word;
   int64_t t;
   int32_t S, N, T, k, ucap, table_cap, log_table_cap, ubits, policy, L, B, nbins;
+  int32_t match_mode;     // avsg_match_mode
+  int32_t merge_pow2;     // power of two >= S (sort size of the merge baseline)
 };
 
 struct GatherParams {

@@ -268,7 +268,83 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 
   // ---- 4. every slot probes its resident id; state checks
   int hit_i[MAXP];
-  if (sMisc[0] == 0) {
+  if (sMisc[0] == 0 && p.match_mode == AVSG_MATCH_MERGE) {
+    // comparison baseline: sort the resident (id, slot) pairs by id (bitonic,
+    // in LDS), then one lane walks the sorted union and the sorted residents
+    // with two pointers.  Same results as the hash probe.
+    int bad = 0;
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      const int32_t x = tok[q];
+      bin[q] = kInvalid;
+      hit_i[q] = -1;
+      if (x == kInvalid) continue;
+      bin[q] = 0;
+      if (x < -1 || x >= N) {
+        bad = 1;
+      } else if (x >= 0) {
+        const int32_t l = lf[q];
+        if (!lru && (l < 0 || l > p.L)) bad = 1;
+        if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
+      }
+    }
+    const int P2 = p.merge_pow2;
+    // [P2] pairs after the last array, rounded up to 8 bytes (one spare word)
+    int2* sPair = reinterpret_cast<int2*>(
+        (reinterpret_cast<uintptr_t>(sDup + (T > 1 ? k + 1 : 0)) + 7) & ~(uintptr_t)7);
+    int32_t* sSlotU = reinterpret_cast<int32_t*>(sPair + P2);              // [S]
+    for (int i = tid; i < P2; i += kMRThreads) {
+      const int32_t x = i < S ? slot_table[i] : -1;
+      sPair[i] = make_int2((x >= 0 && x < N) ? x : INT_MAX, i);
+    }
+    for (int i = tid; i < S; i += kMRThreads) sSlotU[i] = -1;
+    __syncthreads();
+    for (int k2 = 2; k2 <= P2; k2 <<= 1)
+      for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+        for (int i = tid; i < P2; i += kMRThreads) {
+          const int l = i ^ j2;
+          if (l > i) {
+            const int2 a = sPair[i], b = sPair[l];
+            const bool up = (i & k2) == 0;
+            const bool gt = a.x > b.x || (a.x == b.x && a.y > b.y);
+            if (gt == up) {
+              sPair[i] = b;
+              sPair[l] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    if (tid == 0) {
+      int a = 0, b = 0, dup = 0;
+      while (a < nu && b < P2 && sPair[b].x != INT_MAX) {
+        const int32_t ua = sU[a], rb = sPair[b].x;
+        if (ua < rb) {
+          ++a;
+        } else if (ua > rb) {
+          ++b;
+        } else {
+          if (b + 1 < P2 && sPair[b + 1].x == ua) dup = 1;  // id of U held by two slots
+          sUslot[a] = sPair[b].y;
+          sSlotU[sPair[b].y] = a;
+          ++a;
+          ++b;
+        }
+      }
+      if (dup) atomicOr(&sMisc[0], kFlagState);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      if (bin[q] == kInvalid || tok[q] < 0) continue;
+      const int i = sSlotU[s0 + q * 64 + lane];
+      if (i >= 0) {
+        hit_i[q] = i;
+        bin[q] = -1;  // hit
+      }
+    }
+    if (bad) atomicOr(&sMisc[0], kFlagState);
+  } else if (sMisc[0] == 0) {
     int bad = 0;
     const int bmask = (C >> 2) - 1;
     // state checks, and the first bucket of every probe of a group of 4

@@ -107,3 +107,21 @@ def test_parity_full_size(cid):
         assert run.ctx.last_error() == 0
     finally:
         run.close()
+
+
+@pytest.mark.parametrize("name", ["batch_ragged", "mtp_ragged", "lru_small_b", "tiny"])
+def test_parity_merge_matching(name):
+    """The scalar dual-pointer matching baseline gives the same state and
+    outputs as the hash probe."""
+    from gpu_harness import ensure_lib
+    avsg = ensure_lib()
+    w = SMALL[name].replace(steps=min(SMALL[name].steps, 8))
+    say("[parity] %s merge matching" % name)
+    sel = tg.selections(w)
+    run = Runner(w)
+    run.ctx.set_match_mode(avsg.MATCH_MERGE)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+    finally:
+        run.close()

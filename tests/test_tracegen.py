@@ -67,3 +67,14 @@ def test_zipf_head_is_hot():
     sel = tg.selections(w, steps=1)
     hits = sum(int(tg.permutation(w, u)[0] in set(sel[0, u, 0].tolist())) for u in range(16))
     assert hits == 16
+
+
+def test_skewed_mode():
+    """Every 8th unit misses everything, the others repeat their first list."""
+    w = tg.WORKLOADS[2]
+    sk = tg.selections(w, steps=5, mode="skewed")
+    for u in (0, 8, 16):
+        for t in range(1, 5):
+            assert np.intersect1d(sk[t, u, 0], sk[t - 1, u, 0]).size == 0
+    for u in (1, 9, 63):
+        assert all(np.array_equal(sk[0, u], sk[t, u]) for t in range(5))

@@ -29,8 +29,9 @@ _LIB_PATH = os.path.join(_HERE, "libtracegen.so")
 _lib = None
 _lock = threading.Lock()
 
-MODE_NATURAL, MODE_ALL_HIT, MODE_ALL_MISS = 0, 1, 2
-_MODES = {"natural": MODE_NATURAL, "allhit": MODE_ALL_HIT, "allmiss": MODE_ALL_MISS}
+MODE_NATURAL, MODE_ALL_HIT, MODE_ALL_MISS, MODE_SKEWED = 0, 1, 2, 3
+_MODES = {"natural": MODE_NATURAL, "allhit": MODE_ALL_HIT, "allmiss": MODE_ALL_MISS,
+          "skewed": MODE_SKEWED}
 
 
 def build(force: bool = False) -> str:

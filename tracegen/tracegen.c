@@ -178,12 +178,14 @@ static void draw_overlapping(stream_t* st, const int32_t* prev, int64_t k_prev, 
  *   mode 1 (all-hit): every step repeats step 0.
  *   mode 2 (all-miss): token j of step t is window w = (t*T + j) mod (n/k) of
  *     the permutation, sorted; windows are disjoint.
+ *   mode 3 (skewed): units u with u % 8 == 0 follow mode 2, all other units
+ *     follow mode 1, so a few units carry every transfer of a step.
  * Returns 0, or -1 if the arguments cannot be satisfied.
  */
 int tg_selections(uint64_t seed, int64_t units, int64_t n, int64_t k, int64_t T, int64_t steps,
                   double f, double f_shared, double zipf_s, int mode, int32_t* out) {
   if (k <= 0 || k * 2 > n || T < 1 || steps < 1) return -1;
-  if (mode == 2 && (n / k) < 1) return -1;
+  if ((mode == 2 || mode == 3) && (n / k) < 1) return -1;
   double* cdf = zipf_cdf(n, zipf_s);
   int64_t keep = (int64_t)floor(f * (double)k + 0.5);
   int64_t keep_sh = (int64_t)floor(f_shared * (double)k + 0.5);
@@ -201,7 +203,8 @@ int tg_selections(uint64_t seed, int64_t units, int64_t n, int64_t k, int64_t T,
     for (int64_t t = 0; t < steps; ++t) {
       stream_t st = {tg_key3(seed, P_SEL, (uint64_t)u, (uint64_t)t), 0};
       int32_t* cur = out + ((size_t)t * (size_t)units + (size_t)u) * tk;
-      if (mode == 2) {
+      const int umode = mode == 3 ? (u % 8 == 0 ? 2 : 1) : mode;
+      if (umode == 2) {
         for (int64_t j = 0; j < T; ++j) {
           int64_t w = (t * T + j) % (n / k);
           memcpy(cur + j * k, perm + w * k, sizeof(int32_t) * (size_t)k);
@@ -209,7 +212,7 @@ int tg_selections(uint64_t seed, int64_t units, int64_t n, int64_t k, int64_t T,
         }
         continue;
       }
-      if (t == 0 || mode == 1) {
+      if (t == 0 || umode == 1) {
         if (t > 0) { memcpy(cur, cur - (size_t)units * tk, sizeof(int32_t) * tk); continue; }
         draw_overlapping(&st, NULL, 0, 0, NULL, cdf, perm, n, k, mark, cur, tmp);
       } else {
