@@ -1,72 +1,128 @@
 // K3m: split-k decode attention for the latent layout (one shared 576-wide
-// latent row per token, 128 query heads), on MFMA.
+// latent row per token, 64 or 128 query heads), on MFMA.
 //
 // What it computes: for each request and query head h, softmax(scale * q_h
 // K^T) V over exactly the selected tokens, where a selected token's row is
-// the key (576 values) and its first 512 values are the value.  With 128
-// heads sharing each row, QK^T [128 x 576] x [576 x n] and PV [128 x n] x
+// the key (576 values) and its first 512 values are the value.  With many
+// heads sharing each row, QK^T [H x 576] x [576 x n] and PV [H x n] x
 // [n x 512] are real contractions, so they run on v_mfma_f32_16x16x32_bf16.
 //
 // gfx950 mapping:
 //  * A workgroup of Hq/16 waves owns `split_rows` selected tokens of one
-//    request; each wave owns 16 heads.  The tokens' rows are staged through
-//    LDS in chunks of 32 (double buffered, rows padded to 1168 bytes so the
-//    16 rows an MFMA operand reads fall in distinct banks); the loads of the
-//    next chunk are in flight while the current one is multiplied.
+//    request; each wave owns 16 heads (their queries stay in 72 registers,
+//    their 16 x 512 accumulators in 128).
+//  * Rows are staged through three LDS tiles of 32 rows (rows padded to 1168
+//    bytes so the 16 rows an MFMA operand reads fall in distinct banks) by
+//    direct global-to-LDS loads, 16 bytes per lane, with no staging
+//    registers.  Two chunks are in flight while one is multiplied; each wave
+//    issues the same number of copies per chunk, so a vmcnt wait with a
+//    constant count tells it that its copies of the chunk it needs have
+//    landed, and one barrier per chunk makes everybody's copies visible.
+//  * Missed rows (fetch flag set by the matching kernel) are copied from
+//    pinned host memory into the tile; the wave that copied a piece then
+//    stores it from LDS into its slot, so a row crosses the host link once.
+//  * All LDS reads in the loop are inline assembly with waits tied to their
+//    results: the compiler would otherwise order every LDS read after all
+//    outstanding global-to-LDS copies.  K operands and V^T operands are read
+//    one step ahead of the MFMAs that use them.
 //  * Scores are computed transposed, S^T = K Q^T (M = 16 tokens, N = 16
-//    heads, K = 576): the K operand is a plain 16-byte LDS read of a row and
-//    the Q operand stays in registers for the whole split.  In the result
-//    layout each lane owns one head's column, so the online softmax needs only
-//    two cross-lane steps, and the probabilities are already laid out as the B
-//    operand of O^T = V^T P^T.
-//  * V^T operands come from ds_read_b64_tr_b16, the transposing LDS read, so V
-//    is never transposed in memory.
+//    heads, K = 576).  In that result layout each lane owns one head's
+//    column, so the online softmax reduces over 4 lanes with the gfx950 lane
+//    swaps (v_permlane16_swap, v_permlane32_swap), and the probabilities are
+//    already the B operand of O^T = V^T P^T.  V^T operands come from
+//    ds_read_b64_tr_b16, the transposing LDS read (lane i of each 16-lane
+//    group receives element i%4 of the 4 halfwords that lane 4r + i/4
+//    addressed, r = 0..3), so V is never transposed in memory.
 //  * P is split into bf16 hi + lo parts (two MFMAs on the same V fragment):
 //    rounding P to bf16 alone would leave about 1e-3 relative error.
-//  * Missed rows are read from pinned host memory while staging and stored
-//    into their slot (fused transfer), as in the split-layout kernel.
+//  * The reference maximum of the online softmax moves only when a chunk
+//    exceeds it by 2^8, so the accumulators are rescaled rarely; the result
+//    does not depend on the reference chosen.
 //  * Split partials (max, sum, o) are merged by the combine kernel.
+#include <type_traits>
+#include <utility>
+
 #include "avsg_internal.h"
 
 namespace avsg {
 namespace {
 
 constexpr int kDqk = 576, kDv = 512;
-constexpr int kChunk = 32;                  // tokens per LDS tile
-constexpr int kRow = kDqk + 8;              // bf16 per padded LDS row (1168 B)
-constexpr int kKSteps = kDqk / 32;          // 18 MFMA k-steps for QK^T
-constexpr int kMTiles = kDv / 16;           // 32 output tiles per wave
-constexpr int kPiecesPerRow = kDqk / 8;     // 72 16-byte pieces
-constexpr int kPieces = kChunk * kPiecesPerRow;
+constexpr int kChunk = 32;                       // tokens per LDS tile
+constexpr int kRow = kDqk + 8;                   // bf16 per padded LDS row (1168 B)
+constexpr int kRowBytes = 2 * kRow;
+constexpr int kRowPieces = kRow / 8;             // 73 16-byte pieces per padded row
+constexpr int kPiecesPerRow = kDqk / 8;          // 72 of them carry data
+constexpr int kTilePieces = kChunk * kRowPieces; // 2336
+constexpr int kTileInstr = (kTilePieces + 63) / 64;  // 37 wave-wide copies per tile
+constexpr int kTileElems = kChunk * kRow;
+constexpr int kKSteps = kDqk / 32;               // 18 MFMA k-steps for QK^T
+constexpr int kMTiles = kDv / 16;                // 32 output tiles per wave
+constexpr int kBufs = 3;
 constexpr int kMaxSplit = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
-// V^T fragment of 8 tokens (k slots) x 16 dims (m) for the A operand
-__device__ __forceinline__ bf16x8 lds_vt(const uint16_t* p0, const uint16_t* p1) {
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-  const s16x4 v[2] = {a, b};
-  return __builtin_bit_cast(bf16x8, v);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
 
-__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+template <int OFF>
+__device__ __forceinline__ void ds_b128(u32x4& d, uint32_t a) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(a), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_tr(u32x2& d, uint32_t a) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(a), "n"(OFF));
+}
+__device__ __forceinline__ void ds_b64(int2& d, uint32_t a) {
+  asm volatile("ds_read_b64 %0, %1" : "=v"(d) : "v"(a));
+}
+// LDS wait that the compiler sees as producing the tied registers
+template <int N, class A, class B>
+__device__ __forceinline__ void lgkm_wait(A& a, B& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one head's column)
+__device__ __forceinline__ float col_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t sKV[];  // [2][kChunk][kRow]
-  __shared__ int32_t sSlot[kMaxSplit];
-  __shared__ int32_t sSrc[kMaxSplit];
+  extern __shared__ __attribute__((aligned(16))) uint16_t sTile[];  // [kBufs][kChunk][kRow]
+  __shared__ int2 sRow[kMaxSplit];  // (slot, id to fetch from host or -1)
   constexpr int kThreads = NW * 64;
   constexpr int G = NW * 16;  // query heads
+  constexpr int kInstr = (kTileInstr + NW - 1) / NW;     // copies per chunk, first waves
+  constexpr int kFull = kTileInstr - (kInstr - 1) * NW;  // waves issuing kInstr copies
 
   const int nsplit = p.nsplit;
   const int u = blockIdx.x / nsplit;
@@ -86,10 +142,8 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   }
   for (int i = tid; i < ne; i += kThreads) {
     const size_t at = (size_t)uj * p.k + e0 + i;
-    sSlot[i] = p.sel_slot[at];
-    sSrc[i] = (p.fetch && p.fetch[at]) ? p.sel[at] : -1;
+    sRow[i] = make_int2(p.sel_slot[at], (p.fetch && p.fetch[at]) ? p.sel[at] : -1);
   }
-
   // this lane's Q operand: head w*16 + li, dims 32*ks + 8*g .. +8
   bf16x8 qf[kKSteps];
   {
@@ -98,45 +152,83 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
     for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
   __syncthreads();
+  // the queries are in registers before any copy is issued
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
 
+  // this lane's piece of copy x: row << 8 | column, -1 for padding.  The lane
+  // index passes through an empty asm so that the pieces are recomputed per
+  // chunk instead of being held (or spilled) across the loop.
+  auto piece = [&](int x) -> int {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int n = w + x * NW;
+    const int P = n * 64 + ln;
+    const int r = P / kRowPieces, col = P - r * kRowPieces;
+    return (n < kTileInstr && P < kTilePieces && col < kPiecesPerRow) ? (r << 8 | col) : -1;
+  };
   uint16_t* ubase = p.buf_kv + (size_t)u * p.S * kDqk;
   const uint16_t* hbase = p.host_kv + (size_t)u * p.N * kDqk;
-  constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
-  u32x4 pre[kPer];
-  uint32_t fetched = 0;  // bit x: piece x came from host memory
+  const uint32_t row_lds = lds_addr(sRow);
+  const uint32_t tile_lds = lds_addr(sTile);
 
-  // stage chunk c's rows into registers (rows past the split are zero)
-  auto load_chunk = [&](int c) {
-    fetched = 0;
+  // Copies chunk c into tile `buf`.  Rows past the split repeat the split's
+  // last row (their scores are masked), so every wave issues exactly its
+  // kInstr or kInstr-1 copies.  Returns the copies whose row came from host
+  // memory (bit x), which the wave later stores into the rows' slots.
+  auto stage = [&](int c, int buf) -> uint32_t {
+    int2 ri[kInstr];
+    int rc[kInstr];
 #pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      const int pc = tid + x * kThreads;
-      pre[x] = u32x4{0u, 0u, 0u, 0u};
-      if (pc < kPieces) {
-        const int r = pc / kPiecesPerRow, col = pc - r * kPiecesPerRow;
-        const int e = c * kChunk + r;
-        if (e < ne) {
-          const int src = sSrc[e];
-          if (src >= 0) {
-            pre[x] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(hbase + (size_t)src * kDqk + col * 8));
-            fetched |= 1u << x;
-          } else {
-            pre[x] = *reinterpret_cast<const u32x4*>(ubase + (size_t)sSlot[e] * kDqk + col * 8);
-          }
+    for (int x = 0; x < kInstr; ++x) {
+      rc[x] = piece(x);
+      const int e = min(c * kChunk + (rc[x] < 0 ? 0 : rc[x] >> 8), ne - 1);
+      ds_b64(ri[x], row_lds + 8 * e);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int x = 0; x < kInstr; ++x) asm volatile("" : "+v"(ri[x]));
+    uint32_t fetched = 0;
+    uint16_t* tile = sTile + buf * kTileElems;
+#pragma unroll
+    for (int x = 0; x < kInstr; ++x) {
+      const int n = w + x * NW;
+      if (n < kTileInstr) {  // wave-uniform
+        const int r = rc[x] >> 8, col = rc[x] & 255;
+        const bool host = ri[x].y >= 0;
+        const uint16_t* src = host ? hbase + (size_t)ri[x].y * kDqk + col * 8
+                                   : ubase + (size_t)ri[x].x * kDqk + col * 8;
+        if (rc[x] >= 0) {
+          __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + n * 512), 16, 0, 0);
+          if (host && c * kChunk + r < ne) fetched |= 1u << x;
         }
       }
     }
+    return fetched;
   };
-  auto store_chunk = [&](int c, int buf) {
+  // Stores this wave's host-fetched pieces of chunk c from LDS into their slots.
+  auto write_back = [&](int c, int buf, uint32_t fetched) {
+    if (!__builtin_amdgcn_ballot_w64(fetched != 0)) return;
+    int2 ri[kInstr];
+    u32x4 d[kInstr];
+    int rc[kInstr];
 #pragma unroll
-    for (int x = 0; x < kPer; ++x) {
-      const int pc = tid + x * kThreads;
-      if (pc < kPieces) {
-        const int r = pc / kPiecesPerRow, col = pc - r * kPiecesPerRow;
-        *reinterpret_cast<u32x4*>(sKV + (buf * kChunk + r) * kRow + col * 8) = pre[x];
-        if (fetched & (1u << x))
-          *reinterpret_cast<u32x4*>(ubase + (size_t)sSlot[c * kChunk + r] * kDqk + col * 8) = pre[x];
+    for (int x = 0; x < kInstr; ++x) {
+      rc[x] = piece(x);
+      const int n = w + x * NW;
+      const int e = min(c * kChunk + (rc[x] < 0 ? 0 : rc[x] >> 8), ne - 1);
+      ds_b64(ri[x], row_lds + 8 * e);
+      const int nn = n < kTileInstr ? n : 0;
+      ds_b128<0>(d[x], tile_lds + buf * kTileElems * 2 + nn * 1024 + lane * 16);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int x = 0; x < kInstr; ++x) asm volatile("" : "+v"(ri[x]), "+v"(d[x]));
+#pragma unroll
+    for (int x = 0; x < kInstr; ++x) {
+      if (fetched & (1u << x)) {
+        const int col = rc[x] & 255;
+        *reinterpret_cast<u32x4*>(ubase + (size_t)ri[x].x * kDqk + col * 8) = d[x];
       }
     }
   };
@@ -147,23 +239,49 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   const int nchunks = (ne + kChunk - 1) / kChunk;
-  load_chunk(0);
+  uint32_t f_cur = stage(0, 0), f_next = 0;
+  if (nchunks > 1) f_next = stage(1, 1);
+  // per-lane operand addresses within a tile
+  const uint32_t k_off = li * kRowBytes + 16 * g;
+  const uint32_t v_off = (4 * g + (li >> 2)) * kRowBytes + 8 * (li & 3);
+
   for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    store_chunk(c, buf);
-    __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c + 1);
-    const uint16_t* tile = sKV + buf * kChunk * kRow;
+    const int buf = c % kBufs;
+    if (c + 1 < nchunks) {
+      if (w < kFull) vm_wait<kInstr>();
+      else vm_wait<kInstr - 1>();
+    } else {
+      vm_wait<0>();
+    }
+    write_back(c, buf, f_cur);
+    block_barrier();  // chunk c is in LDS; nobody reads tile (c+2)%3 any more
+    uint32_t f_new = 0;
+    if (c + 2 < nchunks) f_new = stage(c + 2, (c + 2) % kBufs);
+    f_cur = f_next;
+    f_next = f_new;
 
     // S^T = K Q^T for tokens 0..15 and 16..31 of the chunk, this wave's heads
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8 k0 = lds_row8(tile + li * kRow + 32 * ks + 8 * g);
-      const bf16x8 k1 = lds_row8(tile + (16 + li) * kRow + 32 * ks + 8 * g);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
-    }
+    const uint32_t ka = tile_lds + buf * kTileElems * 2 + k_off;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    u32x4 kf0[2], kf1[2];
+    ds_b128<0>(kf0[0], ka);
+    ds_b128<16 * kRowBytes>(kf1[0], ka);
+    ds_b128<64>(kf0[1], ka);
+    ds_b128<64 + 16 * kRowBytes>(kf1[1], ka);
+    static_for<0, kKSteps>([&](auto ks_) {
+      constexpr int ks = decltype(ks_)::value, st = ks & 1;
+      if constexpr (ks + 1 < kKSteps) lgkm_wait<2>(kf0[st], kf1[st]);
+      else lgkm_wait<0>(kf0[st], kf1[st]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf0[st]), qf[ks], s0,
+                                                   0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf1[st]), qf[ks], s1,
+                                                   0, 0, 0);
+      if constexpr (ks + 2 < kKSteps) {
+        ds_b128<64 * (ks + 2)>(kf0[st], ka);
+        ds_b128<64 * (ks + 2) + 16 * kRowBytes>(kf1[st], ka);
+      }
+    });
+
     // lane owns head li: tokens 4g+i (s0) and 16+4g+i (s1) of the chunk
     float sv[8];
 #pragma unroll
@@ -175,11 +293,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
     float cm = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) cm = fmaxf(cm, sv[i]);
-    cm = xor_max(xor_max(cm, 16), 32);
-    // lazy rescaling: the reference maximum only moves when the chunk's
-    // maximum exceeds it by more than 8 (log2 units), so the weights stay
-    // below 2^8 and the accumulators are rescaled rarely; the result does not
-    // depend on which reference is used
+    cm = col_max(cm);
     const bool move = cm > m_run + 8.f;
     const float m_new = move ? cm : m_run;
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
@@ -189,30 +303,46 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
     for (int i = 0; i < 8; ++i) {
       const float pv = __builtin_amdgcn_exp2f(sv[i] - m_new);
       ps += pv;
-      const __bf16 h = (__bf16)pv;
-      phi[i] = h;
-      plo[i] = (__bf16)(pv - (float)h);
+      const __bf16 hb = (__bf16)pv;
+      phi[i] = hb;
+      plo[i] = (__bf16)(pv - (float)hb);
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * corr + ps;
+    l_run = l_run * corr + col_sum(ps);
     m_run = m_new;
-    if (__ballot(move)) {
+    if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
       for (int t = 0; t < kMTiles; ++t) acc[t] *= corr;
     }
 
-    // O^T += V^T P^T: V^T fragments by transposing LDS reads.  k slot 8g+r
-    // is token 4g+r for r < 4 and 16+4g+(r-4) otherwise, matching the
-    // layout of the probabilities above.
-    const uint16_t* v0 = tile + (4 * g + (li >> 2)) * kRow + 4 * (li & 3);
-    const uint16_t* v1 = v0 + 16 * kRow;
-#pragma unroll
-    for (int t = 0; t < kMTiles; ++t) {
-      const bf16x8 vt = lds_vt(v0 + 16 * t, v1 + 16 * t);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo, acc[t], 0, 0, 0);
-    }
+    const uint32_t va = tile_lds + buf * kTileElems * 2 + v_off;
+    u32x2 vr[2][4];
+    ds_tr<0>(vr[0][0], va);
+    ds_tr<16 * kRowBytes>(vr[0][1], va);
+    ds_tr<32>(vr[0][2], va);
+    ds_tr<32 + 16 * kRowBytes>(vr[0][3], va);
+    // O^T += V^T P^T, output tiles in pairs.  k slot 8g+r is token 4g+r for
+    // r < 4 and 16+4g+(r-4) otherwise, matching the probabilities above.
+    static_for<0, kMTiles / 2>([&](auto pr_) {
+      constexpr int pr = decltype(pr_)::value, st = pr & 1;
+      if constexpr (pr + 1 < kMTiles / 2) {
+        constexpr int o = 64 * (pr + 1);
+        ds_tr<o>(vr[st ^ 1][0], va);
+        ds_tr<o + 16 * kRowBytes>(vr[st ^ 1][1], va);
+        ds_tr<o + 32>(vr[st ^ 1][2], va);
+        ds_tr<o + 32 + 16 * kRowBytes>(vr[st ^ 1][3], va);
+        asm volatile("s_waitcnt lgkmcnt(4)"
+                     : "+v"(vr[st][0]), "+v"(vr[st][1]), "+v"(vr[st][2]), "+v"(vr[st][3]));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(vr[st][0]), "+v"(vr[st][1]), "+v"(vr[st][2]), "+v"(vr[st][3]));
+      }
+      const u32x2 a2[2] = {vr[st][0], vr[st][1]}, b2[2] = {vr[st][2], vr[st][3]};
+      const bf16x8 vta = __builtin_bit_cast(bf16x8, a2), vtb = __builtin_bit_cast(bf16x8, b2);
+      acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vta, phi, acc[2 * pr], 0, 0, 0);
+      acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtb, phi, acc[2 * pr + 1], 0, 0, 0);
+      acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vta, plo, acc[2 * pr], 0, 0, 0);
+      acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtb, plo, acc[2 * pr + 1], 0, 0, 0);
+    });
   }
 
   // lane holds O[h = w*16 + li][d = 16t + 4g + i]
@@ -237,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
 
 }  // namespace
 
-size_t attn_latent_lds() { return sizeof(uint16_t) * 2 * kChunk * kRow; }
+size_t attn_latent_lds() { return sizeof(uint16_t) * kBufs * kTileElems; }
 
 hipError_t launch_attn_latent(const AttnParams& p0, int dqk, int dv, hipStream_t s) {
   if (dqk != kDqk || dv != kDv || p0.split_rows % kChunk != 0 || p0.split_rows > kMaxSplit)
