@@ -69,7 +69,8 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   off = align256(off + 4 * (size_t)d->units * T * ws->nsplit * (size_t)(c.n_q_heads / c.n_kv_heads) *
                            (size_t)(c.head_dim_v + 2));
   ws->total = off;
-  const int64_t lds_ints = 2 * (int64_t)ws->ucap + ws->table_cap + 2 * 16 * (int64_t)d->nbins +
+  const int64_t lds_ints = 2 * (int64_t)ws->ucap + ws->table_cap + ws->table_cap / 4 +
+                           2 * 16 * (int64_t)d->nbins +
                            d->nbins + 64 + (c.n_q_tokens > 1 ? tk : ws->ucap) +
                            (c.n_q_tokens > 1 ? tk + c.k + 1 : 0);
   d->mr_lds = 4 * (size_t)lds_ints;

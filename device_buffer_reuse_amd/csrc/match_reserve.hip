@@ -15,17 +15,20 @@
 //    two tokens by a rank formula: each element's position in U is found by
 //    binary search in the other list minus the duplicates before it).
 //  * U is hashed into an LDS open-addressing table (load factor <= 0.5,
-//    multiplicative hash).  A cell packs (id << ubits | union index) in 32 bits
-//    and cells are probed four at a time: one 16-byte LDS read fetches a whole
-//    aligned bucket, so a probe rarely needs a second read and never a
-//    dependent one.  Every slot of the buffer then probes its resident id, one
-//    slot per lane, 64 lanes at a time.  Hashing U rather than the slots keeps
-//    the table at 2|U| cells and turns "is this slot a candidate" into the
-//    same probe.
+//    multiplicative hash) of 4-cell buckets.  A cell packs (id << ubits |
+//    union index) in 32 bits.  Insertion takes a position in the home bucket
+//    from a per-bucket attempt counter (one LDS atomic; a full bucket sends
+//    the entry on to the next bucket), so a counter of at most 4 proves that
+//    an id absent from its home bucket is absent from the table.  Every slot
+//    of the buffer then probes its resident id, one slot per lane, 64 lanes
+//    at a time: one 16-byte read fetches the home bucket, a second its
+//    counter, and only the rare probe of an overflowed bucket reads on.
+//    Hashing U rather than the slots keeps the table at 2|U| cells and turns
+//    "is this slot a candidate" into the same probe.
 //  * Victim selection is a stable counting selection: each candidate slot gets
 //    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first).  A
-//    histogram of the bins gives the threshold bin b* that holds the m-th
-//    candidate; only candidates in bins <= b* are ranked, inside their bin in
+//    histogram of the bins, counted 4 bins at a time until they hold m
+//    candidates, gives the threshold bin b* that holds the m-th candidate; only candidates in bins <= b* are ranked, inside their bin in
 //    slot order via ballot/mbcnt per wave plus per-(wave, bin) prefix sums; the
 //    m first candidates in (bin, slot) order are the victims.  No comparison
 //    sort, no order-dependent atomics: the result is deterministic.
@@ -86,29 +89,6 @@ __device__ __forceinline__ int lower_bound_lds(const int32_t* a, int n, int32_t 
 
 constexpr int32_t kEmpty = -1;  // a filled cell has its top bit clear
 
-// Union index of id x, or -1.  Buckets of 4 cells are scanned in order from
-// x's home bucket; insertion fills the first empty cell from the start of the
-// home bucket, so an empty cell in a scanned bucket ends the search.
-__device__ __forceinline__ int hash_find(const int32_t* sHash, int log_cap, int ubits,
-                                         int32_t x) {
-  const int bmask = ((1 << log_cap) >> 2) - 1;
-  uint32_t hb = hash_id(x, log_cap) >> 2;
-  const int umask = (1 << ubits) - 1;
-  int found = -1;
-  while (true) {
-    // an empty cell (-1) shifts to -1, which never equals an id
-    const int4 c = reinterpret_cast<const int4*>(sHash)[hb];
-    found = ((c.x >> ubits) == x) ? (c.x & umask) : found;
-    found = ((c.y >> ubits) == x) ? (c.y & umask) : found;
-    found = ((c.z >> ubits) == x) ? (c.z & umask) : found;
-    found = ((c.w >> ubits) == x) ? (c.w & umask) : found;
-    const bool any_empty = (c.x == kEmpty) | (c.y == kEmpty) | (c.z == kEmpty) | (c.w == kEmpty);
-    if (found >= 0 || any_empty) break;
-    hb = (hb + 1) & bmask;
-  }
-  return found;
-}
-
 // Looks for x in one fetched bucket: returns the union index, -1 if the
 // bucket has an empty cell (x is absent), or -2 if the search must go on.
 __device__ __forceinline__ int bucket_check(const int4 c, int ubits, int32_t x) {
@@ -122,12 +102,24 @@ __device__ __forceinline__ int bucket_check(const int4 c, int ubits, int32_t x) 
   return (found >= 0 || lo < 0) ? found : -2;
 }
 
-__device__ __forceinline__ void hash_insert(int32_t* sHash, int log_cap, int ubits, int32_t x,
-                                            int32_t i) {
-  const int cmask = (1 << log_cap) - 1;
-  uint32_t cell = (hash_id(x, log_cap) >> 2) << 2;
+// Inserts (x, i).  Each bucket of 4 cells has a counter of insertion
+// attempts: the attempt that draws position 0..3 fills that cell (so a
+// bucket's cells fill in order), later attempts move on to the next bucket.
+// A counter <= 4 therefore means that no entry whose home is this bucket
+// lives anywhere else.
+__device__ __forceinline__ void hash_insert(int32_t* sHash, int32_t* sBcnt, int log_cap, int ubits,
+                                            int32_t x, int32_t i) {
+  const int bmask = ((1 << log_cap) >> 2) - 1;
+  uint32_t hb = hash_id(x, log_cap) >> 2;
   const int32_t v = (x << ubits) | i;
-  while (atomicCAS(&sHash[cell], kEmpty, v) != kEmpty) cell = (cell + 1) & cmask;
+  while (true) {
+    const int pos = atomicAdd(&sBcnt[hb], 1);
+    if (pos < 4) {
+      sHash[hb * 4 + pos] = v;
+      return;
+    }
+    hb = (hb + 1) & bmask;
+  }
 }
 
 enum { kFlagRange = 1, kFlagUnsorted = 2, kFlagCapacity = 4, kFlagState = 8 };
@@ -167,7 +159,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const bool lru = p.policy == AVSG_POLICY_BUCKET_LRU;
 
   int32_t* sHash = lds;                      // [C] packed (id, union index) or -1
-  int32_t* sU = sHash + C;                   // [ucap] union, ascending
+  int32_t* sBcnt = sHash + C;                // [C/4] insertion attempts per bucket
+  int32_t* sU = sBcnt + (C >> 2);            // [ucap] union, ascending
   int32_t* sUslot = sU + ucap;               // [ucap] slot of each union entry (+ miss flag)
   int32_t* sCnt = sUslot + ucap;             // [16][nbins] per-wave candidates per bin
   int32_t* sOff = sCnt + kMRWaves * nbins;   // [16][nbins] first rank of (wave, bin)
@@ -182,8 +175,16 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   int32_t* slot_table = p.slot_table + (size_t)u * S;
   int32_t* lifetimes = p.lifetimes + (size_t)u * S;
 
-  // ---- 0. issue the loads of this lane's slots first; they complete while
-  //         the selection is validated, merged and hashed
+  // ---- 0. issue the selection loads, then the loads of this lane's slots;
+  //         the slots complete while the selection is validated and hashed
+  int32_t* stage = (T > 1) ? sMiss : sU;  // T = 1: the list is U itself
+  constexpr int kSelRegs = 4;
+  int32_t selr[kSelRegs];
+#pragma unroll
+  for (int r = 0; r < kSelRegs; ++r) {
+    const int i = tid + r * kMRThreads;
+    selr[r] = i < tk ? sel[i] : 0;
+  }
   const int R = ((S + kMRThreads - 1) / kMRThreads) * 64;  // slots per wave, multiple of 64
   const int s0 = w * R, s1 = min(s0 + R, S);
   int tok[MAXP], lf[MAXP], bin[MAXP], rank[MAXP];
@@ -197,20 +198,30 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       lf[q] = lifetimes[s];
     }
   }
-  int32_t* stage = (T > 1) ? sMiss : sU;  // T = 1: the list is U itself
-  for (int i = tid; i < tk; i += kMRThreads) stage[i] = sel[i];
+#pragma unroll
+  for (int r = 0; r < kSelRegs; ++r) {
+    const int i = tid + r * kMRThreads;
+    if (i < tk) stage[i] = selr[r];
+  }
+  for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) stage[i] = sel[i];
   if (tid < 64) sMisc[tid] = 0;
   for (int i = tid; i < C; i += kMRThreads) sHash[i] = -1;
+  for (int i = tid; i < (C >> 2); i += kMRThreads) sBcnt[i] = 0;
   for (int i = tid; i < ucap; i += kMRThreads) sUslot[i] = -1;
   __syncthreads();
 
-  // ---- 1. validate each token's list: ids in range, strictly ascending
+  // ---- 1. validate each token's list: ids in range, strictly ascending.
+  //         With one token the list is U, and valid ids are hashed in the
+  //         same pass (the table is never used if a flag is raised).
+  const int log_cap = p.log_table_cap, ubits = p.ubits;
   {
     int bad = 0;
     for (int i = tid; i < tk; i += kMRThreads) {
       const int32_t x = stage[i];
-      if (x < 0 || x >= N) bad |= kFlagRange;
+      const bool in_range = x >= 0 && x < N;
+      if (!in_range) bad |= kFlagRange;
       if (i % k != 0 && x <= stage[i - 1]) bad |= kFlagUnsorted;
+      if (T == 1 && in_range) hash_insert(sHash, sBcnt, log_cap, ubits, x, i);
     }
     if (bad) atomicOr(&sMisc[0], bad);
   }
@@ -259,12 +270,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     __syncthreads();
   }
 
-  // ---- 3. hash U into the LDS table
-  const int log_cap = p.log_table_cap, ubits = p.ubits;
-  if (sMisc[0] == 0) {
-    for (int i = tid; i < nu; i += kMRThreads) hash_insert(sHash, log_cap, ubits, sU[i], i);
+  // ---- 3. hash U into the LDS table (two tokens; one token did it above)
+  if (T > 1) {
+    if (sMisc[0] == 0) {
+      for (int i = tid; i < nu; i += kMRThreads) hash_insert(sHash, sBcnt, log_cap, ubits, sU[i], i);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 4. every slot probes its resident id; state checks
   int hit_i[MAXP];
@@ -347,19 +359,24 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   } else if (sMisc[0] == 0) {
     int bad = 0;
     const int bmask = (C >> 2) - 1;
-    // state checks, and the first bucket of every probe of a group of 4
-    // slots read together so their LDS latencies overlap
+    // state checks and the home bucket (cells and attempt counter) of every
+    // probe of a group of (up to) 8 slots, all reads issued together; then
+    // rounds in which every probe still open reads its next bucket
+    constexpr int kGrp = MAXP < 8 ? MAXP : (MAXP > 8 ? 4 : 8);
 #pragma unroll
-    for (int q0 = 0; q0 < MAXP; q0 += 4) {
-      int4 cb[4];
-      bool probe[4];
+    for (int q0 = 0; q0 < MAXP; q0 += kGrp) {
+      int4 cb[kGrp];
+      uint32_t hb[kGrp];
+      int hc[kGrp];   // insertion attempts on the home bucket
+      int res[kGrp];  // union index, -1 absent, -2 searching
 #pragma unroll
-      for (int qq = 0; qq < 4 && q0 + qq < MAXP; ++qq) {
+      for (int qq = 0; qq < kGrp; ++qq) {
         const int q = q0 + qq;
         const int32_t x = tok[q];
         bin[q] = kInvalid;
         hit_i[q] = -1;
-        probe[qq] = false;
+        res[qq] = -1;
+        hb[qq] = 0;
         if (x == kInvalid) continue;
         bin[q] = 0;
         if (x < -1 || x >= N) {
@@ -368,24 +385,41 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
           const int32_t l = lf[q];
           if (!lru && (l < 0 || l > p.L)) bad = 1;
           if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
-          probe[qq] = true;
-          cb[qq] = reinterpret_cast<const int4*>(sHash)[hash_id(x, log_cap) >> 2];
+          res[qq] = -2;
+          hb[qq] = hash_id(x, log_cap) >> 2;
+          cb[qq] = reinterpret_cast<const int4*>(sHash)[hb[qq]];
+          hc[qq] = sBcnt[hb[qq]];
         }
       }
+      // home bucket: absent unless found, or the bucket overflowed
 #pragma unroll
-      for (int qq = 0; qq < 4 && q0 + qq < MAXP; ++qq) {
-        const int q = q0 + qq;
-        if (!probe[qq]) continue;
-        int i = bucket_check(cb[qq], ubits, tok[q]);
-        if (i == -2) {  // full first bucket: continue in the following ones
-          uint32_t hb = ((hash_id(tok[q], log_cap) >> 2) + 1) & bmask;
-          while ((i = bucket_check(reinterpret_cast<const int4*>(sHash)[hb], ubits, tok[q])) == -2)
-            hb = (hb + 1) & bmask;
+      for (int qq = 0; qq < kGrp; ++qq)
+        if (res[qq] == -2) {
+          const int r = bucket_check(cb[qq], ubits, tok[q0 + qq]);
+          res[qq] = r >= 0 ? r : (hc[qq] > 4 ? -2 : -1);
         }
+      while (true) {
+        bool more = false;
+#pragma unroll
+        for (int qq = 0; qq < kGrp; ++qq) more |= res[qq] == -2;
+        if (!__ballot(more)) break;
+#pragma unroll
+        for (int qq = 0; qq < kGrp; ++qq)
+          if (res[qq] == -2) {
+            hb[qq] = (hb[qq] + 1) & bmask;
+            cb[qq] = reinterpret_cast<const int4*>(sHash)[hb[qq]];
+          }
+#pragma unroll
+        for (int qq = 0; qq < kGrp; ++qq)
+          if (res[qq] == -2) res[qq] = bucket_check(cb[qq], ubits, tok[q0 + qq]);
+      }
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) {
+        const int i = res[qq];
         if (i >= 0) {
-          sUslot[i] = s0 + q * 64 + lane;
-          hit_i[q] = i;
-          bin[q] = -1;  // hit
+          sUslot[i] = s0 + (q0 + qq) * 64 + lane;
+          hit_i[q0 + qq] = i;
+          bin[q0 + qq] = -1;  // hit
         }
       }
     }
@@ -438,15 +472,28 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     }
   }
 
-  // ---- 6. misses of U in ascending id order
+  // ---- 6. misses of U in ascending id order (two consecutive entries per
+  //         thread, ranked by two ballots)
   int m = 0;
-  for (int c0 = 0; c0 < nu; c0 += kMRThreads) {
-    const int i = c0 + tid;
-    const bool miss = i < nu && sUslot[i] < 0;
-    int tot;
-    const int pre = block_excl_scan_bit(miss, sWs, &tot);
-    if (miss) sMiss[m + pre] = i;
+  for (int c0 = 0; c0 < nu; c0 += 2 * kMRThreads) {
+    const int i0 = c0 + 2 * tid;
+    const bool m0 = i0 < nu && sUslot[i0] < 0;
+    const bool m1 = i0 + 1 < nu && sUslot[i0 + 1] < 0;
+    const uint64_t b0 = __ballot(m0), b1 = __ballot(m1);
+    if (lane == 0) sWs[w] = __popcll(b0) + __popcll(b1);
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int x = 0; x < kMRWaves; ++x) {
+      const int v = sWs[x];
+      pre += (x < w) ? v : 0;
+      tot += v;
+    }
+    pre += mbcnt64(b0) + mbcnt64(b1);
+    if (m0) sMiss[m + pre] = i0;
+    if (m1) sMiss[m + pre + (m0 ? 1 : 0)] = i0 + 1;
     m += tot;
+    __syncthreads();
   }
 
   // ---- 7. victims: the m first candidates in (bin, slot) order
@@ -455,35 +502,55 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) changed[q] = false;
   if (m > 0) {
-    // per-wave histogram of the candidates' bins: one ballot per (bin, slot
-    // group), counted on the scalar unit; no LDS atomics
-    for (int b = 0; b < nbins; ++b) {
-      int cnt = 0;
+    // per-wave histogram of the candidates' bins (one ballot per (bin, slot
+    // group), counted on the scalar unit, no LDS atomics), built 4 bins at a
+    // time until the bins so far hold m candidates; usually the first 4 do
+    int nb = 0;  // bins counted so far
+    for (int covered = 0; nb < nbins && covered < m;) {
 #pragma unroll
-      for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
-      if (lane == 0) sCnt[w * nbins + b] = cnt;
-    }
-    __syncthreads();
-    // bin totals, their exclusive starts, and the threshold bin b* holding
-    // the m-th candidate (nbins <= 128 <= threads)
-    {
-      int tot = 0;
-      if (tid < nbins)
-        for (int v = 0; v < kMRWaves; ++v) tot += sCnt[v * nbins + tid];
-      int all;
-      const int pre = block_excl_scan(tot, sWs, &all);
-      if (tid < nbins) {
-        sTot[tid] = pre;
-        if (pre < m && pre + tot >= m) sMisc[2] = tid;
+      for (int bb = 0; bb < 4; ++bb) {
+        const int b = nb + bb;
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
+        if (lane == 0 && b < nbins) sCnt[w * nbins + b] = cnt;
       }
+      __syncthreads();
+      // every wave adds up the same counts, so all take the same branch
+      int add = 0;
+#pragma unroll
+      for (int v = 0; v < kMRWaves; ++v)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+          if (nb + bb < nbins) add += sCnt[v * nbins + nb + bb];
+      covered += add;
+      nb = min(nb + 4, nbins);
     }
-    __syncthreads();
-    const int bstar = sMisc[2];
-    for (int idx = tid; idx < kMRWaves * (bstar + 1); idx += kMRThreads) {
-      const int v = idx / (bstar + 1), b = idx - v * (bstar + 1);
-      int off = sTot[b];
-      for (int x = 0; x < v; ++x) off += sCnt[x * nbins + b];
-      sOff[v * nbins + b] = off;
+    // every wave derives the bin totals, their exclusive starts, the
+    // threshold bin b* holding the m-th candidate, and its own first rank
+    // per bin; lane l covers bins l and l + 64 (nbins <= 128)
+    int bstar = nbins;
+    {
+      int tot0 = 0, tot1 = 0, bef0 = 0, bef1 = 0;
+      const int b0 = lane, b1 = lane + 64;
+#pragma unroll
+      for (int v = 0; v < kMRWaves; ++v) {
+        const int c0v = b0 < nb ? sCnt[v * nbins + b0] : 0;
+        const int c1v = b1 < nb ? sCnt[v * nbins + b1] : 0;
+        tot0 += c0v;
+        tot1 += c1v;
+        bef0 += v < w ? c0v : 0;
+        bef1 += v < w ? c1v : 0;
+      }
+      const int inc0 = wave_incl_scan(tot0, lane);
+      const int sum0 = __shfl(inc0, 63, 64);
+      const int inc1 = wave_incl_scan(tot1, lane) + sum0;
+      const int st0 = inc0 - tot0, st1 = inc1 - tot1;
+      const uint64_t r0 = __ballot(b0 < nb && st0 < m && st0 + tot0 >= m);
+      const uint64_t r1 = __ballot(b1 < nb && st1 < m && st1 + tot1 >= m);
+      bstar = r0 ? __builtin_ctzll(r0) : 64 + __builtin_ctzll(r1);
+      if (b0 < nb) sOff[w * nbins + b0] = st0 + bef0;
+      if (b1 < nb) sOff[w * nbins + b1] = st1 + bef1;
     }
     // rank of each candidate in bins <= b* among the wave's candidates of
     // the same bin, in slot order (slot groups in order, lanes in order)
@@ -498,7 +565,6 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         run += __popcll(grp);
       }
     }
-    __syncthreads();
     int2* misses = p.misses + (size_t)u * ucap;
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) {
@@ -519,17 +585,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     if (ev) atomicAdd(&sMisc[1], ev);
   }
 
-  // ---- 8. write the new slot state back
-#pragma unroll
-  for (int q = 0; q < MAXP; ++q) {
-    if (tok[q] == kInvalid) continue;
-    const int s = s0 + q * 64 + lane;
-    lifetimes[s] = lf[q];
-    if (changed[q]) slot_table[s] = tok[q];
-  }
   __syncthreads();
 
-  // ---- 9. per-(token, entry) outputs read off the union
+  // ---- 8. per-(token, entry) outputs read off the union
   for (int i = tid; i < tk; i += kMRThreads) {
     const int mi = (T == 1) ? i : sMap[i];
     const int v = sUslot[mi & ~kDupFlag];
@@ -539,6 +597,16 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     // the row is transferred by the first token that selects it
     p.fetch[(size_t)u * tk + i] = (miss && !(mi & kDupFlag)) ? 1 : 0;
   }
+  // ---- 9. write the new slot state back (registers only, after the
+  //         outputs so that the stores overlap them)
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    if (tok[q] == kInvalid) continue;
+    const int s = s0 + q * 64 + lane;
+    lifetimes[s] = lf[q];
+    if (changed[q]) slot_table[s] = tok[q];
+  }
+
   if (tid == 0) {
     p.n_hit[u] = nu - m;
     p.n_miss[u] = m;
