@@ -54,7 +54,7 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   if (c.kv_layout == AVSG_KV_LATENT) {
     ws->split_rows = 512;  // 4 splits: one 8-wave workgroup per CU for 64 requests
   } else {
-    ws->split_rows = 128;  // one workgroup of the split-layout attention
+    ws->split_rows = 256;  // one workgroup of the split-layout attention
   }
   ws->nsplit = (int32_t)((rows + ws->split_rows - 1) / ws->split_rows);
   const int64_t T = c.n_q_tokens;
@@ -109,6 +109,8 @@ static avsg_status check_config_impl(const avsg_config* c) {
     const int G = c->n_q_heads / c->n_kv_heads;
     if (c->head_dim_qk != 128 || c->head_dim_v != 128) return AVSG_ERR_UNSUPPORTED;
     if (G != 1 && G != 2 && G != 4 && G != 8) return AVSG_ERR_UNSUPPORTED;
+    // entry of a token row by multiply-high: exact while rows * tpe < 2^32
+    if (c->tokens_per_entry > 256) return AVSG_ERR_UNSUPPORTED;
   } else {
     if (c->tokens_per_entry != 1 || c->n_kv_heads != 1) return AVSG_ERR_INVALID_ARG;
     if (c->head_dim_qk != 576 || c->head_dim_v != 512) return AVSG_ERR_UNSUPPORTED;
@@ -391,6 +393,7 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   ap.host_kv = (const uint16_t*)host_dev;
   ap.N = c.n_entries;
   ap.token = 0;
+  ap.gather_first = 0;
   ap.unit_status = unit_status;
   ap.q = q;
   ap.buf_kv = buf_kv;

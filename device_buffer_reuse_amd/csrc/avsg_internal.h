@@ -79,6 +79,7 @@ struct AttnParams {
   int64_t S;
   int32_t units, Hkv, Hq, T, k, tpe, row_elems, nsplit, split_rows;
   int32_t token;              // query token of this launch
+  int32_t gather_first;       // split layout: fetch a split's missed entries before its tiles
   float scale_log2e;
 };
 

@@ -85,7 +85,7 @@ typedef struct avsg_config {
   int32_t head_dim_v;        /* split layout: 128; latent layout: 512 */
   int32_t kv_layout;         /* avsg_kv_layout */
   int32_t n_entries;         /* N: entries per unit in host memory */
-  int32_t tokens_per_entry;  /* 1 (token entries) or 16 (pages); latent layout: 1 */
+  int32_t tokens_per_entry;  /* 1 (token entries) .. 256 (pages); latent layout: 1 */
   int32_t k;                 /* entries selected per query token */
   int32_t n_slots;           /* S: buffer slots per unit */
   int32_t policy;            /* avsg_policy */

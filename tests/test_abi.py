@@ -71,6 +71,7 @@ def test_workspace_sizes_match_layout():
     c = avsg.config_from_workload(w)
     ws = avsg.avsg_workspace_bytes(c)
     misses = 8 * w.units * min(w.k * w.n_q_tokens, w.n_slots)
-    partials = 4 * w.units * 16 * 4 * 130
+    splits = -(-w.k * w.tokens_per_entry // 256)  # 256 token rows per attention split
+    partials = 4 * w.units * splits * 4 * 130
     fetch = w.units * w.n_q_tokens * w.k
     assert misses + partials + fetch <= ws <= misses + partials + fetch + 8 * 1024
