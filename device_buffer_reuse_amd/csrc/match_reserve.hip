@@ -18,8 +18,9 @@
 //    multiplicative hash) of 4-cell buckets.  A cell packs (id << ubits |
 //    union index) in 32 bits.  Insertion takes a position in the home bucket
 //    from a per-bucket attempt counter (one LDS atomic; a full bucket sends
-//    the entry on to the next bucket), so a counter of at most 4 proves that
-//    an id absent from its home bucket is absent from the table.  Every slot
+//    the entry on along its double-hashing sequence), so a counter of at
+//    most 4 proves that an id absent from its home bucket is absent from the
+//    table.  Every slot
 //    of the buffer then probes its resident id, one slot per lane, 64 lanes
 //    at a time: one 16-byte read fetches the home bucket, a second its
 //    counter, and only the rare probe of an overflowed bucket reads on.
@@ -27,11 +28,12 @@
 //    "is this slot a candidate" into the same probe.
 //  * Victim selection is a stable counting selection: each candidate slot gets
 //    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first).  A
-//    histogram of the bins, counted 4 bins at a time until they hold m
-//    candidates, gives the threshold bin b* that holds the m-th candidate; only candidates in bins <= b* are ranked, inside their bin in
-//    slot order via ballot/mbcnt per wave plus per-(wave, bin) prefix sums; the
-//    m first candidates in (bin, slot) order are the victims.  No comparison
-//    sort, no order-dependent atomics: the result is deterministic.
+//    histogram of the bins (the first 4 bins, then the rest only if those
+//    hold fewer than m candidates) gives the threshold bin b* that holds the m-th candidate;
+//    only candidates in bins <= b* are ranked, inside their bin in slot order
+//    via ballot/mbcnt per wave plus per-(wave, bin) prefix sums; the m first
+//    candidates in (bin, slot) order are the victims.  No comparison sort, no
+//    order-dependent atomics: the result is deterministic.
 //  * The r-th miss in ascending id order takes the r-th victim, its row is
 //    listed as (slot, id) for the gather kernel.
 #include "avsg_internal.h"
@@ -45,36 +47,37 @@ constexpr int kDupFlag = 1 << 30;  // token-1 entry also selected by token 0
 __device__ __forceinline__ uint32_t hash_id(int32_t id, int log_cap) {
   return ((uint32_t)id * 0x9E3779B1u) >> (32 - log_cap);
 }
+// Bucket step of an id (odd, so it visits every bucket of the power-of-two
+// table): double hashing keeps overflow chains short, where stepping to the
+// next bucket would let full buckets cluster.
+__device__ __forceinline__ uint32_t hash_step(int32_t id, int log_cap) {
+  return ((((uint32_t)id * 0x85EBCA77u) >> (34 - log_cap)) << 1) | 1u;
+}
 
 __device__ __forceinline__ int mbcnt64(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+// Inclusive scan over the 64 lanes of a wave, on DPP only: shifts by 1, 2,
+// 4, 8 inside each 16-lane row, then row 0's total into rows 1 and 3
+// (row_bcast:15) and rows 0-1's total into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<0x111, 0xF, true>(v);   // row_shr:1
+  v += dpp_i<0x112, 0xF, true>(v);   // row_shr:2
+  v += dpp_i<0x114, 0xF, true>(v);   // row_shr:4
+  v += dpp_i<0x118, 0xF, true>(v);   // row_shr:8
+  v += dpp_i<0x142, 0xA, false>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_i<0x143, 0xC, false>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
-// Exclusive scan over the whole workgroup in thread order; sWs holds 16 ints.
-__device__ __forceinline__ int block_excl_scan(int v, int* sWs, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = wave_incl_scan(v, lane);
-  if (lane == 63) sWs[w] = inc;
-  __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kMRWaves; ++i) {
-    int x = sWs[i];
-    pre += (i < w) ? x : 0;
-    tot += x;
-  }
-  __syncthreads();
-  *total = tot;
-  return pre + inc - v;
+__device__ __forceinline__ int wave_total(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
 }
 
 // number of elements of the sorted array a[0..n) that are < x
@@ -104,13 +107,25 @@ __device__ __forceinline__ int bucket_check(const int4 c, int ubits, int32_t x) 
 
 // Inserts (x, i).  Each bucket of 4 cells has a counter of insertion
 // attempts: the attempt that draws position 0..3 fills that cell (so a
-// bucket's cells fill in order), later attempts move on to the next bucket.
+// bucket's cells fill in order), later attempts move on along x's bucket
+// sequence (home, home + step, ...).
 // A counter <= 4 therefore means that no entry whose home is this bucket
 // lives anywhere else.
+// Union index of x in a fetched bucket, or -1.  A filled cell is (id <<
+// ubits | index) with its top bit clear, so it holds x iff (cell ^ (x <<
+// ubits)) < 2^ubits; an empty cell (-1) never passes for an id in range.
+__device__ __forceinline__ int bucket_find(const int4 c, uint32_t xs, uint32_t lim, int umask) {
+  const bool m0 = (uint32_t)(c.x ^ xs) < lim, m1 = (uint32_t)(c.y ^ xs) < lim;
+  const bool m2 = (uint32_t)(c.z ^ xs) < lim, m3 = (uint32_t)(c.w ^ xs) < lim;
+  const int v = m0 ? c.x : (m1 ? c.y : (m2 ? c.z : c.w));
+  return (m0 | m1 | m2 | m3) ? (v & umask) : -1;
+}
+
 __device__ __forceinline__ void hash_insert(int32_t* sHash, int32_t* sBcnt, int log_cap, int ubits,
                                             int32_t x, int32_t i) {
   const int bmask = ((1 << log_cap) >> 2) - 1;
   uint32_t hb = hash_id(x, log_cap) >> 2;
+  const uint32_t step = hash_step(x, log_cap);
   const int32_t v = (x << ubits) | i;
   while (true) {
     const int pos = atomicAdd(&sBcnt[hb], 1);
@@ -118,7 +133,7 @@ __device__ __forceinline__ void hash_insert(int32_t* sHash, int32_t* sBcnt, int 
       sHash[hb * 4 + pos] = v;
       return;
     }
-    hb = (hb + 1) & bmask;
+    hb = (hb + step) & bmask;
   }
 }
 
@@ -359,6 +374,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   } else if (sMisc[0] == 0) {
     int bad = 0;
     const int bmask = (C >> 2) - 1;
+    const uint32_t lim = 1u << ubits;
+    const int umask = (int)lim - 1;
     // state checks and the home bucket (cells and attempt counter) of every
     // probe of a group of (up to) 8 slots, all reads issued together; then
     // rounds in which every probe still open reads its next bucket
@@ -369,35 +386,29 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       uint32_t hb[kGrp];
       int hc[kGrp];   // insertion attempts on the home bucket
       int res[kGrp];  // union index, -1 absent, -2 searching
+      // branch-free: every lane reads a bucket (in range for any id), and
+      // only lanes holding a resident id use it
 #pragma unroll
       for (int qq = 0; qq < kGrp; ++qq) {
         const int q = q0 + qq;
-        const int32_t x = tok[q];
-        bin[q] = kInvalid;
+        const int32_t x = tok[q], l = lf[q];
+        const bool valid = x != kInvalid;
+        const bool resident = x >= 0 && x < N;
+        const bool bad_l = lru ? (l < 0 || (int64_t)l >= p.t) : (l < 0 || l > p.L);
+        bad |= (valid && (x < -1 || x >= N)) | (resident && bad_l);
+        bin[q] = valid ? 0 : kInvalid;
         hit_i[q] = -1;
-        res[qq] = -1;
-        hb[qq] = 0;
-        if (x == kInvalid) continue;
-        bin[q] = 0;
-        if (x < -1 || x >= N) {
-          bad = 1;
-        } else if (x >= 0) {
-          const int32_t l = lf[q];
-          if (!lru && (l < 0 || l > p.L)) bad = 1;
-          if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
-          res[qq] = -2;
-          hb[qq] = hash_id(x, log_cap) >> 2;
-          cb[qq] = reinterpret_cast<const int4*>(sHash)[hb[qq]];
-          hc[qq] = sBcnt[hb[qq]];
-        }
+        res[qq] = resident ? -2 : -1;
+        hb[qq] = hash_id(x, log_cap) >> 2;
+        cb[qq] = reinterpret_cast<const int4*>(sHash)[hb[qq]];
+        hc[qq] = sBcnt[hb[qq]];
       }
-      // home bucket: absent unless found, or the bucket overflowed
+      // home bucket: absent unless found there, or the bucket overflowed
 #pragma unroll
-      for (int qq = 0; qq < kGrp; ++qq)
-        if (res[qq] == -2) {
-          const int r = bucket_check(cb[qq], ubits, tok[q0 + qq]);
-          res[qq] = r >= 0 ? r : (hc[qq] > 4 ? -2 : -1);
-        }
+      for (int qq = 0; qq < kGrp; ++qq) {
+        const int r = bucket_find(cb[qq], (uint32_t)tok[q0 + qq] << ubits, lim, umask);
+        res[qq] = res[qq] == -2 ? (r >= 0 ? r : (hc[qq] > 4 ? -2 : -1)) : -1;
+      }
       while (true) {
         bool more = false;
 #pragma unroll
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 #pragma unroll
         for (int qq = 0; qq < kGrp; ++qq)
           if (res[qq] == -2) {
-            hb[qq] = (hb[qq] + 1) & bmask;
+            hb[qq] = (hb[qq] + hash_step(tok[q0 + qq], log_cap)) & bmask;
             cb[qq] = reinterpret_cast<const int4*>(sHash)[hb[qq]];
           }
 #pragma unroll
@@ -506,25 +517,25 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     // group), counted on the scalar unit, no LDS atomics), built 4 bins at a
     // time until the bins so far hold m candidates; usually the first 4 do
     int nb = 0;  // bins counted so far
-    for (int covered = 0; nb < nbins && covered < m;) {
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int b = nb + bb;
+    for (int covered = 0, round = 0; round < 2 && nb < nbins && covered < m; ++round) {
+      const int hi = round == 0 ? min(4, nbins) : nbins;
+      for (int b = nb; b < hi; ++b) {
         int cnt = 0;
 #pragma unroll
         for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
-        if (lane == 0 && b < nbins) sCnt[w * nbins + b] = cnt;
+        if (lane == 0) sCnt[w * nbins + b] = cnt;
       }
       __syncthreads();
-      // every wave adds up the same counts, so all take the same branch
-      int add = 0;
-#pragma unroll
-      for (int v = 0; v < kMRWaves; ++v)
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb)
-          if (nb + bb < nbins) add += sCnt[v * nbins + nb + bb];
-      covered += add;
-      nb = min(nb + 4, nbins);
+      // candidates in the bins just counted: every wave adds up the same
+      // counts (one read per lane), so all take the same branch
+      const int nbb = hi - nb;
+      int part = 0;
+      for (int idx = lane; idx < kMRWaves * nbb; idx += 64) {
+        const int v = idx / nbb, b = nb + (idx - v * nbb);
+        part += sCnt[v * nbins + b];
+      }
+      covered += wave_total(part);
+      nb = hi;
     }
     // every wave derives the bin totals, their exclusive starts, the
     // threshold bin b* holding the m-th candidate, and its own first rank
@@ -542,9 +553,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         bef0 += v < w ? c0v : 0;
         bef1 += v < w ? c1v : 0;
       }
-      const int inc0 = wave_incl_scan(tot0, lane);
-      const int sum0 = __shfl(inc0, 63, 64);
-      const int inc1 = wave_incl_scan(tot1, lane) + sum0;
+      const int inc0 = wave_incl_scan(tot0);
+      const int sum0 = __builtin_amdgcn_readlane(inc0, 63);
+      const int inc1 = wave_incl_scan(tot1) + sum0;
       const int st0 = inc0 - tot0, st1 = inc1 - tot1;
       const uint64_t r0 = __ballot(b0 < nb && st0 < m && st0 + tot0 >= m);
       const uint64_t r1 = __ballot(b1 < nb && st1 < m && st1 + tot1 >= m);
@@ -570,7 +581,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     for (int q = 0; q < MAXP; ++q) {
       if (bin[q] < 0 || bin[q] > bstar) continue;
       const int r = sOff[w * nbins + bin[q]] + rank[q];
-      if (r < m) {
+      if (r >= 0 && r < m) {
         const int s = s0 + q * 64 + lane;
         const int i = sMiss[r];
         const int32_t id = sU[i];
