@@ -66,8 +66,8 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->err_word = off;    off = align256(off + 8);
   ws->counters = off;    off = align256(off + 4 * (size_t)d->units * T);
   ws->partials = off;
-  off = align256(off + 4 * (size_t)d->units * T * ws->nsplit * (size_t)(c.n_q_heads / c.n_kv_heads) *
-                           (size_t)(c.head_dim_v + 2));
+  off = align256(off + 4 * (size_t)d->units * T * ws->nsplit *
+                           partial_stride(c.n_q_heads / c.n_kv_heads, c.head_dim_v));
   ws->total = off;
   const int64_t lds_ints = 2 * (int64_t)ws->ucap + ws->table_cap + ws->table_cap / 4 +
                            2 * 16 * (int64_t)d->nbins +
@@ -324,6 +324,9 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
                       int32_t* lifetimes, float* out, const avsg_hit_stats* hs) {
   if (!ctx || !sel_idx || !q || !host_kv || !buf_kv || !slot_table || !lifetimes || !out || !hs ||
       !hs->hit_flag || !hs->sel_slot || !hs->n_hit || !hs->n_miss || !hs->n_evict)
+    return AVSG_ERR_INVALID_ARG;
+  // the kernels move rows, queries and outputs in 16-byte pieces
+  if (((uintptr_t)q | (uintptr_t)host_kv | (uintptr_t)buf_kv | (uintptr_t)out) & 15)
     return AVSG_ERR_INVALID_ARG;
   const void* host_dev = nullptr;
   avsg_status st = device_view_of_pinned(ctx, host_kv, &host_dev);

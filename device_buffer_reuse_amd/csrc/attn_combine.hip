@@ -1,59 +1,107 @@
 // K4: merge of the split-k attention partials of each (unit, token, head), in
 // split order: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), with
-// M = max_s m_s (scores are kept in log2 units).  One workgroup per head row;
-// the split weights are formed once in LDS, then every output element reads
-// its nsplit partials with independent loads.
+// M = max_s m_s (scores are kept in log2 units).
+//
+// One thread per 4 consecutive output values.  With at most 16 splits (every
+// configured workload) a thread issues the loads of all the splits' maxima,
+// sums and 16-byte partial vectors together, so the merge costs one memory
+// round trip; more splits take a loop over the splits.
 #include "avsg_internal.h"
 
 namespace avsg {
 namespace {
 
-constexpr int kCombineThreads = 128;
+constexpr int kCombineThreads = 256;
+constexpr int kMaxFastSplits = 16;
 
+template <int NS>  // NS > 0: exactly NS splits, all loads in flight at once
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParams p, int G, int D) {
-  extern __shared__ float sW[];  // [nsplit] weights
-  __shared__ float sInvL;
-  const int uj = blockIdx.x / G, h = blockIdx.x - (blockIdx.x / G) * G;
+  const int dv4 = D >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  const int64_t total = (int64_t)p.units * p.T * G * dv4;
+  if (idx >= total) return;
+  const int d4 = (int)(idx % dv4);
+  const int64_t rest = idx / dv4;
+  const int h = (int)(rest % G);
+  const int uj = (int)(rest / G);
   const int u = uj / p.T, j = uj - u * p.T;
   const int b = u / p.Hkv, g = u - b * p.Hkv;
-  const int nsplit = p.nsplit, tid = threadIdx.x;
-  float* orow = p.out + ((((size_t)b * p.T + j) * p.Hq) + (size_t)g * G + h) * D;
+  float4* orow = reinterpret_cast<float4*>(
+      p.out + ((((size_t)b * p.T + j) * p.Hq) + (size_t)g * G + h) * D) + d4;
   if (p.unit_status[u] != 0) {
-    for (int d = tid; d < D; d += kCombineThreads) orow[d] = 0.f;
+    *orow = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const size_t ps = (size_t)G * (D + 2);
+  const int nsplit = NS > 0 ? NS : p.nsplit;
+  const size_t ps = partial_stride(G, D);  // floats per split partial, multiple of 4
   const float* pbase = p.partials + (size_t)uj * nsplit * ps;
-  for (int s = tid; s < nsplit; s += kCombineThreads) sW[s] = pbase[s * ps + (size_t)G * D + h];
-  __syncthreads();
-  if (tid == 0) {
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, sW[s]);
-    float lsum = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float wgt = __builtin_amdgcn_exp2f(sW[s] - mx);
-      lsum = fmaf(pbase[s * ps + (size_t)G * D + G + h], wgt, lsum);
-      sW[s] = wgt;
+  const float* mrow = pbase + (size_t)G * D + h;
+  const float* lrow = mrow + G;
+  const float4* orow_s = reinterpret_cast<const float4*>(pbase + (size_t)h * D) + d4;
+  if constexpr (NS > 0) {
+    float m[NS], l[NS];
+    float4 o[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      m[s] = mrow[s * ps];
+      l[s] = lrow[s * ps];
+      o[s] = orow_s[s * (ps / 4)];
     }
-    sInvL = 1.f / lsum;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) mx = fmaxf(mx, m[s]);
+    float lsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float wgt = __builtin_amdgcn_exp2f(m[s] - mx);
+      lsum = fmaf(l[s], wgt, lsum);
+      acc.x = fmaf(o[s].x, wgt, acc.x);
+      acc.y = fmaf(o[s].y, wgt, acc.y);
+      acc.z = fmaf(o[s].z, wgt, acc.z);
+      acc.w = fmaf(o[s].w, wgt, acc.w);
+    }
+    const float inv = 1.f / lsum;
+    *orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  } else {
+    float mx = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, mrow[s * ps]);
+    float lsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nsplit; ++s) {
+      const float wgt = __builtin_amdgcn_exp2f(mrow[s * ps] - mx);
+      lsum = fmaf(lrow[s * ps], wgt, lsum);
+      const float4 o = orow_s[s * (ps / 4)];
+      acc.x = fmaf(o.x, wgt, acc.x);
+      acc.y = fmaf(o.y, wgt, acc.y);
+      acc.z = fmaf(o.z, wgt, acc.z);
+      acc.w = fmaf(o.w, wgt, acc.w);
+    }
+    const float inv = 1.f / lsum;
+    *orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
-  __syncthreads();
-  const float inv = sInvL;
-  for (int d = tid; d < D; d += kCombineThreads) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) acc = fmaf(pbase[s * ps + (size_t)h * D + d], sW[s], acc);
-    orow[d] = acc * inv;
-  }
+}
+
+template <int NS>
+hipError_t launch_ns(const AttnParams& p, int G, int D, hipStream_t s) {
+  const int64_t total = (int64_t)p.units * p.T * G * (D / 4);
+  const dim3 grid((unsigned)((total + kCombineThreads - 1) / kCombineThreads));
+  hipLaunchKernelGGL(attn_combine_kernel<NS>, grid, dim3(kCombineThreads), 0, s, p, G, D);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_combine(const AttnParams& p, int G, int D, hipStream_t s) {
-  const size_t lds = sizeof(float) * (size_t)p.nsplit;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(p.units * p.T * G)),
-                     dim3(kCombineThreads), lds, s, p, G, D);
-  return hipGetLastError();
+  if (D % 4 != 0) return hipErrorInvalidValue;
+  switch (p.nsplit) {
+    case 2: return launch_ns<2>(p, G, D, s);
+    case 3: return launch_ns<3>(p, G, D, s);
+    case 4: return launch_ns<4>(p, G, D, s);
+    case 8: return launch_ns<8>(p, G, D, s);
+    case 16: return launch_ns<kMaxFastSplits>(p, G, D, s);
+    default: return launch_ns<0>(p, G, D, s);
+  }
 }
 
 }  // namespace avsg

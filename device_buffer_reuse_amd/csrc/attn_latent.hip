@@ -354,7 +354,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
       *reinterpret_cast<f32x4*>(orow + (size_t)h * kDv + 16 * t + 4 * g) = acc[t] * inv;
     return;
   }
-  const size_t part_stride = (size_t)G * (kDv + 2);
+  const size_t part_stride = partial_stride(G, kDv);
   float* part = p.partials + ((size_t)uj * nsplit + sp) * part_stride;
 #pragma unroll
   for (int t = 0; t < kMTiles; ++t)

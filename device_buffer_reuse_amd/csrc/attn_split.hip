@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
     sLw[w][hl] = l;
   }
   __syncthreads();
-  const size_t part_stride = (size_t)G * (kD + 2);
+  const size_t part_stride = partial_stride(G, kD);
   float* part = p.partials + ((size_t)uj * nsplit + sp) * part_stride;
   for (int idx = tid; idx < G * kD; idx += kAttnThreads) {
     const int h = idx / kD, d = idx - h * kD;

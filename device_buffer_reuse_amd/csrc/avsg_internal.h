@@ -33,6 +33,12 @@ struct Derived {
 
 bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d);
 
+// Floats of one split partial of a (unit, token): o[G][D], then m[G], l[G],
+// padded to a multiple of 4 so that every partial starts 16-byte aligned.
+inline __host__ __device__ size_t partial_stride(int G, int D) {
+  return (size_t)G * D + (size_t)((2 * G + 3) & ~3);
+}
+
 struct MatchReserveParams {
   const int32_t* sel;     // [units][T][k]
   int32_t* slot_table;    // [units][S]
@@ -74,7 +80,7 @@ struct AttnParams {
   const uint16_t* q;          // [B][T][Hq][dqk]
   uint16_t* buf_kv;           // [units][S][row]
   float* out;                 // [B][T][Hq][dv]
-  float* partials;            // [units*T][nsplit][G][dv + 2]
+  float* partials;            // [units*T][nsplit][partial_stride(G, dv)]
   uint32_t* counters;         // [units*T]
   int64_t S;
   int32_t units, Hkv, Hq, T, k, tpe, row_elems, nsplit, split_rows;

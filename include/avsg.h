@@ -148,10 +148,12 @@ avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes);
  *              each query head over its token's selected entries; 0 for a
  *              unit with a data error.                              written
  *   hit_stats  host struct of device pointers (see avsg_hit_stats). written
- * Returns AVSG_ERR_INVALID_ARG for null pointers, AVSG_ERR_NOT_PINNED if
- * host_kv is not device-accessible pinned host memory, AVSG_ERR_HIP if a
- * launch fails; data errors are reported later by avsg_last_error.  Never
- * waits for the GPU. */
+ * q, host_kv, buf_kv and out must be 16-byte aligned (rows, queries and
+ * outputs move in 16-byte pieces).
+ * Returns AVSG_ERR_INVALID_ARG for null or misaligned pointers,
+ * AVSG_ERR_NOT_PINNED if host_kv is not device-accessible pinned host memory,
+ * AVSG_ERR_HIP if a launch fails; data errors are reported later by
+ * avsg_last_error.  Never waits for the GPU. */
 avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
                       const uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
                       int32_t* lifetimes, float* out, const avsg_hit_stats* hit_stats);
