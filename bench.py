@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--trace", default="natural", choices=["natural", "allhit", "allmiss", "skewed"],
                     help="selection trace of the timed steps (default natural)")
     ap.add_argument("--transfer", type=int, default=0,
-                    help="0 fused (default), 1 balanced gather kernel, 2 per-unit gather kernel")
+                    help="0 fused (default), 1 balanced gather kernel, 2 per-unit gather kernel, "
+                         "3 fused, gather-first")
     ap.add_argument("--ablations", action="store_true",
                     help="also compare transfer modes on a skewed-miss trace and hash vs "
                          "dual-pointer matching")
@@ -280,7 +281,7 @@ def main():
     union_per_step = (n_hit + n_miss) / K
 
     per = {"match_reserve": kern[0] / K, "gather": kern[1] / K, "attention": kern[2] / K}
-    fused = a.transfer == 0
+    fused = a.transfer in (0, 3)
     host_b = miss_per_step * row_bytes          # bytes over the host link per step
     ab = attn_bytes(w)
     # per kernel: algorithmic bytes (HBM / host link) and flops of one launch
@@ -388,7 +389,7 @@ def main():
                    "policy": w.policy, "lifetime_L": w.lifetime_L, "buckets": w.n_buckets,
                    "trace": ("natural: %.0f%% overlap + Zipf(%.1f) tail" % (100 * w.overlap, w.zipf_s)
                              if a.trace == "natural" else a.trace),
-                   "transfer": ["fused", "balanced", "per-unit"][a.transfer],
+                   "transfer": ["fused", "balanced", "per-unit", "fused-gather-first"][a.transfer],
                    "entries_per_step": entries},
         "hit_rate": round(n_hit / max(n_hit + n_miss, 1), 5),
         "miss_rows_per_step": round(miss_per_step, 1),

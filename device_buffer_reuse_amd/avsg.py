@@ -23,7 +23,7 @@ ERR_UNSORTED, ERR_RANGE, ERR_CAPACITY, ERR_STATE = 16, 17, 18, 19
 KV_SPLIT, KV_LATENT = 0, 1
 POLICY_LIFETIME, POLICY_BUCKET_LRU = 0, 1
 HOST_COHERENT = 1
-TRANSFER_FUSED, TRANSFER_BALANCED, TRANSFER_PER_UNIT = 0, 1, 2
+TRANSFER_FUSED, TRANSFER_BALANCED, TRANSFER_PER_UNIT, TRANSFER_FUSED_GATHER_FIRST = 0, 1, 2, 3
 MATCH_HASH, MATCH_MERGE = 0, 1
 
 EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_set_stream",

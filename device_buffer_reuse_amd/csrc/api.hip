@@ -207,7 +207,8 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
 }
 
 avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode) {
-  if (!ctx || mode < AVSG_TRANSFER_FUSED || mode > AVSG_TRANSFER_PER_UNIT) return AVSG_ERR_INVALID_ARG;
+  if (!ctx || mode < AVSG_TRANSFER_FUSED || mode > AVSG_TRANSFER_FUSED_GATHER_FIRST)
+    return AVSG_ERR_INVALID_ARG;
   ctx->transfer_mode = mode;
   return AVSG_OK;
 }
@@ -383,8 +384,10 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   gp.units = ctx->d.units;
   gp.ucap = ctx->ws.ucap;
   gp.row16 = ctx->d.row_elems * 2 / 16;
+  const bool fused = ctx->transfer_mode == AVSG_TRANSFER_FUSED ||
+                     ctx->transfer_mode == AVSG_TRANSFER_FUSED_GATHER_FIRST;
   gp.per_unit = ctx->transfer_mode == AVSG_TRANSFER_PER_UNIT;
-  if (ctx->transfer_mode != AVSG_TRANSFER_FUSED &&
+  if (!fused &&
       launch_gather(gp, gp.per_unit ? ctx->d.units : ctx->gather_grid, ctx->stream) != hipSuccess)
     return AVSG_ERR_HIP;
   prof_mark(ctx, 2);
@@ -392,11 +395,11 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   AttnParams ap;
   ap.sel_slot = hs->sel_slot;
   ap.sel = sel_idx;
-  ap.fetch = ctx->transfer_mode == AVSG_TRANSFER_FUSED ? (const uint8_t*)(ws + ctx->ws.fetch) : nullptr;
+  ap.fetch = fused ? (const uint8_t*)(ws + ctx->ws.fetch) : nullptr;
   ap.host_kv = (const uint16_t*)host_dev;
   ap.N = c.n_entries;
   ap.token = 0;
-  ap.gather_first = 0;
+  ap.gather_first = ctx->transfer_mode == AVSG_TRANSFER_FUSED_GATHER_FIRST ? 1 : 0;
   ap.unit_status = unit_status;
   ap.q = q;
   ap.buf_kv = buf_kv;

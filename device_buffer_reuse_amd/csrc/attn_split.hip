@@ -50,7 +50,9 @@ constexpr int kD = 128;                              // head dim of the split la
 constexpr int kTileRows = 32;                        // token rows per LDS tile
 constexpr int kRowBytes = 4 * kD;                    // K half + V half
 constexpr int kTileBytes = kTileRows * kRowBytes;    // 16 KiB
-constexpr int kBufs = 3;
+constexpr int kBufs = 3;                             // LDS tiles per workgroup
+constexpr int kAhead = kBufs - 1;                    // tiles in flight beyond the one in use
+static_assert(kAhead >= 1 && kAhead <= 3, "tile pipeline depth");
 constexpr int kWaves = kAttnThreads / 64;            // 4
 constexpr int kCopies = kTileBytes / 16 / kAttnThreads;  // 4 per lane per tile
 constexpr int kSplitRows = 256;                      // token rows per workgroup
@@ -280,6 +282,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
     return tpe == 1 ? r : (int)__umulhi((uint32_t)r, tpe_magic);
   };
   const int row_base = 8 * w + (lane >> 5);
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, in a scalar register
   const int copy_off = ((lane >> 4) & 1) * v_off + (lane & 15) * 8;  // elements
   // Copies tile t into buffer `buf`; rows past the split repeat its last row
   // (their scores are masked) so every wave issues exactly kCopies copies.
@@ -306,8 +309,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
       const bool host = ri[x].y >= 0;
       const uint16_t* base = host ? hbase : ubase;
       const uint32_t idx = (uint32_t)(host ? ri[x].y : ri[x].x);
-      const uint16_t* src = base + (size_t)idx * p.row_elems + off;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + (w * kCopies + x) * 1024), 16, 0,
+      // one 32 x 32 -> 64-bit multiply per copy
+      const uint16_t* src = base + (uint64_t)idx * (uint32_t)p.row_elems + off;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + (wu * kCopies + x) * 1024), 16, 0,
                                        0);
       if (host && rt + 2 * x < r1) fetched |= 1u << x;
     }
@@ -350,21 +354,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
     for (int x = 0; x < 8; ++x) o[k][x] = 0.f;
 
   const int ntiles = (r1 - r0 + kTileRows - 1) / kTileRows;
-  uint32_t f_cur = stage(0, 0), f_next = 0;
-  if (ntiles > 1) f_next = stage(1, 1);
+  // fmask[i]: this lane's host-fetched copies of tile t + i
+  uint32_t fmask[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) fmask[i] = i < ntiles ? stage(i, i) : 0u;
   // this lane's two rows of a tile: 8w + rg and 8w + 4 + rg
   const uint32_t lane_off = (8 * w + rg) * kRowBytes + c * 16;
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t % kBufs;
-    if (t + 1 < ntiles) vm_wait<kCopies>();
-    else vm_wait<0>();
-    write_back(t, buf, f_cur);
-    asm volatile("s_barrier" ::: "memory");  // tile t in LDS; tile (t+2)%3 free
-    uint32_t f_new = 0;
-    if (t + 2 < ntiles) f_new = stage(t + 2, (t + 2) % kBufs);
-    f_cur = f_next;
-    f_next = f_new;
+    // tile t has landed once only the copies of the later tiles in flight
+    // (kCopies each) may still be outstanding
+    const int later = min(kAhead - 1, ntiles - 1 - t);
+    if (later <= 0) vm_wait<0>();
+    else if (later == 1) vm_wait<kCopies>();
+    else vm_wait<2 * kCopies>();
+    write_back(t, buf, fmask[0]);
+    asm volatile("s_barrier" ::: "memory");  // tile t in LDS; tile t-1's buffer free
+#pragma unroll
+    for (int i = 0; i + 1 < kAhead; ++i) fmask[i] = fmask[i + 1];
+    fmask[kAhead - 1] = t + kAhead < ntiles ? stage(t + kAhead, (t + kAhead) % kBufs) : 0u;
 
     const uint32_t a = tile_lds + buf * kTileBytes + lane_off;
     u32x4 k0, k1, v0, v1;
@@ -486,7 +495,7 @@ static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
     resident = cus * per_cu;
   }
   AttnParams p = p0;
-  p.gather_first = (int64_t)grid.x > resident ? 1 : 0;
+  if ((int64_t)grid.x > resident) p.gather_first = 1;
   for (int j = 0; j < p0.T; ++j) {
     p.token = j;
     hipLaunchKernelGGL(attn_split_kernel<G>, grid, dim3(kAttnThreads), 0, s, p);

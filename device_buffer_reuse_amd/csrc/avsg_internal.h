@@ -86,6 +86,7 @@ struct AttnParams {
   int32_t units, Hkv, Hq, T, k, tpe, row_elems, nsplit, split_rows;
   int32_t token;              // query token of this launch
   int32_t gather_first;       // split layout: fetch a split's missed entries before its tiles
+                              // (1 forces it; the launcher also sets it for multi-round grids)
   float scale_log2e;
 };
 

@@ -185,16 +185,22 @@ const char* avsg_status_string(avsg_status s);
  *  AVSG_TRANSFER_FUSED (default): the attention workgroup that consumes a
  *    missed row reads it from pinned host memory and stores it into its slot,
  *    so host transfers overlap the HBM reads of the hits; the rows are spread
- *    over all workgroups in selection order.
+ *    over all workgroups in selection order.  In the K/V split layout each
+ *    workgroup either copies its missed rows with the tiles that hold them
+ *    (when all workgroups are resident at once) or first gathers all of them
+ *    into their slots (when the grid runs in several rounds).
  *  AVSG_TRANSFER_BALANCED: a separate kernel copies the global list of missed
  *    rows, split into equal shares over all workgroups, before attention.
  *  AVSG_TRANSFER_PER_UNIT: like BALANCED, but each unit's rows are copied by
  *    one workgroup (request-level assignment; kept for comparison).
+ *  AVSG_TRANSFER_FUSED_GATHER_FIRST: FUSED with the gather-first form in the
+ *    split layout whatever the grid size (the latent layout: as FUSED).
  * Results are identical in every mode. */
 typedef enum avsg_transfer_mode {
   AVSG_TRANSFER_FUSED = 0,
   AVSG_TRANSFER_BALANCED = 1,
-  AVSG_TRANSFER_PER_UNIT = 2
+  AVSG_TRANSFER_PER_UNIT = 2,
+  AVSG_TRANSFER_FUSED_GATHER_FIRST = 3
 } avsg_transfer_mode;
 avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode);
 

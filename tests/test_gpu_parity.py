@@ -55,10 +55,11 @@ def test_parity_small(name):
 
 
 @pytest.mark.parametrize("name", ["batch_ragged", "mtp_ragged", "long_ragged", "mla_ragged"])
-@pytest.mark.parametrize("transfer", [1, 2])
+@pytest.mark.parametrize("transfer", [1, 2, 3])
 def test_parity_transfer_modes(name, transfer):
     """The separate gather kernel (balanced shares, or one workgroup per unit)
-    gives the same state, buffer bytes and outputs as the fused default."""
+    and the fused transfer forced into its gather-first form give the same
+    state, buffer bytes and outputs as the oracle."""
     w = SMALL[name].replace(steps=6)
     say("[parity] %s transfer mode %d" % (name, transfer))
     sel = tg.selections(w)
