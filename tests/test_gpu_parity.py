@@ -40,6 +40,60 @@ SMALL = {
 }
 
 
+# Edge shapes: k equal to the slot count, pages of 3 tokens whose rows straddle
+# the 256-row attention splits, 32-token pages, the largest lifetime and
+# bucket counts, 2 query heads per KV head, a single selected latent row, and
+# a latent head whose selection fits one split.
+EDGE = {
+    "k_eq_S": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=3000, k=200,
+                                      n_slots=200, steps=8),
+    "tpe3_straddle": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=1000,
+                                             tokens_per_entry=3, k=200, n_slots=400, steps=8),
+    "tpe32": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=4, n_entries=300,
+                                     tokens_per_entry=32, k=20, n_slots=40, steps=8),
+    "L126": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=3000, k=150,
+                                    n_slots=400, lifetime_L=126, steps=10),
+    "B127": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=4, n_entries=2000,
+                                    tokens_per_entry=1, k=100, n_slots=300, n_buckets=127, steps=12),
+    "gqa2": tg.WORKLOADS[2].replace(batch=2, n_kv_heads=2, n_q_heads=4, n_entries=3000, k=333,
+                                    n_slots=800, steps=8),
+    "mla_k1": tg.WORKLOADS[5].replace(batch=2, n_entries=100, k=1, n_slots=4, steps=6, overlap=0.0),
+    "mla_one_split": tg.WORKLOADS[5].replace(batch=2, n_entries=2000, k=300, n_slots=600, steps=6),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_parity_edge(name):
+    w = EDGE[name]
+    say("[parity-edge] %s" % name)
+    sel = tg.selections(w)
+    run = Runner(w)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+    finally:
+        run.close()
+
+
+def test_parity_select_everything():
+    """Every entry of the context selected every step (k = N = S): all misses
+    on the first step, all hits afterwards."""
+    w = tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=300, k=300,
+                                n_slots=300, steps=5)
+    say("[parity-edge] select everything")
+    sel = np.broadcast_to(np.arange(w.k, dtype=np.int32), (w.steps, w.units, 1, w.k)).copy()
+    run = Runner(w)
+    try:
+        for t in range(w.steps):
+            r, _ = run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+            if t == 0:
+                assert (r["n_miss"] == w.k).all()
+            else:
+                assert (r["n_hit"] == w.k).all()
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_parity_small(name):
     w = SMALL[name]
