@@ -58,7 +58,9 @@ constexpr int kTileInstr = (kTilePieces + 63) / 64;  // 37 wave-wide copies per 
 constexpr int kTileElems = kChunk * kRow;
 constexpr int kKSteps = kDqk / 32;               // 18 MFMA k-steps for QK^T
 constexpr int kMTiles = kDv / 16;                // 32 output tiles per wave
-constexpr int kBufs = 3;
+constexpr int kBufs = 3;                         // LDS tiles
+constexpr int kAhead = kBufs - 1;                // chunks in flight beyond the one in use
+static_assert(kAhead >= 1 && kAhead <= 3, "chunk pipeline depth");
 constexpr int kMaxSplit = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -239,26 +241,37 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   const int nchunks = (ne + kChunk - 1) / kChunk;
-  uint32_t f_cur = stage(0, 0), f_next = 0;
-  if (nchunks > 1) f_next = stage(1, 1);
+  // fmask[i]: this wave's host-fetched copies of chunk c + i
+  uint32_t fmask[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) fmask[i] = i < nchunks ? stage(i, i) : 0u;
   // per-lane operand addresses within a tile
   const uint32_t k_off = li * kRowBytes + 16 * g;
   const uint32_t v_off = (4 * g + (li >> 2)) * kRowBytes + 8 * (li & 3);
 
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c % kBufs;
-    if (c + 1 < nchunks) {
+    // chunk c has landed once only this wave's copies of the later chunks in
+    // flight (kInstr or kInstr - 1 each) may still be outstanding
+    const int later = min(kAhead - 1, nchunks - 1 - c);
+    if (later <= 0) {
+      vm_wait<0>();
+    } else if (later == 1) {
       if (w < kFull) vm_wait<kInstr>();
       else vm_wait<kInstr - 1>();
     } else {
-      vm_wait<0>();
+      if (w < kFull) vm_wait<2 * kInstr>();
+      else vm_wait<2 * (kInstr - 1)>();
     }
-    write_back(c, buf, f_cur);
-    block_barrier();  // chunk c is in LDS; nobody reads tile (c+2)%3 any more
-    uint32_t f_new = 0;
-    if (c + 2 < nchunks) f_new = stage(c + 2, (c + 2) % kBufs);
-    f_cur = f_next;
-    f_next = f_new;
+    block_barrier();  // chunk c is in LDS; nobody reads chunk c-1's tile any more
+    const uint32_t f_now = fmask[0];
+#pragma unroll
+    for (int i = 0; i + 1 < kAhead; ++i) fmask[i] = fmask[i + 1];
+    fmask[kAhead - 1] = c + kAhead < nchunks ? stage(c + kAhead, (c + kAhead) % kBufs) : 0u;
+    // slot stores of chunk c's host rows, issued after the copies of chunk
+    // c + kAhead: the next chunk's wait (its copies are older) does not wait
+    // for them
+    write_back(c, buf, f_now);
 
     // S^T = K Q^T for tokens 0..15 and 16..31 of the chunk, this wave's heads
     const uint32_t ka = tile_lds + buf * kTileElems * 2 + k_off;

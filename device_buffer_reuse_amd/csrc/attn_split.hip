@@ -369,11 +369,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
     if (later <= 0) vm_wait<0>();
     else if (later == 1) vm_wait<kCopies>();
     else vm_wait<2 * kCopies>();
-    write_back(t, buf, fmask[0]);
     asm volatile("s_barrier" ::: "memory");  // tile t in LDS; tile t-1's buffer free
+    const uint32_t f_now = fmask[0];
 #pragma unroll
     for (int i = 0; i + 1 < kAhead; ++i) fmask[i] = fmask[i + 1];
     fmask[kAhead - 1] = t + kAhead < ntiles ? stage(t + kAhead, (t + kAhead) % kBufs) : 0u;
+    // slot stores of tile t's host rows, issued after the copies of tile
+    // t + kAhead: the next tile's wait (its copies are older) does not wait
+    // for them
+    write_back(t, buf, f_now);
 
     const uint32_t a = tile_lds + buf * kTileBytes + lane_off;
     u32x4 k0, k1, v0, v1;
