@@ -36,6 +36,19 @@ static int32_t next_pow2(int64_t x) {
   return c;
 }
 
+constexpr size_t kMRLdsLimit = 160 * 1024;
+
+// dynamic LDS of match_reserve: table, bucket counters, U and its slots,
+// per-wave bin counts and offsets, bin starts, scratch, miss list, and for
+// two tokens the union map and duplicate counts
+static size_t mr_lds_bytes(const avsg_config& c, const WsLayout& ws, const Derived& d) {
+  const int64_t tk = (int64_t)c.n_q_tokens * c.k;
+  const int64_t ints = 2 * (int64_t)ws.ucap + ws.table_cap + ws.table_cap / 4 +
+                       2 * 16 * (int64_t)d.nbins + d.nbins + 64 +
+                       (c.n_q_tokens > 1 ? tk : ws.ucap) + (c.n_q_tokens > 1 ? tk + c.k + 1 : 0);
+  return 4 * (size_t)ints;
+}
+
 bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   d->units = c.batch * c.n_kv_heads;
   d->G = c.n_q_heads / c.n_kv_heads;
@@ -45,7 +58,11 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   d->nbins = c.policy == AVSG_POLICY_BUCKET_LRU ? c.n_buckets + 1 : c.lifetime_L + 2;
   const int64_t tk = (int64_t)c.n_q_tokens * c.k;
   ws->ucap = (int32_t)(tk < c.n_slots ? tk : c.n_slots);
-  ws->table_cap = next_pow2(2 * (int64_t)ws->ucap);
+  // hash table of U: load factor <= 1/4 (overflowing 4-cell buckets are
+  // rare, so almost every probe ends at its home bucket) where the LDS of
+  // match_reserve allows, else <= 1/2
+  ws->table_cap = next_pow2(4 * (int64_t)ws->ucap);
+  if (mr_lds_bytes(c, *ws, *d) > kMRLdsLimit) ws->table_cap = next_pow2(2 * (int64_t)ws->ucap);
   d->log_table_cap = 0;
   while ((1 << d->log_table_cap) < ws->table_cap) ++d->log_table_cap;
   d->ubits = 1;
@@ -69,15 +86,18 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   off = align256(off + 4 * (size_t)d->units * T * ws->nsplit *
                            partial_stride(c.n_q_heads / c.n_kv_heads, c.head_dim_v));
   ws->total = off;
-  const int64_t lds_ints = 2 * (int64_t)ws->ucap + ws->table_cap + ws->table_cap / 4 +
-                           2 * 16 * (int64_t)d->nbins +
-                           d->nbins + 64 + (c.n_q_tokens > 1 ? tk : ws->ucap) +
-                           (c.n_q_tokens > 1 ? tk + c.k + 1 : 0);
-  d->mr_lds = 4 * (size_t)lds_ints;
+  d->mr_lds = mr_lds_bytes(c, *ws, *d);
   d->merge_pow2 = 64;
   while (d->merge_pow2 < c.n_slots) d->merge_pow2 <<= 1;
-  // merge baseline: one spare word, sorted (id, slot) pairs, slot -> union index
-  d->mr_lds_merge = d->mr_lds + 4 + 8 * (size_t)d->merge_pow2 + 4 * (size_t)c.n_slots;
+  // merge baseline: the table at load factor <= 1/2 (it only validates and
+  // hashes the selection), then one spare word, the sorted (id, slot) pairs
+  // and slot -> union index
+  WsLayout wm = *ws;
+  wm.table_cap = next_pow2(2 * (int64_t)ws->ucap);
+  d->table_cap_merge = wm.table_cap;
+  d->log_table_cap_merge = 0;
+  while ((1 << d->log_table_cap_merge) < wm.table_cap) ++d->log_table_cap_merge;
+  d->mr_lds_merge = mr_lds_bytes(c, wm, *d) + 4 + 8 * (size_t)d->merge_pow2 + 4 * (size_t)c.n_slots;
   return true;
 }
 
@@ -119,7 +139,7 @@ static avsg_status check_config_impl(const avsg_config* c) {
   WsLayout ws;
   Derived d;
   layout_for(*c, &ws, &d);
-  if (d.mr_lds > 160 * 1024) return AVSG_ERR_UNSUPPORTED;
+  if (d.mr_lds > kMRLdsLimit) return AVSG_ERR_UNSUPPORTED;
   // a hash cell packs (id << ubits | union index) with the top bit clear
   if ((int64_t)c->n_entries > ((int64_t)1 << (31 - d.ubits))) return AVSG_ERR_UNSUPPORTED;
   // gather addresses rows with 32-bit piece indices
@@ -359,8 +379,9 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   mp.T = c.n_q_tokens;
   mp.k = c.k;
   mp.ucap = ctx->ws.ucap;
-  mp.table_cap = ctx->ws.table_cap;
-  mp.log_table_cap = ctx->d.log_table_cap;
+  const bool merge = ctx->match_mode == AVSG_MATCH_MERGE;
+  mp.table_cap = merge ? ctx->d.table_cap_merge : ctx->ws.table_cap;
+  mp.log_table_cap = merge ? ctx->d.log_table_cap_merge : ctx->d.log_table_cap;
   mp.ubits = ctx->d.ubits;
   mp.policy = c.policy;
   mp.L = c.lifetime_L;
@@ -369,7 +390,7 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   mp.match_mode = ctx->match_mode;
   mp.merge_pow2 = ctx->d.merge_pow2;
   prof_mark(ctx, 0);
-  const size_t mr_lds = ctx->match_mode == AVSG_MATCH_MERGE ? ctx->d.mr_lds_merge : ctx->d.mr_lds;
+  const size_t mr_lds = merge ? ctx->d.mr_lds_merge : ctx->d.mr_lds;
   if (launch_match_reserve(mp, ctx->d.units, mr_lds, ctx->stream) != hipSuccess)
     return AVSG_ERR_HIP;
   prof_mark(ctx, 1);

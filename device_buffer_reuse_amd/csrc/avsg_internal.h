@@ -29,6 +29,7 @@ struct Derived {
   size_t mr_lds;        // dynamic LDS bytes of match_reserve
   size_t mr_lds_merge;  // the same with the merge baseline's sort buffers
   int32_t merge_pow2;
+  int32_t table_cap_merge, log_table_cap_merge;  // hash table of the merge baseline
 };
 
 bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d);

@@ -14,8 +14,8 @@
 //  * The union U of the iteration's sorted selections is built in LDS (for
 //    two tokens by a rank formula: each element's position in U is found by
 //    binary search in the other list minus the duplicates before it).
-//  * U is hashed into an LDS open-addressing table (load factor <= 0.5,
-//    multiplicative hash) of 4-cell buckets.  A cell packs (id << ubits |
+//  * U is hashed into an LDS open-addressing table (load factor <= 1/4 where
+//    LDS allows, else <= 1/2; multiplicative hash) of 4-cell buckets.  A cell packs (id << ubits |
 //    union index) in 32 bits.  Insertion takes a position in the home bucket
 //    from a per-bucket attempt counter (one LDS atomic; a full bucket sends
 //    the entry on along its double-hashing sequence), so a counter of at
@@ -24,7 +24,7 @@
 //    of the buffer then probes its resident id, one slot per lane, 64 lanes
 //    at a time: one 16-byte read fetches the home bucket, a second its
 //    counter, and only the rare probe of an overflowed bucket reads on.
-//    Hashing U rather than the slots keeps the table at 2|U| cells and turns
+//    Hashing U rather than the slots keeps the table at 4|U| cells and turns
 //    "is this slot a candidate" into the same probe.
 //  * Victim selection is a stable counting selection: each candidate slot gets
 //    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first).  A
@@ -196,22 +196,18 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   constexpr int kSelRegs = 4;
   int32_t selr[kSelRegs];
 #pragma unroll
-  for (int r = 0; r < kSelRegs; ++r) {
-    const int i = tid + r * kMRThreads;
-    selr[r] = i < tk ? sel[i] : 0;
-  }
+  for (int r = 0; r < kSelRegs; ++r) selr[r] = sel[min(tid + r * kMRThreads, tk - 1)];
   const int R = ((S + kMRThreads - 1) / kMRThreads) * 64;  // slots per wave, multiple of 64
   const int s0 = w * R, s1 = min(s0 + R, S);
+  // every lane loads all its slots unconditionally (an index clamped into the
+  // buffer), so the loads are in flight together; lanes past the wave's range
+  // are marked invalid where the values are first used
   int tok[MAXP], lf[MAXP], bin[MAXP], rank[MAXP];
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) {
-    const int s = s0 + q * 64 + lane;
-    tok[q] = kInvalid;
-    lf[q] = 0;
-    if (q * 64 < R && s < s1) {
-      tok[q] = slot_table[s];
-      lf[q] = lifetimes[s];
-    }
+    const int s = min(s0 + q * 64 + lane, S - 1);
+    tok[q] = slot_table[s];
+    lf[q] = lifetimes[s];
   }
 #pragma unroll
   for (int r = 0; r < kSelRegs; ++r) {
@@ -220,8 +216,12 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   }
   for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) stage[i] = sel[i];
   if (tid < 64) sMisc[tid] = 0;
-  for (int i = tid; i < C; i += kMRThreads) sHash[i] = -1;
-  for (int i = tid; i < (C >> 2); i += kMRThreads) sBcnt[i] = 0;
+  {  // table cells -1 and bucket counters 0, 16 bytes per store (C is a multiple of 64)
+    int4* h4 = reinterpret_cast<int4*>(sHash);
+    for (int i = tid; i < (C >> 2); i += kMRThreads) h4[i] = make_int4(-1, -1, -1, -1);
+    int4* b4 = reinterpret_cast<int4*>(sBcnt);
+    for (int i = tid; i < (C >> 4); i += kMRThreads) b4[i] = make_int4(0, 0, 0, 0);
+  }
   for (int i = tid; i < ucap; i += kMRThreads) sUslot[i] = -1;
   __syncthreads();
 
@@ -294,6 +294,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   }
 
   // ---- 4. every slot probes its resident id; state checks
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) {
+    if (!(q * 64 < R && s0 + q * 64 + lane < s1)) {
+      tok[q] = kInvalid;
+      lf[q] = 0;
+    }
+  }
   int hit_i[MAXP];
   if (sMisc[0] == 0 && p.match_mode == AVSG_MATCH_MERGE) {
     // comparison baseline: sort the resident (id, slot) pairs by id (bitonic,
@@ -428,17 +435,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       for (int qq = 0; qq < kGrp; ++qq) {
         const int i = res[qq];
         if (i >= 0) {
-          sUslot[i] = s0 + (q0 + qq) * 64 + lane;
+          // an id of U held by two slots: the second exchange finds the first
+          if (atomicExch(&sUslot[i], s0 + (q0 + qq) * 64 + lane) != -1) bad = 1;
           hit_i[q0 + qq] = i;
           bin[q0 + qq] = -1;  // hit
         }
       }
     }
-    __syncthreads();
-    // an id of U held by two slots: only one of the two stores survived
-#pragma unroll
-    for (int q = 0; q < MAXP; ++q)
-      if (hit_i[q] >= 0 && sUslot[hit_i[q]] != s0 + q * 64 + lane) bad = 1;
     if (bad) atomicOr(&sMisc[0], kFlagState);
   }
   __syncthreads();
