@@ -196,7 +196,7 @@ def ablations(b, w, n):
     out["skewed_transfer"] = skew
     match = {}
     b.load_trace("natural", n + 16)
-    for mode, name in ((0, "hash"), (1, "dual_pointer")):
+    for mode, name in ((0, "hash"), (2, "hash_table"), (1, "dual_pointer")):
         b.ctx.set_match_mode(mode)
         b.reset()
         b.run(0, 16)

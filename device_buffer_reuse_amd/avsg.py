@@ -24,7 +24,7 @@ KV_SPLIT, KV_LATENT = 0, 1
 POLICY_LIFETIME, POLICY_BUCKET_LRU = 0, 1
 HOST_COHERENT = 1
 TRANSFER_FUSED, TRANSFER_BALANCED, TRANSFER_PER_UNIT, TRANSFER_FUSED_GATHER_FIRST = 0, 1, 2, 3
-MATCH_HASH, MATCH_MERGE = 0, 1
+MATCH_HASH, MATCH_MERGE, MATCH_HASH_TABLE = 0, 1, 2
 
 EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_set_stream",
             "avsg_destroy", "avsg_reset", "avsg_step", "avsg_last_error", "avsg_validate_state",

@@ -44,7 +44,7 @@ constexpr size_t kMRLdsLimit = 160 * 1024;
 static size_t mr_lds_bytes(const avsg_config& c, const WsLayout& ws, const Derived& d) {
   const int64_t tk = (int64_t)c.n_q_tokens * c.k;
   const int64_t ints = 2 * (int64_t)ws.ucap + ws.table_cap + ws.table_cap / 4 +
-                       2 * 16 * (int64_t)d.nbins + d.nbins + 64 +
+                       2 * 16 * (int64_t)d.nbins + d.nbins + 128 +
                        (c.n_q_tokens > 1 ? tk : ws.ucap) + (c.n_q_tokens > 1 ? tk + c.k + 1 : 0);
   return 4 * (size_t)ints;
 }
@@ -65,6 +65,12 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   if (mr_lds_bytes(c, *ws, *d) > kMRLdsLimit) ws->table_cap = next_pow2(2 * (int64_t)ws->ucap);
   d->log_table_cap = 0;
   while ((1 << d->log_table_cap) < ws->table_cap) ++d->log_table_cap;
+  // ids of a small context are matched by direct addressing (a membership bit
+  // and a rank base per 32 ids) when that takes no more LDS than the table
+  {
+    const int64_t words = (((int64_t)c.n_entries + 31) / 32 + 3) & ~(int64_t)3;
+    d->direct_words = 2 * words <= (int64_t)ws->table_cap + ws->table_cap / 4 ? (int32_t)words : 0;
+  }
   d->ubits = 1;
   while ((1 << d->ubits) < ws->ucap) ++d->ubits;
   const int64_t rows = (int64_t)c.k * c.tokens_per_entry;
@@ -234,7 +240,8 @@ avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode) {
 }
 
 avsg_status avsg_set_match_mode(avsg_ctx* ctx, int32_t mode) {
-  if (!ctx || (mode != AVSG_MATCH_HASH && mode != AVSG_MATCH_MERGE)) return AVSG_ERR_INVALID_ARG;
+  if (!ctx || (mode != AVSG_MATCH_HASH && mode != AVSG_MATCH_MERGE && mode != AVSG_MATCH_HASH_TABLE))
+    return AVSG_ERR_INVALID_ARG;
   if (mode == AVSG_MATCH_MERGE) {
     if ((int64_t)ctx->d.mr_lds_merge > ctx->lds_max) return AVSG_ERR_UNSUPPORTED;
     if (match_reserve_set_lds(ctx->d.mr_lds_merge) != hipSuccess) return AVSG_ERR_HIP;
@@ -389,6 +396,7 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   mp.nbins = ctx->d.nbins;
   mp.match_mode = ctx->match_mode;
   mp.merge_pow2 = ctx->d.merge_pow2;
+  mp.direct_words = ctx->match_mode == AVSG_MATCH_HASH ? ctx->d.direct_words : 0;
   prof_mark(ctx, 0);
   const size_t mr_lds = merge ? ctx->d.mr_lds_merge : ctx->d.mr_lds;
   if (launch_match_reserve(mp, ctx->d.units, mr_lds, ctx->stream) != hipSuccess)

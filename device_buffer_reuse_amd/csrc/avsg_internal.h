@@ -30,6 +30,7 @@ struct Derived {
   size_t mr_lds_merge;  // the same with the merge baseline's sort buffers
   int32_t merge_pow2;
   int32_t table_cap_merge, log_table_cap_merge;  // hash table of the merge baseline
+  int32_t direct_words;  // membership words of the direct-address match (0: hash table)
 };
 
 bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d);
@@ -59,6 +60,8 @@ struct MatchReserveParams {
   int32_t S, N, T, k, ucap, table_cap, log_table_cap, ubits, policy, L, B, nbins;
   int32_t match_mode;     // avsg_match_mode
   int32_t merge_pow2;     // power of two >= S (sort size of the merge baseline)
+  int32_t direct_words;   // > 0: match through N-bit membership words and rank bases
+                          // (this many words each, multiple of 4) instead of the hash table
 };
 
 struct GatherParams {

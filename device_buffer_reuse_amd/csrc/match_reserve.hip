@@ -121,12 +121,9 @@ __device__ __forceinline__ int bucket_find(const int4 c, uint32_t xs, uint32_t l
   return (m0 | m1 | m2 | m3) ? (v & umask) : -1;
 }
 
-__device__ __forceinline__ void hash_insert(int32_t* sHash, int32_t* sBcnt, int log_cap, int ubits,
-                                            int32_t x, int32_t i) {
-  const int bmask = ((1 << log_cap) >> 2) - 1;
-  uint32_t hb = hash_id(x, log_cap) >> 2;
-  const uint32_t step = hash_step(x, log_cap);
-  const int32_t v = (x << ubits) | i;
+// Inserts cell v, trying buckets hb, hb + step, ... (bmask = buckets - 1).
+__device__ __forceinline__ void hash_insert_at(int32_t* sHash, int32_t* sBcnt, uint32_t bmask,
+                                               uint32_t hb, uint32_t step, int32_t v) {
   while (true) {
     const int pos = atomicAdd(&sBcnt[hb], 1);
     if (pos < 4) {
@@ -135,6 +132,13 @@ __device__ __forceinline__ void hash_insert(int32_t* sHash, int32_t* sBcnt, int 
     }
     hb = (hb + step) & bmask;
   }
+}
+
+__device__ __forceinline__ void hash_insert(int32_t* sHash, int32_t* sBcnt, int log_cap, int ubits,
+                                            int32_t x, int32_t i) {
+  const uint32_t bmask = ((1u << log_cap) >> 2) - 1;
+  hash_insert_at(sHash, sBcnt, bmask, hash_id(x, log_cap) >> 2, hash_step(x, log_cap),
+                 (x << ubits) | i);
 }
 
 enum { kFlagRange = 1, kFlagUnsorted = 2, kFlagCapacity = 4, kFlagState = 8 };
@@ -180,11 +184,20 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   int32_t* sCnt = sUslot + ucap;             // [16][nbins] per-wave candidates per bin
   int32_t* sOff = sCnt + kMRWaves * nbins;   // [16][nbins] first rank of (wave, bin)
   int32_t* sTot = sOff + kMRWaves * nbins;   // [nbins] -> exclusive bin starts
-  int32_t* sMisc = sTot + nbins;             // [64]: 0 flags, 1 evictions, 16.. scan scratch
-  int32_t* sMiss = sMisc + 64;               // [max(ucap, T*k)]; T=2: first holds both lists
+  int32_t* sMisc = sTot + nbins;             // [128]: 0 flags, 1 evictions, 16.. scan scratch,
+                                             // 64.. per-lane sink of masked-off LDS atomics
+  int32_t* sMiss = sMisc + 128;              // [max(ucap, T*k)]; T=2: first holds both lists
   int32_t* sMap = sMiss + (T > 1 ? tk : ucap);  // T=2: [T*k] union index per (token, entry)
   int32_t* sDup = sMap + (T > 1 ? tk : 0);      // T=2: [k+1] duplicates before each A index
   int32_t* sWs = sMisc + 16;
+  int32_t* sSink = sMisc + 64;
+  // direct-address form (dw > 0 words, in place of the hash table): bit x of
+  // the membership words is set iff id x is in U, and the rank base of a word
+  // is the union index of the first id of U in that word, so the union index
+  // of a member x is base[x / 32] + (members of its word below x)
+  const int dw = p.direct_words;
+  uint32_t* sBits = reinterpret_cast<uint32_t*>(sHash);  // [dw]
+  int32_t* sBase = sHash + dw;                            // [dw]
 
   const int32_t* sel = p.sel + (size_t)u * tk;
   int32_t* slot_table = p.slot_table + (size_t)u * S;
@@ -215,8 +228,11 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     if (i < tk) stage[i] = selr[r];
   }
   for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) stage[i] = sel[i];
-  if (tid < 64) sMisc[tid] = 0;
-  {  // table cells -1 and bucket counters 0, 16 bytes per store (C is a multiple of 64)
+  if (tid < 128) sMisc[tid] = 0;
+  if (dw > 0) {  // membership words 0 (dw is a multiple of 4); rank bases need no init
+    int4* b4 = reinterpret_cast<int4*>(sBits);
+    for (int i = tid; i < (dw >> 2); i += kMRThreads) b4[i] = make_int4(0, 0, 0, 0);
+  } else {  // table cells -1 and bucket counters 0, 16 bytes per store (C is a multiple of 64)
     int4* h4 = reinterpret_cast<int4*>(sHash);
     for (int i = tid; i < (C >> 2); i += kMRThreads) h4[i] = make_int4(-1, -1, -1, -1);
     int4* b4 = reinterpret_cast<int4*>(sBcnt);
@@ -231,12 +247,67 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const int log_cap = p.log_table_cap, ubits = p.ubits;
   {
     int bad = 0;
-    for (int i = tid; i < tk; i += kMRThreads) {
+    const uint32_t bmask = ((1u << log_cap) >> 2) - 1;
+    // entries held in registers: the predecessor reads and the first
+    // insertion attempts of all of them are issued together (a lane with
+    // nothing to insert adds to its own sink word instead)
+    int32_t prv[kSelRegs], pos[kSelRegs];
+    uint32_t hb[kSelRegs];
+#pragma unroll
+    for (int r = 0; r < kSelRegs; ++r) prv[r] = stage[max(min(tid + r * kMRThreads, tk) - 1, 0)];
+    if (T == 1 && dw > 0) {
+#pragma unroll
+      for (int r = 0; r < kSelRegs; ++r) {
+        const int i = tid + r * kMRThreads;
+        const int32_t x = selr[r];
+        if (i < tk && x >= 0 && x < N) {
+          atomicOr(&sBits[x >> 5], 1u << (x & 31));
+          if (i == 0 || (prv[r] >> 5) != (x >> 5)) sBase[x >> 5] = i;
+        }
+      }
+    } else if (T == 1) {
+#pragma unroll
+      for (int r = 0; r < kSelRegs; ++r) {
+        const int i = tid + r * kMRThreads;
+        const int32_t x = selr[r];
+        hb[r] = hash_id(x, log_cap) >> 2;
+        pos[r] = atomicAdd((i < tk && x >= 0 && x < N) ? &sBcnt[hb[r]] : &sSink[lane], 1);
+      }
+#pragma unroll
+      for (int r = 0; r < kSelRegs; ++r) {
+        const int i = tid + r * kMRThreads;
+        const int32_t x = selr[r];
+        if (i < tk && x >= 0 && x < N) {
+          const int32_t v = (x << ubits) | i;
+          if (pos[r] < 4)
+            sHash[hb[r] * 4 + pos[r]] = v;
+          else
+            hash_insert_at(sHash, sBcnt, bmask, (hb[r] + hash_step(x, log_cap)) & bmask,
+                           hash_step(x, log_cap), v);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kSelRegs; ++r) {
+      const int i = tid + r * kMRThreads;
+      const int32_t x = selr[r];
+      const bool live = i < tk, in_range = x >= 0 && x < N;
+      // a token's list starts at 0 and, for the second token, at k (T <= 2)
+      bad |= (live && !in_range) ? kFlagRange : 0;
+      bad |= (live && i != 0 && i != k && x <= prv[r]) ? kFlagUnsorted : 0;
+    }
+    for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) {
       const int32_t x = stage[i];
       const bool in_range = x >= 0 && x < N;
       if (!in_range) bad |= kFlagRange;
-      if (i % k != 0 && x <= stage[i - 1]) bad |= kFlagUnsorted;
-      if (T == 1 && in_range) hash_insert(sHash, sBcnt, log_cap, ubits, x, i);
+      const int32_t xp = stage[i - 1];
+      if (i != k && x <= xp) bad |= kFlagUnsorted;
+      if (T == 1 && in_range && dw > 0) {
+        atomicOr(&sBits[x >> 5], 1u << (x & 31));
+        if ((xp >> 5) != (x >> 5)) sBase[x >> 5] = i;
+      } else if (T == 1 && in_range) {
+        hash_insert(sHash, sBcnt, log_cap, ubits, x, i);
+      }
     }
     if (bad) atomicOr(&sMisc[0], bad);
   }
@@ -287,7 +358,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 
   // ---- 3. hash U into the LDS table (two tokens; one token did it above)
   if (T > 1) {
-    if (sMisc[0] == 0) {
+    if (sMisc[0] == 0 && dw > 0) {
+      for (int i = tid; i < nu; i += kMRThreads) {
+        const int32_t x = sU[i];
+        atomicOr(&sBits[x >> 5], 1u << (x & 31));
+        if (i == 0 || (sU[i - 1] >> 5) != (x >> 5)) sBase[x >> 5] = i;
+      }
+    } else if (sMisc[0] == 0) {
       for (int i = tid; i < nu; i += kMRThreads) hash_insert(sHash, sBcnt, log_cap, ubits, sU[i], i);
     }
     __syncthreads();
@@ -378,6 +455,51 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       }
     }
     if (bad) atomicOr(&sMisc[0], kFlagState);
+  } else if (sMisc[0] == 0 && dw > 0) {
+    // direct-address membership: per slot one membership word and the rank
+    // base of that word, the reads of a group of (up to) 8 slots issued
+    // together; exact, so no probe reads on
+    int bad = 0;
+    constexpr int kGrp = MAXP < 8 ? MAXP : 8;
+#pragma unroll
+    for (int q0 = 0; q0 < MAXP; q0 += kGrp) {
+      uint32_t wd[kGrp];
+      int base[kGrp], res[kGrp], prev[kGrp];
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) {
+        const int q = q0 + qq;
+        const int32_t x = tok[q], l = lf[q];
+        const bool valid = x != kInvalid;
+        const bool resident = x >= 0 && x < N;
+        const bool bad_l = lru ? (l < 0 || (int64_t)l >= p.t) : (l < 0 || l > p.L);
+        bad |= (valid && (x < -1 || x >= N)) | (resident && bad_l);
+        bin[q] = valid ? 0 : kInvalid;
+        const int wi = resident ? (x >> 5) : 0;
+        wd[qq] = sBits[wi];
+        base[qq] = sBase[wi];
+      }
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) {
+        const int32_t x = tok[q0 + qq];
+        const uint32_t bit = 1u << (x & 31);
+        const bool member = x >= 0 && x < N && (wd[qq] & bit) != 0;
+        res[qq] = member ? base[qq] + __popc(wd[qq] & (bit - 1)) : -1;
+      }
+      // hits record their slot; an id of U held by two slots is found by the
+      // second exchange (a lane without a hit exchanges with its sink word)
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq)
+        prev[qq] = atomicExch(res[qq] >= 0 ? &sUslot[res[qq]] : &sSink[lane],
+                              s0 + (q0 + qq) * 64 + lane);
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) {
+        const bool hit = res[qq] >= 0;
+        bad |= hit && prev[qq] != -1;
+        hit_i[q0 + qq] = hit ? res[qq] : -1;
+        bin[q0 + qq] = hit ? -1 : bin[q0 + qq];
+      }
+    }
+    if (bad) atomicOr(&sMisc[0], kFlagState);
   } else if (sMisc[0] == 0) {
     int bad = 0;
     const int bmask = (C >> 2) - 1;
@@ -391,8 +513,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     for (int q0 = 0; q0 < MAXP; q0 += kGrp) {
       int4 cb[kGrp];
       uint32_t hb[kGrp];
-      int hc[kGrp];   // insertion attempts on the home bucket
-      int res[kGrp];  // union index, -1 absent, -2 searching
+      int res[kGrp];  // union index, -1 absent, -2 searching, -3 home bucket full
       // branch-free: every lane reads a bucket (in range for any id), and
       // only lanes holding a resident id use it
 #pragma unroll
@@ -408,13 +529,29 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         res[qq] = resident ? -2 : -1;
         hb[qq] = hash_id(x, log_cap) >> 2;
         cb[qq] = reinterpret_cast<const int4*>(sHash)[hb[qq]];
-        hc[qq] = sBcnt[hb[qq]];
       }
-      // home bucket: absent unless found there, or the bucket overflowed
+      // home bucket: found there, or absent if the bucket has an empty cell;
+      // a full home bucket without x needs its attempt counter
 #pragma unroll
       for (int qq = 0; qq < kGrp; ++qq) {
-        const int r = bucket_find(cb[qq], (uint32_t)tok[q0 + qq] << ubits, lim, umask);
-        res[qq] = res[qq] == -2 ? (r >= 0 ? r : (hc[qq] > 4 ? -2 : -1)) : -1;
+        const int4 c = cb[qq];
+        const int r = bucket_find(c, (uint32_t)tok[q0 + qq] << ubits, lim, umask);
+        const bool full = min(min(c.x, c.y), min(c.z, c.w)) >= 0;
+        res[qq] = res[qq] == -2 ? (r >= 0 ? r : (full ? -3 : -1)) : -1;
+      }
+      {  // counters of the (few) full home buckets: more than 4 attempts
+         // means x may live further along its sequence
+        bool any = false;
+#pragma unroll
+        for (int qq = 0; qq < kGrp; ++qq) any |= res[qq] == -3;
+        if (__ballot(any)) {
+          int hc[kGrp];
+#pragma unroll
+          for (int qq = 0; qq < kGrp; ++qq) hc[qq] = sBcnt[res[qq] == -3 ? hb[qq] : 0];
+#pragma unroll
+          for (int qq = 0; qq < kGrp; ++qq)
+            if (res[qq] == -3) res[qq] = hc[qq] > 4 ? -2 : -1;
+        }
       }
       while (true) {
         bool more = false;
@@ -431,15 +568,19 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         for (int qq = 0; qq < kGrp; ++qq)
           if (res[qq] == -2) res[qq] = bucket_check(cb[qq], ubits, tok[q0 + qq]);
       }
+      // hits record their slot; an id of U held by two slots is found by the
+      // second exchange (the results are checked after all are issued)
+      int prev[kGrp];
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq)
+        prev[qq] = atomicExch(res[qq] >= 0 ? &sUslot[res[qq]] : &sSink[lane],
+                              s0 + (q0 + qq) * 64 + lane);
 #pragma unroll
       for (int qq = 0; qq < kGrp; ++qq) {
-        const int i = res[qq];
-        if (i >= 0) {
-          // an id of U held by two slots: the second exchange finds the first
-          if (atomicExch(&sUslot[i], s0 + (q0 + qq) * 64 + lane) != -1) bad = 1;
-          hit_i[q0 + qq] = i;
-          bin[q0 + qq] = -1;  // hit
-        }
+        const bool hit = res[qq] >= 0;
+        bad |= hit && prev[qq] != -1;
+        hit_i[q0 + qq] = hit ? res[qq] : -1;
+        bin[q0 + qq] = hit ? -1 : bin[q0 + qq];
       }
     }
     if (bad) atomicOr(&sMisc[0], kFlagState);
@@ -466,23 +607,29 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     return;
   }
 
-  // ---- 5. policy update and eviction bins (registers)
+  // ---- 5. policy update and eviction bins (registers, branch-free):
+  //         hits take L (or the stamp t); other occupied slots decrement
+  //         (lifetime) and get bin 1 + lifetime, or bin 1 + (B - 1 - bucket)
+  //         (LRU, bucket = min(t - 1 - stamp, B - 1)); empty slots keep bin 0
+  if (!lru) {
 #pragma unroll
-  for (int q = 0; q < MAXP; ++q) {
-    if (tok[q] == kInvalid) continue;
-    if (bin[q] == -1) {
-      lf[q] = lru ? (int32_t)p.t : p.L;
-    } else if (tok[q] >= 0) {
-      if (!lru) {
-        lf[q] = lf[q] > 0 ? lf[q] - 1 : 0;
-        bin[q] = 1 + lf[q];
-      } else {
-        int64_t bucket = p.t - (int64_t)lf[q] - 1;
-        if (bucket > p.B - 1) bucket = p.B - 1;
-        bin[q] = 1 + (p.B - 1 - (int)bucket);
-      }
-    } else {
-      bin[q] = 0;
+    for (int q = 0; q < MAXP; ++q) {
+      const int x = tok[q], l = lf[q];
+      const bool hit = bin[q] == -1, occ = x >= 0;
+      const int dec = max(l - 1, 0);
+      lf[q] = hit ? p.L : (occ ? dec : l);
+      bin[q] = (x == kInvalid || hit) ? bin[q] : (occ ? 1 + dec : 0);
+    }
+  } else {
+    const int32_t t32 = (int32_t)p.t;  // stamps are int32 and below t
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      const int x = tok[q], l = lf[q];
+      const bool hit = bin[q] == -1, occ = x >= 0;
+      const int64_t age = p.t - 1 - (int64_t)l;
+      const int bucket = age < (int64_t)(p.B - 1) ? (int)age : p.B - 1;
+      lf[q] = hit ? t32 : l;
+      bin[q] = (x == kInvalid || hit) ? bin[q] : (occ ? p.B - bucket : 0);
     }
   }
 
@@ -491,8 +638,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   int m = 0;
   for (int c0 = 0; c0 < nu; c0 += 2 * kMRThreads) {
     const int i0 = c0 + 2 * tid;
-    const bool m0 = i0 < nu && sUslot[i0] < 0;
-    const bool m1 = i0 + 1 < nu && sUslot[i0 + 1] < 0;
+    const int v0 = sUslot[min(i0, nu - 1)], v1 = sUslot[min(i0 + 1, nu - 1)];
+    const bool m0 = i0 < nu && v0 < 0;
+    const bool m1 = i0 + 1 < nu && v1 < 0;
     const uint64_t b0 = __ballot(m0), b1 = __ballot(m1);
     if (lane == 0) sWs[w] = __popcll(b0) + __popcll(b1);
     __syncthreads();
@@ -507,7 +655,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     if (m0) sMiss[m + pre] = i0;
     if (m1) sMiss[m + pre + (m0 ? 1 : 0)] = i0 + 1;
     m += tot;
-    __syncthreads();
+    // sWs is reused by the next round; after the last round, the barrier
+    // that follows the bin histogram orders these stores before their reads
+    if (c0 + 2 * kMRThreads < nu) __syncthreads();
   }
 
   // ---- 7. victims: the m first candidates in (bin, slot) order

@@ -206,14 +206,23 @@ avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode);
 
 /* How the selection is matched against the resident ids.
  *  AVSG_MATCH_HASH (default): vectorised hash matching (AVSG abstract): the
- *    selection is hashed into an LDS table and every slot probes it, 64
- *    lanes at a time.
+ *    selection is entered into an LDS table keyed by id and every slot
+ *    looks its resident id up, 64 lanes at a time.  When the context is
+ *    small enough (n_entries / 16 words take no more LDS than the hash
+ *    table), the table is direct-addressed: one membership bit per id and
+ *    one rank base per 32 ids; otherwise it is the open-addressing table.
  *  AVSG_MATCH_MERGE: the scalar dual-pointer baseline the AVSG abstract
  *    compares against: the resident ids are sorted (bitonic sort in LDS) and
  *    one lane walks both sorted lists.  Kept for comparison; needs more LDS
  *    (AVSG_ERR_UNSUPPORTED if the device has too little).
- * Results are identical in both modes. */
-typedef enum avsg_match_mode { AVSG_MATCH_HASH = 0, AVSG_MATCH_MERGE = 1 } avsg_match_mode;
+ *  AVSG_MATCH_HASH_TABLE: AVSG_MATCH_HASH always in its open-addressing
+ *    form (kept for comparison and tests).
+ * Results are identical in every mode. */
+typedef enum avsg_match_mode {
+  AVSG_MATCH_HASH = 0,
+  AVSG_MATCH_MERGE = 1,
+  AVSG_MATCH_HASH_TABLE = 2
+} avsg_match_mode;
 avsg_status avsg_set_match_mode(avsg_ctx* ctx, int32_t mode);
 
 /* Number of split-k partitions the attention of one (unit, token) uses. */

@@ -42,8 +42,8 @@ SMALL = {
 
 # Edge shapes: k equal to the slot count, pages of 3 tokens whose rows straddle
 # the 256-row attention splits, 32-token pages, the largest lifetime and
-# bucket counts, 2 query heads per KV head, a single selected latent row, and
-# a latent head whose selection fits one split.
+# bucket counts, 2 query heads per KV head, a single selected latent row, a
+# latent head whose selection fits one split, and a context of 200000 ids.
 EDGE = {
     "k_eq_S": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=3000, k=200,
                                       n_slots=200, steps=8),
@@ -59,6 +59,10 @@ EDGE = {
                                     n_slots=800, steps=8),
     "mla_k1": tg.WORKLOADS[5].replace(batch=2, n_entries=100, k=1, n_slots=4, steps=6, overlap=0.0),
     "mla_one_split": tg.WORKLOADS[5].replace(batch=2, n_entries=2000, k=300, n_slots=600, steps=6),
+    # a context too large for direct addressing in LDS: the default match
+    # takes the open-addressing hash table
+    "big_context": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=200000,
+                                           k=200, n_slots=400, steps=8),
 }
 
 
@@ -165,16 +169,18 @@ def test_parity_full_size(cid):
 
 
 @pytest.mark.parametrize("name", ["batch_ragged", "mtp_ragged", "lru_small_b", "tiny"])
-def test_parity_merge_matching(name):
-    """The scalar dual-pointer matching baseline gives the same state and
-    outputs as the hash probe."""
+@pytest.mark.parametrize("mode", ["merge", "hash_table"])
+def test_parity_match_modes(name, mode):
+    """The scalar dual-pointer matching baseline and the open-addressing hash
+    table (which the default mode replaces by direct addressing on these
+    small contexts) give the same state and outputs as the oracle."""
     from gpu_harness import ensure_lib
     avsg = ensure_lib()
     w = SMALL[name].replace(steps=min(SMALL[name].steps, 8))
-    say("[parity] %s merge matching" % name)
+    say("[parity] %s %s matching" % (name, mode))
     sel = tg.selections(w)
     run = Runner(w)
-    run.ctx.set_match_mode(avsg.MATCH_MERGE)
+    run.ctx.set_match_mode(avsg.MATCH_MERGE if mode == "merge" else avsg.MATCH_HASH_TABLE)
     try:
         for t in range(w.steps):
             run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
