@@ -28,10 +28,12 @@
 //    "is this slot a candidate" into the same probe.
 //  * Victim selection is a stable counting selection: each candidate slot gets
 //    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first).  A
-//    histogram of the bins (the first 4 bins, then the rest only if those
-//    hold fewer than m candidates) gives the threshold bin b* that holds the m-th candidate;
-//    only candidates in bins <= b* are ranked, inside their bin in slot order
-//    via ballot/mbcnt per wave plus per-(wave, bin) prefix sums; the m first
+//    histogram of the bins gives the threshold bin b* that holds the m-th
+//    candidate: the counts of bins 0..3 per wave form a 64-word (bin, wave)
+//    table that one wave scan turns into every (bin, wave) start, and all
+//    bins are counted only if those four hold fewer than m candidates.  Only
+//    candidates in bins <= b* are ranked, inside their bin in slot order via
+//    ballot/mbcnt per wave plus the (bin, wave) starts; the m first
 //    candidates in (bin, slot) order are the victims.  No comparison sort, no
 //    order-dependent atomics: the result is deterministic.
 //  * The r-th miss in ascending id order takes the r-th victim, its row is
@@ -666,41 +668,50 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) changed[q] = false;
   if (m > 0) {
-    // per-wave histogram of the candidates' bins (one ballot per (bin, slot
-    // group), counted on the scalar unit, no LDS atomics), built 4 bins at a
-    // time until the bins so far hold m candidates; usually the first 4 do
-    int nb = 0;  // bins counted so far
-    for (int covered = 0, round = 0; round < 2 && nb < nbins && covered < m; ++round) {
-      const int hi = round == 0 ? min(4, nbins) : nbins;
-      for (int b = nb; b < hi; ++b) {
+    // per-wave counts of the candidates in bins 0..3 (one ballot per (bin,
+    // slot group), counted on the scalar unit), published as a [bin][wave]
+    // table of 64 words (the sink words, free after the probe); one read per
+    // lane and one wave scan in (bin, wave) order then give every wave the
+    // first rank of each of its bins.  Usually bins 0..3 hold the m victims.
+    int32_t* sC4 = sMisc + 64;
+    int c4 = 0;  // lane b < 4: this wave's count of bin b
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
+      c4 = lane == b ? cnt : c4;
+    }
+    if (lane < 4) sC4[lane * 16 + w] = c4;
+    __syncthreads();
+    const int c = sC4[lane];  // bin lane / 16, wave lane % 16
+    const int inc = wave_incl_scan(c);
+    const bool fast = __builtin_amdgcn_readlane(inc, 63) >= m;  // the same in every wave
+    int bstar = nbins;
+    int off[4] = {0, 0, 0, 0};  // fast: this wave's first rank in bins 0..3
+    if (fast) {
+      bstar = __builtin_ctzll(__ballot((lane & 15) == 15 && inc >= m)) >> 4;
+      const int ex = inc - c;
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) off[b] = __builtin_amdgcn_readlane(ex, b * 16 + wu);
+    } else {
+      // general: histogram of all bins (per wave, in LDS), the bin totals,
+      // their exclusive starts, b* and each wave's first rank per bin; lane
+      // l covers bins l and l + 64 (nbins <= 128)
+      for (int b = 0; b < nbins; ++b) {
         int cnt = 0;
 #pragma unroll
         for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
         if (lane == 0) sCnt[w * nbins + b] = cnt;
       }
       __syncthreads();
-      // candidates in the bins just counted: every wave adds up the same
-      // counts (one read per lane), so all take the same branch
-      const int nbb = hi - nb;
-      int part = 0;
-      for (int idx = lane; idx < kMRWaves * nbb; idx += 64) {
-        const int v = idx / nbb, b = nb + (idx - v * nbb);
-        part += sCnt[v * nbins + b];
-      }
-      covered += wave_total(part);
-      nb = hi;
-    }
-    // every wave derives the bin totals, their exclusive starts, the
-    // threshold bin b* holding the m-th candidate, and its own first rank
-    // per bin; lane l covers bins l and l + 64 (nbins <= 128)
-    int bstar = nbins;
-    {
       int tot0 = 0, tot1 = 0, bef0 = 0, bef1 = 0;
       const int b0 = lane, b1 = lane + 64;
 #pragma unroll
       for (int v = 0; v < kMRWaves; ++v) {
-        const int c0v = b0 < nb ? sCnt[v * nbins + b0] : 0;
-        const int c1v = b1 < nb ? sCnt[v * nbins + b1] : 0;
+        const int c0v = b0 < nbins ? sCnt[v * nbins + b0] : 0;
+        const int c1v = b1 < nbins ? sCnt[v * nbins + b1] : 0;
         tot0 += c0v;
         tot1 += c1v;
         bef0 += v < w ? c0v : 0;
@@ -710,11 +721,11 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       const int sum0 = __builtin_amdgcn_readlane(inc0, 63);
       const int inc1 = wave_incl_scan(tot1) + sum0;
       const int st0 = inc0 - tot0, st1 = inc1 - tot1;
-      const uint64_t r0 = __ballot(b0 < nb && st0 < m && st0 + tot0 >= m);
-      const uint64_t r1 = __ballot(b1 < nb && st1 < m && st1 + tot1 >= m);
+      const uint64_t r0 = __ballot(b0 < nbins && st0 < m && st0 + tot0 >= m);
+      const uint64_t r1 = __ballot(b1 < nbins && st1 < m && st1 + tot1 >= m);
       bstar = r0 ? __builtin_ctzll(r0) : 64 + __builtin_ctzll(r1);
-      if (b0 < nb) sOff[w * nbins + b0] = st0 + bef0;
-      if (b1 < nb) sOff[w * nbins + b1] = st1 + bef1;
+      if (b0 < nbins) sOff[w * nbins + b0] = st0 + bef0;
+      if (b1 < nbins) sOff[w * nbins + b1] = st1 + bef1;
     }
     // rank of each candidate in bins <= b* among the wave's candidates of
     // the same bin, in slot order (slot groups in order, lanes in order)
@@ -729,21 +740,52 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         run += __popcll(grp);
       }
     }
-    int2* misses = p.misses + (size_t)u * ucap;
+    // rank[q] becomes the candidate's rank r among all candidates (m for
+    // slots that are no candidates or lie beyond b*)
+    if (fast) {
 #pragma unroll
-    for (int q = 0; q < MAXP; ++q) {
-      if (bin[q] < 0 || bin[q] > bstar) continue;
-      const int r = sOff[w * nbins + bin[q]] + rank[q];
-      if (r >= 0 && r < m) {
-        const int s = s0 + q * 64 + lane;
-        const int i = sMiss[r];
-        const int32_t id = sU[i];
-        if (tok[q] >= 0) ++ev;
-        tok[q] = id;
-        lf[q] = lru ? (int32_t)p.t : p.L;
-        changed[q] = true;
-        sUslot[i] = s | kMissFlag;
-        misses[r] = make_int2(s, id);
+      for (int q = 0; q < MAXP; ++q) {
+        const int b = bin[q];
+        int o = off[0];
+        o = b == 1 ? off[1] : o;
+        o = b == 2 ? off[2] : o;
+        o = b == 3 ? off[3] : o;
+        rank[q] = (b >= 0 && b <= bstar) ? o + rank[q] : m;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < MAXP; ++q) {
+        const int b = bin[q];
+        const bool cand = b >= 0 && b <= bstar;
+        const int o = sOff[w * nbins + (cand ? b : 0)];
+        rank[q] = cand ? o + rank[q] : m;
+      }
+    }
+    // the candidate of rank r < m takes the r-th miss; the reads of a group
+    // of (up to) 8 slots are issued together (clamped for non-victims)
+    int2* misses = p.misses + (size_t)u * ucap;
+    constexpr int kGrp = MAXP < 8 ? MAXP : 8;
+#pragma unroll
+    for (int q0 = 0; q0 < MAXP; q0 += kGrp) {
+      int r[kGrp], mi[kGrp], idv[kGrp];
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) r[qq] = rank[q0 + qq];
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) mi[qq] = sMiss[min(r[qq], m - 1)];
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) idv[qq] = sU[mi[qq]];
+#pragma unroll
+      for (int qq = 0; qq < kGrp; ++qq) {
+        const int q = q0 + qq;
+        if (r[qq] < m) {
+          const int s = s0 + q * 64 + lane;
+          if (tok[q] >= 0) ++ev;
+          tok[q] = idv[qq];
+          lf[q] = lru ? (int32_t)p.t : p.L;
+          changed[q] = true;
+          sUslot[mi[qq]] = s | kMissFlag;
+          misses[r[qq]] = make_int2(s, idv[qq]);
+        }
       }
     }
     if (ev) atomicAdd(&sMisc[1], ev);
