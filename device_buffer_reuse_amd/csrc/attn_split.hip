@@ -8,31 +8,41 @@
 // The AVSG abstract (arxivdaily 2609.37538) requires the selections to stay
 // exact, so this equals attention over the same rows read from host memory.
 //
-// gfx950 mapping (HBM-bound, VALU):
-//  * A workgroup (4 waves) owns `split_rows` token rows of one (unit, token).
-//    The rows stream through three 16 KiB LDS tiles of 32 rows (K half and V
-//    half of a row, 512 bytes) by direct global-to-LDS copies, 16 bytes per
-//    lane and 4 copies per lane per tile; two tiles are in flight while one
-//    is used.  Every wave issues the same number of copies, so a vmcnt wait
-//    with a constant count tells it that its share of the tile it needs has
-//    landed, and one barrier per tile publishes the tile.
+// gfx950 mapping (HBM-bound; the two contractions on MFMA):
+//  * A workgroup is one wave and owns `split_rows` token rows of one (unit,
+//    token): no barrier anywhere.  The rows stream through three LDS tiles of
+//    32 rows (512 bytes each: K half, V half) by direct global-to-LDS copies
+//    of 16 bytes per lane, 16 per tile: copy x reads rows 2x and 2x + 1, 16
+//    lanes per 256-byte half row, so host memory is read in 256-byte runs
+//    (shorter runs cost link efficiency).  The rows' source addresses are
+//    computed once per tile into a small LDS table.  Inside a half row the
+//    16-byte pieces are permuted by the row index (piece c at slot c ^ (row
+//    mod 16)), which puts the 16 rows an MFMA operand reads in distinct LDS
+//    banks.  Two tiles are in flight while one is used, and a vmcnt wait with
+//    a constant count tells the wave that the tile it needs has landed.
+//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16
+//    (M = 16 rows, N = the unit's G query heads padded to 16 columns, K = 32
+//    dimensions, 4 steps).  In that result layout each lane owns one head's
+//    column, so the online softmax reduces over 4 lanes with the gfx950 lane
+//    swaps, and the probabilities are already the B operand of O^T = V^T P^T
+//    (K = the tile's 32 rows).  V^T operands come from ds_read_b64_tr_b16,
+//    the transposing LDS read, so V is never transposed in memory.  Padding
+//    the heads wastes MFMA work, which is far from the bound; VALU work per
+//    row is what limited the dot-product form of this kernel.
+//  * P is split into bf16 hi + lo parts (two MFMAs on the same V fragment):
+//    rounding P to bf16 alone would leave about 1e-3 relative error.
 //  * Rows whose entry missed are copied from pinned host memory into the tile;
 //    the lane that copied a piece then stores it from LDS into the entry's
 //    slot, so the row crosses the host link once.  When the grid runs in
 //    several rounds of resident workgroups, a workgroup instead first copies
 //    all of its split's missed entries from host memory into their slots
 //    (every host read in flight at once) and then streams only from HBM.
-//  * Each wave owns 8 rows of every tile, 16 lanes per row (16 bytes of the K
-//    half and of the V half each).  q.k uses v_dot2_f32_bf16 on bf16 pairs
-//    (products exact, fp32 sums) and four DPP steps inside the 16-lane row;
-//    p * v accumulates in fp32.
-//  * Each wave keeps its own online softmax per head (the reference maximum
-//    moves only when a tile exceeds it by 2^8, so the accumulators are
-//    rescaled rarely); the four waves merge once at the end of the split, in
-//    wave order, so a tile needs no barrier beyond the one for its copies.
 //  * All LDS reads of the tiles are inline assembly with waits tied to their
 //    results: the compiler would otherwise order every LDS read after all
 //    outstanding global-to-LDS copies.
+//  * The reference maximum of the online softmax moves only when a tile
+//    exceeds it by 2^8, so the accumulators are rescaled rarely; the result
+//    does not depend on the reference chosen.
 //  * Split partials (max, sum, o) go to the workspace and the combine kernel
 //    merges them in split order, so the result does not depend on workgroup
 //    timing.  (Merging inside the last workgroup of each (unit, token) needs
@@ -47,105 +57,23 @@ namespace avsg {
 namespace {
 
 constexpr int kD = 128;                              // head dim of the split layout
-constexpr int kTileRows = 32;                        // token rows per LDS tile
-constexpr int kRowBytes = 4 * kD;                    // K half + V half
-constexpr int kTileBytes = kTileRows * kRowBytes;    // 16 KiB
+constexpr int kChunk = 32;                           // token rows per LDS tile
+constexpr int kCopies = kChunk * 4 * kD / 1024;      // 16 wave-wide copies of 1 KiB per tile
+constexpr int kTileBytes = kCopies * 1024;           // 16 KiB
 constexpr int kBufs = 3;                             // LDS tiles per workgroup
 constexpr int kAhead = kBufs - 1;                    // tiles in flight beyond the one in use
 static_assert(kAhead >= 1 && kAhead <= 3, "tile pipeline depth");
-constexpr int kWaves = kAttnThreads / 64;            // 4
-constexpr int kCopies = kTileBytes / 16 / kAttnThreads;  // 4 per lane per tile
+constexpr int kThreads = 64;                         // one wave per workgroup
 constexpr int kSplitRows = 256;                      // token rows per workgroup
+constexpr int kKSteps = kD / 32;                     // 4 MFMA k-steps for QK^T
+constexpr int kDTiles = kD / 16;                     // 8 output tiles of 16 dimensions
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// sum over the 16 lanes of a DPP row; every lane of the row gets the total
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  v += dpp<0x140>(v);  // row_mirror
-  return v;
-}
-
-// max / sum over the lanes l, l^16, l^32, l^48 (the four rows of a wave)
-__device__ __forceinline__ float rows_max(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Butterfly reduction of G per-lane partial sums over the 16 lanes of a DPP
-// row: at each of four levels a lane adds its partner's values for the half
-// of its heads it keeps (partners c^8 by row_ror:8, c^7 by row_half_mirror,
-// c^2 and c^1 by quad_perm; these span all 16 lanes).  Afterwards lane c
-// holds the full sum of head c >> (4 - log2 G), on 16 / G lanes each.
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float keep, float send) {
-  return keep + __int_as_float(
-                    __builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xF, 0xF, false));
-}
-template <int G>
-__device__ __forceinline__ float head_reduce(const float (&d)[G], int c) {
-  float v[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) v[h] = d[h];
-  int n = G;
-#pragma unroll
-  for (int lvl = 0; lvl < 4; ++lvl) {
-    const bool up = (c >> (3 - lvl)) & 1;
-    const int half = n > 1 ? n / 2 : 1;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float keep = n > 1 ? (up ? v[half + i] : v[i]) : v[i];
-      const float send = n > 1 ? (up ? v[i] : v[half + i]) : v[i];
-      if (lvl == 0) v[i] = dpp_add<0x128>(keep, send);       // row_ror:8
-      else if (lvl == 1) v[i] = dpp_add<0x141>(keep, send);  // row_half_mirror
-      else if (lvl == 2) v[i] = dpp_add<0x4E>(keep, send);   // quad_perm [2,3,0,1]
-      else v[i] = dpp_add<0xB1>(keep, send);                 // quad_perm [1,0,3,2]
-    }
-    n = half;
-  }
-  return v[0];
-}
-// Value of lane c - k * 16 / G (mod 16, by DPP row rotation): with head h on
-// lanes h * 16 / G .., slot k of a lane sees head (own head - k) mod G.
-template <int G, int K>
-__device__ __forceinline__ float rot(float v) {
-  if constexpr (K == 0) {
-    return v;
-  } else {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + K * (16 / G),
-                                                      0xF, 0xF, false));
-  }
-}
-template <int G, int K>
-__device__ __forceinline__ int rot_i(int v) {
-  if constexpr (K == 0) {
-    return v;
-  } else {
-    return __builtin_amdgcn_update_dpp(0, v, 0x120 + K * (16 / G), 0xF, 0xF, false);
-  }
-}
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -154,30 +82,50 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
+template <int OFF>
 __device__ __forceinline__ void ds_b128(u32x4& d, uint32_t a) {
-  asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(a));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(a), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_tr(u32x2& d, uint32_t a) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(a), "n"(OFF));
 }
 __device__ __forceinline__ void ds_b64(int2& d, uint32_t a) {
   asm volatile("ds_read_b64 %0, %1" : "=v"(d) : "v"(a));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_u64(uint64_t& d, uint32_t a) {
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(d) : "v"(a), "n"(OFF));
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// max / sum over the four lanes l, l^16, l^32, l^48 (one head's column)
+__device__ __forceinline__ float col_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int G>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sTile[kBufs * kTileBytes];
-  __shared__ int2 sRow[kSplitRows];   // per entry of the split: (slot, host id or -1)
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sTile[];  // [kBufs][kTileBytes]
+  __shared__ int2 sRow[kSplitRows];      // per entry of the split: (slot, host id or -1)
   __shared__ int32_t sHost[kSplitRows];  // entries to fetch (gather-first)
-  __shared__ int32_t sNHost;
-  __shared__ float sMw[kWaves][G], sLw[kWaves][G];
+  __shared__ uint64_t sSrc[kBufs][kChunk];  // per tile row: source address
+  __shared__ uint64_t sDst[kBufs][kChunk];  // per tile row: slot address (host rows)
 
   const int nsplit = p.nsplit;
   const int u = blockIdx.x / nsplit;
@@ -185,50 +133,70 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
   const int j = p.token;
   const int uj = u * p.T + j;
   const int b = u / p.Hkv, g = u - b * p.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int rg = lane >> 4, c = lane & 15;
+  const int lane = threadIdx.x;
+  const int gq = lane >> 4, li = lane & 15;  // lane group (rows / dims), column (head)
   const int tpe = p.tpe;
   const int n_rows = p.k * tpe;
   const int r0 = sp * p.split_rows, r1 = min(r0 + p.split_rows, n_rows);
   float* orow = p.out + (((size_t)b * p.T + j) * p.Hq + g * G) * kD;
-  if (p.unit_status[u] != 0) {
-    if (nsplit == 1)
-      for (int idx = tid; idx < G * kD; idx += kAttnThreads) orow[idx] = 0.f;
-    return;
-  }
-
   const int e0 = r0 / tpe, e1 = (r1 - 1) / tpe + 1;
-  if (tid == 0) sNHost = 0;
-  __syncthreads();
-  for (int i0 = 0; i0 < e1 - e0; i0 += kAttnThreads) {
-    const int i = i0 + tid;
-    const size_t at = (size_t)uj * p.k + e0 + i;
-    const bool in = i < e1 - e0;
-    const bool fetch = in && p.fetch && p.fetch[at];
-    if (in) sRow[i] = make_int2(p.sel_slot[at], fetch ? p.sel[at] : -1);
-    if (p.gather_first) {
-      // list the entries this split fetches (their order does not matter)
-      const uint64_t m = __builtin_amdgcn_ballot_w64(fetch);
-      int base = 0;
-      if (lane == 0 && m) base = atomicAdd(&sNHost, __popcll(m));
-      base = __shfl(base, 0, 64);
-      if (fetch)
-        sHost[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = i;
+  const int ne = e1 - e0;  // entries of the split, <= kSplitRows
+  // every global load of the prologue is issued before any is used: the
+  // unit's status, the split's (slot, fetch flag, id) per entry (kEnt per
+  // lane, indices clamped into the split) and this lane's Q operand: head li
+  // (zero past the unit's G heads), dims 32 ks + 8 gq .. +8
+  constexpr int kEnt = kSplitRows / kThreads;
+  const int ustat = __builtin_nontemporal_load(p.unit_status + u);
+  int slot_v[kEnt], id_v[kEnt], fl_v[kEnt];
+  // without fetch flags (rows already gathered) the flag loads read the
+  // slot array instead and are ignored
+  const bool has_fetch = p.fetch != nullptr;
+  const uint8_t* fl_src = has_fetch ? p.fetch : reinterpret_cast<const uint8_t*>(p.sel_slot);
+#pragma unroll
+  for (int k = 0; k < kEnt; ++k) {
+    const size_t at = (size_t)uj * p.k + e0 + min(k * kThreads + lane, ne - 1);
+    slot_v[k] = p.sel_slot[at];
+    id_v[k] = p.sel[at];
+    fl_v[k] = fl_src[at];
+  }
+  bf16x8 qf[kKSteps];
+  {
+    const uint16_t* qrow =
+        p.q + (((size_t)b * p.T + j) * p.Hq + g * G + (li < G ? li : 0)) * kD + 8 * gq;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
+      qf[ks] = __builtin_bit_cast(bf16x8, li < G ? v : u32x4{0, 0, 0, 0});
     }
   }
-  uint32_t qf[G][4];
+  // the loads stay above the status branch (one wait for all of them)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 qq = *reinterpret_cast<const uint4*>(
-        p.q + (((size_t)b * p.T + j) * p.Hq + g * G + h) * kD + c * 8);
-    qf[h][0] = qq.x; qf[h][1] = qq.y; qf[h][2] = qq.z; qf[h][3] = qq.w;
+  for (int k = 0; k < kEnt; ++k) asm volatile("" ::"v"(slot_v[k]), "v"(id_v[k]), "v"(fl_v[k]));
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qf[ks]));
+  if (__builtin_amdgcn_readfirstlane(ustat) != 0) {
+    if (nsplit == 1)
+      for (int idx = lane; idx < G * kD; idx += kThreads) orow[idx] = 0.f;
+    return;
   }
-  __syncthreads();
+  int nhost = 0;  // entries of the split to fetch (gather-first)
+#pragma unroll
+  for (int k = 0; k < kEnt; ++k) {
+    const int i = k * kThreads + lane;
+    const bool fetch = has_fetch && i < ne && fl_v[k] != 0;
+    if (i < ne) sRow[i] = make_int2(slot_v[k], fetch ? id_v[k] : -1);
+    if (p.gather_first) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(fetch);
+      if (fetch)
+        sHost[nhost + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = i;
+      nhost += __popcll(m);
+    }
+  }
+  __syncthreads();  // sRow, sHost
   // the queries are in registers before any copy is issued
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-    asm volatile("" : "+v"(qf[h][0]), "+v"(qf[h][1]), "+v"(qf[h][2]), "+v"(qf[h][3]));
+  for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
 
   uint16_t* ubase = p.buf_kv + (size_t)u * p.S * p.row_elems;
   const uint16_t* hbase = p.host_kv + (size_t)u * p.N * p.row_elems;
@@ -241,14 +209,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
   // together (8 16-byte pieces per lane per round), and the tiles then read
   // them from HBM.  Chosen when the grid runs in several rounds of resident
   // workgroups: the host latency is then paid once per workgroup.
-  if (p.gather_first) {
+  if (p.gather_first && nhost > 0) {
     const int pe = p.row_elems >> 3;  // 16-byte pieces per entry
-    const int total = sNHost * pe;
-    for (int q0 = 0; q0 < total; q0 += 8 * kAttnThreads) {
+    const int total = nhost * pe;
+    for (int q0 = 0; q0 < total; q0 += 8 * kThreads) {
       u32x4 v[8];
 #pragma unroll
       for (int bq = 0; bq < 8; ++bq) {
-        const int q = q0 + bq * kAttnThreads + tid;
+        const int q = q0 + bq * kThreads + lane;
         if (q < total) {
           const int k = q / pe, col = q - k * pe;
           v[bq] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
@@ -257,7 +225,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
       }
 #pragma unroll
       for (int bq = 0; bq < 8; ++bq) {
-        const int q = q0 + bq * kAttnThreads + tid;
+        const int q = q0 + bq * kThreads + lane;
         if (q < total) {
           const int k = q / pe, col = q - k * pe;
           *reinterpret_cast<u32x4*>(ubase + (size_t)(uint32_t)sRow[sHost[k]].x * p.row_elems +
@@ -266,110 +234,129 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
       }
     }
     __syncthreads();  // every read of sRow above is done
-    for (int k = tid; k < sNHost; k += kAttnThreads) sRow[sHost[k]].y = -1;
-    // the stores are in L2 before any wave copies those rows into LDS
+    for (int k = lane; k < nhost; k += kThreads) sRow[sHost[k]].y = -1;
+    // the stores are in L2 before the tiles copy those rows into LDS
     vm_wait<0>();
     __syncthreads();
   }
 
-  // This lane's copies of a tile: copy x is row 8w + 2x + lane/32 of the
-  // tile, half (K or V) (lane/16)%2, 16-byte column lane%16; instruction
-  // w*kCopies + x fills bytes [1024 (w*kCopies + x), +1024) of the tile.
   // Entry of a row: r itself for token entries, else r / tpe by an exact
   // multiply-high with ceil(2^32 / tpe) (exact while r * tpe < 2^32).
   const uint32_t tpe_magic = tpe == 1 ? 0u : (uint32_t)((0x100000000ull + tpe - 1) / tpe);
   auto entry_of = [&](int r) -> int {
     return tpe == 1 ? r : (int)__umulhi((uint32_t)r, tpe_magic);
   };
-  const int row_base = 8 * w + (lane >> 5);
-  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, in a scalar register
-  const int copy_off = ((lane >> 4) & 1) * v_off + (lane & 15) * 8;  // elements
-  // Copies tile t into buffer `buf`; rows past the split repeat its last row
-  // (their scores are masked) so every wave issues exactly kCopies copies.
-  // Returns the copies whose row came from host memory (bit x).
+  // LDS tile layout: piece c (16 bytes; 0..15 K half, 16..31 V half) of tile
+  // row r sits at byte 512 r + 256 (c / 16) + 16 ((c % 16) ^ (r % 16)).  Copy
+  // x fills bytes [1024 x, +1024): lane L takes half (L / 16) % 2 of row 2x +
+  // L / 32, piece (L % 16) ^ (row % 16) of it.
+  const uint32_t lane_c = (uint32_t)((lane & 15) ^ (lane >> 5));
+  const uint32_t half_b = (uint32_t)(((lane >> 4) & 1) * v_off * 2);  // bytes to the V rows
+  const uint32_t src_lds = lds_addr(sSrc) + 8 * (lane >> 5);
+  const uint32_t dst_lds = lds_addr(sDst) + 8 * (lane >> 5);
+  // Copies tile t into buffer `buf`.  Rows past the split repeat its last row
+  // (their scores are masked), so every tile takes exactly kCopies copies.
+  // Returns the tile rows that came from host memory (bit r, wave-uniform).
   auto stage = [&](int t, int buf) -> uint32_t {
-    int2 ri[kCopies];
-    int ent[kCopies];
-    const int rt = r0 + t * kTileRows + row_base;
-#pragma unroll
-    for (int x = 0; x < kCopies; ++x) {
-      const int r = min(rt + 2 * x, r1 - 1);
-      ent[x] = entry_of(r);
-      ds_b64(ri[x], row_lds + 8 * (ent[x] - e0));
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed per tile rather than held
+    // lane l < 32: source (and slot) address of tile row l
+    const int rr = r0 + t * kChunk + (ln & 31);
+    const int r = min(rr, r1 - 1);
+    const int e = entry_of(r);
+    int2 ri;
+    ds_b64(ri, row_lds + 8 * (e - e0));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ri)::"memory");
+    const bool host = ri.y >= 0;
+    const uint32_t in_entry = (uint32_t)((r - e * tpe) * kD);
+    const uint16_t* src = (host ? hbase : ubase) +
+                          (uint64_t)(uint32_t)(host ? ri.y : ri.x) * (uint32_t)p.row_elems + in_entry;
+    if (ln < kChunk) {
+      sSrc[buf][ln] = (uint64_t)(uintptr_t)src;
+      sDst[buf][ln] = (uint64_t)(uintptr_t)(ubase + (uint64_t)(uint32_t)ri.x * (uint32_t)p.row_elems +
+                                            in_entry);
     }
+    const uint32_t hmask = (uint32_t)__builtin_amdgcn_ballot_w64(host && rr < r1 && ln < kChunk);
+    asm volatile("" ::: "memory");  // the table stores above precede its reads
+    uint64_t a[kCopies];
+    const uint32_t sa = src_lds + buf * (kChunk * 8);
+    static_for<0, kCopies>([&](auto x_) {
+      constexpr int x = decltype(x_)::value;
+      ds_u64<16 * x>(a[x], sa);
+    });
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int x = 0; x < kCopies; ++x) asm volatile("" : "+v"(ri[x]));
-    uint32_t fetched = 0;
+    for (int x = 0; x < kCopies; ++x) asm volatile("" : "+v"(a[x]));
     uint8_t* tile = sTile + buf * kTileBytes;
 #pragma unroll
     for (int x = 0; x < kCopies; ++x) {
-      const int r = min(rt + 2 * x, r1 - 1);
-      const uint32_t off = (uint32_t)((r - ent[x] * tpe) * kD + copy_off);
-      const bool host = ri[x].y >= 0;
-      const uint16_t* base = host ? hbase : ubase;
-      const uint32_t idx = (uint32_t)(host ? ri[x].y : ri[x].x);
-      // one 32 x 32 -> 64-bit multiply per copy
-      const uint16_t* src = base + (uint64_t)idx * (uint32_t)p.row_elems + off;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + (wu * kCopies + x) * 1024), 16, 0,
-                                       0);
-      if (host && rt + 2 * x < r1) fetched |= 1u << x;
+      const uint8_t* srcx =
+          reinterpret_cast<const uint8_t*>(a[x]) + half_b + 16 * (lane_c ^ ((2 * x) & 15));
+      __builtin_amdgcn_global_load_lds(srcx, (lds_void*)(tile + x * 1024), 16, 0, 0);
     }
-    return fetched;
+    return hmask;
   };
-  // Stores this lane's host-fetched pieces of tile t from LDS into their slots.
-  auto write_back = [&](int t, int buf, uint32_t fetched) {
-    if (!__builtin_amdgcn_ballot_w64(fetched != 0)) return;
-    const int rt = r0 + t * kTileRows + row_base;
-    int2 ri[kCopies];
+  // Stores the host rows of tile t (bit r of hmask) from LDS into their slots.
+  auto write_back = [&](int t, int buf, uint32_t hmask) {
+    if (hmask == 0) return;
+    uint64_t a[kCopies];
     u32x4 d[kCopies];
-#pragma unroll
-    for (int x = 0; x < kCopies; ++x) {
-      const int r = min(rt + 2 * x, r1 - 1);
-      ds_b64(ri[x], row_lds + 8 * (entry_of(r) - e0));
-      ds_b128(d[x], tile_lds + buf * kTileBytes + (w * kCopies + x) * 1024 + lane * 16);
-    }
+    const uint32_t da = dst_lds + buf * (kChunk * 8);
+    const uint32_t ta = tile_lds + buf * kTileBytes + lane * 16;
+    static_for<0, kCopies>([&](auto x_) {
+      constexpr int x = decltype(x_)::value;
+      ds_u64<16 * x>(a[x], da);
+      ds_b128<1024 * x>(d[x], ta);
+    });
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int x = 0; x < kCopies; ++x) asm volatile("" : "+v"(ri[x]), "+v"(d[x]));
+    for (int x = 0; x < kCopies; ++x) asm volatile("" : "+v"(a[x]), "+v"(d[x]));
 #pragma unroll
     for (int x = 0; x < kCopies; ++x) {
-      if (fetched & (1u << x)) {
-        const int r = rt + 2 * x;
-        const int e = entry_of(r);
-        const uint32_t off = (uint32_t)((r - e * tpe) * kD + copy_off);
-        *reinterpret_cast<u32x4*>(ubase + (size_t)(uint32_t)ri[x].x * p.row_elems + off) = d[x];
+      if ((hmask >> (2 * x + (lane >> 5))) & 1) {
+        uint8_t* dst = reinterpret_cast<uint8_t*>(a[x]) + half_b + 16 * (lane_c ^ ((2 * x) & 15));
+        *reinterpret_cast<u32x4*>(dst) = d[x];
       }
     }
   };
 
-  // o[k]: dims c*8 .. c*8+7 of head (hl - k) mod G, hl = this lane's head;
-  // m_run, l_run: the online softmax of head hl over this lane's rows
-  const int hl = c / (16 / G);
-  float o[G][8];
+  // acc[t]: O^T[dims 16 t + 4 gq + i][head li], i = 0..3
+  f32x4 acc[kDTiles];
+#pragma unroll
+  for (int t = 0; t < kDTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-#pragma unroll
-  for (int k = 0; k < G; ++k)
-#pragma unroll
-    for (int x = 0; x < 8; ++x) o[k][x] = 0.f;
 
-  const int ntiles = (r1 - r0 + kTileRows - 1) / kTileRows;
-  // fmask[i]: this lane's host-fetched copies of tile t + i
+  const int ntiles = (r1 - r0 + kChunk - 1) / kChunk;
+  // fmask[i]: the host rows of tile t + i
   uint32_t fmask[kAhead];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) fmask[i] = i < ntiles ? stage(i, i) : 0u;
-  // this lane's two rows of a tile: 8w + rg and 8w + 4 + rg
-  const uint32_t lane_off = (8 * w + rg) * kRowBytes + c * 16;
+  // per-lane operand addresses within a tile (rows 16..31: +8192): K row li,
+  // dims 32 ks + 8 gq .. +8 (piece 4 ks + gq); V^T row R = 4 gq + li / 4, dims
+  // 32 pr + 16 vb + 4 (li % 4) .. +4 (V piece 4 pr + 2 vb + (li % 4) / 2, byte
+  // 8 (li % 2) of it)
+  uint32_t k_off[kKSteps], v_off_l[kDTiles];
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) k_off[ks] = 512 * li + 16 * ((4 * ks + gq) ^ li);
+  {
+    const int R = 4 * gq + (li >> 2);
+#pragma unroll
+    for (int pr = 0; pr < kDTiles / 2; ++pr)
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+        v_off_l[2 * pr + vb] = 512 * R + 256 + 16 * ((4 * pr + 2 * vb + ((li & 3) >> 1)) ^ R) +
+                               8 * (li & 1);
+  }
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t % kBufs;
     // tile t has landed once only the copies of the later tiles in flight
-    // (kCopies each) may still be outstanding
+    // (kCopies each) and later slot stores may still be outstanding
     const int later = min(kAhead - 1, ntiles - 1 - t);
     if (later <= 0) vm_wait<0>();
     else if (later == 1) vm_wait<kCopies>();
-    else vm_wait<2 * kCopies>();
-    asm volatile("s_barrier" ::: "memory");  // tile t in LDS; tile t-1's buffer free
+    else if (later == 2) vm_wait<2 * kCopies>();
+    else vm_wait<3 * kCopies>();
     const uint32_t f_now = fmask[0];
 #pragma unroll
     for (int i = 0; i + 1 < kAhead; ++i) fmask[i] = fmask[i + 1];
@@ -379,105 +366,105 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnParams p) 
     // for them
     write_back(t, buf, f_now);
 
-    const uint32_t a = tile_lds + buf * kTileBytes + lane_off;
-    u32x4 k0, k1, v0, v1;
-    ds_b128(k0, a);
-    ds_b128(k1, a + 4 * kRowBytes);
-    ds_b128(v0, a + 2 * kD);
-    ds_b128(v1, a + 4 * kRowBytes + 2 * kD);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
+    // S^T = K Q^T for rows 0..15 and 16..31 of the tile
+    const uint32_t tb = tile_lds + buf * kTileBytes;
+    u32x4 kf0[kKSteps], kf1[kKSteps];
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      ds_b128<0>(kf0[ks], tb + k_off[ks]);
+      ds_b128<8192>(kf1[ks], tb + k_off[ks]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(kf0[0]), "+v"(kf0[1]), "+v"(kf0[2]), "+v"(kf0[3]), "+v"(kf1[0]),
+                   "+v"(kf1[1]), "+v"(kf1[2]), "+v"(kf1[3]));
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf0[ks]), qf[ks], s0,
+                                                   0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf1[ks]), qf[ks], s1,
+                                                   0, 0, 0);
+    }
+    // V^T operands of the first two output tiles, read while the softmax runs
+    u32x2 vr[2][4];
+    ds_tr<0>(vr[0][0], tb + v_off_l[0]);
+    ds_tr<8192>(vr[0][1], tb + v_off_l[0]);
+    ds_tr<0>(vr[0][2], tb + v_off_l[1]);
+    ds_tr<8192>(vr[0][3], tb + v_off_l[1]);
 
-    const int ra = r0 + t * kTileRows + 8 * w + rg, rb = ra + 4;
-    const float va[8] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y),
-                         bf_lo(v0.z), bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w)};
-    const float vb[8] = {bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
-                         bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
-    float da[G], db[G];
+    // lane owns head li: rows 4 gq + i (s0) and 16 + 4 gq + i (s1) of the tile
+    float sv[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x0 = dot2(qf[h][0], k0.x, 0.f);
-      x0 = dot2(qf[h][1], k0.y, x0);
-      x0 = dot2(qf[h][2], k0.z, x0);
-      da[h] = dot2(qf[h][3], k0.w, x0);
-      float x1 = dot2(qf[h][0], k1.x, 0.f);
-      x1 = dot2(qf[h][1], k1.y, x1);
-      x1 = dot2(qf[h][2], k1.z, x1);
-      db[h] = dot2(qf[h][3], k1.w, x1);
+    for (int i = 0; i < 4; ++i) {
+      const int ra = r0 + t * kChunk + 4 * gq + i, rb = ra + 16;
+      sv[i] = ra < r1 ? s0[i] * p.scale_log2e : -INFINITY;
+      sv[4 + i] = rb < r1 ? s1[i] * p.scale_log2e : -INFINITY;
     }
-    // scores of head hl for rows a and b; rows past the split hold a copy
-    // of its last row and are masked here
-    float sa = head_reduce<G>(da, c) * p.scale_log2e;
-    float sb = head_reduce<G>(db, c) * p.scale_log2e;
-    sa = ra < r1 ? sa : -INFINITY;
-    sb = rb < r1 ? sb : -INFINITY;
-    const float cm = rows_max(fmaxf(sa, sb));
+    float cm = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) cm = fmaxf(cm, sv[i]);
+    cm = col_max(cm);
     const bool move = cm > m_run + 8.f;
-    if (__builtin_amdgcn_ballot_w64(move)) {
-      const float corr = move ? __builtin_amdgcn_exp2f(m_run - cm) : 1.f;  // 0 on a first move
-      m_run = move ? cm : m_run;
-      l_run *= corr;
-      static_for<0, G>([&](auto k_) {
-        constexpr int k = decltype(k_)::value;
-        const float ck = rot<G, k>(corr);
+    const float m_new = move ? cm : m_run;
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+    float ps = 0.f;
+    bf16x8 phi, plo;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) o[k][x] *= ck;
-      });
+    for (int i = 0; i < 8; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(sv[i] - m_new);
+      ps += pv;
+      const __bf16 hb = (__bf16)pv;
+      phi[i] = hb;
+      plo[i] = (__bf16)(pv - (float)hb);
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;  // no valid row yet
-    const float pa = __builtin_amdgcn_exp2f(sa - m_use);
-    const float pb = __builtin_amdgcn_exp2f(sb - m_use);
-    l_run += pa + pb;
-    static_for<0, G>([&](auto k_) {
-      constexpr int k = decltype(k_)::value;
-      const float pak = rot<G, k>(pa), pbk = rot<G, k>(pb);
+    l_run = l_run * corr + col_sum(ps);
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
-      for (int x = 0; x < 8; ++x) o[k][x] = fmaf(pbk, vb[x], fmaf(pak, va[x], o[k][x]));
+      for (int d = 0; d < kDTiles; ++d) acc[d] *= corr;
+    }
+
+    // O^T += V^T P^T, output tiles in pairs.  k slot 8 gq + r is row 4 gq + r
+    // for r < 4 and 16 + 4 gq + (r - 4) otherwise, matching the probabilities.
+    static_for<0, kDTiles / 2>([&](auto pr_) {
+      constexpr int pr = decltype(pr_)::value, st = pr & 1;
+      if constexpr (pr + 1 < kDTiles / 2) {
+        ds_tr<0>(vr[st ^ 1][0], tb + v_off_l[2 * pr + 2]);
+        ds_tr<8192>(vr[st ^ 1][1], tb + v_off_l[2 * pr + 2]);
+        ds_tr<0>(vr[st ^ 1][2], tb + v_off_l[2 * pr + 3]);
+        ds_tr<8192>(vr[st ^ 1][3], tb + v_off_l[2 * pr + 3]);
+        asm volatile("s_waitcnt lgkmcnt(4)"
+                     : "+v"(vr[st][0]), "+v"(vr[st][1]), "+v"(vr[st][2]), "+v"(vr[st][3]));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(vr[st][0]), "+v"(vr[st][1]), "+v"(vr[st][2]), "+v"(vr[st][3]));
+      }
+      const u32x2 a2[2] = {vr[st][0], vr[st][1]}, b2[2] = {vr[st][2], vr[st][3]};
+      const bf16x8 vta = __builtin_bit_cast(bf16x8, a2), vtb = __builtin_bit_cast(bf16x8, b2);
+      acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vta, phi, acc[2 * pr], 0, 0, 0);
+      acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtb, phi, acc[2 * pr + 1], 0, 0, 0);
+      acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vta, plo, acc[2 * pr], 0, 0, 0);
+      acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtb, plo, acc[2 * pr + 1], 0, 0, 0);
     });
   }
 
-  // merge the four row groups of the wave, then the four waves (in order)
-  float* sO = reinterpret_cast<float*>(sTile + (ntiles % kBufs) * kTileBytes);  // [4][G][kD]
-  const float l = rows_sum(l_run);
-  static_for<0, G>([&](auto k_) {
-    constexpr int k = decltype(k_)::value;
-    const int hk = rot_i<G, k>(hl);
+  // lane holds O[head li][d = 16 t + 4 gq + i] (heads li < G are real)
+  if (li >= G) return;
+  if (nsplit == 1) {
+    const float inv = 1.f / l_run;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) o[k][x] = rows_sum(o[k][x]);
-    if (rg == 0) {
-      *reinterpret_cast<float4*>(sO + (w * G + hk) * kD + c * 8) =
-          make_float4(o[k][0], o[k][1], o[k][2], o[k][3]);
-      *reinterpret_cast<float4*>(sO + (w * G + hk) * kD + c * 8 + 4) =
-          make_float4(o[k][4], o[k][5], o[k][6], o[k][7]);
-    }
-  });
-  if (rg == 0 && (c & (16 / G - 1)) == 0) {
-    sMw[w][hl] = m_run;
-    sLw[w][hl] = l;
+    for (int t = 0; t < kDTiles; ++t)
+      *reinterpret_cast<f32x4*>(orow + (size_t)li * kD + 16 * t + 4 * gq) = acc[t] * inv;
+    return;
   }
-  __syncthreads();
   const size_t part_stride = partial_stride(G, kD);
   float* part = p.partials + ((size_t)uj * nsplit + sp) * part_stride;
-  for (int idx = tid; idx < G * kD; idx += kAttnThreads) {
-    const int h = idx / kD, d = idx - h * kD;
-    float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sMw[v][h]);
-    float O = 0.f, L = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float f = sMw[v][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sMw[v][h] - M);
-      O = fmaf(f, sO[(v * G + h) * kD + d], O);
-      L = fmaf(f, sLw[v][h], L);
-    }
-    if (nsplit == 1) {
-      orow[idx] = O / L;
-    } else {
-      part[idx] = O;
-      if (d == 0) {
-        part[G * kD + h] = M;
-        part[G * kD + G + h] = L;
-      }
-    }
+  for (int t = 0; t < kDTiles; ++t)
+    *reinterpret_cast<f32x4*>(part + (size_t)li * kD + 16 * t + 4 * gq) = acc[t];
+  if (gq == 0) {
+    part[G * kD + li] = m_run;
+    part[G * kD + G + li] = l_run;
   }
 }
 
@@ -493,8 +480,11 @@ static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<G>, kAttnThreads,
-                                                     0) != hipSuccess)
+        hipFuncSetAttribute((const void*)attn_split_kernel<G>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kBufs * kTileBytes) !=
+            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<G>, kThreads,
+                                                     kBufs * kTileBytes) != hipSuccess)
       return hipErrorUnknown;
     resident = cus * per_cu;
   }
@@ -502,7 +492,7 @@ static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
   if ((int64_t)grid.x > resident) p.gather_first = 1;
   for (int j = 0; j < p0.T; ++j) {
     p.token = j;
-    hipLaunchKernelGGL(attn_split_kernel<G>, grid, dim3(kAttnThreads), 0, s, p);
+    hipLaunchKernelGGL(attn_split_kernel<G>, grid, dim3(kThreads), kBufs * kTileBytes, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
