@@ -44,7 +44,7 @@ constexpr size_t kMRLdsLimit = 160 * 1024;
 static size_t mr_lds_bytes(const avsg_config& c, const WsLayout& ws, const Derived& d) {
   const int64_t tk = (int64_t)c.n_q_tokens * c.k;
   const int64_t ints = 2 * (int64_t)ws.ucap + ws.table_cap + ws.table_cap / 4 +
-                       2 * 16 * (int64_t)d.nbins + d.nbins + 128 +
+                       2 * 16 * (int64_t)d.nbins + d.nbins + 192 +
                        (c.n_q_tokens > 1 ? tk : ws.ucap) + (c.n_q_tokens > 1 ? tk + c.k + 1 : 0);
   return 4 * (size_t)ints;
 }
@@ -69,7 +69,10 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   // and a rank base per 32 ids) when that takes no more LDS than the table
   {
     const int64_t words = (((int64_t)c.n_entries + 31) / 32 + 3) & ~(int64_t)3;
-    d->direct_words = 2 * words <= (int64_t)ws->table_cap + ws->table_cap / 4 ? (int32_t)words : 0;
+    // (two tokens: a third word array, token 0's membership)
+    const int64_t arrays = c.n_q_tokens > 1 ? 3 : 2;
+    d->direct_words =
+        arrays * words <= (int64_t)ws->table_cap + ws->table_cap / 4 ? (int32_t)words : 0;
   }
   d->ubits = 1;
   while ((1 << d->ubits) < ws->ucap) ++d->ubits;

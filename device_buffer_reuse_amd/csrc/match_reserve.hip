@@ -29,9 +29,9 @@
 //  * Victim selection is a stable counting selection: each candidate slot gets
 //    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first).  A
 //    histogram of the bins gives the threshold bin b* that holds the m-th
-//    candidate: the counts of bins 0..3 per wave form a 64-word (bin, wave)
-//    table that one wave scan turns into every (bin, wave) start, and all
-//    bins are counted only if those four hold fewer than m candidates.  Only
+//    candidate: the counts of bins 0..7 per wave form a 128-word (bin, wave)
+//    table that two chained wave scans turn into every (bin, wave) start, and
+//    all bins are counted only if those eight hold fewer than m candidates.  Only
 //    candidates in bins <= b* are ranked, inside their bin in slot order via
 //    ballot/mbcnt per wave plus the (bin, wave) starts; the m first
 //    candidates in (bin, slot) order are the victims.  No comparison sort, no
@@ -186,9 +186,10 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   int32_t* sCnt = sUslot + ucap;             // [16][nbins] per-wave candidates per bin
   int32_t* sOff = sCnt + kMRWaves * nbins;   // [16][nbins] first rank of (wave, bin)
   int32_t* sTot = sOff + kMRWaves * nbins;   // [nbins] -> exclusive bin starts
-  int32_t* sMisc = sTot + nbins;             // [128]: 0 flags, 1 evictions, 16.. scan scratch,
-                                             // 64.. per-lane sink of masked-off LDS atomics
-  int32_t* sMiss = sMisc + 128;              // [max(ucap, T*k)]; T=2: first holds both lists
+  int32_t* sMisc = sTot + nbins;             // [192]: 0 flags, 1 evictions, 16.. scan scratch,
+                                             // 64.. per-lane sink of masked-off LDS atomics,
+                                             // later the (bin, wave) victim-count table
+  int32_t* sMiss = sMisc + 192;              // [max(ucap, T*k)]; T=2: first holds both lists
   int32_t* sMap = sMiss + (T > 1 ? tk : ucap);  // T=2: [T*k] union index per (token, entry)
   int32_t* sDup = sMap + (T > 1 ? tk : 0);      // T=2: [k+1] duplicates before each A index
   int32_t* sWs = sMisc + 16;
@@ -198,8 +199,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // is the union index of the first id of U in that word, so the union index
   // of a member x is base[x / 32] + (members of its word below x)
   const int dw = p.direct_words;
-  uint32_t* sBits = reinterpret_cast<uint32_t*>(sHash);  // [dw]
+  uint32_t* sBits = reinterpret_cast<uint32_t*>(sHash);  // [dw] (two tokens: first token 1's ids)
   int32_t* sBase = sHash + dw;                            // [dw]
+  uint32_t* sBitsA = sBits + 2 * dw;                      // [dw] two tokens: token 0's ids
 
   const int32_t* sel = p.sel + (size_t)u * tk;
   int32_t* slot_table = p.slot_table + (size_t)u * S;
@@ -230,10 +232,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     if (i < tk) stage[i] = selr[r];
   }
   for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) stage[i] = sel[i];
-  if (tid < 128) sMisc[tid] = 0;
+  if (tid < 192) sMisc[tid] = 0;
   if (dw > 0) {  // membership words 0 (dw is a multiple of 4); rank bases need no init
     int4* b4 = reinterpret_cast<int4*>(sBits);
     for (int i = tid; i < (dw >> 2); i += kMRThreads) b4[i] = make_int4(0, 0, 0, 0);
+    int4* a4 = reinterpret_cast<int4*>(sBitsA);
+    if (T > 1)
+      for (int i = tid; i < (dw >> 2); i += kMRThreads) a4[i] = make_int4(0, 0, 0, 0);
   } else {  // table cells -1 and bucket counters 0, 16 bytes per store (C is a multiple of 64)
     int4* h4 = reinterpret_cast<int4*>(sHash);
     for (int i = tid; i < (C >> 2); i += kMRThreads) h4[i] = make_int4(-1, -1, -1, -1);
@@ -266,6 +271,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
           atomicOr(&sBits[x >> 5], 1u << (x & 31));
           if (i == 0 || (prv[r] >> 5) != (x >> 5)) sBase[x >> 5] = i;
         }
+      }
+    } else if (dw > 0) {  // two tokens: each list's membership bits
+#pragma unroll
+      for (int r = 0; r < kSelRegs; ++r) {
+        const int i = tid + r * kMRThreads;
+        const int32_t x = selr[r];
+        if (i < tk && x >= 0 && x < N) atomicOr(&(i < k ? sBitsA : sBits)[x >> 5], 1u << (x & 31));
       }
     } else if (T == 1) {
 #pragma unroll
@@ -307,6 +319,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       if (T == 1 && in_range && dw > 0) {
         atomicOr(&sBits[x >> 5], 1u << (x & 31));
         if ((xp >> 5) != (x >> 5)) sBase[x >> 5] = i;
+      } else if (in_range && dw > 0) {
+        atomicOr(&(i < k ? sBitsA : sBits)[x >> 5], 1u << (x & 31));
       } else if (T == 1 && in_range) {
         hash_insert(sHash, sBcnt, log_cap, ubits, x, i);
       }
@@ -318,7 +332,56 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // ---- 2. union U of the two lists (T = 2): position of each element =
   //         elements below it in both lists minus duplicates below it
   int nu = k;
-  if (T > 1 && sMisc[0] == 0) {
+  if (T > 1 && sMisc[0] == 0 && dw > 0) {
+    // direct addressing: U's membership words are the two lists' words or'ed;
+    // a block scan of their popcounts gives each word's rank base, the set
+    // bits expand into the sorted U, and each (token, entry) finds its union
+    // index from its word (a token-1 entry is a duplicate if token 0's bit
+    // is set)
+    int run = 0;
+    for (int w0 = 0; w0 < dw; w0 += kMRThreads) {
+      const int wi = w0 + tid;
+      const uint32_t uw = wi < dw ? (sBitsA[wi] | sBits[wi]) : 0u;
+      const int cnt = __popc(uw);
+      const int inc = wave_incl_scan(cnt);
+      if (lane == 63) sWs[w] = inc;
+      __syncthreads();
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int v = 0; v < kMRWaves; ++v) {
+        const int x = sWs[v];
+        pre += (v < w) ? x : 0;
+        tot += x;
+      }
+      const int base = run + pre + inc - cnt;
+      if (wi < dw) {
+        sBits[wi] = uw;
+        sBase[wi] = base;
+      }
+      if (base + cnt <= ucap) {  // a larger U is a capacity error (below)
+        uint32_t rest = uw;
+        for (int r = 0; rest != 0; ++r) {
+          sU[base + r] = wi * 32 + __builtin_ctz(rest);
+          rest &= rest - 1;
+        }
+      }
+      run += tot;
+      __syncthreads();  // sWs is reused; sBits and sBase are complete
+    }
+    nu = run;
+    if (nu > S) {
+      if (tid == 0) sMisc[0] = kFlagCapacity;
+    } else {
+      for (int i = tid; i < tk; i += kMRThreads) {
+        const int32_t x = sMiss[i];
+        const uint32_t word = sBits[x >> 5], bit = 1u << (x & 31);
+        const int pos = sBase[x >> 5] + __popc(word & (bit - 1));
+        const bool dup = i >= k && (sBitsA[x >> 5] & bit) != 0;
+        sMap[i] = pos | (dup ? kDupFlag : 0);
+      }
+    }
+    __syncthreads();
+  } else if (T > 1 && sMisc[0] == 0) {
     const int32_t* A = sMiss;
     const int32_t* Bl = sMiss + k;
     int run = 0;
@@ -359,14 +422,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   }
 
   // ---- 3. hash U into the LDS table (two tokens; one token did it above)
-  if (T > 1) {
-    if (sMisc[0] == 0 && dw > 0) {
-      for (int i = tid; i < nu; i += kMRThreads) {
-        const int32_t x = sU[i];
-        atomicOr(&sBits[x >> 5], 1u << (x & 31));
-        if (i == 0 || (sU[i - 1] >> 5) != (x >> 5)) sBase[x >> 5] = i;
-      }
-    } else if (sMisc[0] == 0) {
+  if (T > 1 && dw == 0) {
+    if (sMisc[0] == 0) {
       for (int i = tid; i < nu; i += kMRThreads) hash_insert(sHash, sBcnt, log_cap, ubits, sU[i], i);
     }
     __syncthreads();
@@ -672,29 +729,53 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     // slot group), counted on the scalar unit), published as a [bin][wave]
     // table of 64 words (the sink words, free after the probe); one read per
     // lane and one wave scan in (bin, wave) order then give every wave the
-    // first rank of each of its bins.  Usually bins 0..3 hold the m victims.
-    int32_t* sC4 = sMisc + 64;
-    int c4 = 0;  // lane b < 4: this wave's count of bin b
+    // first rank of each of its bins.  If bins 0..3 hold fewer than m
+    // candidates (a buffer turning over fast leaves the lowest lifetimes
+    // empty), bins 4..7 are counted the same way into the next 64 words.
+    int32_t* sC8 = sMisc + 64;
+    int c8 = 0;  // lane b < 8: this wave's count of bin b
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       int cnt = 0;
 #pragma unroll
       for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
-      c4 = lane == b ? cnt : c4;
+      c8 = lane == b ? cnt : c8;
     }
-    if (lane < 4) sC4[lane * 16 + w] = c4;
+    if (lane < 4) sC8[lane * 16 + w] = c8;
     __syncthreads();
-    const int c = sC4[lane];  // bin lane / 16, wave lane % 16
-    const int inc = wave_incl_scan(c);
-    const bool fast = __builtin_amdgcn_readlane(inc, 63) >= m;  // the same in every wave
+    const int c0 = sC8[lane];  // bin lane / 16, wave lane % 16
+    const int inc0 = wave_incl_scan(c0);
+    const int tot0 = __builtin_amdgcn_readlane(inc0, 63);
+    int c1 = 0, inc1 = tot0;   // bins 4..7, counted only when needed
+    if (tot0 < m) {  // the same in every wave
+#pragma unroll
+      for (int b = 4; b < 8; ++b) {
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
+        c8 = lane == b ? cnt : c8;
+      }
+      if (lane >= 4 && lane < 8) sC8[64 + (lane - 4) * 16 + w] = c8;
+      __syncthreads();
+      c1 = sC8[64 + lane];  // bin 4 + lane / 16, wave lane % 16
+      inc1 = wave_incl_scan(c1) + tot0;
+    }
+    const bool fast = __builtin_amdgcn_readlane(inc1, 63) >= m;  // the same in every wave
     int bstar = nbins;
-    int off[4] = {0, 0, 0, 0};  // fast: this wave's first rank in bins 0..3
+    int off[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // fast: this wave's first rank in bins 0..7
+    uint32_t nz = ~0u;  // fast: bins 0..7 in which this wave has candidates (bit b)
     if (fast) {
-      bstar = __builtin_ctzll(__ballot((lane & 15) == 15 && inc >= m)) >> 4;
-      const int ex = inc - c;
+      const uint64_t r0 = __ballot((lane & 15) == 15 && inc0 >= m);
+      const uint64_t r1 = __ballot((lane & 15) == 15 && inc1 >= m);
+      bstar = r0 ? (__builtin_ctzll(r0) >> 4) : 4 + (__builtin_ctzll(r1) >> 4);
+      const int ex0 = inc0 - c0, ex1 = inc1 - c1;
       const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) off[b] = __builtin_amdgcn_readlane(ex, b * 16 + wu);
+      for (int b = 0; b < 4; ++b) {
+        off[b] = __builtin_amdgcn_readlane(ex0, b * 16 + wu);
+        off[4 + b] = __builtin_amdgcn_readlane(ex1, b * 16 + wu);
+      }
+      nz = (uint32_t)__ballot(lane < 8 && c8 != 0) | ~0xFFu;
     } else {
       // general: histogram of all bins (per wave, in LDS), the bin totals,
       // their exclusive starts, b* and each wave's first rank per bin; lane
@@ -732,6 +813,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) rank[q] = 0;
     for (int b = 0; b <= bstar; ++b) {
+      if (b < 8 && !((nz >> b) & 1)) continue;  // the wave has no candidate in bin b
       int run = 0;
 #pragma unroll
       for (int q = 0; q < MAXP; ++q) {
@@ -750,6 +832,10 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         o = b == 1 ? off[1] : o;
         o = b == 2 ? off[2] : o;
         o = b == 3 ? off[3] : o;
+        if (bstar >= 4) {  // wave-uniform
+#pragma unroll
+          for (int bb = 4; bb < 8; ++bb) o = b == bb ? off[bb] : o;
+        }
         rank[q] = (b >= 0 && b <= bstar) ? o + rank[q] : m;
       }
     } else {
@@ -788,7 +874,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         }
       }
     }
-    if (ev) atomicAdd(&sMisc[1], ev);
+    ev = wave_total(ev);
+    if (lane == 0 && ev) atomicAdd(&sMisc[1], ev);
   }
 
   __syncthreads();
