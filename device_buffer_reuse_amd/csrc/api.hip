@@ -90,7 +90,6 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->misses = off;      off = align256(off + 8 * (size_t)d->units * ws->ucap);
   ws->fetch = off;       off = align256(off + (size_t)d->units * tk);
   ws->err_word = off;    off = align256(off + 8);
-  ws->counters = off;    off = align256(off + 4 * (size_t)d->units * T);
   ws->partials = off;
   off = align256(off + 4 * (size_t)d->units * T * ws->nsplit *
                            partial_stride(c.n_q_heads / c.n_kv_heads, c.head_dim_v));
@@ -226,7 +225,7 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->transfer_mode = AVSG_TRANSFER_FUSED;
   c->match_mode = AVSG_MATCH_HASH;
   c->lds_max = lds_max;
-  // zero the library-owned workspace words (status, counts, error, counters)
+  // zero the library-owned workspace words (status, counts, error)
   if (launch_fill_i32((int32_t*)c->workspace, 0, c->ws.partials / 4, c->stream) != hipSuccess) {
     delete c;
     return AVSG_ERR_HIP;
@@ -437,7 +436,6 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   ap.buf_kv = buf_kv;
   ap.out = out;
   ap.partials = (float*)(ws + ctx->ws.partials);
-  ap.counters = (uint32_t*)(ws + ctx->ws.counters);
   ap.S = c.n_slots;
   ap.units = ctx->d.units;
   ap.Hkv = c.n_kv_heads;

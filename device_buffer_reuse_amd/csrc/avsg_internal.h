@@ -17,7 +17,7 @@ constexpr int kGatherThreads = 256;
 
 // Layout of the caller's workspace (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t unit_status, miss_count, misses, fetch, err_word, counters, partials, total;
+  size_t unit_status, miss_count, misses, fetch, err_word, partials, total;
   int32_t ucap;       // union capacity per unit = min(T*k, S)
   int32_t table_cap;  // hash table cells, power of two >= 2*ucap
   int32_t nsplit;     // attention splits per (unit, token)
@@ -85,7 +85,6 @@ struct AttnParams {
   uint16_t* buf_kv;           // [units][S][row]
   float* out;                 // [B][T][Hq][dv]
   float* partials;            // [units*T][nsplit][partial_stride(G, dv)]
-  uint32_t* counters;         // [units*T]
   int64_t S;
   int32_t units, Hkv, Hq, T, k, tpe, row_elems, nsplit, split_rows;
   int32_t token;              // query token of this launch
