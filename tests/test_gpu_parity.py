@@ -63,6 +63,13 @@ EDGE = {
     # takes the open-addressing hash table
     "big_context": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=200000,
                                            k=200, n_slots=400, steps=8),
+    # two-token reservations whose victims run past eviction bins 0..3 but
+    # stay within bins 0..7 (lifetime 8, and 7 LRU buckets)
+    "mtp_L8": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003,
+                                      k=300, n_slots=700, lifetime_L=8, steps=12),
+    "mtp_lru_b7": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003,
+                                          k=300, n_slots=700, policy="lru", n_buckets=7,
+                                          steps=12),
 }
 
 
