@@ -359,6 +359,29 @@ def main():
             "transfer_kernel_host_GB/s": round(mb / (kt / nm * 1e-3) / 1e9, 2),
             "transfer_kernel_host_link_frac": round(mb / (kt / nm * 1e-3) / 1e9 / HOST_LINK_GBS, 4)}
         assert b.ctx.last_error() == 0
+        # Offload of the new token (append): every unit writes one token row
+        # into host memory, and into its slot where the entry is resident
+        na = 64
+        tok_elems = w.head_dim_qk if w.latent else w.head_dim_qk + w.head_dim_v
+        rng = np.random.default_rng(1)
+        newkv = torch.from_numpy((rng.standard_normal((w.units, tok_elems)).astype(np.float32)
+                                  .view(np.uint32) >> 16).astype(np.int16)).cuda()
+        ent = b.sel_np[-1][::w.n_kv_heads, 0, 0].astype(np.int64)   # resident in unit b*Hkv
+        pos = torch.from_numpy((ent * w.tokens_per_entry).astype(np.int32)).cuda()
+        st = b.st
+        for _ in range(4):
+            b.ctx.append(newkv, pos, b.host, st.buf_kv, st.slot_table)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(na):
+            b.ctx.append(newkv, pos, b.host, st.buf_kv, st.slot_table)
+        e1.record()
+        torch.cuda.synchronize()
+        assert b.ctx.last_error() == 0
+        a_us = e0.elapsed_time(e1) / na * 1e3
+        extra["append"] = {"us": round(a_us, 2), "host_write_bytes": w.units * tok_elems * 2,
+                           "slot_table_bytes_read": w.units * w.n_slots * 4}
         # pinned hipMemcpy host->device peak, for context
         n = 256 << 20
         src = torch.empty(n, dtype=torch.uint8).pin_memory()

@@ -30,7 +30,7 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_destroy", "avsg_reset", "avsg_step", "avsg_last_error", "avsg_validate_state",
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
-            "avsg_set_transfer_mode", "avsg_set_match_mode"]
+            "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append"]
 
 
 class AvsgError(RuntimeError):
@@ -77,6 +77,7 @@ def load():
         "avsg_reset": ([p, p, p], i32),
         "avsg_step": ([p] * 8 + [ctypes.POINTER(avsg_hit_stats)], i32),
         "avsg_last_error": ([p], i32),
+        "avsg_append": ([p] * 6, i32),
         "avsg_validate_state": ([p, p, p], i32),
         "avsg_get_step": ([p], i64),
         "avsg_set_step": ([p, i64], i32),
@@ -133,6 +134,11 @@ def avsg_step(ctx: int, sel_idx: int, q: int, host_kv: int, buf_kv: int, slot_ta
               lifetimes: int, out: int, hit_stats: avsg_hit_stats) -> int:
     return load().avsg_step(ctx, sel_idx, q, host_kv, buf_kv, slot_table, lifetimes, out,
                             ctypes.byref(hit_stats))
+
+
+def avsg_append(ctx: int, new_kv: int, pos: int, host_kv: int, buf_kv: int,
+                slot_table: int) -> int:
+    return load().avsg_append(ctx, new_kv, pos, host_kv, buf_kv, slot_table)
 
 
 def avsg_last_error(ctx: int) -> int:
@@ -298,6 +304,15 @@ class Context:
                        slot_table.data_ptr(), lifetimes.data_ptr(), out.data_ptr(), stats.struct())
         if st != OK:
             raise AvsgError(st, "avsg_step")
+
+    def append(self, new_kv, pos, host_kv, buf_kv, slot_table):
+        """Offload of the new token: new_kv [batch][Hkv][tok_elems] (bf16 bits
+        as int16), pos [batch] int32, both device tensors."""
+        hptr = host_kv.ptr if isinstance(host_kv, HostBuffer) else int(host_kv)
+        st = avsg_append(self.handle, new_kv.data_ptr(), pos.data_ptr(), hptr, buf_kv.data_ptr(),
+                         slot_table.data_ptr())
+        if st != OK:
+            raise AvsgError(st, "avsg_append")
 
     def last_error(self) -> int:
         return avsg_last_error(self.handle)

@@ -491,6 +491,34 @@ avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const 
   return bits ? AVSG_ERR_STATE : AVSG_OK;
 }
 
+avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
+                        uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table) {
+  if (!ctx || !new_kv || !pos || !host_kv || !buf_kv || !slot_table) return AVSG_ERR_INVALID_ARG;
+  if (((uintptr_t)new_kv | (uintptr_t)host_kv | (uintptr_t)buf_kv) & 15)
+    return AVSG_ERR_INVALID_ARG;
+  const void* host_dev = nullptr;
+  avsg_status st = device_view_of_pinned(ctx, host_kv, &host_dev);
+  if (st != AVSG_OK) return st;
+  const avsg_config& c = ctx->cfg;
+  AppendParams ap;
+  ap.new_kv = new_kv;
+  ap.pos = pos;
+  ap.host_kv = (uint16_t*)host_dev;
+  ap.buf_kv = buf_kv;
+  ap.slot_table = slot_table;
+  ap.err_word = (uint32_t*)(ctx->workspace + ctx->ws.err_word);
+  ap.Hkv = c.n_kv_heads;
+  ap.N = c.n_entries;
+  ap.S = c.n_slots;
+  ap.tpe = c.tokens_per_entry;
+  ap.row_elems = ctx->d.row_elems;
+  ap.latent = c.kv_layout == AVSG_KV_LATENT ? 1 : 0;
+  ap.dqk = c.head_dim_qk;
+  ap.dv = c.head_dim_v;
+  ap.tok_elems = ap.latent ? c.head_dim_qk : c.head_dim_qk + c.head_dim_v;
+  return launch_append(ap, ctx->d.units, ctx->stream) == hipSuccess ? AVSG_OK : AVSG_ERR_HIP;
+}
+
 avsg_status avsg_host_alloc(size_t bytes, unsigned flags, void** host_ptr) {
   if (!host_ptr || bytes == 0) return AVSG_ERR_INVALID_ARG;
   *host_ptr = nullptr;

@@ -93,12 +93,23 @@ struct AttnParams {
   float scale_log2e;
 };
 
+struct AppendParams {
+  const uint16_t* new_kv;     // [units][tok_elems]: the token's K then V, or its latent vector
+  const int32_t* pos;         // [batch]: token position of each request
+  uint16_t* host_kv;          // device-visible address of the pinned host rows [units][N][row]
+  uint16_t* buf_kv;           // [units][S][row]
+  const int32_t* slot_table;  // [units][S]
+  uint32_t* err_word;
+  int32_t Hkv, N, S, tpe, row_elems, tok_elems, dqk, dv, latent;
+};
+
 hipError_t launch_match_reserve(const MatchReserveParams& p, int units, size_t lds, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, int grid, hipStream_t s);
 hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s);
 hipError_t launch_attn_latent(const AttnParams& p, int dqk, int dv, hipStream_t s);
 hipError_t launch_attn_combine(const AttnParams& p, int G, int D, hipStream_t s);
 hipError_t attn_latent_set_lds();
+hipError_t launch_append(const AppendParams& p, int units, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_validate(const int32_t* slot_table, const int32_t* lifetimes, int units, int S,
                            int N, int policy, int L, int64_t t, uint32_t* err, hipStream_t s);

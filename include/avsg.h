@@ -158,8 +158,39 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
                       const uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
                       int32_t* lifetimes, float* out, const avsg_hit_stats* hit_stats);
 
+/* Offload of the newly decoded token (Spin summary, section 2A: Offload,
+ * placing KV data into memory, is a system-managed operation over a
+ * page-based KV substrate; section 2B: physical pages per attention head).
+ * For every request b and KV head g, writes the token's key and value (latent
+ * layout: its latent vector) at token position pos[b] of unit
+ * u = b * n_kv_heads + g: entry e = pos[b] / tokens_per_entry, token row
+ * r = pos[b] % tokens_per_entry.  Split layout: the key goes to elements
+ * [r * head_dim_qk, +head_dim_qk) of the entry's row and the value to
+ * [tokens_per_entry * head_dim_qk + r * head_dim_v, +head_dim_v); latent
+ * layout: the whole row.  The bytes go to host_kv and, if entry e is resident
+ * (a slot s with slot_table[s] == e), to buf_kv at slot s as well, so the
+ * buffer keeps exact copies of host rows.  Slot table, lifetimes and the step
+ * counter do not change (an append is not a selection).
+ *   new_kv     device, bf16 [batch][n_kv_heads][tok_elems], tok_elems =
+ *              head_dim_qk + head_dim_v (split: K then V) or head_dim_qk
+ *              (latent).                                            read only
+ *   pos        device, int32 [batch]: token position in
+ *              [0, n_entries * tokens_per_entry).                   read only
+ *   host_kv    host, pinned, bf16 [units][N][row] (as in avsg_step). written
+ *   buf_kv     device, bf16 [units][S][row].                        in/out
+ *   slot_table device, int32 [units][S].                            read only
+ * new_kv, host_kv and buf_kv must be 16-byte aligned.  A request whose pos is
+ * out of range writes nothing and raises AVSG_ERR_RANGE; a unit where more
+ * than 32 slots hold the entry (an invalid state) writes nothing and raises
+ * AVSG_ERR_STATE (both reported by avsg_last_error).  Returns
+ * AVSG_ERR_INVALID_ARG, AVSG_ERR_NOT_PINNED or AVSG_ERR_HIP as avsg_step.
+ * Stream-ordered with the steps; never waits for the GPU.  The host sees the
+ * written bytes once the stream has been synchronised. */
+avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
+                        uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table);
+
 /* Syncs the stream and returns the highest-precedence data error raised by
- * the steps since the last call (RANGE, then UNSORTED, CAPACITY, STATE), or
+ * the steps and appends since the last call (RANGE, then UNSORTED, CAPACITY, STATE), or
  * AVSG_OK; then clears it. */
 avsg_status avsg_last_error(avsg_ctx* ctx);
 

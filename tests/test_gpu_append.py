@@ -1,0 +1,147 @@
+"""Token append (Offload) on the GPU vs the oracle, through the C ABI.
+
+Decode steps alternate with appends.  After each append the host KV store and
+the device buffer must equal the oracle's copies bit for bit, the slot table
+and lifetimes must be unchanged, and the following steps (whose selections
+contain appended entries) must still match the oracle in state and attention.
+Positions are chosen so that every request appends both into entries that are
+resident (the slot is written through) and into entries that are not."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import tracegen as tg
+from gpu_harness import Runner, say
+from oracle import append as oapp
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "token": tg.WORKLOADS[2].replace(batch=3, n_kv_heads=2, n_q_heads=8, n_entries=5003, k=300,
+                                     n_slots=1000, steps=8),
+    "page16": tg.WORKLOADS[4].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001, k=37,
+                                      n_slots=100, steps=10),
+    "page3": tg.WORKLOADS[4].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1000,
+                                     tokens_per_entry=3, k=200, n_slots=400, steps=8),
+    "mtp": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003, k=300,
+                                   n_slots=700, steps=6),
+    "latent": tg.WORKLOADS[5].replace(batch=3, n_entries=5003, k=700, n_slots=1500, steps=6),
+}
+
+
+def _tok_elems(w):
+    return w.head_dim_qk if w.latent else w.head_dim_qk + w.head_dim_v
+
+
+def _new_tokens(w, rng):
+    x = rng.standard_normal((w.units, _tok_elems(w))).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)  # bf16 bits (finite)
+
+
+def _positions(w, sel_t, rng, t):
+    """Request b appends into an entry of unit b*Hkv's current selection (it
+    is resident after the step) on even steps, else anywhere."""
+    P = w.tokens_per_entry
+    pos = np.empty(w.batch, np.int32)
+    for b in range(w.batch):
+        if t % 2 == 0:
+            e = int(rng.choice(sel_t[b * w.n_kv_heads, 0]))
+        else:
+            e = int(rng.integers(0, w.n_entries))
+        pos[b] = e * P + int(rng.integers(0, P))
+    return pos
+
+
+def _append_and_compare(run, w, new, pos, what):
+    torch = run.torch
+    st_before = run.st.slot_table.cpu().numpy().copy()
+    lf_before = run.st.lifetimes.cpu().numpy().copy()
+    ref_host = run.host.array.copy()
+    status = oapp.append(w, ref_host, new, pos, run.ob.slot_tok, run.ob.buf)
+    run.ctx.append(torch.from_numpy(new.view(np.int16)).cuda(), torch.from_numpy(pos).cuda(),
+                   run.host, run.st.buf_kv, run.st.slot_table)
+    torch.cuda.synchronize()
+    assert np.array_equal(run.host.array, ref_host), "host_kv after append " + what
+    assert np.array_equal(run.st.buf_kv.cpu().numpy().view(np.uint16), run.ob.buf), \
+        "buf_kv after append " + what
+    assert np.array_equal(run.st.slot_table.cpu().numpy(), st_before), "slot_table " + what
+    assert np.array_equal(run.st.lifetimes.cpu().numpy(), lf_before), "lifetimes " + what
+    return status
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_append_parity(name):
+    from device_buffer_reuse_amd import avsg
+    w = CASES[name]
+    say("[append] %s units=%d tpe=%d" % (name, w.units, w.tokens_per_entry))
+    sel = tg.selections(w)
+    rng = np.random.default_rng(len(name))
+    run = Runner(w)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+            pos = _positions(w, sel[t], rng, t)
+            st = _append_and_compare(run, w, _new_tokens(w, rng), pos, "t=%d" % t)
+            assert (st == 0).all()
+        assert run.ctx.last_error() == avsg.OK
+        # an out-of-range position writes nothing for its request and is
+        # reported; the other requests append as usual
+        pos = _positions(w, sel[w.steps - 1], rng, 0)
+        pos[0] = w.n_entries * w.tokens_per_entry
+        st = _append_and_compare(run, w, _new_tokens(w, rng), pos, "range")
+        assert st[0] == oapp.ERR_RANGE
+        assert run.ctx.last_error() == avsg.ERR_RANGE
+        assert run.ctx.last_error() == avsg.OK
+    finally:
+        run.close()
+        run.host.free()
+
+
+@pytest.mark.parametrize("cid", [2, 4, 5])
+def test_append_full_size(cid):
+    """Full workload shapes: after a few steps every unit appends into an
+    entry it holds; the written host rows and slots are compared with the
+    oracle's append applied to copies of those rows."""
+    from device_buffer_reuse_amd import avsg
+    w = tg.WORKLOADS[cid]
+    steps = 4
+    say("[append-full] %s units=%d" % (w.name, w.units))
+    sel = tg.selections(w, steps=steps)
+    run = Runner(w, attn_units=[0, w.units - 1])
+    rng = np.random.default_rng(cid)
+    try:
+        for t in range(steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=(t == steps - 1))
+        pos = _positions(w, sel[steps - 1], rng, 0)
+        new = _new_tokens(w, rng)
+        P = w.tokens_per_entry
+        ent = pos // P
+        units = np.arange(w.units)
+        b_of = units // w.n_kv_heads
+        # expected rows: the oracle's append applied to copies of the touched
+        # rows, each as entry 0 of a one-entry context
+        host_rows = run.host.array[units, ent[b_of]].copy()          # [units][row]
+        slot_tok = run.ob.slot_tok
+        # the slot holding the entry (every unit of request b holds it in
+        # unit b*Hkv; other heads may not): -1 where none does
+        holder = np.array([int(np.nonzero(slot_tok[u] == ent[b_of[u]])[0][0])
+                           if (slot_tok[u] == ent[b_of[u]]).any() else -1 for u in units])
+        assert (holder[::w.n_kv_heads] >= 0).all()
+        exp = np.ascontiguousarray(host_rows[:, None, :])
+        st = oapp.append(w.replace(n_entries=1), exp, new, pos % P)
+        assert (st == 0).all()
+        run.ctx.append(run.torch.from_numpy(new.view(np.int16)).cuda(),
+                       run.torch.from_numpy(pos).cuda(), run.host, run.st.buf_kv,
+                       run.st.slot_table)
+        run.torch.cuda.synchronize()
+        assert np.array_equal(run.host.array[units, ent[b_of]], exp[:, 0])
+        held = units[holder >= 0]
+        idx_u = run.torch.from_numpy(held).cuda()
+        idx_s = run.torch.from_numpy(holder[held]).cuda()
+        got_slots = run.st.buf_kv[idx_u, idx_s].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_slots, exp[held, 0])
+        assert run.ctx.last_error() == avsg.OK
+    finally:
+        run.close()
+        run.host.free()
