@@ -280,7 +280,8 @@ def main():
     miss_per_step = n_miss / K
     union_per_step = (n_hit + n_miss) / K
 
-    per = {"match_reserve": kern[0] / K, "gather": kern[1] / K, "attention": kern[2] / K}
+    per = {"match_reserve": kern[0] / K, "gather": kern[1] / K, "attention": kern[2] / K,
+           "combine": kern[3] / K}
     fused = a.transfer in (0, 3)
     host_b = miss_per_step * row_bytes          # bytes over the host link per step
     ab = attn_bytes(w)
@@ -290,6 +291,9 @@ def main():
         "gather": {"hbm": 0.0 if fused else host_b, "host": 0.0 if fused else host_b, "flop": 0.0},
         "attention": {"hbm": ab + (host_b if fused else 0.0), "host": host_b if fused else 0.0,
                       "flop": float(attn_flops(w))},
+        # the merge of the split partials: no algorithmic bytes of its own
+        # (the outputs are counted with the attention)
+        "combine": {"hbm": 0.0, "host": 0.0, "flop": 0.0},
     }
     peaks = {"hbm": (HBM_PEAK_GBS, "GB/s", 1e9), "host": (HOST_LINK_GBS, "GB/s", 1e9),
              "flop": (MFMA_BF16_TFLOPS if w.latent else FP32_VALU_TFLOPS, "TFLOP/s", 1e12)}
@@ -337,6 +341,7 @@ def main():
             "step_hbm_frac": round(step_bytes / (ms_h / nh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "attention_us": round(kh[2] / nh * 1e3, 2),
             "attention_hbm_frac": round(ab / (kh[2] / nh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "combine_us": round(kh[3] / nh * 1e3, 2),
             "match_reserve_us": round(kh[0] / nh * 1e3, 2)}
         # all-miss: disjoint windows, every entry crosses the host link
         nm = min(K, 32)

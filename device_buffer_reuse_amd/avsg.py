@@ -174,11 +174,11 @@ def avsg_profile_begin(ctx: int, max_steps: int) -> int:
 
 
 def avsg_profile_end(ctx: int):
-    """Returns (status, [ms of match_reserve, gather, attention], steps)."""
-    ms = (ctypes.c_double * 3)()
+    """Returns (status, [ms of match_reserve, gather, attention, combine], steps)."""
+    ms = (ctypes.c_double * 4)()
     n = ctypes.c_int32()
     st = load().avsg_profile_end(ctx, ms, ctypes.byref(n))
-    return st, [ms[0], ms[1], ms[2]], n.value
+    return st, [ms[0], ms[1], ms[2], ms[3]], n.value
 
 
 def avsg_host_alloc(nbytes: int, flags: int = 0):
@@ -346,7 +346,7 @@ class Context:
             raise AvsgError(st, "avsg_profile_begin")
 
     def profile_end(self):
-        """(per-kernel summed ms [match_reserve, gather, attention], steps)"""
+        """(per-stage summed ms [match_reserve, gather, attention, combine], steps)"""
         st, ms, n = avsg_profile_end(self.handle)
         if st != OK:
             raise AvsgError(st, "avsg_profile_end")

@@ -22,13 +22,17 @@ struct avsg_ctx {
   int32_t transfer_mode;         // avsg_transfer_mode
   int32_t match_mode;            // avsg_match_mode
   int lds_max;
-  hipEvent_t* prof_events;       // 4 per profiled step, or null
+  hipEvent_t* prof_events;       // kProfMarks per profiled step, or null
   int32_t prof_max, prof_used;
 };
 
 namespace avsg {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// profiling events per step: before match_reserve, then after match_reserve,
+// gather, attention and combine
+constexpr int kProfMarks = 5;
 
 static int32_t next_pow2(int64_t x) {
   int32_t c = 64;
@@ -260,7 +264,7 @@ avsg_status avsg_set_stream(avsg_ctx* ctx, void* stream) {
 
 static void destroy_prof_events(avsg_ctx* ctx) {
   if (!ctx->prof_events) return;
-  for (int32_t i = 0; i < 4 * ctx->prof_max; ++i)
+  for (int32_t i = 0; i < kProfMarks * ctx->prof_max; ++i)
     if (ctx->prof_events[i]) (void)hipEventDestroy(ctx->prof_events[i]);
   free(ctx->prof_events);
   ctx->prof_events = nullptr;
@@ -269,11 +273,11 @@ static void destroy_prof_events(avsg_ctx* ctx) {
 
 avsg_status avsg_profile_begin(avsg_ctx* ctx, int32_t max_steps) {
   if (!ctx || max_steps < 1 || ctx->prof_events) return AVSG_ERR_INVALID_ARG;
-  ctx->prof_events = (hipEvent_t*)calloc(4 * (size_t)max_steps, sizeof(hipEvent_t));
+  ctx->prof_events = (hipEvent_t*)calloc(kProfMarks * (size_t)max_steps, sizeof(hipEvent_t));
   if (!ctx->prof_events) return AVSG_ERR_INVALID_ARG;
   ctx->prof_max = max_steps;
   ctx->prof_used = 0;
-  for (int32_t i = 0; i < 4 * max_steps; ++i)
+  for (int32_t i = 0; i < kProfMarks * max_steps; ++i)
     if (hipEventCreate(&ctx->prof_events[i]) != hipSuccess) {
       destroy_prof_events(ctx);
       return AVSG_ERR_HIP;
@@ -284,13 +288,13 @@ avsg_status avsg_profile_begin(avsg_ctx* ctx, int32_t max_steps) {
 avsg_status avsg_profile_end(avsg_ctx* ctx, double* ms, int32_t* steps) {
   if (!ctx || !ms || !steps || !ctx->prof_events) return AVSG_ERR_INVALID_ARG;
   avsg_status st = AVSG_OK;
-  ms[0] = ms[1] = ms[2] = 0.0;
+  for (int k = 0; k < kProfMarks - 1; ++k) ms[k] = 0.0;
   if (hipStreamSynchronize(ctx->stream) != hipSuccess) st = AVSG_ERR_HIP;
   for (int32_t i = 0; st == AVSG_OK && i < ctx->prof_used; ++i)
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < kProfMarks - 1; ++k) {
       float x = 0.f;
-      if (hipEventElapsedTime(&x, ctx->prof_events[4 * i + k], ctx->prof_events[4 * i + k + 1]) !=
-          hipSuccess) {
+      hipEvent_t* ev = ctx->prof_events + kProfMarks * i;
+      if (hipEventElapsedTime(&x, ev[k], ev[k + 1]) != hipSuccess) {
         st = AVSG_ERR_HIP;
         break;
       }
@@ -303,7 +307,7 @@ avsg_status avsg_profile_end(avsg_ctx* ctx, double* ms, int32_t* steps) {
 
 static inline void prof_mark(avsg_ctx* ctx, int k) {
   if (ctx->prof_events && ctx->prof_used < ctx->prof_max)
-    (void)hipEventRecord(ctx->prof_events[4 * ctx->prof_used + k], ctx->stream);
+    (void)hipEventRecord(ctx->prof_events[kProfMarks * ctx->prof_used + k], ctx->stream);
 }
 
 avsg_status avsg_destroy(avsg_ctx* ctx) {
@@ -452,6 +456,11 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
                      : launch_attn_split(ap, ctx->d.G, ctx->stream);
   if (e != hipSuccess) return AVSG_ERR_HIP;
   prof_mark(ctx, 3);
+  if (ap.nsplit > 1) {
+    const int G = c.n_q_heads / (c.kv_layout == AVSG_KV_LATENT ? 1 : c.n_kv_heads);
+    if (launch_attn_combine(ap, G, c.head_dim_v, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
+  }
+  prof_mark(ctx, 4);
   if (ctx->prof_events && ctx->prof_used < ctx->prof_max) ctx->prof_used += 1;
   ctx->t += 1;
   return AVSG_OK;

@@ -400,8 +400,7 @@ hipError_t launch_attn_latent(const AttnParams& p0, int dqk, int dv, hipStream_t
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.nsplit == 1) return hipSuccess;
-  return launch_attn_combine(p0, p0.Hq, kDv, s);
+  return hipSuccess;
 }
 
 hipError_t attn_latent_set_lds() {

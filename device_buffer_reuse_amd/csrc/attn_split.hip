@@ -496,8 +496,7 @@ static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.nsplit == 1) return hipSuccess;
-  return launch_attn_combine(p0, G, kD, s);
+  return hipSuccess;
 }
 
 hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s) {

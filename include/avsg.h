@@ -262,11 +262,12 @@ int32_t avsg_attn_splits(const avsg_ctx* ctx);
 /* Per-kernel timing with HIP events on the context's stream (observability,
  * not part of the method).  avsg_profile_begin creates events for up to
  * max_steps later steps; each of those steps records an event before its
- * first kernel and after each of its three kernels (match_reserve, gather,
- * attention).  avsg_profile_end syncs the stream, writes the summed
- * milliseconds of each kernel to ms[0..2] and the number of profiled steps to
- * *steps, and destroys the events.  Returns AVSG_ERR_INVALID_ARG if
- * profiling is not in the expected state. */
+ * first kernel and after each of its four stages (match_reserve, gather,
+ * attention, combine of the split partials; a stage a step does not run
+ * measures as the gap between its neighbours).  avsg_profile_end syncs the
+ * stream, writes the summed milliseconds of each stage to ms[0..3] and the
+ * number of profiled steps to *steps, and destroys the events.  Returns
+ * AVSG_ERR_INVALID_ARG if profiling is not in the expected state. */
 avsg_status avsg_profile_begin(avsg_ctx* ctx, int32_t max_steps);
 avsg_status avsg_profile_end(avsg_ctx* ctx, double* ms, int32_t* steps);
 

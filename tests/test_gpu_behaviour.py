@@ -165,3 +165,26 @@ def test_not_pinned_rejected():
     assert e.value.status == avsg.ERR_NOT_PINNED
     assert ctx.t == 0
     ctx.close()
+
+
+def test_profile_events_per_stage():
+    """Per-stage event timing: every profiled step reports its match_reserve,
+    (absent) gather, attention and combine intervals; profiling does not
+    change the results."""
+    say("[behaviour] profile events")
+    w = W.replace(k=500)   # two attention splits per (unit, token)
+    sel = tg.selections(w)
+    a, oa, _ = _run(w, sel, stop=3)
+    run = Runner(w, host=a.host, track_buf=False)
+    run.ctx.profile_begin(3)
+    for t in range(3):
+        run.gpu_step(sel[t], tg.queries(w, t))
+    ms, n = run.ctx.profile_end()
+    assert n == 3 and len(ms) == 4
+    assert ms[0] > 0 and ms[2] > 0 and ms[3] > 0 and ms[1] >= 0
+    assert run.ctx.attn_splits > 1
+    assert np.array_equal(run.st.out.cpu().numpy(), oa[2])
+    with pytest.raises(Exception):
+        run.ctx.profile_end()   # not profiling any more
+    run.close()
+    a.close()
