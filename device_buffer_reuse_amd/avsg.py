@@ -30,7 +30,8 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_destroy", "avsg_reset", "avsg_step", "avsg_last_error", "avsg_validate_state",
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
-            "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append"]
+            "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
+            "avsg_rebuild_index"]
 
 
 class AvsgError(RuntimeError):
@@ -79,6 +80,7 @@ def load():
         "avsg_last_error": ([p], i32),
         "avsg_append": ([p] * 6, i32),
         "avsg_validate_state": ([p, p, p], i32),
+        "avsg_rebuild_index": ([p, p], i32),
         "avsg_get_step": ([p], i64),
         "avsg_set_step": ([p, i64], i32),
         "avsg_host_alloc": ([sz, ctypes.c_uint, ctypes.POINTER(p)], i32),
@@ -147,6 +149,10 @@ def avsg_last_error(ctx: int) -> int:
 
 def avsg_validate_state(ctx: int, slot_table: int, lifetimes: int) -> int:
     return load().avsg_validate_state(ctx, slot_table, lifetimes)
+
+
+def avsg_rebuild_index(ctx: int, slot_table: int) -> int:
+    return load().avsg_rebuild_index(ctx, slot_table)
 
 
 def avsg_get_step(ctx: int) -> int:
@@ -319,6 +325,9 @@ class Context:
 
     def validate_state(self, slot_table, lifetimes) -> int:
         return avsg_validate_state(self.handle, slot_table.data_ptr(), lifetimes.data_ptr())
+
+    def rebuild_index(self, slot_table) -> int:
+        return avsg_rebuild_index(self.handle, slot_table.data_ptr())
 
     @property
     def t(self) -> int:

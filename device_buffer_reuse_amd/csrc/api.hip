@@ -485,8 +485,9 @@ avsg_status avsg_last_error(avsg_ctx* ctx) {
   return status_from_bits(bits);
 }
 
-avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const int32_t* lifetimes) {
-  if (!ctx || !slot_table || !lifetimes) return AVSG_ERR_INVALID_ARG;
+// Derives the id -> slot map of every unit from slot_table in LDS (and checks
+// lifetimes when given); syncs.  AVSG_ERR_STATE if any unit's map is invalid.
+static avsg_status check_state(avsg_ctx* ctx, const int32_t* slot_table, const int32_t* lifetimes) {
   uint32_t* word = (uint32_t*)(ctx->workspace + ctx->ws.err_word) + 1;
   if (launch_fill_i32((int32_t*)word, 0, 1, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
   const avsg_config& c = ctx->cfg;
@@ -500,6 +501,15 @@ avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const 
   return bits ? AVSG_ERR_STATE : AVSG_OK;
 }
 
+avsg_status avsg_rebuild_index(avsg_ctx* ctx, const int32_t* slot_table) {
+  if (!ctx || !slot_table) return AVSG_ERR_INVALID_ARG;
+  return check_state(ctx, slot_table, nullptr);
+}
+
+avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const int32_t* lifetimes) {
+  if (!ctx || !slot_table || !lifetimes) return AVSG_ERR_INVALID_ARG;
+  return check_state(ctx, slot_table, lifetimes);
+}
 avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
                         uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table) {
   if (!ctx || !new_kv || !pos || !host_kv || !buf_kv || !slot_table) return AVSG_ERR_INVALID_ARG;

@@ -935,11 +935,13 @@ __global__ __launch_bounds__(kMRThreads) void validate_kernel(const int32_t* slo
   int bad = 0;
   for (int s = threadIdx.x; s < S; s += kMRThreads) {
     const int32_t x = slot_table[(size_t)u * S + s];
-    const int32_t l = lifetimes[(size_t)u * S + s];
     if (x < -1 || x >= N) { bad = 1; continue; }
     if (x < 0) continue;
-    if (policy == AVSG_POLICY_LIFETIME && (l < 0 || l > L)) bad = 1;
-    if (policy == AVSG_POLICY_BUCKET_LRU && (l < 0 || (int64_t)l >= t)) bad = 1;
+    if (lifetimes) {  // null: the id map alone
+      const int32_t l = lifetimes[(size_t)u * S + s];
+      if (policy == AVSG_POLICY_LIFETIME && (l < 0 || l > L)) bad = 1;
+      if (policy == AVSG_POLICY_BUCKET_LRU && (l < 0 || (int64_t)l >= t)) bad = 1;
+    }
     uint32_t h = hash_id(x, log_cap);
     while (true) {
       int prev = atomicCAS(&tab[h], -1, x);

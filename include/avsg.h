@@ -199,6 +199,14 @@ avsg_status avsg_last_error(avsg_ctx* ctx);
  * Returns AVSG_OK or AVSG_ERR_STATE. */
 avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const int32_t* lifetimes);
 
+/* No hash index persists between steps: every step derives the id -> slot
+ * map of each unit afresh (in LDS) from the selection and slot_table, so a
+ * buffer state restored from a checkpoint needs no index rebuild before it
+ * is used.  This call derives the map once from slot_table alone and checks
+ * that it is one: every id in [-1, N) and no id in two slots (syncs).
+ * Returns AVSG_OK or AVSG_ERR_STATE. */
+avsg_status avsg_rebuild_index(avsg_ctx* ctx, const int32_t* slot_table);
+
 /* Step counter (decode step of the next avsg_step), for checkpoint/resume. */
 int64_t avsg_get_step(const avsg_ctx* ctx);
 avsg_status avsg_set_step(avsg_ctx* ctx, int64_t t);

@@ -142,10 +142,23 @@ def test_validate_state():
     for t in range(3):
         run.gpu_step(sel[t], tg.queries(W, t))
     assert run.ctx.validate_state(run.st.slot_table, run.st.lifetimes) == avsg.OK
+    assert run.ctx.rebuild_index(run.st.slot_table) == avsg.OK
+    # a lifetime out of range is a state error, but not of the id map
+    lf = run.st.lifetimes[1].cpu().numpy()
+    occ1 = np.nonzero(run.st.slot_table[1].cpu().numpy() >= 0)[0]
+    run.st.lifetimes[1, int(occ1[0])] = W.lifetime_L + 1
+    assert run.ctx.validate_state(run.st.slot_table, run.st.lifetimes) == avsg.ERR_STATE
+    assert run.ctx.rebuild_index(run.st.slot_table) == avsg.OK
+    run.st.lifetimes[1, int(occ1[0])] = int(lf[occ1[0]])
+    # an id held by two slots breaks both
     st = run.st.slot_table[0].cpu().numpy()
     occ = np.nonzero(st >= 0)[0]
     run.st.slot_table[0, int(occ[1])] = int(st[occ[0]])
     assert run.ctx.validate_state(run.st.slot_table, run.st.lifetimes) == avsg.ERR_STATE
+    assert run.ctx.rebuild_index(run.st.slot_table) == avsg.ERR_STATE
+    # an id past the context as well
+    run.st.slot_table[0, int(occ[1])] = W.n_entries
+    assert run.ctx.rebuild_index(run.st.slot_table) == avsg.ERR_STATE
     run.close()
 
 
