@@ -61,10 +61,11 @@ def attend_unit(w, q_bits: np.ndarray, host_kv_unit: np.ndarray, sel_unit: np.nd
 
 
 def attend(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=None,
-           units=None) -> np.ndarray:
+           units=None, lengths=None) -> np.ndarray:
     """float64 out [B][T][Hq][dv] for one step.  host_kv is [units][N][row]
-    (uint16 bf16 bits), sel is [units][T][k].  Units not in `units` are NaN;
-    units with a nonzero status are zero."""
+    (uint16 bf16 bits), sel is [units][T][k], of which the first
+    lengths[u][j] entries are in use (all when lengths is None).  Units not
+    in `units` are NaN; units with a nonzero status are zero."""
     out = np.full((w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_v), np.nan)
     G = w.n_q_heads // w.n_kv_heads
     for u in (range(w.units) if units is None else units):
@@ -73,5 +74,7 @@ def attend(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=N
             if status is not None and status[u] != 0:
                 out[b, j, g * G:(g + 1) * G] = 0.0
             else:
-                out[b, j, g * G:(g + 1) * G] = attend_unit(w, q_bits, host_kv[u], sel[u], u, j)
+                su = sel[u] if lengths is None else [sel[u][jj][:lengths[u][jj]]
+                                                     for jj in range(w.n_q_tokens)]
+                out[b, j, g * G:(g + 1) * G] = attend_unit(w, q_bits, host_kv[u], su, u, j)
     return out

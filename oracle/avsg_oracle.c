@@ -90,6 +90,9 @@ static int32_t find_sorted(const int32_t* a, int32_t n, int32_t x) {
 /*
  * One decode step t of one unit.
  *   sel        [T][k]  selected ids of each query token
+ *   len        [T]     entries of each token's list in use (its first len[j]
+ *                      ids; the rest is ignored), or NULL for k each.  A
+ *                      length outside [1, k] is a range error.
  *   slot_tok   [S]     in/out: id held by each slot, -1 = empty
  *   life       [S]     in/out: lifetime (lifetime policy) or last-selected
  *                      step (LRU policy; -1 for a slot never filled)
@@ -99,9 +102,9 @@ static int32_t find_sorted(const int32_t* a, int32_t n, int32_t x) {
  *   counts     [4]     out: n_hit, n_miss, n_evict, |U|
  * Returns a status; on error the state is unchanged, flags are 0, slots -1.
  */
-int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, int32_t* slot_tok,
-                     int32_t* life, uint8_t* hit_flag, int32_t* sel_slot, int32_t* fill_slot,
-                     int32_t* fill_id, int32_t* counts) {
+int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const int32_t* len,
+                     int32_t* slot_tok, int32_t* life, uint8_t* hit_flag, int32_t* sel_slot,
+                     int32_t* fill_slot, int32_t* fill_id, int32_t* counts) {
   const int32_t S = c->n_slots, N = c->n_entries, T = c->n_tokens, k = c->k;
   const int32_t L = c->lifetime_L, B = c->n_buckets;
   const int32_t tk = T * k;
@@ -109,21 +112,31 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, int32_t
   for (int32_t i = 0; i < tk; ++i) { hit_flag[i] = 0; sel_slot[i] = -1; }
   for (int32_t i = 0; i < 4; ++i) counts[i] = 0;
 
-  /* 1. validate the selection and form the union U */
+  /* 1. validate the selection and form the union U of the lists in use */
   int range_bad = 0, order_bad = 0;
-  for (int32_t j = 0; j < T; ++j)
-    for (int32_t i = 0; i < k; ++i) {
+  int32_t n_used = 0;
+  for (int32_t j = 0; j < T; ++j) {
+    const int32_t nj = len ? len[j] : k;
+    if (nj < 1 || nj > k) { range_bad = 1; continue; }
+    for (int32_t i = 0; i < nj; ++i) {
       int32_t x = sel[j * k + i];
       if (x < 0 || x >= N) range_bad = 1;
       if (i > 0 && x <= sel[j * k + i - 1]) order_bad = 1;
     }
+    n_used += nj;
+  }
   if (range_bad) return OR_ERR_RANGE;
   if (order_bad) return OR_ERR_UNSORTED;
   int32_t* U = (int32_t*)malloc(sizeof(int32_t) * (size_t)(tk > 0 ? tk : 1));
-  memcpy(U, sel, sizeof(int32_t) * (size_t)tk);
-  qsort(U, (size_t)tk, sizeof(int32_t), cmp_i32);
+  n_used = 0;
+  for (int32_t j = 0; j < T; ++j) {
+    const int32_t nj = len ? len[j] : k;
+    memcpy(U + n_used, sel + j * k, sizeof(int32_t) * (size_t)nj);
+    n_used += nj;
+  }
+  qsort(U, (size_t)n_used, sizeof(int32_t), cmp_i32);
   int32_t nu = 0;
-  for (int32_t i = 0; i < tk; ++i)
+  for (int32_t i = 0; i < n_used; ++i)
     if (nu == 0 || U[i] != U[nu - 1]) U[nu++] = U[i];
   if (nu > S) { free(U); return OR_ERR_CAPACITY; }
 
@@ -213,11 +226,15 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, int32_t
     ++r;
   }
 
-  /* 6. per-(token, entry) outputs read off the union */
-  for (int32_t i = 0; i < tk; ++i) {
-    int32_t a = find_sorted(U, nu, sel[i]);
-    sel_slot[i] = uslot[a];
-    hit_flag[i] = uhit[a];
+  /* 6. per-(token, entry) outputs read off the union (entries past a list's
+   *    length keep slot -1 and flag 0) */
+  for (int32_t j = 0; j < T; ++j) {
+    const int32_t nj = len ? len[j] : k;
+    for (int32_t i = j * k; i < j * k + nj; ++i) {
+      int32_t a = find_sorted(U, nu, sel[i]);
+      sel_slot[i] = uslot[a];
+      hit_flag[i] = uhit[a];
+    }
   }
   counts[0] = n_hit;
   counts[1] = m;
@@ -227,16 +244,19 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, int32_t
   return OR_OK;
 }
 
-/* All units of one step (units are independent; OpenMP over units). */
+/* All units of one step (units are independent; OpenMP over units).  len is
+ * [units][T] or NULL. */
 void oracle_step(const oracle_cfg* c, int64_t units, int64_t t, const int32_t* sel,
-                 int32_t* slot_tok, int32_t* life, uint8_t* hit_flag, int32_t* sel_slot,
-                 int32_t* fill_slot, int32_t* fill_id, int32_t* counts, int32_t* status) {
+                 const int32_t* len, int32_t* slot_tok, int32_t* life, uint8_t* hit_flag,
+                 int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts,
+                 int32_t* status) {
   const int64_t tk = (int64_t)c->n_tokens * c->k, S = c->n_slots;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u)
-    status[u] = oracle_unit_step(c, t, sel + u * tk, slot_tok + u * S, life + u * S,
-                                 hit_flag + u * tk, sel_slot + u * tk, fill_slot + u * S,
-                                 fill_id + u * S, counts + u * 4);
+    status[u] = oracle_unit_step(c, t, sel + u * tk, len ? len + u * c->n_tokens : NULL,
+                                 slot_tok + u * S, life + u * S, hit_flag + u * tk,
+                                 sel_slot + u * tk, fill_slot + u * S, fill_id + u * S,
+                                 counts + u * 4);
 }
 
 /* Threads used by oracle_step's loop over units. */

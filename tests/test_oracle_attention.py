@@ -97,3 +97,29 @@ def test_one_dominant_key():
     sel = np.array([[[2, 5, 9, 20, 30, 31, 39]]], np.int32)
     out = oatt.attend(w, _bits(q), _bits(host), sel)
     np.testing.assert_allclose(out[0, 0, 0], 9.0, atol=1e-9)
+
+
+def test_lengths_attend_over_the_prefix_only():
+    """With per-list lengths, attention equals masked SDPA over the first len
+    entries; what follows them (here ids of other entries) plays no part."""
+    w = _tiny(T=1)
+    rng = np.random.default_rng(9)
+    host = _bits(rng.standard_normal((w.units, w.n_entries, w.row_elems)))
+    q = _bits(rng.standard_normal((w.batch, 1, w.n_q_heads, w.head_dim_qk)))
+    sel = np.stack([np.sort(rng.choice(w.n_entries, w.k, replace=False))[None]
+                    for _ in range(w.units)]).astype(np.int32)
+    lens = rng.integers(1, w.k + 1, size=(w.units, 1)).astype(np.int32)
+    got = oatt.attend(w, q, host, sel, lengths=lens)
+    hk = oatt.bf16_to_f64(host)
+    G = w.n_q_heads // w.n_kv_heads
+    for u in range(w.units):
+        b, g = divmod(u, w.n_kv_heads)
+        mask = torch.zeros(w.n_entries, dtype=torch.bool)
+        mask[torch.from_numpy(sel[u, 0, :lens[u, 0]].astype(np.int64))] = True
+        qq = torch.from_numpy(oatt.bf16_to_f64(q[b, 0, g * G:(g + 1) * G]))[None, :, None, :]
+        K = torch.from_numpy(hk[u, :, :w.head_dim_qk])[None, None]
+        V = torch.from_numpy(hk[u, :, w.head_dim_qk:])[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, K.expand(1, G, -1, -1), V.expand(1, G, -1, -1), attn_mask=mask[None, None, None, :],
+            scale=w.softmax_scale)[0, :, 0, :].numpy()
+        assert np.allclose(got[b, 0, g * G:(g + 1) * G], ref, rtol=1e-10, atol=1e-12)

@@ -291,3 +291,58 @@ def test_duplicate_outside_union_is_not_an_error():
     tok[4], life[4] = 9, 1
     st_, _ = oracle.unit_step(S, N, 2, "lifetime", 4, 64, 1, np.array([[1, 5]], np.int32), tok, life)
     assert st_ == oracle.OK
+
+
+@settings(max_examples=40, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(seed=st.integers(0, 2**31 - 1), S=st.integers(4, 32), N=st.integers(8, 256),
+       T=st.integers(1, 2), policy=st.sampled_from(["lifetime", "lru"]),
+       L=st.integers(1, 6), B=st.integers(1, 6))
+def test_oracle_variable_lengths_match_bruteforce(seed, S, N, T, policy, L, B):
+    """Lists shorter than k (PSA abstract: per-token budgets instead of one
+    fixed k): only the first len entries of each list count; the padding
+    after them (here ids out of range and out of order) is ignored and its
+    outputs stay slot -1, flag 0.  The brute-force replay sees only the
+    shortened lists."""
+    rng = np.random.default_rng(seed)
+    k = max(1, min(int(rng.integers(1, max(2, S // T) + 1)), S // T, N // 2))
+    trace = _random_trace(rng, S, N, k, T, 12, overlap=0.6)
+    tok = np.full(S, -1, np.int32)
+    life = np.full(S, -1 if policy == "lru" else 0, np.int32)
+    bb = BruteBuffer(S, N, L, B, policy)
+    for t, sel in enumerate(trace):
+        lens = rng.integers(1, k + 1, size=T).astype(np.int32)
+        padded = sel.copy()
+        for j in range(T):
+            padded[j, lens[j]:] = rng.integers(-5, N + 5, size=k - lens[j])
+            # a shortened list keeps its first len ids (ascending)
+        st_, r = oracle.unit_step(S, N, k, policy, L, B, t, padded, tok, life, lengths=lens)
+        assert st_ == oracle.OK
+        lists = [list(map(int, sel[j, :lens[j]])) for j in range(T)]
+        flags, slots, cnt = bb.step(lists)
+        for j in range(T):
+            assert r["hit_flag"][j, :lens[j]].astype(bool).tolist() == flags[j]
+            assert r["sel_slot"][j, :lens[j]].tolist() == slots[j]
+            assert (r["sel_slot"][j, lens[j]:] == -1).all() and (r["hit_flag"][j, lens[j]:] == 0).all()
+        assert (r["n_hit"], r["n_miss"], r["n_evict"], r["n_union"]) == \
+            (cnt["n_hit"], cnt["n_miss"], cnt["n_evict"], cnt["n_union"])
+        assert tok.tolist() == bb.tok
+        assert life.tolist() == bb.life_array()
+
+
+def test_oracle_length_out_of_range_is_an_error():
+    S, N, k = 16, 100, 5
+    sel = np.array([[3, 9, 20, 41, 77]], np.int32)
+    for bad in (0, -1, k + 1):
+        tok = np.full(S, -1, np.int32)
+        life = np.zeros(S, np.int32)
+        st_, r = oracle.unit_step(S, N, k, "lifetime", 4, 64, 0, sel, tok, life,
+                                  lengths=np.array([bad]))
+        assert st_ == oracle.ERR_RANGE
+        assert (tok == -1).all() and (r["sel_slot"] == -1).all()
+    # all k in use is the fixed-length step
+    tok_a, life_a = np.full(S, -1, np.int32), np.zeros(S, np.int32)
+    tok_b, life_b = np.full(S, -1, np.int32), np.zeros(S, np.int32)
+    _, ra = oracle.unit_step(S, N, k, "lifetime", 4, 64, 0, sel, tok_a, life_a)
+    _, rb = oracle.unit_step(S, N, k, "lifetime", 4, 64, 0, sel, tok_b, life_b,
+                             lengths=np.array([k]))
+    assert np.array_equal(tok_a, tok_b) and np.array_equal(ra["sel_slot"], rb["sel_slot"])
