@@ -31,7 +31,7 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
             "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
-            "avsg_rebuild_index"]
+            "avsg_rebuild_index", "avsg_step_varlen"]
 
 
 class AvsgError(RuntimeError):
@@ -77,6 +77,7 @@ def load():
         "avsg_destroy": ([p], i32),
         "avsg_reset": ([p, p, p], i32),
         "avsg_step": ([p] * 8 + [ctypes.POINTER(avsg_hit_stats)], i32),
+        "avsg_step_varlen": ([p] * 9 + [ctypes.POINTER(avsg_hit_stats)], i32),
         "avsg_last_error": ([p], i32),
         "avsg_append": ([p] * 6, i32),
         "avsg_validate_state": ([p, p, p], i32),
@@ -136,6 +137,12 @@ def avsg_step(ctx: int, sel_idx: int, q: int, host_kv: int, buf_kv: int, slot_ta
               lifetimes: int, out: int, hit_stats: avsg_hit_stats) -> int:
     return load().avsg_step(ctx, sel_idx, q, host_kv, buf_kv, slot_table, lifetimes, out,
                             ctypes.byref(hit_stats))
+
+
+def avsg_step_varlen(ctx: int, sel_idx: int, sel_len: int, q: int, host_kv: int, buf_kv: int,
+                     slot_table: int, lifetimes: int, out: int, hit_stats: avsg_hit_stats) -> int:
+    return load().avsg_step_varlen(ctx, sel_idx, sel_len, q, host_kv, buf_kv, slot_table,
+                                   lifetimes, out, ctypes.byref(hit_stats))
 
 
 def avsg_append(ctx: int, new_kv: int, pos: int, host_kv: int, buf_kv: int,
@@ -303,13 +310,21 @@ class Context:
         if st != OK:
             raise AvsgError(st, "avsg_reset")
 
-    def step(self, sel_idx, q, host_kv, buf_kv, slot_table, lifetimes, out, stats: HitStats):
-        """host_kv: a HostBuffer or an integer address of pinned host memory."""
+    def step(self, sel_idx, q, host_kv, buf_kv, slot_table, lifetimes, out, stats: HitStats,
+             sel_len=None):
+        """host_kv: a HostBuffer or an integer address of pinned host memory;
+        sel_len: optional device int32 [units] list lengths (avsg_step_varlen)."""
         hptr = host_kv.ptr if isinstance(host_kv, HostBuffer) else int(host_kv)
-        st = avsg_step(self.handle, sel_idx.data_ptr(), q.data_ptr(), hptr, buf_kv.data_ptr(),
-                       slot_table.data_ptr(), lifetimes.data_ptr(), out.data_ptr(), stats.struct())
+        if sel_len is None:
+            st = avsg_step(self.handle, sel_idx.data_ptr(), q.data_ptr(), hptr, buf_kv.data_ptr(),
+                           slot_table.data_ptr(), lifetimes.data_ptr(), out.data_ptr(),
+                           stats.struct())
+        else:
+            st = avsg_step_varlen(self.handle, sel_idx.data_ptr(), sel_len.data_ptr(), q.data_ptr(),
+                                  hptr, buf_kv.data_ptr(), slot_table.data_ptr(),
+                                  lifetimes.data_ptr(), out.data_ptr(), stats.struct())
         if st != OK:
-            raise AvsgError(st, "avsg_step")
+            raise AvsgError(st, "avsg_step_varlen" if sel_len is not None else "avsg_step")
 
     def append(self, new_kv, pos, host_kv, buf_kv, slot_table):
         """Offload of the new token: new_kv [batch][Hkv][tok_elems] (bf16 bits

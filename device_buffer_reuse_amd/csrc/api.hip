@@ -353,12 +353,15 @@ static avsg_status device_view_of_pinned(avsg_ctx* ctx, const void* host, const 
   return AVSG_OK;
 }
 
-avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
-                      const uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
-                      int32_t* lifetimes, float* out, const avsg_hit_stats* hs) {
+static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_t* sel_len,
+                             const uint16_t* q, const uint16_t* host_kv, uint16_t* buf_kv,
+                             int32_t* slot_table, int32_t* lifetimes, float* out,
+                             const avsg_hit_stats* hs) {
   if (!ctx || !sel_idx || !q || !host_kv || !buf_kv || !slot_table || !lifetimes || !out || !hs ||
       !hs->hit_flag || !hs->sel_slot || !hs->n_hit || !hs->n_miss || !hs->n_evict)
     return AVSG_ERR_INVALID_ARG;
+  // lengths apply to single-token iterations (a two-token union assumes k each)
+  if (sel_len && ctx->cfg.n_q_tokens != 1) return AVSG_ERR_UNSUPPORTED;
   // the kernels move rows, queries and outputs in 16-byte pieces
   if (((uintptr_t)q | (uintptr_t)host_kv | (uintptr_t)buf_kv | (uintptr_t)out) & 15)
     return AVSG_ERR_INVALID_ARG;
@@ -373,6 +376,7 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
 
   MatchReserveParams mp;
   mp.sel = sel_idx;
+  mp.sel_len = sel_len;
   mp.slot_table = slot_table;
   mp.lifetimes = lifetimes;
   mp.hit_flag = hs->hit_flag;
@@ -429,6 +433,7 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
 
   AttnParams ap;
   ap.sel_slot = hs->sel_slot;
+  ap.sel_len = sel_len;
   ap.sel = sel_idx;
   ap.fetch = fused ? (const uint8_t*)(ws + ctx->ws.fetch) : nullptr;
   ap.host_kv = (const uint16_t*)host_dev;
@@ -464,6 +469,20 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
   if (ctx->prof_events && ctx->prof_used < ctx->prof_max) ctx->prof_used += 1;
   ctx->t += 1;
   return AVSG_OK;
+}
+
+avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
+                      const uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
+                      int32_t* lifetimes, float* out, const avsg_hit_stats* hs) {
+  return step_impl(ctx, sel_idx, nullptr, q, host_kv, buf_kv, slot_table, lifetimes, out, hs);
+}
+
+avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_t* sel_len,
+                             const uint16_t* q, const uint16_t* host_kv, uint16_t* buf_kv,
+                             int32_t* slot_table, int32_t* lifetimes, float* out,
+                             const avsg_hit_stats* hs) {
+  if (!sel_len) return AVSG_ERR_INVALID_ARG;
+  return step_impl(ctx, sel_idx, sel_len, q, host_kv, buf_kv, slot_table, lifetimes, out, hs);
 }
 
 static avsg_status status_from_bits(uint32_t bits) {

@@ -33,6 +33,9 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
     return;
   }
   const int nsplit = NS > 0 ? NS : p.nsplit;
+  // splits holding rows: all of them, or those covering a shortened list
+  const int len = p.sel_len ? min(max(p.sel_len[u], 1), p.k) : p.k;
+  const int nused = min(nsplit, (len * p.tpe + p.split_rows - 1) / p.split_rows);
   const size_t ps = partial_stride(G, D);  // floats per split partial, multiple of 4
   const float* pbase = p.partials + (size_t)uj * nsplit * ps;
   const float* mrow = pbase + (size_t)G * D + h;
@@ -41,11 +44,13 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
   if constexpr (NS > 0) {
     float m[NS], l[NS];
     float4 o[NS];
+    // unused splits reload the last used one and weigh 0
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      m[s] = mrow[s * ps];
-      l[s] = lrow[s * ps];
-      o[s] = orow_s[s * (ps / 4)];
+      const int sl = min(s, nused - 1);
+      m[s] = mrow[sl * ps];
+      l[s] = lrow[sl * ps];
+      o[s] = orow_s[sl * (ps / 4)];
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -54,7 +59,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const float wgt = __builtin_amdgcn_exp2f(m[s] - mx);
+      const float wgt = s < nused ? __builtin_amdgcn_exp2f(m[s] - mx) : 0.f;
       lsum = fmaf(l[s], wgt, lsum);
       acc.x = fmaf(o[s].x, wgt, acc.x);
       acc.y = fmaf(o[s].y, wgt, acc.y);
@@ -65,10 +70,10 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
     *orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   } else {
     float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, mrow[s * ps]);
+    for (int s = 0; s < nused; ++s) mx = fmaxf(mx, mrow[s * ps]);
     float lsum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = 0; s < nused; ++s) {
       const float wgt = __builtin_amdgcn_exp2f(mrow[s * ps] - mx);
       lsum = fmaf(lrow[s * ps], wgt, lsum);
       const float4 o = orow_s[s * (ps / 4)];

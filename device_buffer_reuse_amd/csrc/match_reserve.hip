@@ -176,7 +176,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const int u = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S, N = p.N, T = p.T, k = p.k, ucap = p.ucap, C = p.table_cap;
-  const int nbins = p.nbins, tk = T * k;
+  // tks: stride of a unit's lists; tk: entries in use (one token with a
+  // length array: its first sel_len[u] entries, a length outside [1, k]
+  // being a range error)
+  const int tks = T * k;
+  const int len_in = (T == 1 && p.sel_len) ? p.sel_len[u] : k;
+  const bool len_bad = len_in < 1 || len_in > k;
+  const int nbins = p.nbins, tk = T == 1 ? (len_bad ? 1 : len_in) : tks;
   const bool lru = p.policy == AVSG_POLICY_BUCKET_LRU;
 
   int32_t* sHash = lds;                      // [C] packed (id, union index) or -1
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   int32_t* sBase = sHash + dw;                            // [dw]
   uint32_t* sBitsA = sBits + 2 * dw;                      // [dw] two tokens: token 0's ids
 
-  const int32_t* sel = p.sel + (size_t)u * tk;
+  const int32_t* sel = p.sel + (size_t)u * tks;
   int32_t* slot_table = p.slot_table + (size_t)u * S;
   int32_t* lifetimes = p.lifetimes + (size_t)u * S;
 
@@ -310,6 +316,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       bad |= (live && !in_range) ? kFlagRange : 0;
       bad |= (live && i != 0 && i != k && x <= prv[r]) ? kFlagUnsorted : 0;
     }
+    if (len_bad && tid == 0) bad |= kFlagRange;
     for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) {
       const int32_t x = stage[i];
       const bool in_range = x >= 0 && x < N;
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 
   // ---- 2. union U of the two lists (T = 2): position of each element =
   //         elements below it in both lists minus duplicates below it
-  int nu = k;
+  int nu = T == 1 ? tk : k;
   if (T > 1 && sMisc[0] == 0 && dw > 0) {
     // direct addressing: U's membership words are the two lists' words or'ed;
     // a block scan of their popcounts gives each word's rank base, the set
@@ -649,10 +656,10 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const int flags = sMisc[0];
   if (flags) {
     const int code = flags_to_status(flags);
-    for (int i = tid; i < tk; i += kMRThreads) {
-      p.sel_slot[(size_t)u * tk + i] = -1;
-      p.hit_flag[(size_t)u * tk + i] = 0;
-      p.fetch[(size_t)u * tk + i] = 0;
+    for (int i = tid; i < tks; i += kMRThreads) {
+      p.sel_slot[(size_t)u * tks + i] = -1;
+      p.hit_flag[(size_t)u * tks + i] = 0;
+      p.fetch[(size_t)u * tks + i] = 0;
     }
     if (tid == 0) {
       p.n_hit[u] = 0;
@@ -885,10 +892,16 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     const int mi = (T == 1) ? i : sMap[i];
     const int v = sUslot[mi & ~kDupFlag];
     const bool miss = (v & kMissFlag) != 0;
-    p.sel_slot[(size_t)u * tk + i] = v & ~kMissFlag;
-    p.hit_flag[(size_t)u * tk + i] = miss ? 0 : 1;
+    p.sel_slot[(size_t)u * tks + i] = v & ~kMissFlag;
+    p.hit_flag[(size_t)u * tks + i] = miss ? 0 : 1;
     // the row is transferred by the first token that selects it
-    p.fetch[(size_t)u * tk + i] = (miss && !(mi & kDupFlag)) ? 1 : 0;
+    p.fetch[(size_t)u * tks + i] = (miss && !(mi & kDupFlag)) ? 1 : 0;
+  }
+  // entries past a shortened list: no slot, no transfer
+  for (int i = tk + tid; i < tks; i += kMRThreads) {
+    p.sel_slot[(size_t)u * tks + i] = -1;
+    p.hit_flag[(size_t)u * tks + i] = 0;
+    p.fetch[(size_t)u * tks + i] = 0;
   }
   // ---- 9. write the new slot state back (registers only, after the
   //         outputs so that the stores overlap them)

@@ -61,16 +61,21 @@ class Runner:
         self.ob = oracle.OracleBuffer.for_workload(w, track_buf=track_buf)
         self.attn_units = attn_units
 
-    def gpu_step(self, sel_t, q_t):
+    def gpu_step(self, sel_t, q_t, lengths=None):
         torch = self.torch
+        ln = None if lengths is None else torch.from_numpy(
+            np.ascontiguousarray(lengths, dtype=np.int32).reshape(-1)).cuda()
         self.ctx.step(torch.from_numpy(np.ascontiguousarray(sel_t)).cuda(),
                       torch.from_numpy(q_t.view(np.int16)).cuda(), self.host, self.st.buf_kv,
-                      self.st.slot_table, self.st.lifetimes, self.st.out, self.st.stats)
+                      self.st.slot_table, self.st.lifetimes, self.st.out, self.st.stats,
+                      sel_len=ln)
 
-    def step_and_compare(self, t, sel_t, q_t, check_attn=True, check_buf=False):
-        self.gpu_step(sel_t, q_t)
+    def step_and_compare(self, t, sel_t, q_t, check_attn=True, check_buf=False, lengths=None):
+        """lengths: optional [units] list lengths (one query token)."""
+        self.gpu_step(sel_t, q_t, lengths)
         self.torch.cuda.synchronize()
-        r = self.ob.step(sel_t, self.host.array if self.ob.track_buf else None)
+        ln = None if lengths is None else np.asarray(lengths, np.int32).reshape(-1, 1)
+        r = self.ob.step(sel_t, self.host.array if self.ob.track_buf else None, lengths=ln)
         s = self.st
         assert np.array_equal(s.slot_table.cpu().numpy(), self.ob.slot_tok), "slot_table t=%d" % t
         assert np.array_equal(s.lifetimes.cpu().numpy(), self.ob.life), "lifetimes t=%d" % t
@@ -84,7 +89,8 @@ class Runner:
             assert np.array_equal(s.buf_kv.cpu().numpy().view(np.uint16), self.ob.buf), "buf t=%d" % t
         err = None
         if check_attn:
-            ref = oatt.attend(self.w, q_t, self.host.array, sel_t, r["status"], units=self.attn_units)
+            ref = oatt.attend(self.w, q_t, self.host.array, sel_t, r["status"], units=self.attn_units,
+                              lengths=ln)
             err = check_attention(s.out.cpu().numpy(), ref, "out t=%d" % t)
         return r, err
 

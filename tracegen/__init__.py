@@ -185,6 +185,28 @@ def selections(w: Workload, steps: int | None = None, mode: str = "natural") -> 
     return out
 
 
+def shorten(sel: np.ndarray, seed: int, lo: int, hi: int | None = None,
+            pad: int = -1) -> tuple[np.ndarray, np.ndarray]:
+    """Variable-size selections from fixed-size ones (one query token): for
+    every (step, unit) a length drawn uniformly from [lo, hi] (hi defaults to
+    k), and that many of the k entries, chosen uniformly (numpy generator
+    seeded with `seed`), kept in ascending order at the front of the list;
+    the positions after them hold `pad`.  Returns (lists [steps][units][1][k],
+    lengths [steps][units])."""
+    steps, units, T, k = sel.shape
+    assert T == 1
+    hi = k if hi is None else hi
+    rng = np.random.default_rng(seed)
+    out = np.full_like(sel, pad)
+    lens = rng.integers(lo, hi + 1, size=(steps, units)).astype(np.int32)
+    for t in range(steps):
+        for u in range(units):
+            n = int(lens[t, u])
+            keep = np.sort(rng.choice(k, size=n, replace=False))
+            out[t, u, 0, :n] = sel[t, u, 0, keep]
+    return out, lens
+
+
 def permutation(w: Workload, unit: int) -> np.ndarray:
     out = np.empty(w.n_entries, dtype=np.int32)
     _load().tg_permutation(w.seed, unit, w.n_entries, _ptr(out))
