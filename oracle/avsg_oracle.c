@@ -93,6 +93,12 @@ static int32_t find_sorted(const int32_t* a, int32_t n, int32_t x) {
  *   len        [T]     entries of each token's list in use (its first len[j]
  *                      ids; the rest is ignored), or NULL for k each.  A
  *                      length outside [1, k] is a range error.
+ *   cap                slots this unit may use, [0, cap) (Spin summary,
+ *                      section 2B: the buffer of each request is sized
+ *                      dynamically); slots at or past cap are emptied before
+ *                      the step (a shrink drops what they held).  A cap
+ *                      outside [1, S] is a range error; |U| > cap is a
+ *                      capacity error.
  *   slot_tok   [S]     in/out: id held by each slot, -1 = empty
  *   life       [S]     in/out: lifetime (lifetime policy) or last-selected
  *                      step (LRU policy; -1 for a slot never filled)
@@ -103,9 +109,11 @@ static int32_t find_sorted(const int32_t* a, int32_t n, int32_t x) {
  * Returns a status; on error the state is unchanged, flags are 0, slots -1.
  */
 int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const int32_t* len,
-                     int32_t* slot_tok, int32_t* life, uint8_t* hit_flag, int32_t* sel_slot,
-                     int32_t* fill_slot, int32_t* fill_id, int32_t* counts) {
-  const int32_t S = c->n_slots, N = c->n_entries, T = c->n_tokens, k = c->k;
+                     int32_t cap, int32_t* slot_tok, int32_t* life, uint8_t* hit_flag,
+                     int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts) {
+  const int32_t S_all = c->n_slots, N = c->n_entries, T = c->n_tokens, k = c->k;
+  /* the slots in use: [0, S) */
+  const int32_t S = cap;
   const int32_t L = c->lifetime_L, B = c->n_buckets;
   const int32_t tk = T * k;
   int status = OR_OK;
@@ -125,6 +133,7 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
     }
     n_used += nj;
   }
+  if (cap < 1 || cap > S_all) range_bad = 1;
   if (range_bad) return OR_ERR_RANGE;
   if (order_bad) return OR_ERR_UNSORTED;
   int32_t* U = (int32_t*)malloc(sizeof(int32_t) * (size_t)(tk > 0 ? tk : 1));
@@ -150,6 +159,12 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
     }
   }
   if (status != OR_OK) { free(U); return status; }
+
+  /* slots past the capacity are emptied */
+  for (int32_t s = S; s < S_all; ++s) {
+    slot_tok[s] = -1;
+    life[s] = c->policy == OR_LRU ? -1 : 0;
+  }
 
   /* 2. match U against the resident ids: two-pointer merge of two sorted lists */
   resident_t* R = (resident_t*)malloc(sizeof(resident_t) * (size_t)S);
@@ -245,15 +260,16 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
 }
 
 /* All units of one step (units are independent; OpenMP over units).  len is
- * [units][T] or NULL. */
+ * [units][T] or NULL, cap [units] or NULL (every unit uses all S slots). */
 void oracle_step(const oracle_cfg* c, int64_t units, int64_t t, const int32_t* sel,
-                 const int32_t* len, int32_t* slot_tok, int32_t* life, uint8_t* hit_flag,
-                 int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts,
-                 int32_t* status) {
+                 const int32_t* len, const int32_t* cap, int32_t* slot_tok, int32_t* life,
+                 uint8_t* hit_flag, int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id,
+                 int32_t* counts, int32_t* status) {
   const int64_t tk = (int64_t)c->n_tokens * c->k, S = c->n_slots;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u)
     status[u] = oracle_unit_step(c, t, sel + u * tk, len ? len + u * c->n_tokens : NULL,
+                                 cap ? cap[u] : c->n_slots,
                                  slot_tok + u * S, life + u * S, hit_flag + u * tk,
                                  sel_slot + u * tk, fill_slot + u * S, fill_id + u * S,
                                  counts + u * 4);

@@ -346,3 +346,70 @@ def test_oracle_length_out_of_range_is_an_error():
     _, rb = oracle.unit_step(S, N, k, "lifetime", 4, 64, 0, sel, tok_b, life_b,
                              lengths=np.array([k]))
     assert np.array_equal(tok_a, tok_b) and np.array_equal(ra["sel_slot"], rb["sel_slot"])
+
+
+@settings(max_examples=40, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(seed=st.integers(0, 2**31 - 1), S=st.integers(6, 32), N=st.integers(16, 256),
+       policy=st.sampled_from(["lifetime", "lru"]), L=st.integers(1, 6), B=st.integers(1, 6))
+def test_oracle_capacity_matches_bruteforce(seed, S, N, policy, L, B):
+    """Per-unit capacity (Spin summary, section 2B: buffer elasticity): with
+    capacity c the unit behaves as a buffer of c slots, slots past c stay
+    empty, and a shrink empties the slots it removes before the step.  The
+    brute-force replay runs on the first c slots, its tail emptied by hand."""
+    rng = np.random.default_rng(seed)
+    k = max(1, min(int(rng.integers(1, S // 2 + 1)), N // 2))
+    trace = _random_trace(rng, S, N, k, 1, 14, overlap=0.6)
+    tok = np.full(S, -1, np.int32)
+    reset = -1 if policy == "lru" else 0
+    life = np.full(S, reset, np.int32)
+    bb = BruteBuffer(S, N, L, B, policy)
+    for t, sel in enumerate(trace):
+        cap = int(rng.integers(k, S + 1))
+        for s in range(cap, S):
+            bb.tok[s], bb.last[s] = -1, None
+        bb.S = cap
+        st_, r = oracle.unit_step(S, N, k, policy, L, B, t, sel, tok, life, cap=cap)
+        assert st_ == oracle.OK
+        flags, slots, cnt = bb.step([list(map(int, l)) for l in sel])
+        assert r["hit_flag"].astype(bool).tolist() == flags
+        assert r["sel_slot"].tolist() == slots
+        assert (r["n_hit"], r["n_miss"], r["n_evict"]) == (cnt["n_hit"], cnt["n_miss"], cnt["n_evict"])
+        assert tok[:cap].tolist() == bb.tok[:cap] and (tok[cap:] == -1).all()
+        assert life[:cap].tolist() == bb.life_array() and (life[cap:] == reset).all()
+
+
+def test_oracle_capacity_errors_change_nothing():
+    S, N, k = 12, 100, 5
+    sel = np.array([3, 9, 20, 41, 77], np.int32)
+    tok = np.full(S, -1, np.int32)
+    life = np.zeros(S, np.int32)
+    oracle.unit_step(S, N, k, "lifetime", 4, 64, 0, sel, tok, life)
+    before = (tok.copy(), life.copy())
+    for cap, want in ((0, oracle.ERR_RANGE), (-1, oracle.ERR_RANGE), (S + 1, oracle.ERR_RANGE),
+                      (4, oracle.ERR_CAPACITY)):
+        st_, _ = oracle.unit_step(S, N, k, "lifetime", 4, 64, 1, sel, tok, life, cap=cap)
+        assert st_ == want
+        assert np.array_equal(tok, before[0]) and np.array_equal(life, before[1])
+    # a constant capacity equal to S is the unsized step
+    st_, r = oracle.unit_step(S, N, k, "lifetime", 4, 64, 1, sel, tok, life, cap=S)
+    assert st_ == oracle.OK and r["n_hit"] == k
+
+
+def test_plan_capacity_worked_example_and_invariants():
+    from oracle.plan import plan_capacity
+    # spare 6 shared 1 : 3 -> floor(6/4) = 1 and floor(18/4) = 4
+    assert plan_capacity([2, 3], [0, 2], 11, 8).tolist() == [3, 7]
+    # capped at S, and the plan that does not fit
+    assert plan_capacity([2, 3], [0, 100], 40, 8).tolist() == [2, 8]
+    assert plan_capacity([5, 6], [1, 1], 10, 8) is None
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        n, S = int(rng.integers(1, 10)), int(rng.integers(1, 50))
+        d = rng.integers(1, S + 1, n)
+        r = rng.integers(0, 30, n)
+        b = int(rng.integers(0, 2 * n * S))
+        cap = plan_capacity(d, r, b, S)
+        if d.sum() > b:
+            assert cap is None
+            continue
+        assert (cap >= d).all() and (cap <= S).all() and cap.sum() <= b
