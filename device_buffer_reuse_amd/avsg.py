@@ -31,7 +31,8 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
             "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
-            "avsg_rebuild_index", "avsg_step_varlen"]
+            "avsg_rebuild_index", "avsg_step_varlen", "avsg_set_capacity",
+            "avsg_plan_capacity"]
 
 
 class AvsgError(RuntimeError):
@@ -82,6 +83,8 @@ def load():
         "avsg_append": ([p] * 6, i32),
         "avsg_validate_state": ([p, p, p], i32),
         "avsg_rebuild_index": ([p, p], i32),
+        "avsg_set_capacity": ([p, p], i32),
+        "avsg_plan_capacity": ([ctypes.c_int32, p, p, i64, ctypes.c_int32, p], i32),
         "avsg_get_step": ([p], i64),
         "avsg_set_step": ([p, i64], i32),
         "avsg_host_alloc": ([sz, ctypes.c_uint, ctypes.POINTER(p)], i32),
@@ -160,6 +163,20 @@ def avsg_validate_state(ctx: int, slot_table: int, lifetimes: int) -> int:
 
 def avsg_rebuild_index(ctx: int, slot_table: int) -> int:
     return load().avsg_rebuild_index(ctx, slot_table)
+
+
+def avsg_set_capacity(ctx: int, cap: int | None) -> int:
+    return load().avsg_set_capacity(ctx, cap)
+
+
+def avsg_plan_capacity(demand: np.ndarray, reuse: np.ndarray, budget: int, n_slots: int):
+    """Returns (status, cap int32 array)."""
+    demand = np.ascontiguousarray(demand, dtype=np.int32)
+    reuse = np.ascontiguousarray(reuse, dtype=np.int32)
+    cap = np.zeros(demand.shape[0], dtype=np.int32)
+    st = load().avsg_plan_capacity(int(demand.shape[0]), demand.ctypes.data, reuse.ctypes.data,
+                                   int(budget), int(n_slots), cap.ctypes.data)
+    return st, cap
 
 
 def avsg_get_step(ctx: int) -> int:
@@ -340,6 +357,13 @@ class Context:
 
     def validate_state(self, slot_table, lifetimes) -> int:
         return avsg_validate_state(self.handle, slot_table.data_ptr(), lifetimes.data_ptr())
+
+    def set_capacity(self, cap):
+        """cap: device int32 tensor [units] (kept alive by the caller), or None."""
+        self._cap = cap
+        st = avsg_set_capacity(self.handle, None if cap is None else cap.data_ptr())
+        if st != OK:
+            raise AvsgError(st, "avsg_set_capacity")
 
     def rebuild_index(self, slot_table) -> int:
         return avsg_rebuild_index(self.handle, slot_table.data_ptr())

@@ -21,6 +21,7 @@ struct avsg_ctx {
   const void* pinned_device;     // its device-visible address
   int32_t transfer_mode;         // avsg_transfer_mode
   int32_t match_mode;            // avsg_match_mode
+  const int32_t* cap;            // device [units] buffer size of each unit, or null (S)
   int lds_max;
   hipEvent_t* prof_events;       // kProfMarks per profiled step, or null
   int32_t prof_max, prof_used;
@@ -224,6 +225,7 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->t = 0;
   c->pinned_checked = nullptr;
   c->pinned_device = nullptr;
+  c->cap = nullptr;
   c->prof_events = nullptr;
   c->prof_max = c->prof_used = 0;
   c->transfer_mode = AVSG_TRANSFER_FUSED;
@@ -377,6 +379,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   MatchReserveParams mp;
   mp.sel = sel_idx;
   mp.sel_len = sel_len;
+  mp.cap = ctx->cap;
   mp.slot_table = slot_table;
   mp.lifetimes = lifetimes;
   mp.hit_flag = hs->hit_flag;
@@ -529,6 +532,31 @@ avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const 
   if (!ctx || !slot_table || !lifetimes) return AVSG_ERR_INVALID_ARG;
   return check_state(ctx, slot_table, lifetimes);
 }
+avsg_status avsg_set_capacity(avsg_ctx* ctx, const int32_t* cap) {
+  if (!ctx) return AVSG_ERR_INVALID_ARG;
+  ctx->cap = cap;
+  return AVSG_OK;
+}
+
+avsg_status avsg_plan_capacity(int32_t units, const int32_t* demand, const int32_t* reuse,
+                               int64_t budget, int32_t n_slots, int32_t* cap) {
+  if (units < 1 || !demand || !reuse || !cap || n_slots < 1) return AVSG_ERR_INVALID_ARG;
+  int64_t mandatory = 0, weights = 0;
+  for (int32_t u = 0; u < units; ++u) {
+    if (demand[u] < 1 || demand[u] > n_slots || reuse[u] < 0) return AVSG_ERR_INVALID_ARG;
+    mandatory += demand[u];
+    weights += (int64_t)reuse[u] + 1;
+  }
+  if (mandatory > budget) return AVSG_ERR_CAPACITY;
+  const __int128 spare = budget - mandatory;
+  for (int32_t u = 0; u < units; ++u) {
+    const __int128 extra = spare * ((int64_t)reuse[u] + 1) / weights;
+    const __int128 c = (__int128)demand[u] + extra;
+    cap[u] = c < (__int128)n_slots ? (int32_t)c : n_slots;
+  }
+  return AVSG_OK;
+}
+
 avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
                         uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table) {
   if (!ctx || !new_kv || !pos || !host_kv || !buf_kv || !slot_table) return AVSG_ERR_INVALID_ARG;

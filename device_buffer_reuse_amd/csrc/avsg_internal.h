@@ -44,6 +44,7 @@ inline __host__ __device__ size_t partial_stride(int G, int D) {
 struct MatchReserveParams {
   const int32_t* sel;     // [units][T][k]
   const int32_t* sel_len; // [units] entries in use of each unit's list (T = 1), or null: k
+  const int32_t* cap;     // [units] slots in use of each unit's buffer, or null: S
   int32_t* slot_table;    // [units][S]
   int32_t* lifetimes;     // [units][S]
   uint8_t* hit_flag;      // [units][T][k]

@@ -182,6 +182,11 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const int tks = T * k;
   const int len_in = (T == 1 && p.sel_len) ? p.sel_len[u] : k;
   const bool len_bad = len_in < 1 || len_in > k;
+  // slots in use: [0, cap) (the unit's buffer size; slots past it are
+  // emptied by this step); a capacity outside [1, S] is a range error
+  const int cap_in = p.cap ? p.cap[u] : S;
+  const bool cap_bad = cap_in < 1 || cap_in > S;
+  const int cap = cap_bad ? S : cap_in;
   const int nbins = p.nbins, tk = T == 1 ? (len_bad ? 1 : len_in) : tks;
   const bool lru = p.policy == AVSG_POLICY_BUCKET_LRU;
 
@@ -316,7 +321,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       bad |= (live && !in_range) ? kFlagRange : 0;
       bad |= (live && i != 0 && i != k && x <= prv[r]) ? kFlagUnsorted : 0;
     }
-    if (len_bad && tid == 0) bad |= kFlagRange;
+    if ((len_bad || cap_bad) && tid == 0) bad |= kFlagRange;
+    // one token: U is the list itself
+    if (T == 1 && tk > cap && tid == 0) bad |= kFlagCapacity;
     for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) {
       const int32_t x = stage[i];
       const bool in_range = x >= 0 && x < N;
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       __syncthreads();  // sWs is reused; sBits and sBase are complete
     }
     nu = run;
-    if (nu > S) {
+    if (nu > cap) {
       if (tid == 0) sMisc[0] = kFlagCapacity;
     } else {
       for (int i = tid; i < tk; i += kMRThreads) {
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     if (tid == 0) sDup[k] = run;
     __syncthreads();
     nu = 2 * k - sDup[k];
-    if (nu > S) {
+    if (nu > cap) {
       if (tid == 0) sMisc[0] = kFlagCapacity;
     } else {
       for (int i = tid; i < k; i += kMRThreads) {
@@ -437,9 +444,16 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   }
 
   // ---- 4. every slot probes its resident id; state checks
+  // slots at or past the capacity that hold something are emptied at the
+  // end of the step (bit q); they take no part in it
+  const int32_t life_empty = lru ? -1 : 0;
+  uint32_t drop = 0;
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) {
-    if (!(q * 64 < R && s0 + q * 64 + lane < s1)) {
+    const int s = s0 + q * 64 + lane;
+    const bool in_buf = q * 64 < R && s < s1;
+    if (in_buf && s >= cap && (tok[q] != -1 || lf[q] != life_empty)) drop |= 1u << q;
+    if (!(in_buf && s < cap)) {
       tok[q] = kInvalid;
       lf[q] = 0;
     }
@@ -471,7 +485,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         (reinterpret_cast<uintptr_t>(sDup + (T > 1 ? k + 1 : 0)) + 7) & ~(uintptr_t)7);
     int32_t* sSlotU = reinterpret_cast<int32_t*>(sPair + P2);              // [S]
     for (int i = tid; i < P2; i += kMRThreads) {
-      const int32_t x = i < S ? slot_table[i] : -1;
+      const int32_t x = i < cap ? slot_table[i] : -1;
       sPair[i] = make_int2((x >= 0 && x < N) ? x : INT_MAX, i);
     }
     for (int i = tid; i < S; i += kMRThreads) sSlotU[i] = -1;
@@ -907,8 +921,14 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   //         outputs so that the stores overlap them)
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) {
-    if (tok[q] == kInvalid) continue;
     const int s = s0 + q * 64 + lane;
+    if (tok[q] == kInvalid) {
+      if ((drop >> q) & 1) {
+        slot_table[s] = -1;
+        lifetimes[s] = life_empty;
+      }
+      continue;
+    }
     lifetimes[s] = lf[q];
     if (changed[q]) slot_table[s] = tok[q];
   }

@@ -176,6 +176,32 @@ avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
                              int32_t* slot_table, int32_t* lifetimes, float* out,
                              const avsg_hit_stats* hit_stats);
 
+/* Buffer size per unit (Spin summary, section 2B, buffer elasticity: each
+ * request's device buffer is sized dynamically, mandatory pages for the
+ * current step plus buffer pages kept for locality).  `cap` is a device
+ * int32 array [batch][n_kv_heads] read by every later step when it runs
+ * (update its contents between steps, stream-ordered), or NULL for S slots
+ * each.  A step lets unit u use slots [0, cap[u]) only and empties the slots
+ * at or past cap[u] (slot -1, lifetime 0 or stamp -1): shrinking a unit's
+ * buffer drops the entries it held there, which stay exact in host memory.
+ * cap[u] outside [1, S] is a range error and |U| > cap[u] a capacity error
+ * of that unit (its state then stays untouched, as for every data error).
+ * The pointer is kept by the context; the caller owns the array. */
+avsg_status avsg_set_capacity(avsg_ctx* ctx, const int32_t* cap);
+
+/* The capacity planner (host arrays, host only): gives each of `units`
+ * units its mandatory slots demand[u] (the size of its next union, in
+ * [1, n_slots]) and shares the rest of a slot budget over all units in
+ * proportion to reuse[u] + 1 (reuse: the unit's recent hits, >= 0), rounded
+ * down: cap[u] = min(n_slots, demand[u] + floor(spare * (reuse[u] + 1) /
+ * sum(reuse + 1))), spare = budget - sum(demand).  The pages give no
+ * formula; this is the plain reading of "mandatory plus buffer pages, with
+ * throughput per request weighed against contention".  Returns
+ * AVSG_ERR_CAPACITY if the mandatory slots exceed the budget (admit fewer
+ * requests), AVSG_ERR_INVALID_ARG for null pointers or values out of range. */
+avsg_status avsg_plan_capacity(int32_t units, const int32_t* demand, const int32_t* reuse,
+                               int64_t budget, int32_t n_slots, int32_t* cap);
+
 /* Offload of the newly decoded token (Spin summary, section 2A: Offload,
  * placing KV data into memory, is a system-managed operation over a
  * page-based KV substrate; section 2B: physical pages per attention head).

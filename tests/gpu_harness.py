@@ -70,12 +70,19 @@ class Runner:
                       self.st.slot_table, self.st.lifetimes, self.st.out, self.st.stats,
                       sel_len=ln)
 
+    def set_caps(self, caps):
+        """Per-unit buffer sizes for the following steps (None: all slots)."""
+        self.caps = None if caps is None else np.asarray(caps, np.int32).copy()
+        self.cap_dev = None if caps is None else self.torch.from_numpy(self.caps).cuda()
+        self.ctx.set_capacity(self.cap_dev)
+
     def step_and_compare(self, t, sel_t, q_t, check_attn=True, check_buf=False, lengths=None):
         """lengths: optional [units] list lengths (one query token)."""
         self.gpu_step(sel_t, q_t, lengths)
         self.torch.cuda.synchronize()
         ln = None if lengths is None else np.asarray(lengths, np.int32).reshape(-1, 1)
-        r = self.ob.step(sel_t, self.host.array if self.ob.track_buf else None, lengths=ln)
+        r = self.ob.step(sel_t, self.host.array if self.ob.track_buf else None, lengths=ln,
+                         caps=getattr(self, "caps", None))
         s = self.st
         assert np.array_equal(s.slot_table.cpu().numpy(), self.ob.slot_tok), "slot_table t=%d" % t
         assert np.array_equal(s.lifetimes.cpu().numpy(), self.ob.life), "lifetimes t=%d" % t

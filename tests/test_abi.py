@@ -75,3 +75,31 @@ def test_workspace_sizes_match_layout():
     partials = 4 * w.units * splits * 4 * 130
     fetch = w.units * w.n_q_tokens * w.k
     assert misses + partials + fetch <= ws <= misses + partials + fetch + 8 * 1024
+
+
+def test_plan_capacity_matches_its_definition():
+    """The host planner of the library against the plain definition in the
+    oracle, on random inputs, plus its error returns.  No GPU needed."""
+    import numpy as np
+    from oracle.plan import plan_capacity
+    avsg = _lib()
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        n, S = int(rng.integers(1, 40)), int(rng.integers(1, 20000))
+        d = rng.integers(1, S + 1, n).astype(np.int32)
+        r = rng.integers(0, 5000, n).astype(np.int32)
+        b = int(rng.integers(0, 2 * n * S + 2))
+        st, cap = avsg.avsg_plan_capacity(d, r, b, S)
+        want = plan_capacity(d, r, b, S)
+        if want is None:
+            assert st == avsg.ERR_CAPACITY
+        else:
+            assert st == avsg.OK and np.array_equal(cap, want)
+    st, _ = avsg.avsg_plan_capacity(np.array([0], np.int32), np.array([0], np.int32), 10, 5)
+    assert st == avsg.ERR_INVALID_ARG
+    st, _ = avsg.avsg_plan_capacity(np.array([2], np.int32), np.array([-1], np.int32), 10, 5)
+    assert st == avsg.ERR_INVALID_ARG
+    # huge budgets do not overflow
+    st, cap = avsg.avsg_plan_capacity(np.array([1, 1], np.int32), np.array([2**31 - 2, 0], np.int32),
+                                      2**62, 1000)
+    assert st == avsg.OK and cap.tolist() == [1000, 1000]

@@ -1,0 +1,123 @@
+"""Per-unit buffer sizes (avsg_set_capacity) on the GPU vs the oracle,
+through the C ABI.  Capacities change between steps: constant below S,
+shrinking below the occupied slots (their entries are dropped), growing
+again, and out of range or below |U| for one unit (a data error of that unit
+only).  State, buffer bytes and attention must match the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import tracegen as tg
+from gpu_harness import Runner, say, ensure_lib
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "token": tg.WORKLOADS[2].replace(batch=3, n_kv_heads=2, n_q_heads=8, n_entries=5003, k=300,
+                                     n_slots=1000, steps=12),
+    "mtp": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003, k=300,
+                                   n_slots=700, steps=10),
+    "lru_pages": tg.WORKLOADS[4].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001, k=37,
+                                         n_slots=100, steps=14),
+    "latent": tg.WORKLOADS[5].replace(batch=3, n_entries=5003, k=700, n_slots=1500, steps=8),
+    "slots_16k": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=40000,
+                                         k=2000, n_slots=16384, steps=6),
+}
+
+
+def _caps(w, t, rng, union):
+    """Step t's capacities: full, then random sizes between |U| and S, with a
+    deep shrink (to |U|) on step 3 and back to S on step 5."""
+    S = w.n_slots
+    if t < 2:
+        return np.full(w.units, S, np.int32)
+    if t == 3:
+        return union.astype(np.int32)
+    if t == 5:
+        return np.full(w.units, S, np.int32)
+    return rng.integers(union, S + 1).astype(np.int32)
+
+
+def _union_sizes(sel_t):
+    return np.array([len(np.unique(sel_t[u])) for u in range(sel_t.shape[0])])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_capacity_parity(name):
+    w = CASES[name]
+    say("[capacity] %s units=%d S=%d" % (name, w.units, w.n_slots))
+    sel = tg.selections(w)
+    rng = np.random.default_rng(len(name))
+    run = Runner(w)
+    try:
+        for t in range(w.steps):
+            run.set_caps(_caps(w, t, rng, _union_sizes(sel[t])))
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+            st = run.st.slot_table.cpu().numpy()
+            for u in range(w.units):
+                assert (st[u, run.caps[u]:] == -1).all()
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("mode", ["merge", "hash_table"])
+def test_capacity_match_modes(mode):
+    avsg = ensure_lib()
+    w = CASES["token"].replace(steps=7)
+    say("[capacity] %s" % mode)
+    sel = tg.selections(w)
+    rng = np.random.default_rng(4)
+    run = Runner(w)
+    run.ctx.set_match_mode(avsg.MATCH_MERGE if mode == "merge" else avsg.MATCH_HASH_TABLE)
+    try:
+        for t in range(w.steps):
+            run.set_caps(_caps(w, t, rng, _union_sizes(sel[t])))
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+    finally:
+        run.close()
+
+
+def test_capacity_errors_are_unit_errors():
+    avsg = ensure_lib()
+    w = CASES["token"].replace(steps=5)
+    say("[capacity] errors")
+    sel = tg.selections(w)
+    run = Runner(w)
+    try:
+        run.step_and_compare(0, sel[0], tg.queries(w, 0), check_buf=True)
+        for t, bad, want in ((1, 0, avsg.ERR_RANGE), (2, w.n_slots + 1, avsg.ERR_RANGE),
+                             (3, w.k - 1, avsg.ERR_CAPACITY), (4, w.k, avsg.OK)):
+            caps = np.full(w.units, w.n_slots, np.int32)
+            caps[1] = bad
+            run.set_caps(caps)
+            r, _ = run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+            assert r["status"][1] == want and (np.delete(r["status"], 1) == 0).all()
+            assert run.ctx.last_error() == want
+        run.set_caps(None)
+    finally:
+        run.close()
+
+
+def test_plan_then_step():
+    """The planner's capacities for the next step's unions, then the step."""
+    avsg = ensure_lib()
+    from oracle.plan import plan_capacity
+    w = CASES["token"].replace(steps=6)
+    say("[capacity] planned")
+    sel = tg.selections(w)
+    run = Runner(w)
+    reuse = np.zeros(w.units, np.int32)
+    try:
+        for t in range(w.steps):
+            demand = _union_sizes(sel[t]).astype(np.int32)
+            budget = int(demand.sum() + 0.3 * w.units * (w.n_slots - w.k))
+            st, caps = avsg.avsg_plan_capacity(demand, reuse, budget, w.n_slots)
+            assert st == avsg.OK
+            assert np.array_equal(caps, plan_capacity(demand, reuse, budget, w.n_slots))
+            run.set_caps(caps)
+            r, _ = run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+            reuse = r["n_hit"].astype(np.int32)
+    finally:
+        run.close()
