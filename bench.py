@@ -322,7 +322,8 @@ def main():
                 d[res + "_" + unit] = round(ach, 2)
                 d[res + "_frac"] = round(ach / pk, 4)
         kernels[name] = d
-    dominant = max(per, key=per.get)
+    # the longest kernel among those with algorithmic work of their own
+    dominant = max((n for n in per if any(v > 0 for v in use[n].values())), key=per.get)
     du = use[dominant]
     best = max((r for r in ("hbm", "host", "flop") if du[r] > 0),
                key=lambda r: du[r] / (per[dominant] * 1e-3) / peaks[r][2] / peaks[r][0])
