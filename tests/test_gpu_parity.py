@@ -41,7 +41,7 @@ SMALL = {
 
 
 # Edge shapes: k equal to the slot count, pages of 3 tokens whose rows straddle
-# the 256-row attention splits, 32-token pages, the largest lifetime and
+# the 256-row attention splits, 32- and 256-token pages, the largest lifetime and
 # bucket counts, 2 query heads per KV head, a single selected latent row, a
 # latent head whose selection fits one split, and a context of 200000 ids.
 EDGE = {
@@ -51,6 +51,10 @@ EDGE = {
                                              tokens_per_entry=3, k=200, n_slots=400, steps=8),
     "tpe32": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=4, n_entries=300,
                                      tokens_per_entry=32, k=20, n_slots=40, steps=8),
+    # the largest page the kernels take: 256 tokens (128 KiB rows), one page
+    # per 256-row attention split
+    "tpe256": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=4, n_entries=40,
+                                      tokens_per_entry=256, k=6, n_slots=12, steps=8),
     "L126": tg.WORKLOADS[2].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=3000, k=150,
                                     n_slots=400, lifetime_L=126, steps=10),
     "B127": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=4, n_entries=2000,
