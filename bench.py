@@ -132,13 +132,24 @@ class Bench:
         return ms, kern
 
 
-def attn_bytes(w):
-    """Algorithmic bytes of one attention launch: the selected K/V rows, the
-    slot list, the queries and the fp32 outputs."""
-    kv = w.units * w.n_q_tokens * w.k * w.tokens_per_entry * (w.head_dim_qk +
-                                                               (0 if w.latent else w.head_dim_v)) * 2
-    return kv + w.units * w.n_q_tokens * w.k * 4 + w.batch * w.n_q_tokens * w.n_q_heads * (
+def attn_bytes(w, union_entries=None):
+    """Algorithmic bytes of the attention of one step: the selected K/V rows,
+    the slot list, the queries and the fp32 outputs.  With two query tokens
+    in the split layout the rows of the union are read once (union_entries:
+    the union's entries summed over units)."""
+    row = w.tokens_per_entry * (w.head_dim_qk + (0 if w.latent else w.head_dim_v)) * 2
+    entries = w.units * w.n_q_tokens * w.k
+    if union_entries is not None and w.n_q_tokens > 1 and not w.latent:
+        entries = union_entries
+    return entries * (row + 4) + w.batch * w.n_q_tokens * w.n_q_heads * (
         w.head_dim_qk * 2 + w.head_dim_v * 4)
+
+
+def union_entries(sel):
+    """Entries of the union of each unit's query tokens, summed over units,
+    averaged over the steps of sel [steps][units][T][k]."""
+    return float(np.mean([sum(len(np.unique(sel[t, u])) for u in range(sel.shape[1]))
+                          for t in range(sel.shape[0])]))
 
 
 def attn_flops(w):
@@ -299,7 +310,7 @@ def main():
            "combine": kern[3] / K}
     fused = a.transfer in (0, 3)
     host_b = miss_per_step * row_bytes          # bytes over the host link per step
-    ab = attn_bytes(w)
+    ab = attn_bytes(w, union_per_step)
     # per kernel: algorithmic bytes (HBM / host link) and flops of one launch
     use = {
         "match_reserve": {"hbm": match_bytes(w, miss_per_step), "host": 0.0, "flop": 0.0},
@@ -350,13 +361,14 @@ def main():
         b.reset()
         b.run(0, 1)
         _, kh = b.timed(1, nh + 1, profile=True)
-        step_bytes = ab + match_bytes(w, 0)
+        ab_h = attn_bytes(w, union_entries(b.sel_np[1:]))
+        step_bytes = ab_h + match_bytes(w, 0)
         extra["all_hit"] = {
             "steps": nh, "ms_per_step": round(ms_h / nh, 4),
             "step_hbm_GB/s": round(step_bytes / (ms_h / nh * 1e-3) / 1e9, 1),
             "step_hbm_frac": round(step_bytes / (ms_h / nh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "attention_us": round(kh[2] / nh * 1e3, 2),
-            "attention_hbm_frac": round(ab / (kh[2] / nh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "attention_hbm_frac": round(ab_h / (kh[2] / nh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "combine_us": round(kh[3] / nh * 1e3, 2),
             "match_reserve_us": round(kh[0] / nh * 1e3, 2)}
         # all-miss: disjoint windows, every entry crosses the host link
