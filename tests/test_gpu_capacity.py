@@ -121,3 +121,39 @@ def test_plan_then_step():
             reuse = r["n_hit"].astype(np.int32)
     finally:
         run.close()
+
+
+def test_lengths_capacity_and_appends_together():
+    """Variable list lengths, changing buffer sizes and appends interleaved
+    over one trace, on paged entries under the LRU policy: every step's
+    state, buffer bytes and attention against the oracle."""
+    import torch
+    from oracle import append as oapp
+    w = CASES["lru_pages"].replace(steps=12)
+    say("[capacity] lengths + sizes + appends")
+    sel, lens = tg.shorten(tg.selections(w), 11, 1)
+    rng = np.random.default_rng(12)
+    run = Runner(w)
+    try:
+        for t in range(w.steps):
+            caps = rng.integers(lens[t], w.n_slots + 1).astype(np.int32)
+            if t == 6:
+                caps = lens[t].astype(np.int32)   # shrink to the mandatory slots
+            run.set_caps(caps)
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True, lengths=lens[t])
+            # every request appends a token into an entry its first head holds
+            pos = np.array([sel[t, b * w.n_kv_heads, 0, 0] * w.tokens_per_entry + t % 16
+                            for b in range(w.batch)], np.int32)
+            x = rng.standard_normal((w.units, w.head_dim_qk + w.head_dim_v)).astype(np.float32)
+            new = (x.view(np.uint32) >> 16).astype(np.uint16)
+            ref_host = run.host.array.copy()
+            oapp.append(w, ref_host, new, pos, run.ob.slot_tok, run.ob.buf)
+            run.ctx.append(torch.from_numpy(new.view(np.int16)).cuda(), torch.from_numpy(pos).cuda(),
+                           run.host, run.st.buf_kv, run.st.slot_table)
+            torch.cuda.synchronize()
+            assert np.array_equal(run.host.array, ref_host)
+            assert np.array_equal(run.st.buf_kv.cpu().numpy().view(np.uint16), run.ob.buf)
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+        run.host.free()

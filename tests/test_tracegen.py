@@ -78,3 +78,22 @@ def test_skewed_mode():
             assert np.intersect1d(sk[t, u, 0], sk[t - 1, u, 0]).size == 0
     for u in (1, 9, 63):
         assert all(np.array_equal(sk[0, u], sk[t, u]) for t in range(5))
+
+
+def test_shorten_keeps_sorted_subsets():
+    """Variable-size lists: each (step, unit) keeps `len` of its entries, in
+    ascending order, at the front; the rest is padding; lengths in range."""
+    w = tg.WORKLOADS[2].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=3000, k=100,
+                                n_slots=300, steps=5)
+    sel = tg.selections(w)
+    out, lens = tg.shorten(sel, 3, 10, 60)
+    assert out.shape == sel.shape and lens.shape == (w.steps, w.units)
+    assert lens.min() >= 10 and lens.max() <= 60
+    for t in range(w.steps):
+        for u in range(w.units):
+            n = lens[t, u]
+            kept = out[t, u, 0, :n]
+            assert (np.diff(kept) > 0).all() and np.isin(kept, sel[t, u, 0]).all()
+            assert (out[t, u, 0, n:] == -1).all()
+    again, lens2 = tg.shorten(sel, 3, 10, 60)
+    assert np.array_equal(again, out) and np.array_equal(lens2, lens)
