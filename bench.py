@@ -273,7 +273,7 @@ def main():
     a = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus > 1 or world > 1:
-        print("bench.py measures one GPU: the slot buffer's units are independent and this build "
+        print("bench.py measures one GPU: the slot buffer's units are independent and the library "
               "runs on a single MI355X; --gpus %d is not supported" % max(a.gpus, world),
               file=sys.stderr)
         sys.exit(2)

@@ -180,7 +180,7 @@ const char* avsg_status_string(avsg_status s) {
     case AVSG_ERR_INVALID_ARG: return "invalid argument";
     case AVSG_ERR_NOT_PINNED: return "host_kv is not pinned device-mapped host memory";
     case AVSG_ERR_HIP: return "HIP runtime error";
-    case AVSG_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case AVSG_ERR_UNSUPPORTED: return "configuration not supported by the library's kernels";
     case AVSG_ERR_UNSORTED: return "selection not strictly ascending";
     case AVSG_ERR_RANGE: return "selected id out of range";
     case AVSG_ERR_CAPACITY: return "selection union exceeds buffer slots";

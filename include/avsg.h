@@ -49,7 +49,7 @@ typedef enum avsg_status {
   AVSG_ERR_INVALID_ARG = 1,  /* null pointer, bad config, workspace too small */
   AVSG_ERR_NOT_PINNED = 2,   /* host_kv is not pinned, device-mapped host memory */
   AVSG_ERR_HIP = 3,          /* a HIP runtime call failed */
-  AVSG_ERR_UNSUPPORTED = 4,  /* config valid but outside this build's kernels */
+  AVSG_ERR_UNSUPPORTED = 4,  /* config valid but outside the library's kernels */
   /* data errors, found on the GPU and reported by avsg_last_error */
   AVSG_ERR_UNSORTED = 16,    /* a token's selection is not strictly ascending */
   AVSG_ERR_RANGE = 17,       /* a selected id is outside [0, n_entries) */
@@ -108,7 +108,7 @@ typedef struct avsg_ctx avsg_ctx;
 
 /* Checks a configuration on the host only (no GPU needed).  Returns AVSG_OK,
  * AVSG_ERR_INVALID_ARG (inconsistent values) or AVSG_ERR_UNSUPPORTED (a shape
- * the kernels of this build do not handle). */
+ * the library's kernels do not handle). */
 avsg_status avsg_check_config(const avsg_config* cfg);
 
 /* Bytes of device workspace a context for cfg needs (0 if cfg is invalid).
