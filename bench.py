@@ -237,15 +237,16 @@ def ablations(b, w, n):
     return out
 
 
-def cpu_baseline(w, t_start, seconds):
+def cpu_baseline(w, t_start, seconds, threads=1):
     """The oracle (state machine + float64 attention) on the same workload,
-    from step t_start on, until `seconds` have elapsed."""
+    from step t_start on, until `seconds` have elapsed, with `threads`
+    threads (the state machine's OpenMP loop over units and numpy's BLAS)."""
     import tracegen as tg
     import oracle
     from oracle import attention as oatt
     from threadpoolctl import threadpool_limits
-    lim = threadpool_limits(1)
-    oracle.set_threads(1)
+    lim = threadpool_limits(threads)
+    oracle.set_threads(threads)
     steps_needed = t_start + 64
     sel = tg.selections(w, steps=steps_needed)
     host = tg.fill_kv(w)
@@ -261,12 +262,12 @@ def cpu_baseline(w, t_start, seconds):
         t += 1
     el = time.perf_counter() - t0
     del lim
-    return {"value": done * w.entries_per_step / el, "unit": "entries/s", "cores": 1,
+    return {"value": done * w.entries_per_step / el, "unit": "entries/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d decode steps (t=%d..%d) of the same workload, all %d units: C state "
-                      "machine + float64 numpy attention, one thread" % (done, t_start,
-                                                                         t_start + done - 1,
-                                                                         w.units)}
+                      "machine + float64 numpy attention, %s" % (
+                          done, t_start, t_start + done - 1, w.units,
+                          "one thread" if threads == 1 else "%d threads" % threads)}
 
 
 def main():
@@ -526,6 +527,10 @@ def main():
     line.update(extra)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_seconds)
+        # the same oracle on every host thread the process may use
+        nthr = len(os.sched_getaffinity(0))
+        if nthr > 1:
+            line["cpu_baseline_all_threads"] = cpu_baseline(w, W, a.cpu_seconds, nthr)
     print(json.dumps(line), flush=True)
     b.ctx.close()
     b.host.free()
