@@ -201,3 +201,41 @@ def test_profile_events_per_stage():
         run.ctx.profile_end()   # not profiling any more
     run.close()
     a.close()
+
+
+def test_new_entry_points_reject_bad_arguments():
+    """Argument errors of the append, the variable-length step and the
+    capacity call are reported synchronously and enqueue nothing."""
+    import ctypes
+    import torch
+    avsg = ensure_lib()
+    say("[behaviour] argument errors of append / varlen / capacity")
+    cfg = avsg.config_from_workload(W)
+    ctx = avsg.Context(cfg)
+    st = avsg.State(cfg)
+    ctx.reset(st.slot_table, st.lifetimes)
+    host = avsg.HostBuffer((W.units, W.n_entries, W.row_elems))
+    plain = np.zeros((W.units, W.n_entries, W.row_elems), np.uint16)
+    new = torch.zeros((W.units, W.head_dim_qk + W.head_dim_v), dtype=torch.int16, device="cuda")
+    pos = torch.zeros(W.batch, dtype=torch.int32, device="cuda")
+    lib = avsg.load()
+    # unpinned host memory, a misaligned token, null pointers
+    assert lib.avsg_append(ctx.handle, new.data_ptr(), pos.data_ptr(), plain.ctypes.data,
+                           st.buf_kv.data_ptr(), st.slot_table.data_ptr()) == avsg.ERR_NOT_PINNED
+    assert lib.avsg_append(ctx.handle, new.data_ptr() + 2, pos.data_ptr(), host.ptr,
+                           st.buf_kv.data_ptr(), st.slot_table.data_ptr()) == avsg.ERR_INVALID_ARG
+    assert lib.avsg_append(ctx.handle, None, pos.data_ptr(), host.ptr, st.buf_kv.data_ptr(),
+                           st.slot_table.data_ptr()) == avsg.ERR_INVALID_ARG
+    # the variable-length step needs its length array
+    sel = torch.from_numpy(tg.selections(W, steps=1)[0]).cuda()
+    q = torch.from_numpy(tg.queries(W, 0).view(np.int16)).cuda()
+    hs = st.stats.struct()
+    assert lib.avsg_step_varlen(ctx.handle, sel.data_ptr(), None, q.data_ptr(), host.ptr,
+                                st.buf_kv.data_ptr(), st.slot_table.data_ptr(),
+                                st.lifetimes.data_ptr(), st.out.data_ptr(),
+                                ctypes.byref(hs)) == avsg.ERR_INVALID_ARG
+    assert lib.avsg_set_capacity(None, None) == avsg.ERR_INVALID_ARG
+    assert ctx.t == 0
+    assert ctx.last_error() == avsg.OK
+    ctx.close()
+    host.free()
