@@ -104,7 +104,7 @@ class Bench:
         lens = getattr(self, "len_dev", None)
         for t in range(t0, t1):
             if lens is not None:
-                rc = lib.avsg_step_varlen(h, sel0 + t * selb, lens.data_ptr() + t * lens.shape[1] * 4,
+                rc = lib.avsg_step_varlen(h, sel0 + t * selb, lens.data_ptr() + t * lens[0].numel() * 4,
                                           q0 + (t % self.total) * qb, *args, hsp)
             else:
                 rc = lib.avsg_step(h, sel0 + t * selb, q0 + (t % self.total) * qb, *args, hsp)
@@ -393,36 +393,35 @@ def main():
             "transfer_kernel_host_GB/s": round(mb / (kt / nm * 1e-3) / 1e9, 2),
             "transfer_kernel_host_link_frac": round(mb / (kt / nm * 1e-3) / 1e9 / HOST_LINK_GBS, 4)}
         assert b.ctx.last_error() == 0
-        # selections of a different size per unit (PSA-style budgets,
-        # lengths uniform in [k/8, k]), single-token workloads only
-        if w.n_q_tokens == 1:
-            nv = min(K, 64)
-            b.load_varlen(32 + nv, max(1, w.k // 8))
-            b.reset()
-            b.run(0, 32)
-            ms_v, _ = b.timed(32, 32 + nv)
-            b.reset()
-            b.run(0, 32)
-            _, kv = b.timed(32, 32 + nv, profile=True)
-            b.reset()
-            b.run(0, 32)
-            accv = [torch.zeros(w.units, dtype=torch.int64, device="cuda") for _ in range(2)]
-            b.run(32, 32 + nv, stats=accv)
-            vh, vm = int(accv[0].sum()), int(accv[1].sum())
-            ent_v = float(b.len_np[32:32 + nv].sum()) * w.tokens_per_entry / nv
-            hb_v = vm / nv * row_bytes
-            extra["varlen"] = {
-                "steps": nv, "lengths": "uniform in [k/8, k] per unit and step, a random "
-                                        "subset of the natural trace's list",
-                "ms_per_step": round(ms_v / nv, 4),
-                "entries_per_step": round(ent_v, 1),
-                "entries_per_s": round(ent_v / (ms_v / nv * 1e-3), 1),
-                "hit_rate": round(vh / max(vh + vm, 1), 5),
-                "host_bytes_per_step": int(hb_v),
-                "attention_us": round(kv[2] / nv * 1e3, 2),
-                "attention_host_GB/s": round(hb_v / (kv[2] / nv * 1e-3) / 1e9, 2),
-                "match_reserve_us": round(kv[0] / nv * 1e3, 2)}
-            assert b.ctx.last_error() == 0
+        # selections of a different size per list (PSA-style budgets,
+        # lengths uniform in [k/8, k])
+        nv = min(K, 64)
+        b.load_varlen(32 + nv, max(1, w.k // 8))
+        b.reset()
+        b.run(0, 32)
+        ms_v, _ = b.timed(32, 32 + nv)
+        b.reset()
+        b.run(0, 32)
+        _, kv = b.timed(32, 32 + nv, profile=True)
+        b.reset()
+        b.run(0, 32)
+        accv = [torch.zeros(w.units, dtype=torch.int64, device="cuda") for _ in range(2)]
+        b.run(32, 32 + nv, stats=accv)
+        vh, vm = int(accv[0].sum()), int(accv[1].sum())
+        ent_v = float(b.len_np[32:32 + nv].sum()) * w.tokens_per_entry / nv
+        hb_v = vm / nv * row_bytes
+        extra["varlen"] = {
+            "steps": nv, "lengths": "uniform in [k/8, k] per list and step, a random "
+                                    "subset of the natural trace's list",
+            "ms_per_step": round(ms_v / nv, 4),
+            "entries_per_step": round(ent_v, 1),
+            "entries_per_s": round(ent_v / (ms_v / nv * 1e-3), 1),
+            "hit_rate": round(vh / max(vh + vm, 1), 5),
+            "host_bytes_per_step": int(hb_v),
+            "attention_us": round(kv[2] / nv * 1e3, 2),
+            "attention_host_GB/s": round(hb_v / (kv[2] / nv * 1e-3) / 1e9, 2),
+            "match_reserve_us": round(kv[0] / nv * 1e3, 2)}
+        assert b.ctx.last_error() == 0
         # buffer sizes from the planner: every unit's union is mandatory, and
         # a quarter of the remaining slots (units x (S - |U|)) is shared by
         # reuse measured over the warm-up steps; timed on the natural trace

@@ -362,8 +362,6 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   if (!ctx || !sel_idx || !q || !host_kv || !buf_kv || !slot_table || !lifetimes || !out || !hs ||
       !hs->hit_flag || !hs->sel_slot || !hs->n_hit || !hs->n_miss || !hs->n_evict)
     return AVSG_ERR_INVALID_ARG;
-  // lengths apply to single-token iterations (a two-token union assumes k each)
-  if (sel_len && ctx->cfg.n_q_tokens != 1) return AVSG_ERR_UNSUPPORTED;
   // the kernels move rows, queries and outputs in 16-byte pieces
   if (((uintptr_t)q | (uintptr_t)host_kv | (uintptr_t)buf_kv | (uintptr_t)out) & 15)
     return AVSG_ERR_INVALID_ARG;

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
   }
   const int nsplit = NS > 0 ? NS : p.nsplit;
   // splits holding rows: all of them, or those covering a shortened list
-  const int len = p.sel_len ? min(max(p.sel_len[u], 1), p.k) : p.k;
+  const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
   const int nused = min(nsplit, (len * p.tpe + p.split_rows - 1) / p.split_rows);
   const size_t ps = partial_stride(G, D);  // floats per split partial, multiple of 4
   const float* pbase = p.partials + (size_t)uj * nsplit * ps;

@@ -134,9 +134,9 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   const int b = u;  // one latent head per request
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  // a shortened list (length array): its first sel_len[u] entries (clamped
+  // a shortened list (length array): its first sel_len[u][j] entries (clamped
   // into [1, k]; a unit with an invalid length has failed and is zeroed)
-  const int len = p.sel_len ? min(max(p.sel_len[u], 1), p.k) : p.k;
+  const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
   const int e0 = sp * p.split_rows, e1 = min(e0 + p.split_rows, len);
   if (e0 >= e1) return;  // a split past the list's end (merged as empty)
   const int ne = e1 - e0;

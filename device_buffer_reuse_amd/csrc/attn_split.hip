@@ -136,10 +136,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   const int lane = threadIdx.x;
   const int gq = lane >> 4, li = lane & 15;  // lane group (rows / dims), column (head)
   const int tpe = p.tpe;
-  // a shortened list (length array, one token): its first sel_len[u]
-  // entries; a length outside [1, k] marks a unit whose step failed, whose
-  // workgroups read at most k entries and then zero its outputs
-  const int len = p.sel_len ? min(max(p.sel_len[u], 1), p.k) : p.k;
+  // a shortened list (length array): its first sel_len[u][j] entries; a
+  // length outside [1, k] marks a unit whose step failed, whose workgroups
+  // read at most k entries and then zero its outputs
+  const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
   const int n_rows = len * tpe;
   const int r0 = sp * p.split_rows, r1 = min(r0 + p.split_rows, n_rows);
   if (r0 >= n_rows) return;  // a split past the list's end (merged as empty)

@@ -43,7 +43,7 @@ inline __host__ __device__ size_t partial_stride(int G, int D) {
 
 struct MatchReserveParams {
   const int32_t* sel;     // [units][T][k]
-  const int32_t* sel_len; // [units] entries in use of each unit's list (T = 1), or null: k
+  const int32_t* sel_len; // [units][T] entries in use of each token's list, or null: k
   const int32_t* cap;     // [units] slots in use of each unit's buffer, or null: S
   int32_t* slot_table;    // [units][S]
   int32_t* lifetimes;     // [units][S]
@@ -78,7 +78,7 @@ struct GatherParams {
 
 struct AttnParams {
   const int32_t* sel_slot;    // [units][T][k]
-  const int32_t* sel_len;     // [units] entries in use (T = 1), or null: k
+  const int32_t* sel_len;     // [units][T] entries in use of each list, or null: k
   const int32_t* sel;         // [units][T][k] selected ids
   const uint8_t* fetch;       // [units][T][k] or null: rows to read from host and store
   const uint16_t* host_kv;    // device-visible address of the pinned host rows

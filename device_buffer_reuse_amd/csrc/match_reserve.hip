@@ -176,18 +176,22 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const int u = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S, N = p.N, T = p.T, k = p.k, ucap = p.ucap, C = p.table_cap;
-  // tks: stride of a unit's lists; tk: entries in use (one token with a
-  // length array: its first sel_len[u] entries, a length outside [1, k]
-  // being a range error)
+  // tks: stride of a unit's lists.  With a length array token j uses the
+  // first sel_len[u][j] entries of its list (ka for token 0, kb for token 1;
+  // a length outside [1, k] is a range error); tk: one token, the entries
+  // in use; two tokens, the whole [2][k] array, of which live(i) are in use
   const int tks = T * k;
-  const int len_in = (T == 1 && p.sel_len) ? p.sel_len[u] : k;
-  const bool len_bad = len_in < 1 || len_in > k;
+  const int len_in = p.sel_len ? p.sel_len[u * T] : k;
+  const int len1_in = (T > 1 && p.sel_len) ? p.sel_len[u * T + 1] : k;
+  const bool len_bad = len_in < 1 || len_in > k || len1_in < 1 || len1_in > k;
+  const int ka = len_bad ? 1 : len_in, kb = len_bad ? 1 : len1_in;
   // slots in use: [0, cap) (the unit's buffer size; slots past it are
   // emptied by this step); a capacity outside [1, S] is a range error
   const int cap_in = p.cap ? p.cap[u] : S;
   const bool cap_bad = cap_in < 1 || cap_in > S;
   const int cap = cap_bad ? S : cap_in;
-  const int nbins = p.nbins, tk = T == 1 ? (len_bad ? 1 : len_in) : tks;
+  const int nbins = p.nbins, tk = T == 1 ? ka : tks;
+  auto live = [&](int i) -> bool { return T == 1 ? i < tk : (i < k ? i < ka : i - k < kb); };
   const bool lru = p.policy == AVSG_POLICY_BUCKET_LRU;
 
   int32_t* sHash = lds;                      // [C] packed (id, union index) or -1
@@ -288,7 +292,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       for (int r = 0; r < kSelRegs; ++r) {
         const int i = tid + r * kMRThreads;
         const int32_t x = selr[r];
-        if (i < tk && x >= 0 && x < N) atomicOr(&(i < k ? sBitsA : sBits)[x >> 5], 1u << (x & 31));
+        if (i < tk && live(i) && x >= 0 && x < N)
+          atomicOr(&(i < k ? sBitsA : sBits)[x >> 5], 1u << (x & 31));
       }
     } else if (T == 1) {
 #pragma unroll
@@ -316,15 +321,16 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     for (int r = 0; r < kSelRegs; ++r) {
       const int i = tid + r * kMRThreads;
       const int32_t x = selr[r];
-      const bool live = i < tk, in_range = x >= 0 && x < N;
+      const bool in_use = i < tk && live(i), in_range = x >= 0 && x < N;
       // a token's list starts at 0 and, for the second token, at k (T <= 2)
-      bad |= (live && !in_range) ? kFlagRange : 0;
-      bad |= (live && i != 0 && i != k && x <= prv[r]) ? kFlagUnsorted : 0;
+      bad |= (in_use && !in_range) ? kFlagRange : 0;
+      bad |= (in_use && i != 0 && i != k && x <= prv[r]) ? kFlagUnsorted : 0;
     }
     if ((len_bad || cap_bad) && tid == 0) bad |= kFlagRange;
     // one token: U is the list itself
     if (T == 1 && tk > cap && tid == 0) bad |= kFlagCapacity;
     for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) {
+      if (!live(i)) continue;
       const int32_t x = stage[i];
       const bool in_range = x >= 0 && x < N;
       if (!in_range) bad |= kFlagRange;
@@ -387,6 +393,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       if (tid == 0) sMisc[0] = kFlagCapacity;
     } else {
       for (int i = tid; i < tk; i += kMRThreads) {
+        if (!live(i)) continue;
         const int32_t x = sMiss[i];
         const uint32_t word = sBits[x >> 5], bit = 1u << (x & 31);
         const int pos = sBase[x >> 5] + __popc(word & (bit - 1));
@@ -396,38 +403,39 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     }
     __syncthreads();
   } else if (T > 1 && sMisc[0] == 0) {
+    // token 0's ka ids and token 1's kb ids, each sorted
     const int32_t* A = sMiss;
     const int32_t* Bl = sMiss + k;
     int run = 0;
-    for (int c0 = 0; c0 < k; c0 += kMRThreads) {
+    for (int c0 = 0; c0 < ka; c0 += kMRThreads) {
       const int i = c0 + tid;
       bool dup = false;
-      if (i < k) {
-        const int lb = lower_bound_lds(Bl, k, A[i]);
-        dup = lb < k && Bl[lb] == A[i];
+      if (i < ka) {
+        const int lb = lower_bound_lds(Bl, kb, A[i]);
+        dup = lb < kb && Bl[lb] == A[i];
       }
       int tot;
       const int pre = block_excl_scan_bit(dup, sWs, &tot);
-      if (i < k) sDup[i] = run + pre;
+      if (i < ka) sDup[i] = run + pre;
       run += tot;
     }
-    if (tid == 0) sDup[k] = run;
+    if (tid == 0) sDup[ka] = run;
     __syncthreads();
-    nu = 2 * k - sDup[k];
+    nu = ka + kb - sDup[ka];
     if (nu > cap) {
       if (tid == 0) sMisc[0] = kFlagCapacity;
     } else {
-      for (int i = tid; i < k; i += kMRThreads) {
+      for (int i = tid; i < ka; i += kMRThreads) {
         const int32_t a = A[i];
-        const int pos = i + lower_bound_lds(Bl, k, a) - sDup[i];
+        const int pos = i + lower_bound_lds(Bl, kb, a) - sDup[i];
         sU[pos] = a;
         sMap[i] = pos;
       }
-      for (int j = tid; j < k; j += kMRThreads) {
+      for (int j = tid; j < kb; j += kMRThreads) {
         const int32_t b = Bl[j];
-        const int la = lower_bound_lds(A, k, b);
+        const int la = lower_bound_lds(A, ka, b);
         const int pos = la + j - sDup[la];
-        const bool dup = la < k && A[la] == b;
+        const bool dup = la < ka && A[la] == b;
         sU[pos] = b;  // a duplicate writes the same value at the same position
         sMap[k + j] = pos | (dup ? kDupFlag : 0);
       }
@@ -903,6 +911,12 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 
   // ---- 8. per-(token, entry) outputs read off the union
   for (int i = tid; i < tk; i += kMRThreads) {
+    if (T > 1 && !live(i)) {  // past a shortened list: no slot, no transfer
+      p.sel_slot[(size_t)u * tks + i] = -1;
+      p.hit_flag[(size_t)u * tks + i] = 0;
+      p.fetch[(size_t)u * tks + i] = 0;
+      continue;
+    }
     const int mi = (T == 1) ? i : sMap[i];
     const int v = sUslot[mi & ~kDupFlag];
     const bool miss = (v & kMissFlag) != 0;

@@ -158,19 +158,20 @@ avsg_status avsg_step(avsg_ctx* ctx, const int32_t* sel_idx, const uint16_t* q,
                       const uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
                       int32_t* lifetimes, float* out, const avsg_hit_stats* hit_stats);
 
-/* avsg_step with a selection length per unit, for selections whose size
- * varies by request and head (the PSA abstract: the KV budget is adapted per
- * token and layer to the attention weights instead of one fixed k).
- *   sel_len    device, int32 [batch][n_kv_heads]: unit u uses the first
- *              sel_len[u] ids of sel_idx[u] (strictly ascending, in [0, N));
- *              the rest of its k positions are ignored, and their hit_flag,
- *              sel_slot outputs are 0 and -1.                     read only
- * All other arguments and results as avsg_step, with k read as sel_len[u]
- * for unit u.  A length outside [1, k] is a data error of that unit
- * (AVSG_ERR_RANGE).  Attention splits past a unit's length do no work, so a
- * long list is spread over as many workgroups as its rows need whatever the
- * other units' lengths.  Only single-token iterations (n_q_tokens = 1):
- * otherwise AVSG_ERR_UNSUPPORTED.  AVSG_ERR_INVALID_ARG if sel_len is null. */
+/* avsg_step with a selection length per list, for selections whose size
+ * varies by request, head and query token (the PSA abstract: the KV budget
+ * is adapted per token and layer to the attention weights instead of one
+ * fixed k).
+ *   sel_len    device, int32 [batch][n_kv_heads][T]: token j of unit u uses
+ *              the first sel_len[u][j] ids of sel_idx[u][j] (strictly
+ *              ascending, in [0, N)); the rest of its k positions are
+ *              ignored, and their hit_flag, sel_slot outputs are 0 and -1.
+ *                                                                  read only
+ * All other arguments and results as avsg_step, with the union U formed
+ * from the lists in use.  A length outside [1, k] is a data error of that
+ * unit (AVSG_ERR_RANGE).  Attention splits past a list's length do no work,
+ * so a long list is spread over as many workgroups as its rows need whatever
+ * the other lists' lengths.  AVSG_ERR_INVALID_ARG if sel_len is null. */
 avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_t* sel_len,
                              const uint16_t* q, const uint16_t* host_kv, uint16_t* buf_kv,
                              int32_t* slot_table, int32_t* lifetimes, float* out,

@@ -77,10 +77,11 @@ class Runner:
         self.ctx.set_capacity(self.cap_dev)
 
     def step_and_compare(self, t, sel_t, q_t, check_attn=True, check_buf=False, lengths=None):
-        """lengths: optional [units] list lengths (one query token)."""
+        """lengths: optional list lengths, [units] or [units][T]."""
         self.gpu_step(sel_t, q_t, lengths)
         self.torch.cuda.synchronize()
-        ln = None if lengths is None else np.asarray(lengths, np.int32).reshape(-1, 1)
+        ln = None if lengths is None else np.asarray(lengths, np.int32).reshape(
+            self.w.units, self.w.n_q_tokens)
         r = self.ob.step(sel_t, self.host.array if self.ob.track_buf else None, lengths=ln,
                          caps=getattr(self, "caps", None))
         s = self.st

@@ -99,17 +99,48 @@ def test_varlen_bad_length_is_a_unit_error():
         run.close()
 
 
-def test_varlen_two_tokens_unsupported():
+MTP_CASES = {
+    "mtp": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003, k=300,
+                                   n_slots=700, steps=10),
+    "mtp_pages": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001,
+                                         tokens_per_entry=16, k=37, n_slots=100, steps=10),
+    "mla_mtp": tg.WORKLOADS[5].replace(batch=2, n_q_tokens=2, overlap_shared=0.5, n_entries=5003,
+                                       k=600, n_slots=1300, steps=6),
+}
+
+
+@pytest.mark.parametrize("name,mode", [(n, "hash") for n in MTP_CASES] +
+                         [("mtp", "hash_table"), ("mtp", "merge")])
+def test_varlen_two_tokens(name, mode):
+    """Two query tokens with a length per token: the union is formed from
+    the lists in use (direct-addressed, sorted-list and merge forms), a row
+    is fetched by the first token whose list in use holds it, and each
+    token attends over its own prefix."""
     avsg = ensure_lib()
-    import torch
-    w = tg.WORKLOADS[3].replace(batch=1, n_kv_heads=2, n_q_heads=8, n_entries=3000, k=100,
-                                n_slots=300, steps=1)
-    say("[varlen] two tokens")
-    run = Runner(w, track_buf=False)
+    w = MTP_CASES[name]
+    say("[varlen] two tokens %s %s" % (name, mode))
+    sel, lens = tg.shorten(tg.selections(w), 21, 1)
+    lens[0, 0] = [1, w.k]          # one entry beside a full list
+    lens[1, -1] = [w.k, 1]
+    full = tg.selections(w)
+    sel[0, 0, 1] = full[0, 0, 1]
+    sel[1, -1, 0] = full[1, -1, 0]
+    run = Runner(w)
+    if mode == "merge":
+        run.ctx.set_match_mode(avsg.MATCH_MERGE)
+    elif mode == "hash_table":
+        run.ctx.set_match_mode(avsg.MATCH_HASH_TABLE)
     try:
-        with pytest.raises(avsg.AvsgError) as e:
-            run.gpu_step(tg.selections(w)[0], tg.queries(w, 0), lengths=np.full(w.units, 50))
-        assert e.value.status == avsg.ERR_UNSUPPORTED
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True, lengths=lens[t])
+        assert run.ctx.last_error() == 0
+        # a bad length of either token is a range error of that unit
+        ln = lens[w.steps - 1].copy()
+        ln[1, 1] = w.k + 1
+        r, _ = run.step_and_compare(w.steps, sel[w.steps - 1], tg.queries(w, w.steps - 1),
+                                    check_buf=True, lengths=ln)
+        assert r["status"][1] == avsg.ERR_RANGE
+        assert run.ctx.last_error() == avsg.ERR_RANGE
     finally:
         run.close()
 

@@ -187,24 +187,24 @@ def selections(w: Workload, steps: int | None = None, mode: str = "natural") -> 
 
 def shorten(sel: np.ndarray, seed: int, lo: int, hi: int | None = None,
             pad: int = -1) -> tuple[np.ndarray, np.ndarray]:
-    """Variable-size selections from fixed-size ones (one query token): for
-    every (step, unit) a length drawn uniformly from [lo, hi] (hi defaults to
-    k), and that many of the k entries, chosen uniformly (numpy generator
-    seeded with `seed`), kept in ascending order at the front of the list;
-    the positions after them hold `pad`.  Returns (lists [steps][units][1][k],
-    lengths [steps][units])."""
+    """Variable-size selections from fixed-size ones: for every (step, unit,
+    query token) a length drawn uniformly from [lo, hi] (hi defaults to k),
+    and that many of the k entries, chosen uniformly (numpy generator seeded
+    with `seed`), kept in ascending order at the front of the list; the
+    positions after them hold `pad`.  Returns (lists [steps][units][T][k],
+    lengths [steps][units] for one token, else [steps][units][T])."""
     steps, units, T, k = sel.shape
-    assert T == 1
     hi = k if hi is None else hi
     rng = np.random.default_rng(seed)
     out = np.full_like(sel, pad)
-    lens = rng.integers(lo, hi + 1, size=(steps, units)).astype(np.int32)
+    lens = rng.integers(lo, hi + 1, size=(steps, units, T)).astype(np.int32)
     for t in range(steps):
         for u in range(units):
-            n = int(lens[t, u])
-            keep = np.sort(rng.choice(k, size=n, replace=False))
-            out[t, u, 0, :n] = sel[t, u, 0, keep]
-    return out, lens
+            for j in range(T):
+                n = int(lens[t, u, j])
+                keep = np.sort(rng.choice(k, size=n, replace=False))
+                out[t, u, j, :n] = sel[t, u, j, keep]
+    return out, (lens[:, :, 0] if T == 1 else lens)
 
 
 def permutation(w: Workload, unit: int) -> np.ndarray:
