@@ -170,6 +170,12 @@ __device__ __forceinline__ int block_excl_scan_bit(bool v, int* sWs, int* total)
   return pre + mbcnt64(m);
 }
 
+// entry i of a unit's [T][k] selection array is in use: before end0 in the
+// first list, or before end1 (= k + length) in the second
+__device__ __forceinline__ bool in_use_at(int i, int k, int end0, int end1) {
+  return i < k ? i < end0 : i < end1;
+}
+
 template <int MAXP>
 __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveParams p) {
   extern __shared__ int32_t lds[];
@@ -179,7 +185,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // tks: stride of a unit's lists.  With a length array token j uses the
   // first sel_len[u][j] entries of its list (ka for token 0, kb for token 1;
   // a length outside [1, k] is a range error); tk: one token, the entries
-  // in use; two tokens, the whole [2][k] array, of which live(i) are in use
+  // in use; two tokens, the whole [2][k] array, of which the entries that
+  // in_use_at() accepts are in use
   const int tks = T * k;
   const int len_in = p.sel_len ? p.sel_len[u * T] : k;
   const int len1_in = (T > 1 && p.sel_len) ? p.sel_len[u * T + 1] : k;
@@ -191,7 +198,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const bool cap_bad = cap_in < 1 || cap_in > S;
   const int cap = cap_bad ? S : cap_in;
   const int nbins = p.nbins, tk = T == 1 ? ka : tks;
-  auto live = [&](int i) -> bool { return T == 1 ? i < tk : (i < k ? i < ka : i - k < kb); };
+  // entry i of the [T][k] array is in use: one token, i < tk; two tokens,
+  // i < ka in token 0's list or i - k < kb in token 1's
+  const int live_end0 = T == 1 ? tk : ka, live_end1 = k + kb;
   const bool lru = p.policy == AVSG_POLICY_BUCKET_LRU;
 
   int32_t* sHash = lds;                      // [C] packed (id, union index) or -1
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       for (int r = 0; r < kSelRegs; ++r) {
         const int i = tid + r * kMRThreads;
         const int32_t x = selr[r];
-        if (i < tk && live(i) && x >= 0 && x < N)
+        if (i < tk && in_use_at(i, k, live_end0, live_end1) && x >= 0 && x < N)
           atomicOr(&(i < k ? sBitsA : sBits)[x >> 5], 1u << (x & 31));
       }
     } else if (T == 1) {
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     for (int r = 0; r < kSelRegs; ++r) {
       const int i = tid + r * kMRThreads;
       const int32_t x = selr[r];
-      const bool in_use = i < tk && live(i), in_range = x >= 0 && x < N;
+      const bool in_use = i < tk && in_use_at(i, k, live_end0, live_end1), in_range = x >= 0 && x < N;
       // a token's list starts at 0 and, for the second token, at k (T <= 2)
       bad |= (in_use && !in_range) ? kFlagRange : 0;
       bad |= (in_use && i != 0 && i != k && x <= prv[r]) ? kFlagUnsorted : 0;
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     // one token: U is the list itself
     if (T == 1 && tk > cap && tid == 0) bad |= kFlagCapacity;
     for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) {
-      if (!live(i)) continue;
+      if (!in_use_at(i, k, live_end0, live_end1)) continue;
       const int32_t x = stage[i];
       const bool in_range = x >= 0 && x < N;
       if (!in_range) bad |= kFlagRange;
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       if (tid == 0) sMisc[0] = kFlagCapacity;
     } else {
       for (int i = tid; i < tk; i += kMRThreads) {
-        if (!live(i)) continue;
+        if (!in_use_at(i, k, live_end0, live_end1)) continue;
         const int32_t x = sMiss[i];
         const uint32_t word = sBits[x >> 5], bit = 1u << (x & 31);
         const int pos = sBase[x >> 5] + __popc(word & (bit - 1));
@@ -456,12 +465,18 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // end of the step (bit q); they take no part in it
   const int32_t life_empty = lru ? -1 : 0;
   uint32_t drop = 0;
+  if (cap < S) {  // the whole workgroup: only a sized buffer empties slots
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      const int s = s0 + q * 64 + lane;
+      if (q * 64 < R && s < s1 && s >= cap && (tok[q] != -1 || lf[q] != life_empty))
+        drop |= 1u << q;
+    }
+  }
+  const int s_use = min(s1, cap);  // this wave's slots in use end here
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) {
-    const int s = s0 + q * 64 + lane;
-    const bool in_buf = q * 64 < R && s < s1;
-    if (in_buf && s >= cap && (tok[q] != -1 || lf[q] != life_empty)) drop |= 1u << q;
-    if (!(in_buf && s < cap)) {
+    if (!(q * 64 < R && s0 + q * 64 + lane < s_use)) {
       tok[q] = kInvalid;
       lf[q] = 0;
     }
@@ -911,7 +926,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
 
   // ---- 8. per-(token, entry) outputs read off the union
   for (int i = tid; i < tk; i += kMRThreads) {
-    if (T > 1 && !live(i)) {  // past a shortened list: no slot, no transfer
+    if (T > 1 && !in_use_at(i, k, live_end0, live_end1)) {  // past a shortened list: no slot, no transfer
       p.sel_slot[(size_t)u * tks + i] = -1;
       p.hit_flag[(size_t)u * tks + i] = 0;
       p.fetch[(size_t)u * tks + i] = 0;
@@ -935,16 +950,19 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   //         outputs so that the stores overlap them)
 #pragma unroll
   for (int q = 0; q < MAXP; ++q) {
+    if (tok[q] == kInvalid) continue;
     const int s = s0 + q * 64 + lane;
-    if (tok[q] == kInvalid) {
-      if ((drop >> q) & 1) {
-        slot_table[s] = -1;
-        lifetimes[s] = life_empty;
-      }
-      continue;
-    }
     lifetimes[s] = lf[q];
     if (changed[q]) slot_table[s] = tok[q];
+  }
+  if (drop) {
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      if ((drop >> q) & 1) {
+        slot_table[s0 + q * 64 + lane] = -1;
+        lifetimes[s0 + q * 64 + lane] = life_empty;
+      }
+    }
   }
 
   if (tid == 0) {
