@@ -489,6 +489,19 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         extra["pinned_memcpy_h2d_GB/s"] = round(4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
+        # a plain device-to-device copy of 1 GiB: HBM bytes read + written
+        del src, dst
+        xa = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        xb = torch.empty_like(xa)
+        xb.copy_(xa)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(4):
+            xb.copy_(xa)
+        e1.record()
+        torch.cuda.synchronize()
+        extra["hbm_copy_GB/s"] = round(4 * 2 * xa.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del xa, xb
     if a.ablations:
         extra["ablations"] = ablations(b, w, min(K, 32))
     if a.calibrate_copy:
