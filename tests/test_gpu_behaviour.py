@@ -77,6 +77,18 @@ def test_checkpoint_resume():
     for i, t in enumerate(range(5, 10)):
         run.gpu_step(sel[t], tg.queries(w, t))
         assert torch.equal(run.st.out, outs[i][0]) and torch.equal(run.st.slot_table, outs[i][1])
+    # into a fresh context with its own workspace: no state lives in the
+    # library between steps, so the restored arrays and counter suffice
+    fresh = Runner(w, host=run.host, track_buf=False)
+    fresh.st.slot_table.copy_(snap[0]); fresh.st.lifetimes.copy_(snap[1])
+    fresh.st.buf_kv.copy_(snap[2])
+    from device_buffer_reuse_amd import avsg
+    assert fresh.ctx.rebuild_index(fresh.st.slot_table) == avsg.OK
+    fresh.ctx.t = snap[3]
+    for i, t in enumerate(range(5, 10)):
+        fresh.gpu_step(sel[t], tg.queries(w, t))
+        assert torch.equal(fresh.st.out, outs[i][0]) and torch.equal(fresh.st.slot_table, outs[i][1])
+    fresh.close()
     run.close()
 
 
