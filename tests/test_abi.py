@@ -103,3 +103,14 @@ def test_plan_capacity_matches_its_definition():
     st, cap = avsg.avsg_plan_capacity(np.array([1, 1], np.int32), np.array([2**31 - 2, 0], np.int32),
                                       2**62, 1000)
     assert st == avsg.OK and cap.tolist() == [1000, 1000]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asking for several exits with status 2 and
+    says so, before touching any device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
