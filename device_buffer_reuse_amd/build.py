@@ -46,6 +46,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+NATIVE_SRC = os.path.join(HERE, "..", "tests", "native", "avsg_native_steps.cpp")
+NATIVE_BIN = os.path.join(HERE, "..", "tests", "native", "avsg_native_steps")
+
+
+def build_native_test(verbose: bool = False) -> str:
+    """Compile the test program that calls libavsg through its C ABI alone
+    (linked against the in-tree library, found through its rpath)."""
+    tmp = NATIVE_BIN + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-o", tmp, NATIVE_SRC,
+           "-L" + HERE, "-lavsg", "-Wl,-rpath,$ORIGIN/../../device_buffer_reuse_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("native test build failed:\n%s" % r.stderr)
+    os.replace(tmp, NATIVE_BIN)
+    if verbose:
+        print("built", os.path.normpath(NATIVE_BIN))
+    return NATIVE_BIN
+
+
 def needs_build() -> bool:
     if not os.path.exists(LIB):
         return True
