@@ -128,8 +128,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   __shared__ uint64_t sDst[kBufs][kChunk];  // per tile row: slot address (host rows)
 
   const int nsplit = p.nsplit;
-  const int u = blockIdx.x / nsplit;
-  const int sp = blockIdx.x - u * nsplit;
+  // workgroups are dealt to the 8 XCDs in turn (workgroup i on XCD i mod 8);
+  // when the grid divides by 8, XCD x takes the x-th eighth of the (unit,
+  // split) range, so every split of a unit runs behind the same L2 (a later
+  // token's launch finds the rows an earlier one read or stored there)
+  const int nb = (int)gridDim.x;
+  const int bid = (nb & 7) == 0 ? (int)(blockIdx.x & 7) * (nb >> 3) + (int)(blockIdx.x >> 3)
+                                : (int)blockIdx.x;
+  const int u = bid / nsplit;
+  const int sp = bid - u * nsplit;
   const int j = p.token;
   const int uj = u * p.T + j;
   const int b = u / p.Hkv, g = u - b * p.Hkv;
