@@ -17,7 +17,12 @@ constexpr int kMaxFastSplits = 16;
 template <int NS>  // NS > 0: exactly NS splits, all loads in flight at once
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParams p, int G, int D) {
   const int dv4 = D >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  // the same XCD-aware order as the attention launches: XCD x merges the
+  // x-th eighth of the outputs, whose partials its own L2 wrote
+  const int nb = (int)gridDim.x;
+  const int bid = (nb & 7) == 0 ? (int)(blockIdx.x & 7) * (nb >> 3) + (int)(blockIdx.x >> 3)
+                                : (int)blockIdx.x;
+  const int64_t idx = (int64_t)bid * kCombineThreads + threadIdx.x;
   const int64_t total = (int64_t)p.units * p.T * G * dv4;
   if (idx >= total) return;
   const int d4 = (int)(idx % dv4);

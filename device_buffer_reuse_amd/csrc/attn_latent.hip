@@ -127,8 +127,14 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   constexpr int kFull = kTileInstr - (kInstr - 1) * NW;  // waves issuing kInstr copies
 
   const int nsplit = p.nsplit;
-  const int u = blockIdx.x / nsplit;
-  const int sp = blockIdx.x - u * nsplit;
+  // workgroups are dealt to the 8 XCDs in turn; when the grid divides by 8,
+  // XCD x takes the x-th eighth of the (request, split) range, so a
+  // request's splits, and later its combine, share one L2
+  const int nb = (int)gridDim.x;
+  const int bid = (nb & 7) == 0 ? (int)(blockIdx.x & 7) * (nb >> 3) + (int)(blockIdx.x >> 3)
+                                : (int)blockIdx.x;
+  const int u = bid / nsplit;
+  const int sp = bid - u * nsplit;
   const int j = p.token;
   const int uj = u * p.T + j;
   const int b = u;  // one latent head per request
