@@ -349,6 +349,19 @@ def main():
             "kernel": dominant,
             "per_launch": int(du[best]) if best != "flop" else du[best]}
 
+    # the whole step against its roofline: the larger of its algorithmic HBM
+    # time and its host-link time.  HBM: the selected rows (hits read, missed
+    # rows written into their slots, which the fused transfer never reads
+    # back), the metadata, queries and outputs; a separate gather also reads
+    # the missed rows back.
+    step_hbm = ab + match_bytes(w, miss_per_step) + (0.0 if fused else host_b)
+    t_hbm, t_link = step_hbm / (HBM_PEAK_GBS * 1e9), host_b / (HOST_LINK_GBS * 1e9)
+    t_step = ms / K * 1e-3
+    step_roof = {"hbm_bytes": int(step_hbm), "host_bytes": int(host_b),
+                 "t_hbm_us": round(t_hbm * 1e6, 2), "t_link_us": round(t_link * 1e6, 2),
+                 "bound": "host-link" if t_link >= t_hbm else "hbm",
+                 "frac": round(max(t_hbm, t_link) / t_step, 4)}
+
     extra = {}
     if not a.no_extra:
         # all-hit: step 0 fills the buffer, later steps reuse every entry
@@ -535,6 +548,7 @@ def main():
         "union_per_step": round(union_per_step, 1),
         "kernels": kernels,
         "roofline": roof,
+        "step_roofline": step_roof,
     }
     line.update(extra)
     if not a.no_cpu_baseline:
