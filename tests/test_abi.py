@@ -114,3 +114,21 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/avsg.h is a C header: it compiles as pedantic C99 (and C++)
+    with no HIP or torch headers."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use_avsg.c"
+    src.write_text('#include "avsg.h"\nint main(void) { avsg_config c; (void)c; '
+                   'return (int)AVSG_OK; }\n')
+    inc = os.path.join(ROOT, "include")
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++11")):
+        if shutil.which(cc) is None:
+            pytest.skip("%s not available" % cc)
+        lang = ["-x", "c++"] if cc == "g++" else []
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                            "-I", inc] + lang + [str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
