@@ -326,6 +326,8 @@ def main():
              "flop": (MFMA_BF16_TFLOPS if w.latent else FP32_VALU_TFLOPS, "TFLOP/s", 1e12)}
     kernels = {}
     for name, u in use.items():
+        if name == "gather" and fused:
+            continue   # not launched: the fused transfer runs inside the attention
         t = per[name] * 1e-3
         d = {"us": round(per[name] * 1e3, 2)}
         for res, (pk, unit, scale) in peaks.items():
