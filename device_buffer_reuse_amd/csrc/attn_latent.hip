@@ -11,10 +11,15 @@
 //  * A workgroup of Hq/16 waves owns `split_rows` selected tokens of one
 //    request; each wave owns 16 heads (their queries stay in 72 registers,
 //    their 16 x 512 accumulators in 128).
-//  * Rows are staged through three LDS tiles of 32 rows (rows padded to 1168
-//    bytes so the 16 rows an MFMA operand reads fall in distinct banks) by
-//    direct global-to-LDS loads, 16 bytes per lane, with no staging
-//    registers.  Two chunks are in flight while one is multiplied; each wave
+//  * Rows are staged through three LDS tiles of 32 rows by direct
+//    global-to-LDS loads, 16 bytes per lane, with no staging registers.
+//    Rows are padded to 1184 bytes and 16-byte piece c of tile row r sits
+//    at position c ^ swz(r), swz(r) = bit 2 of r xor bit 3 of r: with the 64
+//    four-byte LDS banks of gfx950 (and with 32) both operand reads are then
+//    free of bank conflicts (the K read, 16 rows x 16 bytes per 16 lanes,
+//    and the transposing V read, 8 rows x 32 bytes per 32 lanes).  swz
+//    depends on row bits 0..3 only, so rows r and r + 16 share it and the
+//    second half of a tile is reached by a constant offset.  Two chunks are in flight while one is multiplied; each wave
 //    issues the same number of copies per chunk, so a vmcnt wait with a
 //    constant count tells it that its copies of the chunk it needs have
 //    landed, and one barrier per chunk makes everybody's copies visible.
@@ -49,11 +54,11 @@ namespace {
 
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kChunk = 32;                       // tokens per LDS tile
-constexpr int kRow = kDqk + 8;                   // bf16 per padded LDS row (1168 B)
+constexpr int kRow = kDqk + 16;                  // bf16 per padded LDS row (1184 B)
 constexpr int kRowBytes = 2 * kRow;
-constexpr int kRowPieces = kRow / 8;             // 73 16-byte pieces per padded row
+constexpr int kRowPieces = kRow / 8;             // 74 16-byte pieces per padded row
 constexpr int kPiecesPerRow = kDqk / 8;          // 72 of them carry data
-constexpr int kTilePieces = kChunk * kRowPieces; // 2336
+constexpr int kTilePieces = kChunk * kRowPieces; // 2368
 constexpr int kTileInstr = (kTilePieces + 63) / 64;  // 37 wave-wide copies per tile
 constexpr int kTileElems = kChunk * kRow;
 constexpr int kKSteps = kDqk / 32;               // 18 MFMA k-steps for QK^T
@@ -76,6 +81,9 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<I + 1, N>(f);
   }
 }
+
+// position offset (xor) of the pieces of tile row r: bit 2 of r xor bit 3
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
     for (int x = 0; x < kInstr; ++x) {
       const int n = w + x * NW;
       if (n < kTileInstr) {  // wave-uniform
-        const int r = rc[x] >> 8, col = rc[x] & 255;
+        const int r = rc[x] >> 8, col = (rc[x] & 255) ^ swz(rc[x] >> 8);  // the row's piece
         const bool host = ri[x].y >= 0;
         const uint16_t* src = host ? hbase + (size_t)ri[x].y * kDqk + col * 8
                                    : ubase + (size_t)ri[x].x * kDqk + col * 8;
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
 #pragma unroll
     for (int x = 0; x < kInstr; ++x) {
       if (fetched & (1u << x)) {
-        const int col = rc[x] & 255;
+        const int col = (rc[x] & 255) ^ swz(rc[x] >> 8);
         *reinterpret_cast<u32x4*>(ubase + (size_t)ri[x].x * kDqk + col * 8) = d[x];
       }
     }
@@ -256,8 +264,12 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) fmask[i] = i < nchunks ? stage(i, i) : 0u;
   // per-lane operand addresses within a tile
-  const uint32_t k_off = li * kRowBytes + 16 * g;
-  const uint32_t v_off = (4 * g + (li >> 2)) * kRowBytes + 8 * (li & 3);
+  // K: row li, piece 4 ks + g.  V^T: row 4g + li/4, bytes 8 (li & 3) of the
+  // group's first 32 bytes (pieces 0, 1) and of its last 32 (pieces 2, 3)
+  const uint32_t k_off = li * kRowBytes + 16 * (g ^ swz(li));
+  const int vr_row = 4 * g + (li >> 2);
+  const uint32_t v_off0 = vr_row * kRowBytes + 16 * (((li & 3) >> 1) ^ swz(vr_row)) + 8 * (li & 1);
+  const uint32_t v_off1 = vr_row * kRowBytes + 16 * ((((li & 3) >> 1) | 2) ^ swz(vr_row)) + 8 * (li & 1);
 
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c % kBufs;
@@ -337,22 +349,23 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
       for (int t = 0; t < kMTiles; ++t) acc[t] *= corr;
     }
 
-    const uint32_t va = tile_lds + buf * kTileElems * 2 + v_off;
+    const uint32_t va0 = tile_lds + buf * kTileElems * 2 + v_off0;
+    const uint32_t va1 = tile_lds + buf * kTileElems * 2 + v_off1;
     u32x2 vr[2][4];
-    ds_tr<0>(vr[0][0], va);
-    ds_tr<16 * kRowBytes>(vr[0][1], va);
-    ds_tr<32>(vr[0][2], va);
-    ds_tr<32 + 16 * kRowBytes>(vr[0][3], va);
+    ds_tr<0>(vr[0][0], va0);
+    ds_tr<16 * kRowBytes>(vr[0][1], va0);
+    ds_tr<0>(vr[0][2], va1);
+    ds_tr<16 * kRowBytes>(vr[0][3], va1);
     // O^T += V^T P^T, output tiles in pairs.  k slot 8g+r is token 4g+r for
     // r < 4 and 16+4g+(r-4) otherwise, matching the probabilities above.
     static_for<0, kMTiles / 2>([&](auto pr_) {
       constexpr int pr = decltype(pr_)::value, st = pr & 1;
       if constexpr (pr + 1 < kMTiles / 2) {
         constexpr int o = 64 * (pr + 1);
-        ds_tr<o>(vr[st ^ 1][0], va);
-        ds_tr<o + 16 * kRowBytes>(vr[st ^ 1][1], va);
-        ds_tr<o + 32>(vr[st ^ 1][2], va);
-        ds_tr<o + 32 + 16 * kRowBytes>(vr[st ^ 1][3], va);
+        ds_tr<o>(vr[st ^ 1][0], va0);
+        ds_tr<o + 16 * kRowBytes>(vr[st ^ 1][1], va0);
+        ds_tr<o>(vr[st ^ 1][2], va1);
+        ds_tr<o + 16 * kRowBytes>(vr[st ^ 1][3], va1);
         asm volatile("s_waitcnt lgkmcnt(4)"
                      : "+v"(vr[st][0]), "+v"(vr[st][1]), "+v"(vr[st][2]), "+v"(vr[st][3]));
       } else {
