@@ -920,9 +920,11 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     }
     ev = wave_total(ev);
     if (lane == 0 && ev) atomicAdd(&sMisc[1], ev);
+    // the victims' union entries and the eviction count are read below; with
+    // no miss (m is the same in every wave) nothing was written since the
+    // probe's barrier, so only this branch needs one
+    __syncthreads();
   }
-
-  __syncthreads();
 
   // ---- 8. per-(token, entry) outputs read off the union
   for (int i = tid; i < tk; i += kMRThreads) {
