@@ -253,17 +253,27 @@ def cpu_baseline(w, t_start, seconds, threads=1):
     ob = oracle.OracleBuffer.for_workload(w)
     for t in range(t_start):
         ob.step(sel[t])
-    done, t0 = 0, time.perf_counter()
+    done, t0, t_state = 0, time.perf_counter(), 0.0
     t = t_start
     while time.perf_counter() - t0 < seconds and t < steps_needed:
+        ts = time.perf_counter()
         r = ob.step(sel[t])
+        t_state += time.perf_counter() - ts
         oatt.attend(w, tg.queries(w, t), host, sel[t], r["status"])
         done += 1
         t += 1
     el = time.perf_counter() - t0
     del lim
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": done * w.entries_per_step / el, "unit": "entries/s", "cores": threads,
             "kind": "oracle",
+            "state_only_value": done * w.entries_per_step / t_state,
+            "cpu_model": cpu,
             "sample": "%d decode steps (t=%d..%d) of the same workload, all %d units: C state "
                       "machine + float64 numpy attention, %s" % (
                           done, t_start, t_start + done - 1, w.units,
@@ -517,6 +527,19 @@ def main():
         torch.cuda.synchronize()
         extra["hbm_copy_GB/s"] = round(4 * 2 * xa.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
         del xa, xb
+        # a plain library bf16 GEMM (8192^3, contiguous operands): the matrix
+        # cores' reachable rate beside the 2.5 PFLOP/s dense specification
+        ga = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
+        gb = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16).contiguous()
+        gc = torch.mm(ga, gb)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(8):
+            torch.mm(ga, gb, out=gc)
+        e1.record()
+        torch.cuda.synchronize()
+        extra["gemm_bf16_TFLOP/s"] = round(8 * 2 * 8192.0 ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        del ga, gb, gc
     if a.ablations:
         extra["ablations"] = ablations(b, w, min(K, 32))
     if a.calibrate_copy:
