@@ -165,6 +165,21 @@ def match_bytes(w, misses_per_step):
     return tk * 4 + w.units * w.n_slots * 4 * 3 + tk * 5 + misses_per_step * (4 + 8)
 
 
+def step_roofline(attn_b, match_b, host_b, fused, t_step):
+    """The whole step against its roofline: the larger of its algorithmic HBM
+    time and its host-link time, over the measured step time t_step (s).
+    HBM: the attention's bytes (hits read, missed rows written into their
+    slots, which the fused transfer never reads back; metadata, queries and
+    outputs) and match_reserve's; a separate gather also reads the missed
+    rows back (host_b more)."""
+    step_hbm = attn_b + match_b + (0.0 if fused else host_b)
+    t_hbm, t_link = step_hbm / (HBM_PEAK_GBS * 1e9), host_b / (HOST_LINK_GBS * 1e9)
+    return {"hbm_bytes": int(step_hbm), "host_bytes": int(host_b),
+            "t_hbm_us": round(t_hbm * 1e6, 2), "t_link_us": round(t_link * 1e6, 2),
+            "bound": "host-link" if t_link >= t_hbm else "hbm",
+            "frac": round(max(t_hbm, t_link) / t_step, 4)}
+
+
 KERNEL_SOURCES = {"attention": ("attn_split_kernel<4>", ["attn_split.hip", "avsg_internal.h"]),
                   "match_reserve": ("match_reserve_kernel<8>", ["match_reserve.hip", "avsg_internal.h"])}
 
@@ -361,18 +376,7 @@ def main():
             "kernel": dominant,
             "per_launch": int(du[best]) if best != "flop" else du[best]}
 
-    # the whole step against its roofline: the larger of its algorithmic HBM
-    # time and its host-link time.  HBM: the selected rows (hits read, missed
-    # rows written into their slots, which the fused transfer never reads
-    # back), the metadata, queries and outputs; a separate gather also reads
-    # the missed rows back.
-    step_hbm = ab + match_bytes(w, miss_per_step) + (0.0 if fused else host_b)
-    t_hbm, t_link = step_hbm / (HBM_PEAK_GBS * 1e9), host_b / (HOST_LINK_GBS * 1e9)
-    t_step = ms / K * 1e-3
-    step_roof = {"hbm_bytes": int(step_hbm), "host_bytes": int(host_b),
-                 "t_hbm_us": round(t_hbm * 1e6, 2), "t_link_us": round(t_link * 1e6, 2),
-                 "bound": "host-link" if t_link >= t_hbm else "hbm",
-                 "frac": round(max(t_hbm, t_link) / t_step, 4)}
+    step_roof = step_roofline(ab, match_bytes(w, miss_per_step), host_b, fused, ms / K * 1e-3)
 
     extra = {}
     if not a.no_extra:

@@ -88,3 +88,18 @@ def test_counter_summary_is_refused_after_a_source_change(tmp_path, monkeypatch)
     assert bench.counter_traffic("attention", "allhit") is None
     # the other kernel's counters stay valid
     assert bench.counter_traffic("match_reserve", "allhit") is not None
+
+
+def test_step_roofline_takes_the_larger_time():
+    # 80 MB over 8 TB/s = 10 us of HBM, 0.64 MB over 64 GB/s = 10 us of link:
+    # a tie counts as host-link; a 20 us step reaches half of it
+    r = bench.step_roofline(70e6, 10e6, 0.64e6, True, 20e-6)
+    assert r["t_hbm_us"] == 10.0 and r["t_link_us"] == 10.0
+    assert r["bound"] == "host-link" and r["frac"] == 0.5
+    # a separate gather reads the missed rows back: host bytes count on HBM too
+    r = bench.step_roofline(70e6, 10e6, 8e6, False, 250e-6)
+    assert r["hbm_bytes"] == 88000000 and r["t_hbm_us"] == 11.0
+    assert r["bound"] == "host-link" and r["t_link_us"] == 125.0 and r["frac"] == 0.5
+    # no host traffic: HBM-bound
+    r = bench.step_roofline(70e6, 10e6, 0, True, 40e-6)
+    assert r["bound"] == "hbm" and r["frac"] == 0.25
