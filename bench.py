@@ -262,7 +262,7 @@ def cpu_baseline(w, t_start, seconds, threads=1):
     from threadpoolctl import threadpool_limits
     lim = threadpool_limits(threads)
     oracle.set_threads(threads)
-    steps_needed = t_start + 64
+    steps_needed = t_start + 192  # the time bound ends the sample first
     sel = tg.selections(w, steps=steps_needed)
     host = tg.fill_kv(w)
     ob = oracle.OracleBuffer.for_workload(w)
