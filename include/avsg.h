@@ -186,7 +186,8 @@ avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
  * at or past cap[u] (slot -1, lifetime 0 or stamp -1): shrinking a unit's
  * buffer drops the entries it held there, which stay exact in host memory.
  * cap[u] outside [1, S] is a range error and |U| > cap[u] a capacity error
- * of that unit (its state then stays untouched, as for every data error).
+ * of that unit (its state then stays untouched, as for every data error:
+ * a step with any data error leaves the slots past cap[u] as they were).
  * The pointer is kept by the context; the caller owns the array. */
 avsg_status avsg_set_capacity(avsg_ctx* ctx, const int32_t* cap);
 

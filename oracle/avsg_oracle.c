@@ -95,10 +95,12 @@ static int32_t find_sorted(const int32_t* a, int32_t n, int32_t x) {
  *                      length outside [1, k] is a range error.
  *   cap                slots this unit may use, [0, cap) (Spin summary,
  *                      section 2B: the buffer of each request is sized
- *                      dynamically); slots at or past cap are emptied before
- *                      the step (a shrink drops what they held).  A cap
- *                      outside [1, S] is a range error; |U| > cap is a
- *                      capacity error.
+ *                      dynamically); slots at or past cap take no part in
+ *                      the step and are emptied once every check has passed
+ *                      (a shrink drops what they held; an error, which
+ *                      leaves the whole state unchanged, takes precedence).
+ *                      A cap outside [1, S] is a range error; |U| > cap is
+ *                      a capacity error.
  *   slot_tok   [S]     in/out: id held by each slot, -1 = empty
  *   life       [S]     in/out: lifetime (lifetime policy) or last-selected
  *                      step (LRU policy; -1 for a slot never filled)
@@ -160,13 +162,9 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
   }
   if (status != OR_OK) { free(U); return status; }
 
-  /* slots past the capacity are emptied */
-  for (int32_t s = S; s < S_all; ++s) {
-    slot_tok[s] = -1;
-    life[s] = c->policy == OR_LRU ? -1 : 0;
-  }
-
-  /* 2. match U against the resident ids: two-pointer merge of two sorted lists */
+  /* 2. match U against the resident ids of the slots in use: two-pointer
+   *    merge of two sorted lists.  Nothing is written to the state until
+   *    this last check has passed. */
   resident_t* R = (resident_t*)malloc(sizeof(resident_t) * (size_t)S);
   int32_t nr = 0;
   for (int32_t s = 0; s < S; ++s)
@@ -194,6 +192,13 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
   }
   free(R);
   if (status != OR_OK) { free(U); free(uslot); free(uhit); free(selected_slot); return status; }
+
+  /* every check has passed: the slots past the capacity are emptied (they
+   * take no part in the match above, and are never candidates below) */
+  for (int32_t s = S; s < S_all; ++s) {
+    slot_tok[s] = -1;
+    life[s] = c->policy == OR_LRU ? -1 : 0;
+  }
 
   int32_t n_hit = 0;
   for (int32_t a = 0; a < nu; ++a) n_hit += uhit[a];

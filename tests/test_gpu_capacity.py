@@ -100,6 +100,44 @@ def test_capacity_errors_are_unit_errors():
         run.close()
 
 
+def test_state_error_with_shrink_keeps_state():
+    """A duplicated id of U in one unit while every unit's buffer shrinks:
+    that unit reports a state error and keeps all of its slots, the ones
+    past its size included (the error takes precedence over the shrink);
+    the other units shrink and step as the oracle says."""
+    avsg = ensure_lib()
+    w = CASES["token"].replace(steps=3)
+    say("[capacity] state error with a shrink")
+    sel = tg.selections(w)
+    run = Runner(w)
+    try:
+        for t in range(2):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+        bad = 1
+        st = run.st.slot_table[bad].cpu().numpy()
+        occ = np.nonzero(st >= 0)[0]
+        cap = w.k + 10
+        assert occ.max() >= cap, "an occupied slot past the new size"
+        below = occ[occ < cap]
+        x = int(np.intersect1d(st[below], sel[2][bad, 0])[0])
+        other = int(below[st[below] != x][0])
+        run.st.slot_table[bad, other] = x
+        run.ob.slot_tok[bad, other] = x
+        before = (run.st.slot_table[bad].cpu().numpy().copy(),
+                  run.st.lifetimes[bad].cpu().numpy().copy())
+        run.set_caps(np.full(w.units, cap, np.int32))
+        r, _ = run.step_and_compare(2, sel[2], tg.queries(w, 2), check_buf=True)
+        assert r["status"][bad] == avsg.ERR_STATE and (np.delete(r["status"], bad) == 0).all()
+        assert np.array_equal(run.st.slot_table[bad].cpu().numpy(), before[0])
+        assert np.array_equal(run.st.lifetimes[bad].cpu().numpy(), before[1])
+        good = run.st.slot_table.cpu().numpy()[np.arange(w.units) != bad]
+        assert (good[:, cap:] == -1).all()
+        assert run.ctx.last_error() == avsg.ERR_STATE
+        run.set_caps(None)
+    finally:
+        run.close()
+
+
 def test_plan_then_step():
     """The planner's capacities for the next step's unions, then the step."""
     avsg = ensure_lib()

@@ -395,6 +395,32 @@ def test_oracle_capacity_errors_change_nothing():
     assert st_ == oracle.OK and r["n_hit"] == k
 
 
+@pytest.mark.parametrize("policy", ["lifetime", "lru"])
+def test_oracle_state_error_with_shrink_changes_nothing(policy):
+    """A state error found while a smaller buffer size is set leaves every
+    slot untouched, the ones past the size included: the error takes
+    precedence over the shrink (an erroneous step changes no state)."""
+    S, N = 8, 64
+    life_occ = 3 if policy == "lifetime" else 0   # a valid lifetime / stamp at t = 1
+    empty = 0 if policy == "lifetime" else -1
+    # id 5 held by slots 1 and 5 (both below the size 6), slot 7 (past it) holds 20
+    tok = np.array([1, 5, 9, -1, -1, 5, -1, 20], np.int32)
+    life = np.array([life_occ, life_occ, life_occ, empty, empty, life_occ, empty, life_occ],
+                    np.int32)
+    before = (tok.copy(), life.copy())
+    st_, r = oracle.unit_step(S, N, 3, policy, 4, 64, 1, np.array([[1, 5, 9]], np.int32), tok,
+                              life, cap=6)
+    assert st_ == oracle.ERR_STATE
+    assert np.array_equal(tok, before[0]) and np.array_equal(life, before[1])
+    assert (r["sel_slot"] == -1).all() and not r["hit_flag"].any() and r["n_miss"] == 0
+    # the same state without the duplicate: the step runs and empties slot 7
+    tok[5], life[5] = -1, empty
+    st_, r = oracle.unit_step(S, N, 3, policy, 4, 64, 1, np.array([[1, 5, 9]], np.int32), tok,
+                              life, cap=6)
+    assert st_ == oracle.OK and r["n_hit"] == 3
+    assert tok[7] == -1 and life[7] == empty
+
+
 def test_plan_capacity_worked_example_and_invariants():
     from oracle.plan import plan_capacity
     # spare 6 shared 1 : 3 -> floor(6/4) = 1 and floor(18/4) = 4
