@@ -8,7 +8,9 @@ does, and shares no code with it.
 
   avsg_oracle.c   the state machine of one step per unit (plain C, qsort and
                   a two-pointer merge), compiled with gcc on first use
-  attention.py    float64 attention over the selected rows (numpy)
+  attention.c     float64 attention over the selected rows (plain C loops,
+                  OpenMP over (unit, token, head)), in the same library
+  attention.py    the same attention in numpy, and the wrapper of the C one
 
 Parity pins: the state machine is checked against a separate brute-force
 replay, hand-worked traces, closed forms and invariants; attention against
@@ -26,7 +28,7 @@ import numpy as np
 from . import attention  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "avsg_oracle.c")
+_SRCS = [os.path.join(_HERE, "avsg_oracle.c"), os.path.join(_HERE, "attention.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 _lock = threading.Lock()
@@ -37,10 +39,11 @@ LIFETIME, LRU = 0, 1
 
 def build(force: bool = False) -> str:
     """Compile liboracle.so with gcc: -O2, no intrinsics, OpenMP over units."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB_PATH) or any(
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(s) for s in _SRCS):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", _SRC,
-                               "-o", tmp])
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11"] + _SRCS +
+                              ["-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -48,6 +51,12 @@ def build(force: bool = False) -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_slots", "n_entries", "n_tokens", "k", "policy", "lifetime_L", "n_buckets")]
+
+
+class AttnCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "n_kv_heads", "n_q_heads", "n_tokens", "head_dim_qk", "head_dim_v",
+                 "latent", "tokens_per_entry", "n_entries", "k")] + [("scale", ctypes.c_double)]
 
 
 def _load():
@@ -64,6 +73,8 @@ def _load():
             lib.oracle_step.restype = None
             lib.oracle_set_threads.argtypes = [ctypes.c_int]
             lib.oracle_set_threads.restype = None
+            lib.oracle_attend.argtypes = [ctypes.POINTER(AttnCfg)] + [p] * 6
+            lib.oracle_attend.restype = None
             _lib = lib
     return _lib
 
@@ -74,7 +85,8 @@ def _p(a: np.ndarray) -> int:
 
 
 def set_threads(n: int) -> None:
-    """Threads of the state machine's OpenMP loop over units."""
+    """Threads of the OpenMP loops (state machine: over units; attention:
+    over (unit, token, head))."""
     _load().oracle_set_threads(int(n))
 
 

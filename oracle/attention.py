@@ -78,3 +78,33 @@ def attend(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=N
                                                      for jj in range(w.n_q_tokens)]
                 out[b, j, g * G:(g + 1) * G] = attend_unit(w, q_bits, host_kv[u], su, u, j)
     return out
+
+
+def attend_native(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=None,
+                  lengths=None, threads=None) -> np.ndarray:
+    """The same attention as `attend`, computed by the oracle library's C
+    loops in double precision (attention.c), with OpenMP over (unit, token,
+    head); every unit is computed.  threads: OpenMP threads (None: leave the
+    current setting)."""
+    import ctypes
+    from oracle import AttnCfg, _load, set_threads
+    lib = _load()
+    if threads is not None:
+        set_threads(threads)
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    assert host_kv.dtype == np.uint16 and host_kv.flags.c_contiguous
+    assert host_kv.shape == (w.units, w.n_entries, w.row_elems)
+    assert sel.shape == (w.units, w.n_q_tokens, w.k)
+    assert q_bits.shape == (w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_qk)
+    ln = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32).reshape(
+        w.units, w.n_q_tokens)
+    stt = None if status is None else np.ascontiguousarray(status, dtype=np.int32).reshape(w.units)
+    out = np.empty((w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_v), np.float64)
+    cfg = AttnCfg(w.batch, w.n_kv_heads, w.n_q_heads, w.n_q_tokens, w.head_dim_qk, w.head_dim_v,
+                  1 if w.latent else 0, w.tokens_per_entry, w.n_entries, w.k,
+                  float(w.softmax_scale))
+    lib.oracle_attend(ctypes.byref(cfg), q_bits.ctypes.data, host_kv.ctypes.data, sel.ctypes.data,
+                      None if ln is None else ln.ctypes.data, None if stt is None else stt.ctypes.data,
+                      out.ctypes.data)
+    return out

@@ -1,4 +1,5 @@
-"""Pins of the oracle's attention against a library routine and closed forms.
+"""Pins of the oracle's attention against a library routine and closed forms,
+for both of its forms: the numpy one and the C one (attention.c, OpenMP).
 CPU only."""
 from __future__ import annotations
 
@@ -17,13 +18,23 @@ def _tiny(latent=False, tpe=1, Hkv=2, G=4, dqk=16, dv=16, N=40, k=7, T=2, batch=
                                    n_slots=2 * T * k)
 
 
+IMPLS = ["numpy", "c"]
+
+
+def _attend(impl, w, q, host, sel, lengths=None):
+    if impl == "numpy":
+        return oatt.attend(w, q, host, sel, lengths=lengths)
+    return oatt.attend_native(w, q, np.ascontiguousarray(host), sel, lengths=lengths, threads=3)
+
+
 def _bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bits by truncation (test data only)."""
     return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+@pytest.mark.parametrize("impl", IMPLS)
 @pytest.mark.parametrize("layout", ["token", "page", "latent"])
-def test_matches_masked_sdpa(layout):
+def test_matches_masked_sdpa(layout, impl):
     """Attention over the selected set equals torch's scaled_dot_product_attention
     over ALL positions with a boolean mask that keeps the selected ones, with
     torch's own grouped-query head mapping (enable_gqa)."""
@@ -38,7 +49,7 @@ def test_matches_masked_sdpa(layout):
     q = _bits(rng.standard_normal((w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_qk)))
     sel = np.stack([np.stack([np.sort(rng.choice(w.n_entries, w.k, replace=False))
                               for _ in range(w.n_q_tokens)]) for _ in range(w.units)]).astype(np.int32)
-    out = oatt.attend(w, q, host, sel)
+    out = _attend(impl, w, q, host, sel)
 
     # dense K/V over every position of every unit, token-major
     tpe = w.tokens_per_entry
@@ -63,7 +74,8 @@ def test_matches_masked_sdpa(layout):
         np.testing.assert_allclose(out[:, j], ref[:, :, 0].numpy(), rtol=1e-12, atol=1e-12)
 
 
-def test_equal_keys_give_mean_of_values():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_equal_keys_give_mean_of_values(impl):
     """All selected keys equal => uniform weights => o = mean of the values."""
     w = _tiny(T=1, batch=1, Hkv=1)
     rng = np.random.default_rng(3)
@@ -71,23 +83,25 @@ def test_equal_keys_give_mean_of_values():
     host[0, :, :w.head_dim_qk] = host[0, 0, :w.head_dim_qk]
     q = _bits(rng.standard_normal((1, 1, w.n_q_heads, w.head_dim_qk)))
     sel = np.sort(rng.choice(w.n_entries, w.k, replace=False)).astype(np.int32)[None, None]
-    out = oatt.attend(w, q, host, sel)
+    out = _attend(impl, w, q, host, sel)
     V = oatt.bf16_to_f64(host[0, sel[0, 0], w.head_dim_qk:])
     np.testing.assert_allclose(out[0, 0], np.broadcast_to(V.mean(0), out[0, 0].shape), atol=1e-12)
 
 
-def test_single_entry_returns_its_value():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_single_entry_returns_its_value(impl):
     w = _tiny(T=1, batch=1, Hkv=1, k=1)
     rng = np.random.default_rng(4)
     host = _bits(rng.standard_normal((1, w.n_entries, w.row_elems)))
     q = _bits(rng.standard_normal((1, 1, w.n_q_heads, w.head_dim_qk)))
     sel = np.array([[[11]]], np.int32)
-    out = oatt.attend(w, q, host, sel)
+    out = _attend(impl, w, q, host, sel)
     V = oatt.bf16_to_f64(host[0, 11, w.head_dim_qk:])
     np.testing.assert_allclose(out[0, 0], np.broadcast_to(V, out[0, 0].shape), atol=0)
 
 
-def test_one_dominant_key():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_one_dominant_key(impl):
     """A key far more aligned with q than the others takes all the weight."""
     w = _tiny(T=1, batch=1, Hkv=1, G=1)
     host = np.zeros((1, w.n_entries, w.row_elems), np.float32)
@@ -95,11 +109,12 @@ def test_one_dominant_key():
     host[0, 9, :w.head_dim_qk] = 8.0
     q = np.full((1, 1, 1, w.head_dim_qk), 8.0, np.float32)
     sel = np.array([[[2, 5, 9, 20, 30, 31, 39]]], np.int32)
-    out = oatt.attend(w, _bits(q), _bits(host), sel)
+    out = _attend(impl, w, _bits(q), _bits(host), sel)
     np.testing.assert_allclose(out[0, 0, 0], 9.0, atol=1e-9)
 
 
-def test_lengths_attend_over_the_prefix_only():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_lengths_attend_over_the_prefix_only(impl):
     """With per-list lengths, attention equals masked SDPA over the first len
     entries; what follows them (here ids of other entries) plays no part."""
     w = _tiny(T=1)
@@ -109,7 +124,7 @@ def test_lengths_attend_over_the_prefix_only():
     sel = np.stack([np.sort(rng.choice(w.n_entries, w.k, replace=False))[None]
                     for _ in range(w.units)]).astype(np.int32)
     lens = rng.integers(1, w.k + 1, size=(w.units, 1)).astype(np.int32)
-    got = oatt.attend(w, q, host, sel, lengths=lens)
+    got = _attend(impl, w, q, host, sel, lengths=lens)
     hk = oatt.bf16_to_f64(host)
     G = w.n_q_heads // w.n_kv_heads
     for u in range(w.units):
@@ -123,3 +138,23 @@ def test_lengths_attend_over_the_prefix_only():
             qq, K.expand(1, G, -1, -1), V.expand(1, G, -1, -1), attn_mask=mask[None, None, None, :],
             scale=w.softmax_scale)[0, :, 0, :].numpy()
         assert np.allclose(got[b, 0, g * G:(g + 1) * G], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_native_threads_and_failed_units():
+    """The C attention gives the same bits on 1 and on 5 threads (each (unit,
+    token, head) is computed by one thread, in selection order), and a unit
+    whose step failed yields zeros."""
+    w = _tiny(tpe=2)
+    rng = np.random.default_rng(11)
+    host = _bits(rng.standard_normal((w.units, w.n_entries, w.row_elems)))
+    q = _bits(rng.standard_normal((w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_qk)))
+    sel = np.stack([np.stack([np.sort(rng.choice(w.n_entries, w.k, replace=False))
+                              for _ in range(w.n_q_tokens)]) for _ in range(w.units)]).astype(np.int32)
+    status = np.zeros(w.units, np.int32)
+    status[1] = 17
+    a = oatt.attend_native(w, q, host, sel, status, threads=1)
+    b = oatt.attend_native(w, q, host, sel, status, threads=5)
+    assert np.array_equal(a, b)
+    G = w.n_q_heads // w.n_kv_heads
+    assert (a[0, :, G:2 * G] == 0).all()   # unit 1 = request 0, KV head 1
+    np.testing.assert_allclose(a, oatt.attend(w, q, host, sel, status), rtol=1e-12, atol=1e-13)
