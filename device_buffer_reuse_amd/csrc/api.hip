@@ -5,6 +5,8 @@
 
 #include <new>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "avsg_internal.h"
 
 struct avsg_ctx {
@@ -355,10 +357,18 @@ static avsg_status device_view_of_pinned(avsg_ctx* ctx, const void* host, const 
   return AVSG_OK;
 }
 
+// A roctx range over the host-side enqueue of one call (a step or an
+// append), so a trace with markers shows each call's kernels under its name.
+struct RoctxRange {
+  explicit RoctxRange(const char* name) { roctxRangePushA(name); }
+  ~RoctxRange() { roctxRangePop(); }
+};
+
 static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_t* sel_len,
                              const uint16_t* q, const uint16_t* host_kv, uint16_t* buf_kv,
                              int32_t* slot_table, int32_t* lifetimes, float* out,
                              const avsg_hit_stats* hs) {
+  RoctxRange range(sel_len ? "avsg_step_varlen" : "avsg_step");
   if (!ctx || !sel_idx || !q || !host_kv || !buf_kv || !slot_table || !lifetimes || !out || !hs ||
       !hs->hit_flag || !hs->sel_slot || !hs->n_hit || !hs->n_miss || !hs->n_evict)
     return AVSG_ERR_INVALID_ARG;
@@ -557,6 +567,7 @@ avsg_status avsg_plan_capacity(int32_t units, const int32_t* demand, const int32
 
 avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
                         uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table) {
+  RoctxRange range("avsg_append");
   if (!ctx || !new_kv || !pos || !host_kv || !buf_kv || !slot_table) return AVSG_ERR_INVALID_ARG;
   if (((uintptr_t)new_kv | (uintptr_t)host_kv | (uintptr_t)buf_kv) & 15)
     return AVSG_ERR_INVALID_ARG;

@@ -64,30 +64,90 @@ def test_match_bytes_of_the_batch_workload():
     assert bench.match_bytes(w, 100) - bench.match_bytes(w, 0) == 100 * 12
 
 
-def test_counter_summary_is_read_for_the_current_source():
-    for kernel in ("attention", "match_reserve"):
-        for trace in ("allhit", "natural"):
-            v = bench.counter_traffic(kernel, trace)
-            assert isinstance(v, int) and v > 0, (kernel, trace)
-    # the attention reads at least its algorithmic bytes
-    assert bench.counter_traffic("attention", "allhit") >= bench.attn_bytes(tg.WORKLOADS[2])
-    assert bench.counter_traffic("combine", "allhit") is None
-    assert bench.counter_traffic("attention", "skewed") is None
+def _counters_file(root, kernels):
+    """A counter summary in the committed format, for the long workload."""
+    import json
+    body = {"calibration": {"fetch_scale": 2.0, "write_scale": 1.0}, "kernels": kernels}
+    (root / "profiles").mkdir(parents=True, exist_ok=True)
+    (root / "profiles" / "counters_long.md").write_text(
+        "# counters\n\n```json\n" + json.dumps(body, indent=1) + "\n```\n")
+
+
+def _copy_sources(root):
+    shutil.copytree(os.path.join(bench.ROOT, "device_buffer_reuse_amd", "csrc"),
+                    root / "device_buffer_reuse_amd" / "csrc")
+
+
+def test_counter_summary_is_read_for_the_current_source(tmp_path, monkeypatch):
+    root = tmp_path / "repo"
+    _copy_sources(root)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    name = bench.KERNEL_SOURCES["attention"][4]
+    _counters_file(root, {name: {"source_sha256_16": bench.kernel_source_hash(name),
+                                 "read_bytes_natural": 300, "write_bytes_natural": 40,
+                                 "read_bytes_allhit": 200, "write_bytes_allhit": 4}})
+    assert bench.counter_traffic("attention", "natural", 4) == 340
+    assert bench.counter_traffic("attention", "allhit", 4) == 204
+    assert bench.counter_traffic("attention", "skewed", 4) is None
+    assert bench.counter_traffic("combine", "natural", 4) is None
+    assert bench.counter_traffic("match_reserve", "natural", 4) is None
 
 
 def test_counter_summary_is_refused_after_a_source_change(tmp_path, monkeypatch):
     root = tmp_path / "repo"
-    (root / "profiles").mkdir(parents=True)
-    shutil.copy(os.path.join(bench.ROOT, "profiles", "counters_batch.md"), root / "profiles")
-    shutil.copytree(os.path.join(bench.ROOT, "device_buffer_reuse_amd", "csrc"),
-                    root / "device_buffer_reuse_amd" / "csrc")
+    _copy_sources(root)
     monkeypatch.setattr(bench, "ROOT", str(root))
-    assert bench.counter_traffic("attention", "allhit") is not None
+    att, mr = bench.KERNEL_SOURCES["attention"][4], bench.KERNEL_SOURCES["match_reserve"][4]
+    _counters_file(root, {n: {"source_sha256_16": bench.kernel_source_hash(n),
+                              "read_bytes_natural": 10, "write_bytes_natural": 1} for n in (att, mr)})
+    assert bench.counter_traffic("attention", "natural", 4) == 11
     src = root / "device_buffer_reuse_amd" / "csrc" / "attn_split.hip"
     src.write_text(src.read_text() + "\n// changed\n")
-    assert bench.counter_traffic("attention", "allhit") is None
+    assert bench.counter_traffic("attention", "natural", 4) is None
     # the other kernel's counters stay valid
-    assert bench.counter_traffic("match_reserve", "allhit") is not None
+    assert bench.counter_traffic("match_reserve", "natural", 4) == 11
+
+
+def test_committed_counter_summaries_parse():
+    """Every committed counter summary holds a JSON block with per-kernel
+    source hashes and byte counts."""
+    import glob
+    import json
+    import re
+    for path in glob.glob(os.path.join(bench.ROOT, "profiles", "counters_*.md")):
+        m = re.search(r"```json\n(.*?)```", open(path).read(), re.S)
+        if not m:
+            continue
+        data = json.loads(m.group(1))
+        for name, k in data["kernels"].items():
+            assert len(k["source_sha256_16"]) == 16, (path, name)
+            assert any(key.startswith("read_bytes_") for key in k), (path, name)
+
+
+def test_dominant_roofline_picks_the_longest_kernel_and_its_resource():
+    w = tg.WORKLOADS[4]
+    use = bench.kernel_use(w, miss_per_step=2000, union_per_step=256 * 128, fused=True)
+    per = {"match_reserve": 6.0, "gather": 0.0, "attention": 300.0, "combine": 4.0}
+    r = bench.dominant_roofline(use, per)
+    assert r["kernel"] == "attention" and r["bound"] == "host-link"
+    host = 2000 * w.row_bytes
+    assert r["achieved"] == round(host / 300e-6 / 1e9, 2) and r["frac"] == round(host / 300e-6 / 64e9, 4)
+    # all hits: no host bytes, the attention is HBM-bound
+    use = bench.kernel_use(w, miss_per_step=0, union_per_step=256 * 128, fused=True)
+    r = bench.dominant_roofline(use, {"match_reserve": 6.0, "gather": 0.0, "attention": 50.0,
+                                      "combine": 4.0})
+    assert r["bound"] == "hbm" and r["per_step_work"] == bench.attn_bytes(w)
+    # the latent attention's flops are priced at the bf16 matrix-core peak
+    t = bench.kernel_table(bench.kernel_use(tg.WORKLOADS[5], 0, 64 * 2048, True),
+                           {"match_reserve": 10.0, "gather": 0.0, "attention": 50.0,
+                            "combine": 10.0}, True)
+    assert t["attention"]["flop_frac"] == round(bench.attn_flops(tg.WORKLOADS[5]) / 50e-6 / 2.5e15, 4)
+    assert "gather" not in t
+
+
+def test_bench_arguments_default_to_the_long_context_workload():
+    a = bench.parse([])
+    assert a.workload == 4 and a.passes >= 5 and a.fill >= 64 and a.gpus == 1
 
 
 def test_step_roofline_takes_the_larger_time():
