@@ -34,9 +34,14 @@
 //  * Rows whose entry missed are copied from pinned host memory into the tile;
 //    the lane that copied a piece then stores it from LDS into the entry's
 //    slot, so the row crosses the host link once.  When the grid runs in
-//    several rounds of resident workgroups, a workgroup instead first copies
-//    all of its split's missed entries from host memory into their slots
-//    (every host read in flight at once) and then streams only from HBM.
+//    several rounds of resident workgroups, the workgroup has a second wave
+//    instead, which copies all of the split's missed entries from host memory
+//    into their slots (every host read in flight at once) while the first
+//    wave streams the split's tiles from HBM in selection order; the first
+//    wave waits (on an LDS flag) only at the first tile that holds a missed
+//    row.  The host link then stays busy while tiles stream: with one wave
+//    doing both, all resident workgroups fetched, then all streamed, in
+//    lock-step rounds.
 //  * All LDS reads of the tiles are inline assembly with waits tied to their
 //    results: the compiler would otherwise order every LDS read after all
 //    outstanding global-to-LDS copies.
@@ -48,6 +53,7 @@
 //    timing.  (Merging inside the last workgroup of each (unit, token) needs
 //    an agent-scope release in every workgroup, which writes back the XCD's
 //    L2 each time and cost more than the extra launch.)
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -67,6 +73,7 @@ constexpr int kThreads = 64;                         // one wave per workgroup
 constexpr int kSplitRows = 256;                      // token rows per workgroup
 constexpr int kKSteps = kD / 32;                     // 4 MFMA k-steps for QK^T
 constexpr int kDTiles = kD / 16;                     // 8 output tiles of 16 dimensions
+constexpr int kGatherDepth = 4;                      // gather-first: host loads per lane per round
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -96,9 +103,19 @@ __device__ __forceinline__ void ds_tr(u32x2& d, uint32_t a) {
 __device__ __forceinline__ void ds_b64(int2& d, uint32_t a) {
   asm volatile("ds_read_b64 %0, %1" : "=v"(d) : "v"(a));
 }
+__device__ __forceinline__ void ds_b32(int& d, uint32_t a) {
+  asm volatile("ds_read_b32 %0, %1" : "=v"(d) : "v"(a));
+}
 template <int OFF>
 __device__ __forceinline__ void ds_u64(uint64_t& d, uint32_t a) {
   asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(d) : "v"(a), "n"(OFF));
+}
+// LDS word read that completes before the next instruction (an LDS flag
+// polled while global-to-LDS copies of other addresses are in flight)
+__device__ __forceinline__ int ds_i32_now(uint32_t a) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -119,13 +136,19 @@ __device__ __forceinline__ float col_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
+// GF (gather-first): two waves per workgroup, wave 1 fetching the split's
+// missed entries into their slots while wave 0 computes; else one wave that
+// copies missed rows from host memory into its tiles.
+template <int G, bool GF>
+__global__ __launch_bounds__(GF ? 2 * kThreads : kThreads)
+__attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sTile[];  // [kBufs][kTileBytes]
   __shared__ int2 sRow[kSplitRows];      // per entry of the split: (slot, host id or -1)
   __shared__ int32_t sHost[kSplitRows];  // entries to fetch (gather-first)
   __shared__ uint64_t sSrc[kBufs][kChunk];  // per tile row: source address
   __shared__ uint64_t sDst[kBufs][kChunk];  // per tile row: slot address (host rows)
+  __shared__ int32_t sGathered;          // gather-first: wave 1 has stored every missed entry
+  __shared__ int32_t sNHost;             // gather-first: entries to fetch
 
   const int nsplit = p.nsplit;
   // workgroups are dealt to the 8 XCDs in turn (workgroup i on XCD i mod 8);
@@ -140,7 +163,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   const int j = p.token;
   const int uj = u * p.T + j;
   const int b = u / p.Hkv, g = u - b * p.Hkv;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kThreads - 1);
+  const int wave = GF ? (int)(threadIdx.x / kThreads) : 0;  // GF: 0 computes, 1 fetches
   const int gq = lane >> 4, li = lane & 15;  // lane group (rows / dims), column (head)
   const int tpe = p.tpe;
   // a shortened list (length array): its first sel_len[u][j] entries; a
@@ -164,15 +188,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   // slot array instead and are ignored
   const bool has_fetch = p.fetch != nullptr;
   const uint8_t* fl_src = has_fetch ? p.fetch : reinterpret_cast<const uint8_t*>(p.sel_slot);
-#pragma unroll
-  for (int k = 0; k < kEnt; ++k) {
-    const size_t at = (size_t)uj * p.k + e0 + min(k * kThreads + lane, ne - 1);
-    slot_v[k] = p.sel_slot[at];
-    id_v[k] = p.sel[at];
-    fl_v[k] = fl_src[at];
-  }
   bf16x8 qf[kKSteps];
-  {
+  if (wave == 0) {  // (gather-first: wave 1 reads the split's entries from LDS)
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) {
+      const size_t at = (size_t)uj * p.k + e0 + min(k * kThreads + lane, ne - 1);
+      slot_v[k] = p.sel_slot[at];
+      id_v[k] = p.sel[at];
+      fl_v[k] = fl_src[at];
+    }
     const uint16_t* qrow =
         p.q + (((size_t)b * p.T + j) * p.Hq + g * G + (li < G ? li : 0)) * kD + 8 * gq;
 #pragma unroll
@@ -186,26 +210,32 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   for (int k = 0; k < kEnt; ++k) asm volatile("" ::"v"(slot_v[k]), "v"(id_v[k]), "v"(fl_v[k]));
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qf[ks]));
-  if (__builtin_amdgcn_readfirstlane(ustat) != 0) {
-    if (nsplit == 1)
+  if (__builtin_amdgcn_readfirstlane(ustat) != 0) {  // the same in both waves
+    if (nsplit == 1 && wave == 0)
       for (int idx = lane; idx < G * kD; idx += kThreads) orow[idx] = 0.f;
     return;
   }
-  int nhost = 0;  // entries of the split to fetch (gather-first)
+  if (wave == 0) {
+    int nhost = 0;  // entries of the split to fetch (gather-first)
 #pragma unroll
-  for (int k = 0; k < kEnt; ++k) {
-    const int i = k * kThreads + lane;
-    const bool fetch = has_fetch && i < ne && fl_v[k] != 0;
-    if (i < ne) sRow[i] = make_int2(slot_v[k], fetch ? id_v[k] : -1);
-    if (p.gather_first) {
-      const uint64_t m = __builtin_amdgcn_ballot_w64(fetch);
-      if (fetch)
-        sHost[nhost + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = i;
-      nhost += __popcll(m);
+    for (int k = 0; k < kEnt; ++k) {
+      const int i = k * kThreads + lane;
+      const bool fetch = has_fetch && i < ne && fl_v[k] != 0;
+      if (i < ne) sRow[i] = make_int2(slot_v[k], fetch ? id_v[k] : -1);
+      if (GF) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(fetch);
+        if (fetch)
+          sHost[nhost + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = i;
+        nhost += __popcll(m);
+      }
+    }
+    if (GF && lane == 0) {
+      sNHost = nhost;
+      sGathered = 0;
     }
   }
-  __syncthreads();  // sRow, sHost
+  __syncthreads();  // sRow, sHost, sNHost, sGathered
   // the queries are in registers before any copy is issued
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
@@ -216,41 +246,73 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   const uint32_t row_lds = lds_addr(sRow);
   const uint32_t tile_lds = lds_addr(sTile);
 
-  // Gather-first: the split's missed entries go from pinned host memory into
-  // their slots before any tile, all of the workgroup's host reads in flight
-  // together (8 16-byte pieces per lane per round), and the tiles then read
-  // them from HBM.  Chosen when the grid runs in several rounds of resident
-  // workgroups: the host latency is then paid once per workgroup.
-  if (p.gather_first && nhost > 0) {
+  // Gather-first, wave 1: the split's missed entries go from pinned host
+  // memory into their slots, kGatherDepth 16-byte pieces per lane in flight
+  // per round; once every store is complete, the flag tells wave 0 that the
+  // tiles may copy those slots.  Wave 1 then exits.
+  if (GF && wave == 1) {
+    const int nhost = sNHost;
     const int pe = p.row_elems >> 3;  // 16-byte pieces per entry
     const int total = nhost * pe;
-    for (int q0 = 0; q0 < total; q0 += 8 * kThreads) {
-      u32x4 v[8];
+    const uint32_t host_lds = lds_addr(sHost);
+    // per round: the entries of this lane's kGatherDepth pieces (LDS reads
+    // in inline assembly, so that the compiler does not order them behind
+    // the stores of the previous round), then the host loads and the slot
+    // stores, each back to back.  Piece indices are clamped into the list: a lane past its
+    // end re-reads the list's last piece and writes the same 16 bytes to the
+    // same place as the lane that owns it, so no branch (and no wait per
+    // store) is needed.
+    for (int q0 = 0; q0 < total; q0 += kGatherDepth * kThreads) {
+      int qv[kGatherDepth], ev[kGatherDepth];
+      int2 rv[kGatherDepth];
 #pragma unroll
-      for (int bq = 0; bq < 8; ++bq) {
-        const int q = q0 + bq * kThreads + lane;
-        if (q < total) {
-          const int k = q / pe, col = q - k * pe;
-          v[bq] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-              hbase + (size_t)(uint32_t)sRow[sHost[k]].y * p.row_elems + col * 8));
-        }
+      for (int bq = 0; bq < kGatherDepth; ++bq) {
+        qv[bq] = min(q0 + bq * kThreads + lane, total - 1);
+        ds_b32(ev[bq], host_lds + 4 * (qv[bq] / pe));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int bq = 0; bq < kGatherDepth; ++bq) asm volatile("" : "+v"(ev[bq]));
+#pragma unroll
+      for (int bq = 0; bq < kGatherDepth; ++bq) ds_b64(rv[bq], row_lds + 8 * ev[bq]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int bq = 0; bq < kGatherDepth; ++bq) asm volatile("" : "+v"(rv[bq]));
+      u32x4 v[kGatherDepth];
+#pragma unroll
+      for (int bq = 0; bq < kGatherDepth; ++bq) {
+        const int col = qv[bq] - (qv[bq] / pe) * pe;
+        v[bq] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            hbase + (size_t)(uint32_t)rv[bq].y * p.row_elems + col * 8));
       }
 #pragma unroll
-      for (int bq = 0; bq < 8; ++bq) {
-        const int q = q0 + bq * kThreads + lane;
-        if (q < total) {
-          const int k = q / pe, col = q - k * pe;
-          *reinterpret_cast<u32x4*>(ubase + (size_t)(uint32_t)sRow[sHost[k]].x * p.row_elems +
-                                    col * 8) = v[bq];
-        }
+      for (int bq = 0; bq < kGatherDepth; ++bq) {
+        const int col = qv[bq] - (qv[bq] / pe) * pe;
+        *reinterpret_cast<u32x4*>(ubase + (size_t)(uint32_t)rv[bq].x * p.row_elems + col * 8) =
+            v[bq];
       }
     }
-    __syncthreads();  // every read of sRow above is done
-    for (int k = lane; k < nhost; k += kThreads) sRow[sHost[k]].y = -1;
-    // the stores are in L2 before the tiles copy those rows into LDS
-    vm_wait<0>();
-    __syncthreads();
+    vm_wait<0>();  // the stores are complete (in L2) before the flag is raised
+    if (lane == 0) __hip_atomic_store(&sGathered, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return;
   }
+  // gather-first, wave 0: the first tile that holds a missed row (ntiles if
+  // none); the tiles before it are staged at once, and wave 1's flag is
+  // awaited once, right before that tile is staged
+  int t_miss = 1 << 30;
+  if (GF) {
+    const int nhost = sNHost;
+    if (nhost > 0) {
+      const int first_row = max((e0 + sHost[0]) * tpe - r0, 0);  // sHost is in entry order
+      t_miss = first_row / kChunk;
+    }
+  }
+  auto await_gathered = [&]() {
+    // wave 1 raises the flag after its slot stores are complete; the tile
+    // copies that follow are issued only after the raised flag has been read
+    while (__builtin_amdgcn_readfirstlane(ds_i32_now(lds_addr(&sGathered))) == 0)
+      __builtin_amdgcn_s_sleep(2);
+  };
 
   // Entry of a row: r itself for token entries, else r / tpe by an exact
   // multiply-high with ceil(2^32 / tpe) (exact while r * tpe < 2^32).
@@ -279,7 +341,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
     int2 ri;
     ds_b64(ri, row_lds + 8 * (e - e0));
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ri)::"memory");
-    const bool host = ri.y >= 0;
+    // gather-first: every row is read from its slot (the tiles that hold a
+    // missed row are staged only after wave 1 has stored all of them)
+    const bool host = !GF && ri.y >= 0;
     const uint32_t in_entry = (uint32_t)((r - e * tpe) * kD);
     const uint16_t* src = (host ? hbase : ubase) +
                           (uint64_t)(uint32_t)(host ? ri.y : ri.x) * (uint32_t)p.row_elems + in_entry;
@@ -342,7 +406,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   // fmask[i]: the host rows of tile t + i
   uint32_t fmask[kAhead];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) fmask[i] = i < ntiles ? stage(i, i) : 0u;
+  for (int i = 0; i < kAhead; ++i) {
+    if (GF && i == t_miss) await_gathered();
+    fmask[i] = i < ntiles ? stage(i, i) : 0u;
+  }
   // per-lane operand addresses within a tile (rows 16..31: +8192): K row li,
   // dims 32 ks + 8 gq .. +8 (piece 4 ks + gq); V^T row R = 4 gq + li / 4, dims
   // 32 pr + 16 vb + 4 (li % 4) .. +4 (V piece 4 pr + 2 vb + (li % 4) / 2, byte
@@ -360,7 +427,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
                                8 * (li & 1);
   }
 
-  for (int t = 0; t < ntiles; ++t) {
+  // one tile: wait for its copies, stage tile t + kAhead, compute
+  auto tile_step = [&](int t) {
     const int buf = t % kBufs;
     // tile t has landed once only the copies of the later tiles in flight
     // (kCopies each) and later slot stores may still be outstanding
@@ -458,7 +526,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
       acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vta, plo, acc[2 * pr], 0, 0, 0);
       acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vtb, plo, acc[2 * pr + 1], 0, 0, 0);
     });
+  };
+  int t = 0;
+  if (GF) {
+    // iterations that stage only tiles before t_miss, then the one wait
+    // (when t_miss < kAhead it was taken before the first tiles were staged)
+    for (const int t_end = min(ntiles, t_miss - kAhead); t < t_end; ++t) tile_step(t);
+    if (t_miss >= kAhead && t_miss < ntiles) await_gathered();
   }
+  for (; t < ntiles; ++t) tile_step(t);
 
   // lane holds O[head li][d = 16 t + 4 gq + i] (heads li < G are real)
   if (li >= G) return;
@@ -482,30 +558,52 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
 
 }  // namespace
 
+// Workgroups of the one-wave form that device `dev` holds at once, per
+// grouped-query width (index log2 G), computed once per device.
+constexpr int kMaxDevices = 64;
+static std::mutex g_resident_mutex;
+static int g_resident[kMaxDevices][4];
+
+template <int G>
+static hipError_t resident_workgroups(int* out) {
+  constexpr int gi = G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3));
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_resident_mutex);
+  if (g_resident[dev][gi] == 0) {
+    int cus = 0, per_cu = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<G, false>,
+                                                       kThreads, kBufs * kTileBytes);
+    if (e != hipSuccess) return e;
+    g_resident[dev][gi] = cus * per_cu > 0 ? cus * per_cu : 1;
+  }
+  *out = g_resident[dev][gi];
+  return hipSuccess;
+}
+
 template <int G>
 static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
   // one launch per query token: a row that several tokens select is fetched
   // by the first of them, and later tokens read it from the buffer
   const dim3 grid((unsigned)(p0.units * p0.nsplit));
-  static int resident = 0;  // workgroups the device holds at once
-  if (resident == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipFuncSetAttribute((const void*)attn_split_kernel<G>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kBufs * kTileBytes) !=
-            hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<G>, kThreads,
-                                                     kBufs * kTileBytes) != hipSuccess)
-      return hipErrorUnknown;
-    resident = cus * per_cu;
-  }
+  int resident = 0;
+  hipError_t e = resident_workgroups<G>(&resident);
+  if (e != hipSuccess) return e;
+  // the two-wave gather-first form when the grid runs in several rounds of
+  // resident workgroups (or when asked for)
+  const bool gf = p0.gather_first != 0 || (int64_t)grid.x > resident;
   AttnParams p = p0;
-  if ((int64_t)grid.x > resident) p.gather_first = 1;
   for (int j = 0; j < p0.T; ++j) {
     p.token = j;
-    hipLaunchKernelGGL(attn_split_kernel<G>, grid, dim3(kThreads), kBufs * kTileBytes, s, p);
-    hipError_t e = hipGetLastError();
+    if (gf)
+      hipLaunchKernelGGL((attn_split_kernel<G, true>), grid, dim3(2 * kThreads), kBufs * kTileBytes,
+                         s, p);
+    else
+      hipLaunchKernelGGL((attn_split_kernel<G, false>), grid, dim3(kThreads), kBufs * kTileBytes, s,
+                         p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -272,14 +272,16 @@ const char* avsg_status_string(avsg_status s);
  *    so host transfers overlap the HBM reads of the hits; the rows are spread
  *    over all workgroups in selection order.  In the K/V split layout each
  *    workgroup either copies its missed rows with the tiles that hold them
- *    (when all workgroups are resident at once) or first gathers all of them
- *    into their slots (when the grid runs in several rounds).
+ *    (when all workgroups are resident at once) or, when the grid runs in
+ *    several rounds, has a second wave that gathers all of them into their
+ *    slots while the first streams the tiles before the first missed row.
  *  AVSG_TRANSFER_BALANCED: a separate kernel copies the global list of missed
  *    rows, split into equal shares over all workgroups, before attention.
  *  AVSG_TRANSFER_PER_UNIT: like BALANCED, but each unit's rows are copied by
  *    one workgroup (request-level assignment; kept for comparison).
- *  AVSG_TRANSFER_FUSED_GATHER_FIRST: FUSED with the gather-first form in the
- *    split layout whatever the grid size (the latent layout: as FUSED).
+ *  AVSG_TRANSFER_FUSED_GATHER_FIRST: FUSED with the two-wave gather-first
+ *    form in the split layout whatever the grid size (the latent layout: as
+ *    FUSED).
  * Results are identical in every mode. */
 typedef enum avsg_transfer_mode {
   AVSG_TRANSFER_FUSED = 0,
