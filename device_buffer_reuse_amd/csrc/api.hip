@@ -3,6 +3,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include <rocprofiler-sdk-roctx/roctx.h>
@@ -19,8 +20,6 @@ struct avsg_ctx {
   int gather_grid;
   char* workspace;
   int64_t t;
-  const void* pinned_checked;    // last host_kv pointer found pinned
-  const void* pinned_device;     // its device-visible address
   int32_t transfer_mode;         // avsg_transfer_mode
   int32_t match_mode;            // avsg_match_mode
   const int32_t* cap;            // device [units] buffer size of each unit, or null (S)
@@ -116,6 +115,47 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   return true;
 }
 
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+  int num_cus;
+  int lds_max;          // dynamic LDS a kernel of this device may be launched with
+};
+static std::mutex g_dev_mutex;
+static bool g_dev_ready[kMaxDevices];
+static DeviceInfo g_dev[kMaxDevices];
+
+// Once per device, with that device current: its unit count and LDS limit,
+// and the LDS limits of the kernels that need more than the default (set to
+// the device maximum, so contexts with different sizes never lower each
+// other's).
+static avsg_status device_setup(int* dev_out, DeviceInfo* info) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return AVSG_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return AVSG_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  if (!g_dev_ready[dev]) {
+    DeviceInfo di{};
+    if (hipDeviceGetAttribute(&di.num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&di.lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        match_reserve_set_lds((size_t)di.lds_max) != hipSuccess ||
+        attn_latent_set_lds() != hipSuccess) {
+      (void)hipGetLastError();
+      return AVSG_ERR_HIP;
+    }
+    g_dev[dev] = di;
+    g_dev_ready[dev] = true;
+  }
+  *dev_out = dev;
+  *info = g_dev[dev];
+  return AVSG_OK;
+}
+
+// The separate gather kernel keeps the prefix of all units' miss counts in
+// the default LDS of a workgroup.
+static bool gather_fits(int units) { return 4 * ((size_t)units + 1) <= 64 * 1024; }
+
 }  // namespace avsg
 
 using namespace avsg;
@@ -203,30 +243,16 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->cfg = *cfg;
   layout_for(*cfg, &c->ws, &c->d);
   if (ws_bytes < c->ws.total) { delete c; return AVSG_ERR_INVALID_ARG; }
-  if (hipGetDevice(&c->device) != hipSuccess) { delete c; return AVSG_ERR_HIP; }
-  int lds_max = 0;
-  if (hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device) !=
-          hipSuccess ||
-      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) !=
-          hipSuccess) {
-    delete c;
-    return AVSG_ERR_HIP;
-  }
+  DeviceInfo di;
+  st = device_setup(&c->device, &di);
+  if (st != AVSG_OK) { delete c; return st; }
+  c->num_cus = di.num_cus;
+  const int lds_max = di.lds_max;
   if ((int64_t)c->d.mr_lds > lds_max) { delete c; return AVSG_ERR_UNSUPPORTED; }
-  if (c->d.mr_lds > 64 * 1024 && match_reserve_set_lds(c->d.mr_lds) != hipSuccess) {
-    delete c;
-    return AVSG_ERR_HIP;
-  }
-  if (cfg->kv_layout == AVSG_KV_LATENT && attn_latent_set_lds() != hipSuccess) {
-    delete c;
-    return AVSG_ERR_HIP;
-  }
   c->gather_grid = c->num_cus * 2;
   c->stream = (hipStream_t)stream;
   c->workspace = (char*)workspace;
   c->t = 0;
-  c->pinned_checked = nullptr;
-  c->pinned_device = nullptr;
   c->cap = nullptr;
   c->prof_events = nullptr;
   c->prof_max = c->prof_used = 0;
@@ -245,6 +271,8 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
 avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode) {
   if (!ctx || mode < AVSG_TRANSFER_FUSED || mode > AVSG_TRANSFER_FUSED_GATHER_FIRST)
     return AVSG_ERR_INVALID_ARG;
+  if ((mode == AVSG_TRANSFER_BALANCED || mode == AVSG_TRANSFER_PER_UNIT) && !gather_fits(ctx->d.units))
+    return AVSG_ERR_UNSUPPORTED;
   ctx->transfer_mode = mode;
   return AVSG_OK;
 }
@@ -252,10 +280,9 @@ avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode) {
 avsg_status avsg_set_match_mode(avsg_ctx* ctx, int32_t mode) {
   if (!ctx || (mode != AVSG_MATCH_HASH && mode != AVSG_MATCH_MERGE && mode != AVSG_MATCH_HASH_TABLE))
     return AVSG_ERR_INVALID_ARG;
-  if (mode == AVSG_MATCH_MERGE) {
-    if ((int64_t)ctx->d.mr_lds_merge > ctx->lds_max) return AVSG_ERR_UNSUPPORTED;
-    if (match_reserve_set_lds(ctx->d.mr_lds_merge) != hipSuccess) return AVSG_ERR_HIP;
-  }
+  // (the kernel's LDS limit is the device maximum, set once per device)
+  if (mode == AVSG_MATCH_MERGE && (int64_t)ctx->d.mr_lds_merge > ctx->lds_max)
+    return AVSG_ERR_UNSUPPORTED;
   ctx->match_mode = mode;
   return AVSG_OK;
 }
@@ -342,8 +369,10 @@ avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes) {
   return AVSG_OK;
 }
 
-static avsg_status device_view_of_pinned(avsg_ctx* ctx, const void* host, const void** dev) {
-  if (host == ctx->pinned_checked) { *dev = ctx->pinned_device; return AVSG_OK; }
+// The device-visible address of pinned host memory, looked up on every call
+// (a buffer freed and allocated again may come back at the same host address
+// with a different mapping).
+static avsg_status device_view_of_pinned(const void* host, const void** dev) {
   hipPointerAttribute_t attr;
   memset(&attr, 0, sizeof(attr));
   if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
@@ -351,8 +380,6 @@ static avsg_status device_view_of_pinned(avsg_ctx* ctx, const void* host, const 
     return AVSG_ERR_NOT_PINNED;
   }
   if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) return AVSG_ERR_NOT_PINNED;
-  ctx->pinned_checked = host;
-  ctx->pinned_device = attr.devicePointer;
   *dev = attr.devicePointer;
   return AVSG_OK;
 }
@@ -376,9 +403,14 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   if (((uintptr_t)q | (uintptr_t)host_kv | (uintptr_t)buf_kv | (uintptr_t)out) & 15)
     return AVSG_ERR_INVALID_ARG;
   const void* host_dev = nullptr;
-  avsg_status st = device_view_of_pinned(ctx, host_kv, &host_dev);
+  avsg_status st = device_view_of_pinned(host_kv, &host_dev);
   if (st != AVSG_OK) return st;
   const avsg_config& c = ctx->cfg;
+  const bool fused = ctx->transfer_mode == AVSG_TRANSFER_FUSED ||
+                     ctx->transfer_mode == AVSG_TRANSFER_FUSED_GATHER_FIRST;
+  // checked before anything is launched: slots are never reserved for rows
+  // that no kernel would copy
+  if (!fused && !gather_fits(ctx->d.units)) return AVSG_ERR_UNSUPPORTED;
   char* ws = ctx->workspace;
   int32_t* unit_status = (int32_t*)(ws + ctx->ws.unit_status);
   int32_t* miss_count = (int32_t*)(ws + ctx->ws.miss_count);
@@ -434,8 +466,6 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   gp.units = ctx->d.units;
   gp.ucap = ctx->ws.ucap;
   gp.row16 = ctx->d.row_elems * 2 / 16;
-  const bool fused = ctx->transfer_mode == AVSG_TRANSFER_FUSED ||
-                     ctx->transfer_mode == AVSG_TRANSFER_FUSED_GATHER_FIRST;
   gp.per_unit = ctx->transfer_mode == AVSG_TRANSFER_PER_UNIT;
   if (!fused &&
       launch_gather(gp, gp.per_unit ? ctx->d.units : ctx->gather_grid, ctx->stream) != hipSuccess)
@@ -572,7 +602,7 @@ avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* po
   if (((uintptr_t)new_kv | (uintptr_t)host_kv | (uintptr_t)buf_kv) & 15)
     return AVSG_ERR_INVALID_ARG;
   const void* host_dev = nullptr;
-  avsg_status st = device_view_of_pinned(ctx, host_kv, &host_dev);
+  avsg_status st = device_view_of_pinned(host_kv, &host_dev);
   if (st != AVSG_OK) return st;
   const avsg_config& c = ctx->cfg;
   AppendParams ap;

@@ -132,3 +132,17 @@ def test_header_is_plain_c(tmp_path):
         r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
                             "-I", inc] + lang + [str(src)], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_binding_argument_counts_match_the_header():
+    """Every ctypes signature of the binding has as many arguments as the
+    header declares for that function."""
+    avsg = _lib()
+    lib = avsg.load()
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in avsg.EXPORTED:
+        m = re.search(r"\b%s\s*\(([^)]*)\)" % name, text)
+        assert m, name
+        params = m.group(1).strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert len(getattr(lib, name).argtypes) == n, (name, n)
