@@ -32,7 +32,8 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
             "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
             "avsg_rebuild_index", "avsg_step_varlen", "avsg_set_capacity",
-            "avsg_plan_capacity"]
+            "avsg_plan_capacity", "avsg_step_static"]
+STATIC_SCRATCH_BYTES = 64 << 20   # AVSG_STATIC_SCRATCH_BYTES
 
 
 class AvsgError(RuntimeError):
@@ -79,6 +80,7 @@ def load():
         "avsg_reset": ([p, p, p], i32),
         "avsg_step": ([p] * 8 + [ctypes.POINTER(avsg_hit_stats)], i32),
         "avsg_step_varlen": ([p] * 9 + [ctypes.POINTER(avsg_hit_stats)], i32),
+        "avsg_step_static": ([cfgp, i64, p] + [p] * 7 + [ctypes.POINTER(avsg_hit_stats)], i32),
         "avsg_last_error": ([p], i32),
         "avsg_append": ([p] * 6, i32),
         "avsg_validate_state": ([p, p, p], i32),
@@ -146,6 +148,13 @@ def avsg_step_varlen(ctx: int, sel_idx: int, sel_len: int, q: int, host_kv: int,
                      slot_table: int, lifetimes: int, out: int, hit_stats: avsg_hit_stats) -> int:
     return load().avsg_step_varlen(ctx, sel_idx, sel_len, q, host_kv, buf_kv, slot_table,
                                    lifetimes, out, ctypes.byref(hit_stats))
+
+
+def avsg_step_static(cfg: avsg_config, t: int, stream: int, sel_idx: int, q: int, host_kv: int,
+                     buf_kv: int, slot_table: int, lifetimes: int, out: int,
+                     hit_stats: avsg_hit_stats) -> int:
+    return load().avsg_step_static(ctypes.byref(cfg), t, stream or None, sel_idx, q, host_kv,
+                                   buf_kv, slot_table, lifetimes, out, ctypes.byref(hit_stats))
 
 
 def avsg_append(ctx: int, new_kv: int, pos: int, host_kv: int, buf_kv: int,

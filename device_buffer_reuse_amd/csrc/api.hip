@@ -115,19 +115,27 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   return true;
 }
 
+// Workspace of avsg_step_static: device memory of the library itself, one
+// copy per GPU (each device holds its own at its own address), kept until
+// the process ends.  Host code never uses this name as an address: it takes
+// each device's address from hipGetSymbolAddress once (device_setup).
+constexpr size_t kStaticScratchBytes = AVSG_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
   int num_cus;
   int lds_max;          // dynamic LDS a kernel of this device may be launched with
+  void* scratch_ptr;    // this device's copy of `scratch`
 };
 static std::mutex g_dev_mutex;
 static bool g_dev_ready[kMaxDevices];
 static DeviceInfo g_dev[kMaxDevices];
 
 // Once per device, with that device current: its unit count and LDS limit,
-// and the LDS limits of the kernels that need more than the default (set to
-// the device maximum, so contexts with different sizes never lower each
-// other's).
+// the LDS limits of the kernels that need more than the default (set to the
+// device maximum, so contexts with different sizes never lower each
+// other's), and the device address of the static workspace.
 static avsg_status device_setup(int* dev_out, DeviceInfo* info) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return AVSG_ERR_HIP;
@@ -135,15 +143,18 @@ static avsg_status device_setup(int* dev_out, DeviceInfo* info) {
   std::lock_guard<std::mutex> lock(g_dev_mutex);
   if (!g_dev_ready[dev]) {
     DeviceInfo di{};
+    void* ptr = nullptr;
     if (hipDeviceGetAttribute(&di.num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
             hipSuccess ||
         hipDeviceGetAttribute(&di.lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
             hipSuccess ||
         match_reserve_set_lds((size_t)di.lds_max) != hipSuccess ||
-        attn_latent_set_lds() != hipSuccess) {
+        attn_latent_set_lds() != hipSuccess ||
+        hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
       (void)hipGetLastError();
       return AVSG_ERR_HIP;
     }
+    di.scratch_ptr = ptr;
     g_dev[dev] = di;
     g_dev_ready[dev] = true;
   }
@@ -524,6 +535,37 @@ avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
                              const avsg_hit_stats* hs) {
   if (!sel_len) return AVSG_ERR_INVALID_ARG;
   return step_impl(ctx, sel_idx, sel_len, q, host_kv, buf_kv, slot_table, lifetimes, out, hs);
+}
+
+avsg_status avsg_step_static(const avsg_config* cfg, int64_t t, void* stream,
+                             const int32_t* sel_idx, const uint16_t* q, const uint16_t* host_kv,
+                             uint16_t* buf_kv, int32_t* slot_table, int32_t* lifetimes, float* out,
+                             const avsg_hit_stats* hs) {
+  avsg_status st = check_config_impl(cfg);
+  if (st != AVSG_OK) return st;
+  if (t < 0 || t > INT32_MAX || !hs || !hs->unit_status) return AVSG_ERR_INVALID_ARG;
+  // the context lives on this stack frame: nothing is allocated
+  avsg_ctx c{};
+  c.cfg = *cfg;
+  layout_for(*cfg, &c.ws, &c.d);
+  if (c.ws.total > kStaticScratchBytes) return AVSG_ERR_UNSUPPORTED;
+  DeviceInfo di;
+  st = device_setup(&c.device, &di);
+  if (st != AVSG_OK) return st;
+  if ((int64_t)c.d.mr_lds > di.lds_max) return AVSG_ERR_UNSUPPORTED;
+  c.num_cus = di.num_cus;
+  c.lds_max = di.lds_max;
+  c.gather_grid = di.num_cus * 2;
+  c.stream = (hipStream_t)stream;
+  c.workspace = (char*)di.scratch_ptr;
+  c.t = t;
+  c.transfer_mode = AVSG_TRANSFER_FUSED;
+  c.match_mode = AVSG_MATCH_HASH;
+  // the step's words that accumulate (the error bits) start at zero: the
+  // array keeps whatever the previous call on this device left
+  if (launch_fill_i32((int32_t*)(c.workspace + c.ws.err_word), 0, 2, c.stream) != hipSuccess)
+    return AVSG_ERR_HIP;
+  return step_impl(&c, sel_idx, nullptr, q, host_kv, buf_kv, slot_table, lifetimes, out, hs);
 }
 
 static avsg_status status_from_bits(uint32_t bits) {

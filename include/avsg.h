@@ -177,6 +177,36 @@ avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
                              int32_t* slot_table, int32_t* lifetimes, float* out,
                              const avsg_hit_stats* hit_stats);
 
+/* avsg_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * context and no caller workspace.  The step's scratch (per-unit status and
+ * miss lists, fetch flags, error words, split partials) is a device array
+ * inside the library, AVSG_STATIC_SCRATCH_BYTES per GPU, held by every GPU
+ * the library runs on until the process ends; the call itself allocates
+ * nothing (no hipMalloc, no host or device allocation by any library).
+ *   cfg        host, the configuration (as avsg_create's)
+ *   t          the decode step (the caller keeps the counter: 0 after an
+ *              emptied buffer, then +1 per call), in [0, 2^31)
+ *   stream     hipStream_t to enqueue on (NULL = the null stream), of the
+ *              current device
+ *   the rest   exactly as avsg_step, with the fused transfer and the hash
+ *              match; hit_stats->unit_status is required (it is where data
+ *              errors are reported, per unit: there is no context to hold an
+ *              error word for avsg_last_error).
+ * Returns AVSG_ERR_UNSUPPORTED if the configuration's scratch exceeds
+ * AVSG_STATIC_SCRATCH_BYTES (see avsg_workspace_bytes) and otherwise the
+ * codes of avsg_check_config and avsg_step.  Results are bit-identical to
+ * avsg_step's on the same inputs.  Every call on one GPU uses that GPU's one
+ * array, which keeps the previous call's contents: calls that may overlap in
+ * time on one GPU (other streams, other host threads) race, so serialise
+ * them (one stream, or events).  The first call on a device also looks up
+ * that device's copy of the array and sets the kernels' LDS limits. */
+#define AVSG_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+avsg_status avsg_step_static(const avsg_config* cfg, int64_t t, void* stream,
+                             const int32_t* sel_idx, const uint16_t* q, const uint16_t* host_kv,
+                             uint16_t* buf_kv, int32_t* slot_table, int32_t* lifetimes, float* out,
+                             const avsg_hit_stats* hit_stats);
+
 /* Buffer size per unit (Spin summary, section 2B, buffer elasticity: each
  * request's device buffer is sized dynamically, mandatory pages for the
  * current step plus buffer pages kept for locality).  `cap` is a device
