@@ -281,8 +281,11 @@ def dominant_roofline(use, per_us):
             "kernel_us": round(per_us[dom], 2)}
 
 
-KERNEL_SOURCES = {"attention": {4: "attn_split_kernel<4>", 5: "attn_latent_kernel<8>"},
-                  "match_reserve": {4: "match_reserve_kernel<1>", 5: "match_reserve_kernel<8>"}}
+# kernel (as rocprofv3 names it) that carries each stage of a workload's step
+KERNEL_SOURCES = {"attention": {2: "attn_split_kernel<4, false>", 3: "attn_split_kernel<4, false>",
+                                4: "attn_split_kernel<4, true>", 5: "attn_latent_kernel<8>"},
+                  "match_reserve": {2: "match_reserve_kernel<8>", 3: "match_reserve_kernel<8>",
+                                    4: "match_reserve_kernel<1>", 5: "match_reserve_kernel<8>"}}
 KERNEL_FILES = {"attn_split_kernel": "attn_split.hip", "attn_latent_kernel": "attn_latent.hip",
                 "match_reserve_kernel": "match_reserve.hip", "attn_combine_kernel": "attn_combine.hip"}
 
