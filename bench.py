@@ -466,6 +466,10 @@ def extras(b, a):
         "ms_per_step": round(statistics.median(per_pass), 4),
         "hit_rate": round(ch / max(ch + cm, 1), 5),
         "host_bytes_per_step": int(cm / K * w.row_bytes)}
+    # the host KV reached through the two-level directory (256-entry
+    # segments in pinned host memory, the top level in HBM), over the same
+    # rows: entry e of unit u at pool row u * N + e
+    out["host_directory"] = host_directory(b, a, t0, K)
     # Offload of the new token (append): every unit writes one token row into
     # host memory, and into its slot where the entry is resident
     na = 64
@@ -528,6 +532,46 @@ def extras(b, a):
     out["gemm_bf16_TFLOP/s"] = round(8 * 2 * 8192.0 ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
     del ga, gb, gc
     return out
+
+
+DIR_SEG = 256   # entries per second-level segment of the host directory
+
+
+def metadata_bytes(units, n_entries, seg=DIR_SEG):
+    """Bytes of the host-row metadata of a context of n_entries entries per
+    unit: a flat table in HBM (one int32 pool row per entry) against the two
+    levels (an int32 segment index per `seg` entries in HBM, the int32 rows
+    of the segments in host memory)."""
+    n_seg = -(-n_entries // seg)
+    return {"entries_per_unit": n_entries, "flat_table_hbm_bytes": 4 * units * n_entries,
+            "top_level_hbm_bytes": 4 * units * n_seg, "segments_host_bytes": 4 * units * n_seg * seg,
+            "hbm_ratio": round(n_entries / n_seg, 1)}
+
+
+def host_directory(b, a, t0, K):
+    """The natural trace with host rows reached through the two-level
+    directory, and its metadata sizes against a flat table."""
+    torch, w, avsg = b.torch, b.w, b.avsg
+    n_seg = -(-w.n_entries // DIR_SEG)
+    segs = avsg.HostBuffer((w.units * n_seg, DIR_SEG), dtype=np.int32)
+    rows = np.arange(w.units * n_seg * DIR_SEG, dtype=np.int64).reshape(w.units, n_seg * DIR_SEG)
+    rows = rows - np.arange(w.units)[:, None] * (n_seg * DIR_SEG - w.n_entries)   # u * N + e
+    rows[:, w.n_entries:] = -1
+    segs.array[...] = rows.reshape(w.units * n_seg, DIR_SEG).astype(np.int32)
+    top = torch.arange(w.units * n_seg, dtype=torch.int32, device="cuda").reshape(w.units, n_seg)
+    b.ctx.set_host_directory(top, segs, DIR_SEG, w.units * n_seg, w.units * w.n_entries)
+    b.load_trace("natural", t0 + K)
+    ms, _, kern = b.passes(t0, t0 + K, 1, a.passes)
+    b.ctx.set_host_directory(None, None, 0, 0, 0)
+    assert b.ctx.last_error() == 0
+    segs.free()
+    ctx_tokens = [32768, 131072, 1 << 20]
+    return {"seg_entries": DIR_SEG, "ms_per_step": round(ms, 5),
+            "match_reserve_us": round(kern["match_reserve"], 2),
+            "attention_us": round(kern["attention"], 2),
+            "metadata": metadata_bytes(w.units, w.n_entries),
+            "metadata_by_context_tokens": {
+                str(n): metadata_bytes(w.units, -(-n // w.tokens_per_entry)) for n in ctx_tokens}}
 
 
 def cpu_baseline(w, host_kv, t_start, seconds, threads=1):

@@ -32,7 +32,7 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
             "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
             "avsg_rebuild_index", "avsg_step_varlen", "avsg_set_capacity",
-            "avsg_plan_capacity", "avsg_step_static"]
+            "avsg_plan_capacity", "avsg_step_static", "avsg_set_host_directory"]
 STATIC_SCRATCH_BYTES = 64 << 20   # AVSG_STATIC_SCRATCH_BYTES
 
 
@@ -86,6 +86,7 @@ def load():
         "avsg_validate_state": ([p, p, p], i32),
         "avsg_rebuild_index": ([p, p], i32),
         "avsg_set_capacity": ([p, p], i32),
+        "avsg_set_host_directory": ([p, p, p, ctypes.c_int32, ctypes.c_int32, i64], i32),
         "avsg_plan_capacity": ([ctypes.c_int32, p, p, i64, ctypes.c_int32, p], i32),
         "avsg_get_step": ([p], i64),
         "avsg_set_step": ([p, i64], i32),
@@ -176,6 +177,11 @@ def avsg_rebuild_index(ctx: int, slot_table: int) -> int:
 
 def avsg_set_capacity(ctx: int, cap: int | None) -> int:
     return load().avsg_set_capacity(ctx, cap)
+
+
+def avsg_set_host_directory(ctx: int, top: int | None, segments: int | None, seg_entries: int,
+                            n_segments: int, pool_rows: int) -> int:
+    return load().avsg_set_host_directory(ctx, top, segments, seg_entries, n_segments, pool_rows)
 
 
 def avsg_plan_capacity(demand: np.ndarray, reuse: np.ndarray, budget: int, n_slots: int):
@@ -373,6 +379,17 @@ class Context:
         st = avsg_set_capacity(self.handle, None if cap is None else cap.data_ptr())
         if st != OK:
             raise AvsgError(st, "avsg_set_capacity")
+
+    def set_host_directory(self, top, segments, seg_entries: int, n_segments: int, pool_rows: int):
+        """top: device int32 tensor [units][n_seg] (kept alive by the caller),
+        segments: a HostBuffer of int32 [n_segments][seg_entries]; top=None
+        returns to the flat host KV."""
+        self._dir = (top, segments)
+        st = avsg_set_host_directory(self.handle, None if top is None else top.data_ptr(),
+                                     None if top is None else segments.ptr, seg_entries,
+                                     n_segments, pool_rows)
+        if st != OK:
+            raise AvsgError(st, "avsg_set_host_directory")
 
     def rebuild_index(self, slot_table) -> int:
         return avsg_rebuild_index(self.handle, slot_table.data_ptr())

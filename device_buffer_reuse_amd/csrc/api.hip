@@ -23,6 +23,7 @@ struct avsg_ctx {
   int32_t transfer_mode;         // avsg_transfer_mode
   int32_t match_mode;            // avsg_match_mode
   const int32_t* cap;            // device [units] buffer size of each unit, or null (S)
+  avsg::HostDir dir;             // two-level host directory (null top: flat host KV)
   int lds_max;
   hipEvent_t* prof_events;       // kProfMarks per profiled step, or null
   int32_t prof_max, prof_used;
@@ -95,6 +96,7 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->miss_count = off;  off = align256(off + 4 * (size_t)d->units);
   ws->misses = off;      off = align256(off + 8 * (size_t)d->units * ws->ucap);
   ws->fetch = off;       off = align256(off + (size_t)d->units * tk);
+  ws->host_row = off;    off = align256(off + 4 * (size_t)d->units * tk);
   ws->err_word = off;    off = align256(off + 8);
   ws->partials = off;
   off = align256(off + 4 * (size_t)d->units * T * ws->nsplit *
@@ -461,6 +463,8 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   mp.match_mode = ctx->match_mode;
   mp.merge_pow2 = ctx->d.merge_pow2;
   mp.direct_words = ctx->match_mode == AVSG_MATCH_HASH ? ctx->d.direct_words : 0;
+  mp.dir = ctx->dir;
+  mp.host_row = (int32_t*)(ws + ctx->ws.host_row);
   prof_mark(ctx, 0);
   const size_t mr_lds = merge ? ctx->d.mr_lds_merge : ctx->d.mr_lds;
   if (launch_match_reserve(mp, ctx->d.units, mr_lds, ctx->stream) != hipSuccess)
@@ -478,6 +482,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   gp.ucap = ctx->ws.ucap;
   gp.row16 = ctx->d.row_elems * 2 / 16;
   gp.per_unit = ctx->transfer_mode == AVSG_TRANSFER_PER_UNIT;
+  gp.pooled = ctx->dir.top != nullptr;
   if (!fused &&
       launch_gather(gp, gp.per_unit ? ctx->d.units : ctx->gather_grid, ctx->stream) != hipSuccess)
     return AVSG_ERR_HIP;
@@ -488,6 +493,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   ap.sel_len = sel_len;
   ap.sel = sel_idx;
   ap.fetch = fused ? (const uint8_t*)(ws + ctx->ws.fetch) : nullptr;
+  ap.host_row = ctx->dir.top ? (const int32_t*)(ws + ctx->ws.host_row) : nullptr;
   ap.host_kv = (const uint16_t*)host_dev;
   ap.N = c.n_entries;
   ap.token = 0;
@@ -618,6 +624,31 @@ avsg_status avsg_set_capacity(avsg_ctx* ctx, const int32_t* cap) {
   return AVSG_OK;
 }
 
+avsg_status avsg_set_host_directory(avsg_ctx* ctx, const int32_t* top, const int32_t* segments,
+                                    int32_t seg_entries, int32_t n_segments, int64_t pool_rows) {
+  if (!ctx) return AVSG_ERR_INVALID_ARG;
+  if (!top) {  // back to the flat host KV
+    ctx->dir = HostDir{};
+    return AVSG_OK;
+  }
+  if (!segments || seg_entries < 1 || seg_entries > (1 << 20) ||
+      (seg_entries & (seg_entries - 1)) != 0 || n_segments < 1 || pool_rows < 1 ||
+      pool_rows > INT32_MAX || ((int64_t)n_segments << 20) > ((int64_t)1 << 40))
+    return AVSG_ERR_INVALID_ARG;
+  const void* seg_dev = nullptr;
+  avsg_status st = device_view_of_pinned(segments, &seg_dev);
+  if (st != AVSG_OK) return st;
+  HostDir d{};
+  d.top = top;
+  d.segments = (const int32_t*)seg_dev;
+  while ((1 << d.seg_log2) < seg_entries) ++d.seg_log2;
+  d.n_seg = (int32_t)(((int64_t)ctx->cfg.n_entries + seg_entries - 1) / seg_entries);
+  d.n_segments = n_segments;
+  d.pool_rows = pool_rows;
+  ctx->dir = d;
+  return AVSG_OK;
+}
+
 avsg_status avsg_plan_capacity(int32_t units, const int32_t* demand, const int32_t* reuse,
                                int64_t budget, int32_t n_slots, int32_t* cap) {
   if (units < 1 || !demand || !reuse || !cap || n_slots < 1) return AVSG_ERR_INVALID_ARG;
@@ -654,6 +685,7 @@ avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* po
   ap.buf_kv = buf_kv;
   ap.slot_table = slot_table;
   ap.err_word = (uint32_t*)(ctx->workspace + ctx->ws.err_word);
+  ap.dir = ctx->dir;
   ap.Hkv = c.n_kv_heads;
   ap.N = c.n_entries;
   ap.S = c.n_slots;

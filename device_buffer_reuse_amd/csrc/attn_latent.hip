@@ -162,7 +162,9 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   }
   for (int i = tid; i < ne; i += kThreads) {
     const size_t at = (size_t)uj * p.k + e0 + i;
-    sRow[i] = make_int2(p.sel_slot[at], (p.fetch && p.fetch[at]) ? p.sel[at] : -1);
+    // host row of a fetched entry: its id (flat host KV) or its pool row
+    sRow[i] = make_int2(p.sel_slot[at],
+                        (p.fetch && p.fetch[at]) ? (p.host_row ? p.host_row : p.sel)[at] : -1);
   }
   // this lane's Q operand: head w*16 + li, dims 32*ks + 8*g .. +8
   bf16x8 qf[kKSteps];
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
     return (n < kTileInstr && P < kTilePieces && col < kPiecesPerRow) ? (r << 8 | col) : -1;
   };
   uint16_t* ubase = p.buf_kv + (size_t)u * p.S * kDqk;
-  const uint16_t* hbase = p.host_kv + (size_t)u * p.N * kDqk;
+  const uint16_t* hbase = p.host_kv + (p.host_row ? 0 : (size_t)u * p.N * kDqk);
   const uint32_t row_lds = lds_addr(sRow);
   const uint32_t tile_lds = lds_addr(sTile);
 

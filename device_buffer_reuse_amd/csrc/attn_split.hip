@@ -188,13 +188,16 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
   // slot array instead and are ignored
   const bool has_fetch = p.fetch != nullptr;
   const uint8_t* fl_src = has_fetch ? p.fetch : reinterpret_cast<const uint8_t*>(p.sel_slot);
+  // host row of a fetched entry: its id in the unit's part of a flat host KV,
+  // or its pool row (host directory)
+  const int32_t* id_src = p.host_row ? p.host_row : p.sel;
   bf16x8 qf[kKSteps];
   if (wave == 0) {  // (gather-first: wave 1 reads the split's entries from LDS)
 #pragma unroll
     for (int k = 0; k < kEnt; ++k) {
       const size_t at = (size_t)uj * p.k + e0 + min(k * kThreads + lane, ne - 1);
       slot_v[k] = p.sel_slot[at];
-      id_v[k] = p.sel[at];
+      id_v[k] = id_src[at];
       fl_v[k] = fl_src[at];
     }
     const uint16_t* qrow =
@@ -241,7 +244,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
   for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
 
   uint16_t* ubase = p.buf_kv + (size_t)u * p.S * p.row_elems;
-  const uint16_t* hbase = p.host_kv + (size_t)u * p.N * p.row_elems;
+  const uint16_t* hbase = p.host_kv + (p.host_row ? 0 : (size_t)u * p.N * p.row_elems);
   const int v_off = tpe * kD;  // elements from an entry's K rows to its V rows
   const uint32_t row_lds = lds_addr(sRow);
   const uint32_t tile_lds = lds_addr(sTile);

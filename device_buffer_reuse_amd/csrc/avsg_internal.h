@@ -17,7 +17,7 @@ constexpr int kGatherThreads = 256;
 
 // Layout of the caller's workspace (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t unit_status, miss_count, misses, fetch, err_word, partials, total;
+  size_t unit_status, miss_count, misses, fetch, host_row, err_word, partials, total;
   int32_t ucap;       // union capacity per unit = min(T*k, S)
   int32_t table_cap;  // hash table cells, power of two >= 2*ucap
   int32_t nsplit;     // attention splits per (unit, token)
@@ -40,6 +40,15 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d);
 inline __host__ __device__ size_t partial_stride(int G, int D) {
   return (size_t)G * D + (size_t)((2 * G + 3) & ~3);
 }
+
+// Two-level directory of the host KV pool: entry e of unit u is pool row
+// segments[top[u][e >> seg_log2]][e & (2^seg_log2 - 1)] (-1: not mapped).
+struct HostDir {
+  const int32_t* top;       // device [units][n_seg]: segment index, -1 = none (null: flat host KV)
+  const int32_t* segments;  // device-visible pinned host [n_segments][2^seg_log2]: pool row or -1
+  int32_t seg_log2, n_seg, n_segments;
+  int64_t pool_rows;
+};
 
 struct MatchReserveParams {
   const int32_t* sel;     // [units][T][k]
@@ -64,16 +73,20 @@ struct MatchReserveParams {
   int32_t merge_pow2;     // power of two >= S (sort size of the merge baseline)
   int32_t direct_words;   // > 0: match through N-bit membership words and rank bases
                           // (this many words each, multiple of 4) instead of the hash table
+  // host KV through a two-level directory (null dir_top: flat [units][N][row])
+  HostDir dir;
+  int32_t* host_row;      // workspace [units][T][k]: pool row of each fetched entry (directory)
 };
 
 struct GatherParams {
-  const int2* misses;
+  const int2* misses;     // (slot, id), or (slot, pool row) with a host directory
   const int32_t* miss_count;
   const uint4* host_kv;   // device-visible address of the pinned host rows
   uint4* buf_kv;
   int64_t N, S;
   int32_t units, ucap, row16;
   int32_t per_unit;       // 1: workgroup u copies unit u's rows (request-level)
+  int32_t pooled;         // 1: misses carry pool rows of one shared host array
 };
 
 struct AttnParams {
@@ -81,6 +94,8 @@ struct AttnParams {
   const int32_t* sel_len;     // [units][T] entries in use of each list, or null: k
   const int32_t* sel;         // [units][T][k] selected ids
   const uint8_t* fetch;       // [units][T][k] or null: rows to read from host and store
+  const int32_t* host_row;    // [units][T][k] pool row of each fetched entry, or null: flat
+                              // host KV, row u * N + sel
   const uint16_t* host_kv;    // device-visible address of the pinned host rows
   int64_t N;
   const int32_t* unit_status; // [units]
@@ -103,6 +118,7 @@ struct AppendParams {
   uint16_t* buf_kv;           // [units][S][row]
   const int32_t* slot_table;  // [units][S]
   uint32_t* err_word;
+  HostDir dir;                // null dir.top: flat host KV
   int32_t Hkv, N, S, tpe, row_elems, tok_elems, dqk, dv, latent;
 };
 

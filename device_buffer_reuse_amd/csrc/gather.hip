@@ -90,8 +90,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherParams p) 
           cur_unit = lo;
         }
         const int2 ms = p.misses[(size_t)cur_unit * p.ucap + (row - (uint32_t)sPre[cur_unit])];
+        // ms.y: the row's id in its unit, or its pool row (host directory)
         const u32x4* src = reinterpret_cast<const u32x4*>(p.host_kv) +
-                           ((size_t)cur_unit * p.N + ms.y) * row16 + col;
+                           ((p.pooled ? 0 : (size_t)cur_unit * p.N) + (uint32_t)ms.y) * row16 + col;
         const u32x4 x = __builtin_nontemporal_load(src);
         v[e] = make_uint4(x.x, x.y, x.z, x.w);
         dst[e] = p.buf_kv + ((size_t)cur_unit * p.S + ms.x) * row16 + col;

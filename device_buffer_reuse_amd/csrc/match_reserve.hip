@@ -690,8 +690,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   }
   __syncthreads();
 
-  const int flags = sMisc[0];
-  if (flags) {
+  // a data error: the unit keeps its state (nothing has been written to it)
+  // and its outputs say so
+  auto fail_unit = [&](int flags) {
     const int code = flags_to_status(flags);
     for (int i = tid; i < tks; i += kMRThreads) {
       p.sel_slot[(size_t)u * tks + i] = -1;
@@ -707,6 +708,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       if (p.user_status) p.user_status[u] = code;
       atomicOr(p.err_word, 1u << (code - 16));
     }
+  };
+  if (sMisc[0]) {
+    fail_unit(sMisc[0]);
     return;
   }
 
@@ -761,6 +765,53 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     // sWs is reused by the next round; after the last round, the barrier
     // that follows the bin histogram orders these stores before their reads
     if (c0 + 2 * kMRThreads < nu) __syncthreads();
+  }
+
+  // ---- 6b. with a host directory: the pool row of every miss, read
+  //          through the two-level directory (top level in device memory,
+  //          segment in pinned host memory) before anything is written; an
+  //          entry without a row is a range error of the unit.  The probe's
+  //          table is dead by now and holds the rows: sRowOf[r] for miss r,
+  //          sURow[i] for union entry i.
+  int32_t* sRowOf = lds;
+  int32_t* sURow = lds + ucap;
+  const bool dir = p.dir.top != nullptr;
+  if (dir && m > 0) {  // (m is the same in every wave)
+    __syncthreads();   // the miss list is complete
+    const int32_t* top = p.dir.top + (size_t)u * p.dir.n_seg;
+    const int lg = p.dir.seg_log2;
+    const int32_t emask = (int32_t)((1u << lg) - 1);
+    int bad = 0;
+    constexpr int kDirGrp = 4;  // misses per thread whose reads are in flight together
+    for (int r0 = 0; r0 < m; r0 += kDirGrp * kMRThreads) {
+      int32_t idr[kDirGrp], seg[kDirGrp], row[kDirGrp];
+#pragma unroll
+      for (int g = 0; g < kDirGrp; ++g) {
+        const int r = min(r0 + g * kMRThreads + tid, m - 1);
+        idr[g] = sU[sMiss[r]];
+        seg[g] = top[idr[g] >> lg];
+      }
+#pragma unroll
+      for (int g = 0; g < kDirGrp; ++g) {
+        const bool ok = seg[g] >= 0 && seg[g] < p.dir.n_segments;
+        row[g] = p.dir.segments[((size_t)(ok ? seg[g] : 0) << lg) + (idr[g] & emask)];
+        row[g] = ok ? row[g] : -1;
+      }
+#pragma unroll
+      for (int g = 0; g < kDirGrp; ++g) {
+        const int r = r0 + g * kMRThreads + tid;
+        if (r < m) {
+          bad |= row[g] < 0 || (int64_t)row[g] >= p.dir.pool_rows;
+          sRowOf[r] = row[g];
+        }
+      }
+    }
+    if (bad) atomicOr(&sMisc[0], kFlagRange);
+    __syncthreads();
+    if (sMisc[0]) {
+      fail_unit(sMisc[0]);
+      return;
+    }
   }
 
   // ---- 7. victims: the m first candidates in (bin, slot) order
@@ -897,13 +948,16 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     constexpr int kGrp = MAXP < 8 ? MAXP : 8;
 #pragma unroll
     for (int q0 = 0; q0 < MAXP; q0 += kGrp) {
-      int r[kGrp], mi[kGrp], idv[kGrp];
+      int r[kGrp], mi[kGrp], idv[kGrp], rowv[kGrp];
 #pragma unroll
       for (int qq = 0; qq < kGrp; ++qq) r[qq] = rank[q0 + qq];
 #pragma unroll
       for (int qq = 0; qq < kGrp; ++qq) mi[qq] = sMiss[min(r[qq], m - 1)];
 #pragma unroll
-      for (int qq = 0; qq < kGrp; ++qq) idv[qq] = sU[mi[qq]];
+      for (int qq = 0; qq < kGrp; ++qq) {
+        idv[qq] = sU[mi[qq]];
+        rowv[qq] = dir ? sRowOf[min(r[qq], m - 1)] : 0;
+      }
 #pragma unroll
       for (int qq = 0; qq < kGrp; ++qq) {
         const int q = q0 + qq;
@@ -914,7 +968,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
           lf[q] = lru ? (int32_t)p.t : p.L;
           changed[q] = true;
           sUslot[mi[qq]] = s | kMissFlag;
-          misses[r[qq]] = make_int2(s, idv[qq]);
+          if (dir) sURow[mi[qq]] = rowv[qq];
+          // the transfer list: the row's id, or its pool row with a directory
+          misses[r[qq]] = make_int2(s, dir ? rowv[qq] : idv[qq]);
         }
       }
     }
@@ -940,7 +996,9 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     p.sel_slot[(size_t)u * tks + i] = v & ~kMissFlag;
     p.hit_flag[(size_t)u * tks + i] = miss ? 0 : 1;
     // the row is transferred by the first token that selects it
-    p.fetch[(size_t)u * tks + i] = (miss && !(mi & kDupFlag)) ? 1 : 0;
+    const bool fetch = miss && !(mi & kDupFlag);
+    p.fetch[(size_t)u * tks + i] = fetch ? 1 : 0;
+    if (dir) p.host_row[(size_t)u * tks + i] = fetch ? sURow[mi & ~kDupFlag] : -1;
   }
   // entries past a shortened list: no slot, no transfer
   for (int i = tk + tid; i < tks; i += kMRThreads) {

@@ -221,6 +221,35 @@ avsg_status avsg_step_static(const avsg_config* cfg, int64_t t, void* stream,
  * The pointer is kept by the context; the caller owns the array. */
 avsg_status avsg_set_capacity(avsg_ctx* ctx, const int32_t* cap);
 
+/* Host KV through a two-level directory (Spin summary, section 2C:
+ * hierarchical metadata; a small top-level directory on the GPU points to
+ * second-level segments allocated on demand in CPU memory, so metadata
+ * follows the mapped working set instead of the largest logical context, and
+ * the latency-critical level stays on the GPU).  After this call host_kv
+ * (of avsg_step, avsg_step_varlen and avsg_append) is a pool of pool_rows
+ * rows [pool_rows][row], and entry e of unit u lives at pool row
+ *   segments[top[u][e / seg_entries]][e % seg_entries]
+ *   top        device, int32 [units][ceil(n_entries / seg_entries)]: the
+ *              segment of each range of seg_entries entries, -1 = none.  The
+ *              context keeps the pointer; contents are read by each step
+ *              (update them between steps, stream-ordered).     read only
+ *   segments   host, pinned (avsg_host_alloc), int32 [n_segments][seg_entries]:
+ *              pool row of each entry, -1 = not mapped.  Kept by the
+ *              context; read by the GPU during steps and appends.  read only
+ *   seg_entries power of two in [1, 2^20]; n_segments >= 1; pool_rows in
+ *              [1, 2^31).
+ * Only missed entries are looked up (one top-level read in device memory and
+ * one 4-byte read of host memory each, before any state changes): a selected
+ * entry that misses and has no valid row (no segment, -1, or a row outside
+ * the pool) is a range error of its unit (AVSG_ERR_RANGE, the unit's state
+ * untouched); an entry still resident in the buffer hits without a lookup.
+ * An append to an entry without a valid row writes nothing and raises
+ * AVSG_ERR_RANGE.  top = NULL returns to the flat host KV [units][N][row].
+ * Returns AVSG_ERR_INVALID_ARG for bad sizes, AVSG_ERR_NOT_PINNED if segments
+ * is not pinned device-mapped host memory.  Not valid with avsg_step_static. */
+avsg_status avsg_set_host_directory(avsg_ctx* ctx, const int32_t* top, const int32_t* segments,
+                                    int32_t seg_entries, int32_t n_segments, int64_t pool_rows);
+
 /* The capacity planner (host arrays, host only): gives each of `units`
  * units its mandatory slots demand[u] (the size of its next union, in
  * [1, n_slots]) and shares the rest of a slot budget over all units in

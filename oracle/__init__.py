@@ -67,9 +67,9 @@ def _load():
             lib = ctypes.CDLL(_LIB_PATH)
             p = ctypes.c_void_p
             lib.oracle_unit_step.argtypes = ([ctypes.POINTER(_Cfg), ctypes.c_int64, p, p,
-                                              ctypes.c_int32] + [p] * 7)
+                                              ctypes.c_int32] + [p] * 8)
             lib.oracle_unit_step.restype = ctypes.c_int
-            lib.oracle_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, ctypes.c_int64] + [p] * 11
+            lib.oracle_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, ctypes.c_int64] + [p] * 12
             lib.oracle_step.restype = None
             lib.oracle_set_threads.argtypes = [ctypes.c_int]
             lib.oracle_set_threads.restype = None
@@ -122,12 +122,15 @@ class OracleBuffer:
                     if self.track_buf else None)
 
     def step(self, sel: np.ndarray, host_kv: np.ndarray | None = None,
-             lengths: np.ndarray | None = None, caps: np.ndarray | None = None) -> dict:
+             lengths: np.ndarray | None = None, caps: np.ndarray | None = None,
+             mapped: np.ndarray | None = None) -> dict:
         """Advance one step with selections sel [units][T][k], of which the
         first lengths[u][j] entries of each list are in use (all k when
         lengths is None), unit u using slots [0, caps[u]) (all S when caps
-        is None; slots past it are emptied).  When the buffer is tracked,
-        reserved slots receive host_kv[u][id] byte for byte."""
+        is None; slots past it are emptied).  mapped [units][N] (bool):
+        entries that have a host row (all when None); a miss without one is
+        a range error of its unit.  When the buffer is tracked, reserved
+        slots receive host_kv[u][id] byte for byte."""
         c = self.cfg
         sel = np.ascontiguousarray(sel, dtype=np.int32)
         assert sel.shape == (self.units, c.n_tokens, c.k)
@@ -145,12 +148,14 @@ class OracleBuffer:
         assert tk > 0
         if caps is not None:
             caps = np.ascontiguousarray(caps, dtype=np.int32).reshape(self.units)
+        if mapped is not None:
+            mapped = np.ascontiguousarray(mapped, dtype=np.uint8).reshape(self.units, c.n_entries)
         _load().oracle_step(ctypes.byref(c), self.units, self.t, _p(sel),
                             None if lengths is None else _p(lengths),
                             None if caps is None else _p(caps), _p(self.slot_tok),
                             _p(self.life), _p(res["hit_flag"]), _p(res["sel_slot"]),
                             _p(res["fill_slot"]), _p(res["fill_id"]), _p(res["counts"]),
-                            _p(res["status"]))
+                            _p(res["status"]), None if mapped is None else _p(mapped))
         res["n_hit"] = res["counts"][:, 0].copy()
         res["n_miss"] = res["counts"][:, 1].copy()
         res["n_evict"] = res["counts"][:, 2].copy()
@@ -175,11 +180,12 @@ class OracleBuffer:
 
 
 def unit_step(n_slots, n_entries, k, policy, lifetime_L, n_buckets, t, sel, slot_tok, life,
-              lengths=None, cap=None):
+              lengths=None, cap=None, mapped=None):
     """Single-unit call for small hand-built cases: returns (status, result
     dict) and updates slot_tok / life (int32 arrays) in place.  lengths: the
     entries in use of each token's list (default: all k); cap: slots in use
-    (default: all n_slots)."""
+    (default: all n_slots); mapped: [N] bool, entries with a host row
+    (default: all)."""
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     if sel.ndim == 1:
         sel = sel[None, :]
@@ -193,9 +199,10 @@ def unit_step(n_slots, n_entries, k, policy, lifetime_L, n_buckets, t, sel, slot
     fi = np.zeros(n_slots, np.int32)
     cnt = np.zeros(4, np.int32)
     ln = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32).reshape(T)
+    mp = None if mapped is None else np.ascontiguousarray(mapped, dtype=np.uint8).reshape(n_entries)
     st = _load().oracle_unit_step(ctypes.byref(cfg), t, _p(sel), None if ln is None else _p(ln),
                                   n_slots if cap is None else int(cap), _p(slot_tok), _p(life), _p(hit),
-                                  _p(ss), _p(fs), _p(fi), _p(cnt))
+                                  _p(ss), _p(fs), _p(fi), _p(cnt), None if mp is None else _p(mp))
     m = int(cnt[1])
     return st, dict(hit_flag=hit, sel_slot=ss, fill_slot=fs[:m].copy(), fill_id=fi[:m].copy(),
                     n_hit=int(cnt[0]), n_miss=m, n_evict=int(cnt[2]), n_union=int(cnt[3]))

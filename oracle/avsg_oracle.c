@@ -108,11 +108,17 @@ static int32_t find_sorted(const int32_t* a, int32_t n, int32_t x) {
  *   sel_slot   [T][k]  out: slot that holds the entry after this step
  *   fill_slot, fill_id [S] out: the m reservations, in miss order
  *   counts     [4]     out: n_hit, n_miss, n_evict, |U|
+ *   mapped     [N]     1 if entry x has a row in host memory (a host KV
+ *                      reached through a directory, Spin summary section
+ *                      2C), or NULL: every entry has one.  A miss without a
+ *                      row cannot be transferred: a range error, found
+ *                      after every other check.
  * Returns a status; on error the state is unchanged, flags are 0, slots -1.
  */
 int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const int32_t* len,
                      int32_t cap, int32_t* slot_tok, int32_t* life, uint8_t* hit_flag,
-                     int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts) {
+                     int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts,
+                     const uint8_t* mapped) {
   const int32_t S_all = c->n_slots, N = c->n_entries, T = c->n_tokens, k = c->k;
   /* the slots in use: [0, S) */
   const int32_t S = cap;
@@ -193,16 +199,22 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
   free(R);
   if (status != OR_OK) { free(U); free(uslot); free(uhit); free(selected_slot); return status; }
 
+  int32_t n_hit = 0;
+  for (int32_t a = 0; a < nu; ++a) n_hit += uhit[a];
+  const int32_t m = nu - n_hit;
+
+  /* every miss must have a row to transfer */
+  if (mapped)
+    for (int32_t a = 0; a < nu; ++a)
+      if (!uhit[a] && !mapped[U[a]]) status = OR_ERR_RANGE;
+  if (status != OR_OK) { free(U); free(uslot); free(uhit); free(selected_slot); return status; }
+
   /* every check has passed: the slots past the capacity are emptied (they
    * take no part in the match above, and are never candidates below) */
   for (int32_t s = S; s < S_all; ++s) {
     slot_tok[s] = -1;
     life[s] = c->policy == OR_LRU ? -1 : 0;
   }
-
-  int32_t n_hit = 0;
-  for (int32_t a = 0; a < nu; ++a) n_hit += uhit[a];
-  const int32_t m = nu - n_hit;
 
   /* 3. policy update of the slots (all slots; the caller's arrays) */
   for (int32_t s = 0; s < S; ++s) {
@@ -265,11 +277,12 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
 }
 
 /* All units of one step (units are independent; OpenMP over units).  len is
- * [units][T] or NULL, cap [units] or NULL (every unit uses all S slots). */
+ * [units][T] or NULL, cap [units] or NULL (every unit uses all S slots),
+ * mapped [units][N] or NULL (every entry has a host row). */
 void oracle_step(const oracle_cfg* c, int64_t units, int64_t t, const int32_t* sel,
                  const int32_t* len, const int32_t* cap, int32_t* slot_tok, int32_t* life,
                  uint8_t* hit_flag, int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id,
-                 int32_t* counts, int32_t* status) {
+                 int32_t* counts, int32_t* status, const uint8_t* mapped) {
   const int64_t tk = (int64_t)c->n_tokens * c->k, S = c->n_slots;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u)
@@ -277,7 +290,7 @@ void oracle_step(const oracle_cfg* c, int64_t units, int64_t t, const int32_t* s
                                  cap ? cap[u] : c->n_slots,
                                  slot_tok + u * S, life + u * S, hit_flag + u * tk,
                                  sel_slot + u * tk, fill_slot + u * S, fill_id + u * S,
-                                 counts + u * 4);
+                                 counts + u * 4, mapped ? mapped + u * c->n_entries : NULL);
 }
 
 /* Threads used by oracle_step's loop over units. */

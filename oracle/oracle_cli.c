@@ -36,7 +36,8 @@ typedef struct {
 
 int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const int32_t* len,
                      int32_t cap, int32_t* slot_tok, int32_t* life, uint8_t* hit_flag,
-                     int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts);
+                     int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts,
+                     const uint8_t* mapped);
 void oracle_attend(const oracle_attn_cfg* c, const uint16_t* q, const uint16_t* host_kv,
                    const int32_t* sel, const int32_t* len, const int32_t* status, double* out);
 
@@ -83,7 +84,7 @@ static int run_state(void) {
     const int32_t cap = (int32_t)rd();
     for (int64_t e = 0; e < tk; ++e) sel[e] = (int32_t)rd();
     const int st = oracle_unit_step(&c, t, sel, NULL, cap < 0 ? c.n_slots : cap, tok, life, flags,
-                                    slots, fs, fi, counts);
+                                    slots, fs, fi, counts, NULL);
     printf("%d %d %d %d %d\n", st, counts[0], counts[1], counts[2], counts[3]);
     for (int64_t e = 0; e < tk; ++e) fl[e] = flags[e];
     print_i32(fl, tk);

@@ -64,8 +64,8 @@ def test_status_strings():
 
 def test_workspace_sizes_match_layout():
     """Workspace holds per-unit miss lists (8 B per union capacity), a fetch
-    flag per selected entry, split partials and a few words; its size follows
-    the config."""
+    flag and a host pool row (4 B, used with a host directory) per selected
+    entry, split partials and a few words; its size follows the config."""
     avsg = _lib()
     w = tg.WORKLOADS[2]
     c = avsg.config_from_workload(w)
@@ -74,7 +74,8 @@ def test_workspace_sizes_match_layout():
     splits = -(-w.k * w.tokens_per_entry // 256)  # 256 token rows per attention split
     partials = 4 * w.units * splits * 4 * 130
     fetch = w.units * w.n_q_tokens * w.k
-    assert misses + partials + fetch <= ws <= misses + partials + fetch + 8 * 1024
+    host_row = 4 * fetch
+    assert misses + partials + fetch + host_row <= ws <= misses + partials + fetch + host_row + 8 * 1024
 
 
 def test_plan_capacity_matches_its_definition():

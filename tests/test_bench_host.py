@@ -163,3 +163,15 @@ def test_step_roofline_takes_the_larger_time():
     # no host traffic: HBM-bound
     r = bench.step_roofline(70e6, 10e6, 0, True, 40e-6)
     assert r["bound"] == "hbm" and r["frac"] == 0.25
+
+
+def test_metadata_bytes_of_the_directory():
+    # 256 units of 8192 entries: a flat int32 table is 8 MiB of HBM, the
+    # top level of 256-entry segments 32 KiB; the segments (host) hold the rows
+    m = bench.metadata_bytes(256, 8192, 256)
+    assert m["flat_table_hbm_bytes"] == 4 * 256 * 8192 == 8388608
+    assert m["top_level_hbm_bytes"] == 4 * 256 * 32 and m["segments_host_bytes"] == 8388608
+    assert m["hbm_ratio"] == 256.0
+    # a context that is not a whole number of segments rounds the top level up
+    m = bench.metadata_bytes(2, 1000, 256)
+    assert m["top_level_hbm_bytes"] == 4 * 2 * 4 and m["segments_host_bytes"] == 4 * 2 * 4 * 256

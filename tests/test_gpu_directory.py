@@ -1,0 +1,257 @@
+"""The host KV reached through the two-level directory (avsg_set_host_directory)
+on the GPU, against the oracle on the same data laid out flat.  The pool
+holds every (unit, entry) row at a random place, with spare rows of bf16 NaN,
+so a row read from the wrong place shows in the attention output; the buffer
+bytes, the slot state and the attention must match the oracle's, in every
+transfer mode.  Entries without a row are range errors of their unit when
+they miss; appends write through the directory."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import tracegen as tg
+import oracle
+from oracle import attention as oatt
+from oracle import append as oapp
+from gpu_harness import check_attention, ensure_lib, say
+from directory_inputs import build_directory, permuted_pool
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "token": (tg.WORKLOADS[2].replace(batch=3, n_kv_heads=2, n_q_heads=8, n_entries=3001, k=300,
+                                      n_slots=900, steps=8), 64),
+    "mtp": (tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=3001, k=200,
+                                    n_slots=700, steps=6), 16),
+    "lru_pages": (tg.WORKLOADS[4].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=601, k=37,
+                                          n_slots=100, steps=8), 4),
+    "latent": (tg.WORKLOADS[5].replace(batch=2, n_entries=3001, k=600, n_slots=1500, steps=5), 256),
+}
+
+
+class DirRun:
+    """GPU context reading a permuted pool through a directory, beside the
+    oracle reading the flat rows."""
+
+    def __init__(self, w, seg, rng, mapping_filter=None, mode=None):
+        import torch
+        avsg = ensure_lib()
+        self.avsg, self.torch, self.w, self.seg = avsg, torch, w, seg
+        self.flat = tg.fill_kv(w)
+        pool, mapping = permuted_pool(self.flat, rng, extra_rows=w.units * 3)
+        if mapping_filter is not None:
+            mapping = {key: r for key, r in mapping.items() if mapping_filter(*key)}
+        self.mapping = mapping
+        top, segs = build_directory(mapping, w.units, w.n_entries, seg, spare_segments=1)
+        self.mapped = np.zeros((w.units, w.n_entries), bool)
+        for (u, e) in mapping:
+            self.mapped[u, e] = True
+        self.pool = avsg.HostBuffer(pool.shape)
+        self.pool.array[...] = pool
+        self.segs = avsg.HostBuffer(segs.shape, dtype=np.int32)
+        self.segs.array[...] = segs
+        self.top = torch.from_numpy(top).cuda()
+        self.cfg = avsg.config_from_workload(w)
+        self.ctx = avsg.Context(self.cfg)
+        if mode is not None:
+            self.ctx.set_transfer_mode(mode)
+        self.ctx.set_host_directory(self.top, self.segs, seg, len(segs), len(pool))
+        self.st = avsg.State(self.cfg)
+        self.ctx.reset(self.st.slot_table, self.st.lifetimes)
+        self.ob = oracle.OracleBuffer.for_workload(w, track_buf=True)
+
+    def step(self, t, sel_t):
+        torch, w, s = self.torch, self.w, self.st
+        q = tg.queries(w, t)
+        self.ctx.step(torch.from_numpy(np.ascontiguousarray(sel_t)).cuda(),
+                      torch.from_numpy(q.view(np.int16)).cuda(), self.pool, s.buf_kv,
+                      s.slot_table, s.lifetimes, s.out, s.stats)
+        torch.cuda.synchronize()
+        r = self.ob.step(sel_t, self.flat, mapped=self.mapped)
+        what = "t=%d" % t
+        assert np.array_equal(s.slot_table.cpu().numpy(), self.ob.slot_tok), what
+        assert np.array_equal(s.lifetimes.cpu().numpy(), self.ob.life), what
+        assert np.array_equal(s.stats.sel_slot.cpu().numpy(), r["sel_slot"]), what
+        assert np.array_equal(s.stats.hit_flag.cpu().numpy(), r["hit_flag"]), what
+        assert np.array_equal(s.stats.n_miss.cpu().numpy(), r["n_miss"]), what
+        assert np.array_equal(s.stats.unit_status.cpu().numpy(), r["status"]), what
+        assert np.array_equal(s.buf_kv.cpu().numpy().view(np.uint16), self.ob.buf), what
+        ref = oatt.attend(w, q, self.flat, sel_t, r["status"])
+        check_attention(s.out.cpu().numpy(), ref, what)
+        return r
+
+    def close(self):
+        self.ctx.close()
+        self.pool.free()
+        self.segs.free()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_directory_parity(name):
+    w, seg = CASES[name]
+    say("[directory] %s seg=%d units=%d" % (name, seg, w.units))
+    sel = tg.selections(w)
+    run = DirRun(w, seg, np.random.default_rng(len(name)))
+    try:
+        for t in range(w.steps):
+            r = run.step(t, sel[t])
+            assert (r["status"] == 0).all()
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_directory_transfer_modes(mode):
+    w, seg = CASES["token"]
+    w = w.replace(steps=5)
+    say("[directory] transfer mode %d" % mode)
+    sel = tg.selections(w)
+    run = DirRun(w, seg, np.random.default_rng(40 + mode), mode=mode)
+    try:
+        for t in range(w.steps):
+            run.step(t, sel[t])
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
+def test_unmapped_misses_are_unit_errors():
+    """Unit 1 lacks rows for a few entries: a step where one of them misses
+    is a range error of unit 1 alone, which keeps its state."""
+    avsg = ensure_lib()
+    w, seg = CASES["token"]
+    w = w.replace(steps=8)
+    sel = tg.selections(w)
+    holes = set(int(x) for x in np.unique(sel[3:, 1]))   # selected from step 3 on
+    holes = set(sorted(holes - set(int(x) for x in np.unique(sel[:3, 1])))[:3])
+    say("[directory] unmapped entries %s" % sorted(holes))
+    run = DirRun(w, seg, np.random.default_rng(77), mapping_filter=lambda u, e: not (u == 1 and e in holes))
+    errors = 0
+    try:
+        for t in range(w.steps):
+            before = run.st.slot_table[1].cpu().numpy().copy()
+            r = run.step(t, sel[t])
+            assert (np.delete(r["status"], 1) == 0).all()
+            if r["status"][1] != 0:
+                assert r["status"][1] == avsg.ERR_RANGE
+                assert np.array_equal(run.st.slot_table[1].cpu().numpy(), before)
+                errors += 1
+        assert errors > 0
+        assert run.ctx.last_error() == avsg.ERR_RANGE
+    finally:
+        run.close()
+
+
+def test_append_through_the_directory():
+    import torch
+    avsg = ensure_lib()
+    w, seg = CASES["lru_pages"]
+    say("[directory] append")
+    sel = tg.selections(w)
+    run = DirRun(w, seg, np.random.default_rng(91),
+                 mapping_filter=lambda u, e: not (u == w.units - 1 and e == 599))
+    rng = np.random.default_rng(3)
+    try:
+        for t in range(4):
+            run.step(t, sel[t])
+            pos = np.array([sel[t, b * w.n_kv_heads, 0, 0] * w.tokens_per_entry + t
+                            for b in range(w.batch)], np.int32)
+            x = rng.standard_normal((w.units, w.head_dim_qk + w.head_dim_v)).astype(np.float32)
+            new = (x.view(np.uint32) >> 16).astype(np.uint16)
+            oapp.append(w, run.flat, new, pos, run.ob.slot_tok, run.ob.buf)
+            run.ctx.append(torch.from_numpy(new.view(np.int16)).cuda(), torch.from_numpy(pos).cuda(),
+                           run.pool, run.st.buf_kv, run.st.slot_table)
+            torch.cuda.synchronize()
+            for (u, e), row in run.mapping.items():
+                assert np.array_equal(run.pool.array[row], run.flat[u, e]), (u, e)
+            assert np.array_equal(run.st.buf_kv.cpu().numpy().view(np.uint16), run.ob.buf)
+        assert run.ctx.last_error() == 0
+        # an append to an entry without a row writes nothing and is a range error
+        snapshot = run.pool.array.copy()
+        pos = np.zeros(w.batch, np.int32)
+        pos[-1] = 599 * w.tokens_per_entry
+        new = np.ones((w.units, w.head_dim_qk + w.head_dim_v), np.uint16)
+        run.ctx.append(torch.from_numpy(new.view(np.int16)).cuda(), torch.from_numpy(pos).cuda(),
+                       run.pool, run.st.buf_kv, run.st.slot_table)
+        torch.cuda.synchronize()
+        assert run.ctx.last_error() == avsg.ERR_RANGE
+        changed = np.nonzero((run.pool.array != snapshot).any(axis=1))[0]
+        last = w.units - w.n_kv_heads          # first unit of the last request
+        want = {run.mapping[(u, 0)] for u in range(last)}
+        want |= {run.mapping[(u, 599)] for u in range(last, w.units - 1)}
+        assert set(changed.tolist()) == want   # the last unit's entry 599 has no row
+    finally:
+        run.close()
+
+
+def test_directory_bad_arguments():
+    import torch
+    avsg = ensure_lib()
+    w, _ = CASES["token"]
+    cfg = avsg.config_from_workload(w)
+    ctx = avsg.Context(cfg)
+    top = torch.zeros((w.units, 64), dtype=torch.int32, device="cuda")
+    segs = avsg.HostBuffer((2, 64), dtype=np.int32)
+    try:
+        for seg, nseg, rows in ((48, 2, 10), (0, 2, 10), (64, 0, 10), (64, 2, 0), (64, 2, 2**31)):
+            st = avsg.avsg_set_host_directory(ctx.handle, top.data_ptr(), segs.ptr, seg, nseg, rows)
+            assert st == avsg.ERR_INVALID_ARG, (seg, nseg, rows)
+        unpinned = np.zeros((2, 64), np.int32)
+        st = avsg.avsg_set_host_directory(ctx.handle, top.data_ptr(), unpinned.ctypes.data, 64, 2, 10)
+        assert st == avsg.ERR_NOT_PINNED
+        assert avsg.avsg_set_host_directory(ctx.handle, top.data_ptr(), segs.ptr, 64, 2, 10) == avsg.OK
+        assert avsg.avsg_set_host_directory(ctx.handle, None, None, 0, 0, 0) == avsg.OK
+    finally:
+        ctx.close()
+        segs.free()
+
+
+def test_directory_full_size_long_context():
+    """The long-context workload at full size (256 units, 8192 pages of
+    8 KiB each) with its host rows reached through a directory of 256-entry
+    segments: state every step, attention on sampled units."""
+    import torch
+    avsg = ensure_lib()
+    w = tg.WORKLOADS[4]
+    seg, steps = 256, 24
+    say("[directory] full size long, %d steps" % steps)
+    n_seg = -(-w.n_entries // seg)
+    host = avsg.HostBuffer((w.units, w.n_entries, w.row_elems))
+    tg.fill_kv(w, out=host.array)
+    # pool = the same rows; entry e of unit u at pool row u * N + e, one
+    # segment per (unit, range of 256 entries), numbered in reverse so the
+    # top level is not the identity
+    segs = avsg.HostBuffer((w.units * n_seg, seg), dtype=np.int32)
+    order = np.arange(w.units * n_seg)[::-1].reshape(w.units, n_seg).astype(np.int32)
+    for u in range(w.units):
+        for s in range(n_seg):
+            segs.array[order[u, s]] = u * w.n_entries + s * seg + np.arange(seg)
+    top = torch.from_numpy(order.copy()).cuda()
+    cfg = avsg.config_from_workload(w)
+    ctx = avsg.Context(cfg)
+    ctx.set_host_directory(top, segs, seg, w.units * n_seg, w.units * w.n_entries)
+    st = avsg.State(cfg)
+    ctx.reset(st.slot_table, st.lifetimes)
+    ob = oracle.OracleBuffer.for_workload(w)
+    sel = tg.selections(w, steps=steps)
+    units = [0, 37, 128, 255]
+    try:
+        for t in range(steps):
+            q = tg.queries(w, t)
+            ctx.step(torch.from_numpy(sel[t]).cuda(), torch.from_numpy(q.view(np.int16)).cuda(),
+                     host.ptr, st.buf_kv, st.slot_table, st.lifetimes, st.out, st.stats)
+            torch.cuda.synchronize()
+            r = ob.step(sel[t])
+            assert np.array_equal(st.slot_table.cpu().numpy(), ob.slot_tok), t
+            assert np.array_equal(st.lifetimes.cpu().numpy(), ob.life), t
+            assert np.array_equal(st.stats.sel_slot.cpu().numpy(), r["sel_slot"]), t
+            if t in (0, steps - 1):
+                ref = oatt.attend(w, q, host.array, sel[t], r["status"], units=units)
+                check_attention(st.out.cpu().numpy(), ref, "t=%d" % t)
+        assert ctx.last_error() == 0
+    finally:
+        ctx.close()
+        host.free()
+        segs.free()
