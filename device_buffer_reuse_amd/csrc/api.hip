@@ -99,8 +99,10 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->host_row = off;    off = align256(off + 4 * (size_t)d->units * tk);
   ws->err_word = off;    off = align256(off + 8);
   ws->partials = off;
-  off = align256(off + 4 * (size_t)d->units * T * ws->nsplit *
-                           partial_stride(c.n_q_heads / c.n_kv_heads, c.head_dim_v));
+  const size_t part_bytes = c.kv_layout == AVSG_KV_LATENT
+                                ? latent_partial_bytes(c.n_q_heads, c.head_dim_v)
+                                : 4 * partial_stride(c.n_q_heads / c.n_kv_heads, c.head_dim_v);
+  off = align256(off + (size_t)d->units * T * ws->nsplit * part_bytes);
   ws->total = off;
   d->mr_lds = mr_lds_bytes(c, *ws, *d);
   d->merge_pow2 = 64;
@@ -521,7 +523,9 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   prof_mark(ctx, 3);
   if (ap.nsplit > 1) {
     const int G = c.n_q_heads / (c.kv_layout == AVSG_KV_LATENT ? 1 : c.n_kv_heads);
-    if (launch_attn_combine(ap, G, c.head_dim_v, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
+    if (launch_attn_combine(ap, G, c.head_dim_v, c.kv_layout == AVSG_KV_LATENT, ctx->stream) !=
+        hipSuccess)
+      return AVSG_ERR_HIP;
   }
   prof_mark(ctx, 4);
   if (ctx->prof_events && ctx->prof_used < ctx->prof_max) ctx->prof_used += 1;

@@ -92,25 +92,105 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
   }
 }
 
+// The latent layout's partials: each split's output normalized by its own
+// sum, as fp16, then its maxima and sums as fp32 (latent_partial_bytes):
+// out = sum_s l_s 2^(m_s - M) on_s / sum_s l_s 2^(m_s - M).  One thread per 4
+// consecutive outputs; with NS > 0 splits all loads are issued together, NS
+// = 0 loops over the context's split count.
 template <int NS>
-hipError_t launch_ns(const AttnParams& p, int G, int D, hipStream_t s) {
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_latent_kernel(AttnParams p, int G,
+                                                                              int D) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  const int dv4 = D >> 2;
+  const int nb = (int)gridDim.x;
+  const int bid = (nb & 7) == 0 ? (int)(blockIdx.x & 7) * (nb >> 3) + (int)(blockIdx.x >> 3)
+                                : (int)blockIdx.x;
+  const int64_t idx = (int64_t)bid * kCombineThreads + threadIdx.x;
+  const int64_t total = (int64_t)p.units * p.T * G * dv4;
+  if (idx >= total) return;
+  const int d4 = (int)(idx % dv4);
+  const int64_t rest = idx / dv4;
+  const int h = (int)(rest % G);
+  const int uj = (int)(rest / G);
+  const int u = uj / p.T, j = uj - u * p.T;
+  float4* orow = reinterpret_cast<float4*>(p.out + (((size_t)u * p.T + j) * p.Hq + h) * D) + d4;
+  if (p.unit_status[u] != 0) {
+    *orow = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int nsplit = NS > 0 ? NS : p.nsplit;
+  const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
+  const int nused = min(nsplit, (len + p.split_rows - 1) / p.split_rows);
+  const size_t pb = latent_partial_bytes(G, D);
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(p.partials) + (size_t)uj * nsplit * pb;
+  auto load = [&](int s, float& m, float& l, f16x4& o) {
+    const uint8_t* ps = base + (size_t)s * pb;
+    const float* pm = reinterpret_cast<const float*>(ps + (size_t)G * D * 2);
+    m = pm[h];
+    l = pm[G + h];
+    o = *(reinterpret_cast<const f16x4*>(ps + ((size_t)h * D) * 2) + d4);
+  };
+  float lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float wgt, const f16x4& o) {
+    lsum += wgt;
+    acc.x = fmaf((float)o[0], wgt, acc.x);
+    acc.y = fmaf((float)o[1], wgt, acc.y);
+    acc.z = fmaf((float)o[2], wgt, acc.z);
+    acc.w = fmaf((float)o[3], wgt, acc.w);
+  };
+  if constexpr (NS > 0) {
+    float m[NS], l[NS];
+    f16x4 o[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) load(min(s, nused - 1), m[s], l[s], o[s]);  // unused: weigh 0
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) mx = fmaxf(mx, m[s]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) add(s < nused ? l[s] * __builtin_amdgcn_exp2f(m[s] - mx) : 0.f, o[s]);
+  } else {
+    float mx = -INFINITY;
+    for (int s = 0; s < nused; ++s) {
+      float m, l;
+      f16x4 o;
+      load(s, m, l, o);
+      mx = fmaxf(mx, m);
+    }
+    for (int s = 0; s < nused; ++s) {
+      float m, l;
+      f16x4 o;
+      load(s, m, l, o);
+      add(l * __builtin_amdgcn_exp2f(m - mx), o);
+    }
+  }
+  const float inv = 1.f / lsum;
+  *orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+template <int NS>
+hipError_t launch_ns(const AttnParams& p, int G, int D, bool latent, hipStream_t s) {
   const int64_t total = (int64_t)p.units * p.T * G * (D / 4);
   const dim3 grid((unsigned)((total + kCombineThreads - 1) / kCombineThreads));
-  hipLaunchKernelGGL(attn_combine_kernel<NS>, grid, dim3(kCombineThreads), 0, s, p, G, D);
+  if (latent) {
+    hipLaunchKernelGGL(attn_combine_latent_kernel<NS>, grid, dim3(kCombineThreads), 0, s, p, G, D);
+  } else {
+    hipLaunchKernelGGL(attn_combine_kernel<NS>, grid, dim3(kCombineThreads), 0, s, p, G, D);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_combine(const AttnParams& p, int G, int D, hipStream_t s) {
+hipError_t launch_attn_combine(const AttnParams& p, int G, int D, bool latent, hipStream_t s) {
   if (D % 4 != 0) return hipErrorInvalidValue;
   switch (p.nsplit) {
-    case 2: return launch_ns<2>(p, G, D, s);
-    case 3: return launch_ns<3>(p, G, D, s);
-    case 4: return launch_ns<4>(p, G, D, s);
-    case 8: return launch_ns<8>(p, G, D, s);
-    case 16: return launch_ns<kMaxFastSplits>(p, G, D, s);
-    default: return launch_ns<0>(p, G, D, s);
+    case 2: return launch_ns<2>(p, G, D, latent, s);
+    case 3: return launch_ns<3>(p, G, D, latent, s);
+    case 4: return launch_ns<4>(p, G, D, latent, s);
+    case 8: return launch_ns<8>(p, G, D, latent, s);
+    case 16: return launch_ns<kMaxFastSplits>(p, G, D, latent, s);
+    default: return launch_ns<0>(p, G, D, latent, s);
   }
 }
 

@@ -43,7 +43,12 @@
 //  * The reference maximum of the online softmax moves only when a chunk
 //    exceeds it by 2^8, so the accumulators are rescaled rarely; the result
 //    does not depend on the reference chosen.
-//  * Split partials (max, sum, o) are merged by the combine kernel.
+//  * Split partials are merged by the combine kernel: each holds the split's
+//    output normalized by its own sum, as fp16 (half the bytes of fp32; the
+//    normalized values are convex combinations of value rows, bounded by
+//    them, and fp16 rounding adds about 1.5e-4 relative L1 to the merged
+//    output, against the 1e-3 tolerance), with the split's maximum and sum
+//    in fp32.
 #include <type_traits>
 #include <utility>
 
@@ -154,10 +159,12 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   const int e0 = sp * p.split_rows, e1 = min(e0 + p.split_rows, len);
   if (e0 >= e1) return;  // a split past the list's end (merged as empty)
   const int ne = e1 - e0;
-  float* orow = p.out + ((size_t)b * p.T + j) * p.Hq * kDv;
+  // (recomputed where it is written: kept live across the chunk loop it
+  // would take a register the loop needs)
+  auto out_rows = [&]() { return p.out + ((size_t)b * p.T + j) * p.Hq * kDv; };
   if (p.unit_status[u] != 0) {
     if (nsplit == 1)
-      for (int idx = tid; idx < G * kDv; idx += kThreads) orow[idx] = 0.f;
+      for (int idx = tid; idx < G * kDv; idx += kThreads) out_rows()[idx] = 0.f;
     return;
   }
   for (int i = tid; i < ne; i += kThreads) {
@@ -384,22 +391,33 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   }
 
   // lane holds O[h = w*16 + li][d = 16t + 4g + i]
-  const int h = w * 16 + li;
+  // (from a fresh thread index: a value kept from before the chunk loop
+  // would occupy a register through it)
+  int tid_end = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid_end));
+  const int h = (tid_end >> 6) * 16 + (tid_end & 15);
   if (nsplit == 1) {
     const float inv = 1.f / l_run;
 #pragma unroll
     for (int t = 0; t < kMTiles; ++t)
-      *reinterpret_cast<f32x4*>(orow + (size_t)h * kDv + 16 * t + 4 * g) = acc[t] * inv;
+      *reinterpret_cast<f32x4*>(out_rows() + (size_t)h * kDv + 16 * t + 4 * g) = acc[t] * inv;
     return;
   }
-  const size_t part_stride = partial_stride(G, kDv);
-  float* part = p.partials + ((size_t)uj * nsplit + sp) * part_stride;
+  uint8_t* part = reinterpret_cast<uint8_t*>(p.partials) +
+                  ((size_t)uj * nsplit + sp) * latent_partial_bytes(G, kDv);
+  _Float16* po = reinterpret_cast<_Float16*>(part);
+  float* pm = reinterpret_cast<float*>(part + (size_t)G * kDv * 2);
+  const float inv = 1.f / l_run;
 #pragma unroll
-  for (int t = 0; t < kMTiles; ++t)
-    *reinterpret_cast<f32x4*>(part + (size_t)h * kDv + 16 * t + 4 * g) = acc[t];
+  for (int t = 0; t < kMTiles; ++t) {
+    const f32x4 v = acc[t] * inv;
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<f16x4*>(po + (size_t)h * kDv + 16 * t + 4 * g) = hv;
+  }
   if (g == 0) {
-    part[G * kDv + h] = m_run;
-    part[G * kDv + G + h] = l_run;
+    pm[h] = m_run;
+    pm[G + h] = l_run;
   }
 }
 

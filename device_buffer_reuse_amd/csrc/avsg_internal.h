@@ -50,6 +50,12 @@ struct HostDir {
   int64_t pool_rows;
 };
 
+// Bytes of one split partial of the latent layout: o[G][D] normalized by the
+// split's sum, as fp16, then m[G] and l[G] as fp32, padded to 16 bytes.
+inline __host__ __device__ size_t latent_partial_bytes(int G, int D) {
+  return ((size_t)G * D * 2 + (size_t)8 * G + 15) & ~(size_t)15;
+}
+
 struct MatchReserveParams {
   const int32_t* sel;     // [units][T][k]
   const int32_t* sel_len; // [units][T] entries in use of each token's list, or null: k
@@ -102,7 +108,8 @@ struct AttnParams {
   const uint16_t* q;          // [B][T][Hq][dqk]
   uint16_t* buf_kv;           // [units][S][row]
   float* out;                 // [B][T][Hq][dv]
-  float* partials;            // [units*T][nsplit][partial_stride(G, dv)]
+  float* partials;            // [units*T][nsplit][partial_stride(G, dv)] floats, or (latent
+                              // layout) [units*T][nsplit][latent_partial_bytes(G, dv)] bytes
   int64_t S;
   int32_t units, Hkv, Hq, T, k, tpe, row_elems, nsplit, split_rows;
   int32_t token;              // query token of this launch
@@ -126,7 +133,7 @@ hipError_t launch_match_reserve(const MatchReserveParams& p, int units, size_t l
 hipError_t launch_gather(const GatherParams& p, int grid, hipStream_t s);
 hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s);
 hipError_t launch_attn_latent(const AttnParams& p, int dqk, int dv, hipStream_t s);
-hipError_t launch_attn_combine(const AttnParams& p, int G, int D, hipStream_t s);
+hipError_t launch_attn_combine(const AttnParams& p, int G, int D, bool latent, hipStream_t s);
 hipError_t attn_latent_set_lds();
 hipError_t launch_append(const AppendParams& p, int units, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
