@@ -32,7 +32,8 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
             "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
             "avsg_rebuild_index", "avsg_step_varlen", "avsg_set_capacity",
-            "avsg_plan_capacity", "avsg_step_static", "avsg_set_host_directory"]
+            "avsg_plan_capacity", "avsg_step_static", "avsg_set_host_directory",
+            "avsg_set_gather_workgroups"]
 STATIC_SCRATCH_BYTES = 64 << 20   # AVSG_STATIC_SCRATCH_BYTES
 
 
@@ -50,7 +51,7 @@ class avsg_config(ctypes.Structure):
                 ("tokens_per_entry", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("n_slots", ctypes.c_int32), ("policy", ctypes.c_int32),
                 ("lifetime_L", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("attn_split_rows", ctypes.c_int32)]
 
 
 class avsg_hit_stats(ctypes.Structure):
@@ -68,6 +69,11 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libavsg.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    # torch carries its own copy of the HIP runtime under the same soname
+    # (libamdhip64.so.7).  Loaded first, it is the copy libavsg binds to; were
+    # libavsg loaded first, the process would hold two runtimes and the one
+    # that initialises second finds no GPU.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     cfgp = ctypes.POINTER(avsg_config)
@@ -96,6 +102,7 @@ def load():
         "avsg_attn_splits": ([p], ctypes.c_int32),
         "avsg_profile_begin": ([p, ctypes.c_int32], i32),
         "avsg_set_transfer_mode": ([p, ctypes.c_int32], i32),
+        "avsg_set_gather_workgroups": ([p, ctypes.c_int32], i32),
         "avsg_set_match_mode": ([p, ctypes.c_int32], i32),
         "avsg_profile_end": ([p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)], i32),
     }
@@ -210,6 +217,10 @@ def avsg_set_transfer_mode(ctx: int, mode: int) -> int:
     return load().avsg_set_transfer_mode(ctx, mode)
 
 
+def avsg_set_gather_workgroups(ctx: int, n: int) -> int:
+    return load().avsg_set_gather_workgroups(ctx, n)
+
+
 def avsg_set_match_mode(ctx: int, mode: int) -> int:
     return load().avsg_set_match_mode(ctx, mode)
 
@@ -240,18 +251,18 @@ def avsg_host_free(ptr: int) -> int:
 
 def config(batch, n_kv_heads, n_q_heads, n_q_tokens, head_dim_qk, head_dim_v, kv_layout,
            n_entries, tokens_per_entry, k, n_slots, policy, lifetime_L, n_buckets,
-           softmax_scale) -> avsg_config:
+           softmax_scale, attn_split_rows=0) -> avsg_config:
     return avsg_config(batch, n_kv_heads, n_q_heads, n_q_tokens, head_dim_qk, head_dim_v,
                        kv_layout, n_entries, tokens_per_entry, k, n_slots, policy, lifetime_L,
-                       n_buckets, softmax_scale)
+                       n_buckets, softmax_scale, attn_split_rows)
 
 
-def config_from_workload(w) -> avsg_config:
+def config_from_workload(w, attn_split_rows: int = 0) -> avsg_config:
     """avsg_config of a tracegen.Workload (shapes and policy only)."""
     return config(w.batch, w.n_kv_heads, w.n_q_heads, w.n_q_tokens, w.head_dim_qk, w.head_dim_v,
                   KV_LATENT if w.latent else KV_SPLIT, w.n_entries, w.tokens_per_entry, w.k,
                   w.n_slots, POLICY_BUCKET_LRU if w.policy == "lru" else POLICY_LIFETIME,
-                  w.lifetime_L, w.n_buckets, w.softmax_scale)
+                  w.lifetime_L, w.n_buckets, w.softmax_scale, attn_split_rows)
 
 
 class HostBuffer:
@@ -408,6 +419,11 @@ class Context:
         st = avsg_set_transfer_mode(self.handle, mode)
         if st != OK:
             raise AvsgError(st, "avsg_set_transfer_mode")
+
+    def set_gather_workgroups(self, n: int):
+        st = avsg_set_gather_workgroups(self.handle, n)
+        if st != OK:
+            raise AvsgError(st, "avsg_set_gather_workgroups")
 
     def set_match_mode(self, mode: int):
         st = avsg_set_match_mode(self.handle, mode)

@@ -84,7 +84,9 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   d->ubits = 1;
   while ((1 << d->ubits) < ws->ucap) ++d->ubits;
   const int64_t rows = (int64_t)c.k * c.tokens_per_entry;
-  if (c.kv_layout == AVSG_KV_LATENT) {
+  if (c.attn_split_rows > 0) {
+    ws->split_rows = c.attn_split_rows;
+  } else if (c.kv_layout == AVSG_KV_LATENT) {
     ws->split_rows = 512;  // 4 splits: one 8-wave workgroup per CU for 64 requests
   } else {
     ws->split_rows = 256;  // one workgroup of the split-layout attention
@@ -190,6 +192,10 @@ static avsg_status check_config_impl(const avsg_config* c) {
   if (c->policy == AVSG_POLICY_LIFETIME && c->lifetime_L > 126) return AVSG_ERR_UNSUPPORTED;
   if (c->policy == AVSG_POLICY_BUCKET_LRU && c->n_buckets > 127) return AVSG_ERR_UNSUPPORTED;
   if (c->kv_layout != AVSG_KV_SPLIT && c->kv_layout != AVSG_KV_LATENT) return AVSG_ERR_INVALID_ARG;
+  if (c->attn_split_rows != 0 &&
+      (c->attn_split_rows < 32 || c->attn_split_rows % 32 != 0 ||
+       c->attn_split_rows > (c->kv_layout == AVSG_KV_LATENT ? 512 : 256)))
+    return AVSG_ERR_INVALID_ARG;
   if (!(c->softmax_scale > 0.f)) return AVSG_ERR_INVALID_ARG;
   if ((int64_t)c->batch * c->n_kv_heads > (1 << 20)) return AVSG_ERR_UNSUPPORTED;
   if (c->n_q_tokens > 2) return AVSG_ERR_UNSUPPORTED;
@@ -371,6 +377,12 @@ avsg_status avsg_set_step(avsg_ctx* ctx, int64_t t) {
 }
 
 int32_t avsg_attn_splits(const avsg_ctx* ctx) { return ctx ? ctx->ws.nsplit : 0; }
+
+avsg_status avsg_set_gather_workgroups(avsg_ctx* ctx, int32_t n) {
+  if (!ctx || n < 0 || n > 65535) return AVSG_ERR_INVALID_ARG;
+  ctx->gather_grid = n == 0 ? ctx->num_cus * 2 : n;
+  return AVSG_OK;
+}
 
 avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes) {
   if (!ctx || !slot_table || !lifetimes) return AVSG_ERR_INVALID_ARG;

@@ -613,7 +613,7 @@ static hipError_t launch_g(const AttnParams& p0, hipStream_t s) {
 }
 
 hipError_t launch_attn_split(const AttnParams& p, int G, hipStream_t s) {
-  if (p.split_rows != kSplitRows) return hipErrorInvalidValue;
+  if (p.split_rows > kSplitRows || p.split_rows % kChunk != 0) return hipErrorInvalidValue;
   switch (G) {
     case 1: return launch_g<1>(p, s);
     case 2: return launch_g<2>(p, s);

@@ -92,6 +92,11 @@ typedef struct avsg_config {
   int32_t lifetime_L;        /* L >= 1 (lifetime policy) */
   int32_t n_buckets;         /* B >= 1 (bucketed LRU) */
   float softmax_scale;       /* multiplies q.k before the softmax */
+  /* token rows per attention workgroup (split-k): 0 = the library's choice
+   * (256 for the split layout, 512 for the latent layout), else a multiple
+   * of 32 in [32, 256] (split layout) or [32, 512] (latent layout).  Results
+   * other than the attention output's rounding do not depend on it. */
+  int32_t attn_split_rows;
 } avsg_config;
 
 /* Per-step outputs besides the attention result; all device pointers. */
@@ -373,6 +378,12 @@ avsg_status avsg_set_match_mode(avsg_ctx* ctx, int32_t mode);
 
 /* Number of split-k partitions the attention of one (unit, token) uses. */
 int32_t avsg_attn_splits(const avsg_ctx* ctx);
+
+/* Workgroups of the separate gather kernel (transfer modes BALANCED; the
+ * list of missed rows is split into that many equal shares): 0 = the
+ * library's choice (two per compute unit), else [1, 65535].  Results do not
+ * depend on it. */
+avsg_status avsg_set_gather_workgroups(avsg_ctx* ctx, int32_t n);
 
 /* Per-kernel timing with HIP events on the context's stream (observability,
  * not part of the method).  avsg_profile_begin creates events for up to

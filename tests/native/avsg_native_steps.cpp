@@ -58,6 +58,7 @@ int main(int argc, char** argv) {
   cfg.lifetime_L = 3;
   cfg.n_buckets = 64;
   cfg.softmax_scale = 1.0f / 11.313708498984761f;
+  cfg.attn_split_rows = 0;  // the library's choice
   CHECK(avsg_check_config(&cfg) == AVSG_OK);
   const int units = B * Hkv, row = 2 * D, Hq = Hkv * G;
 

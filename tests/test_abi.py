@@ -30,12 +30,28 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     avsg = _lib()
-    lib = ctypes.CDLL(avsg.LIB_PATH)
+    lib = avsg.load()
     names = _declared()
     assert len(names) >= 14
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(avsg.EXPORTED) == names
+
+
+def test_one_hip_runtime_in_the_process():
+    """The binding loads libavsg after torch, so the library binds to the HIP
+    runtime torch carries instead of bringing a second copy into the process
+    (two runtimes cannot both open the GPU).  Run in a fresh interpreter that
+    loads the binding before anything imports torch."""
+    import subprocess
+    import sys
+    _lib()
+    code = ("from device_buffer_reuse_amd import avsg; avsg.load(); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout
+    libs = eval(out.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
 
 
 def test_config_checks_host_only():
@@ -147,3 +163,20 @@ def test_binding_argument_counts_match_the_header():
         params = m.group(1).strip()
         n = 0 if params in ("", "void") else params.count(",") + 1
         assert len(getattr(lib, name).argtypes) == n, (name, n)
+
+
+def test_split_rows_out_of_range_are_refused():
+    """avsg_config.attn_split_rows: 0 or a multiple of 32 up to 256 (split
+    layout) or 512 (latent layout); host-only check."""
+    avsg = _lib()
+    for wl, good, bad in ((2, [0, 32, 128, 256], [16, 48, 288, -32]),
+                          (5, [0, 32, 96, 512], [16, 530, 1024])):
+        for rows in good:
+            assert avsg.avsg_check_config(avsg.config_from_workload(tg.WORKLOADS[wl], rows)) == avsg.OK
+        for rows in bad:
+            cfg = avsg.config_from_workload(tg.WORKLOADS[wl], attn_split_rows=rows)
+            assert avsg.avsg_check_config(cfg) == avsg.ERR_INVALID_ARG, (wl, rows)
+    # fewer rows per split: more splits, a larger workspace
+    a = avsg.avsg_workspace_bytes(avsg.config_from_workload(tg.WORKLOADS[2], 0))
+    b = avsg.avsg_workspace_bytes(avsg.config_from_workload(tg.WORKLOADS[2], 64))
+    assert b > a
