@@ -33,47 +33,58 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
   const int b = u / p.Hkv, g = u - b * p.Hkv;
   float4* orow = reinterpret_cast<float4*>(
       p.out + ((((size_t)b * p.T + j) * p.Hq) + (size_t)g * G + h) * D) + d4;
-  if (p.unit_status[u] != 0) {
-    *orow = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
   const int nsplit = NS > 0 ? NS : p.nsplit;
-  // splits holding rows: all of them, or those covering a shortened list
-  const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
-  const int nused = min(nsplit, (len * p.tpe + p.split_rows - 1) / p.split_rows);
   const size_t ps = partial_stride(G, D);  // floats per split partial, multiple of 4
   const float* pbase = p.partials + (size_t)uj * nsplit * ps;
   const float* mrow = pbase + (size_t)G * D + h;
   const float* lrow = mrow + G;
   const float4* orow_s = reinterpret_cast<const float4*>(pbase + (size_t)h * D) + d4;
   if constexpr (NS > 0) {
+    // every split's partial is loaded together with the unit's status and
+    // list length (one memory round trip); splits past a shortened list
+    // hold stale values and are dropped by selection, never by a weight
+    const int status = p.unit_status[u];
+    const int len_in = p.sel_len ? p.sel_len[uj] : p.k;
     float m[NS], l[NS];
     float4 o[NS];
-    // unused splits reload the last used one and weigh 0
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int sl = min(s, nused - 1);
-      m[s] = mrow[sl * ps];
-      l[s] = lrow[sl * ps];
-      o[s] = orow_s[sl * (ps / 4)];
+      m[s] = mrow[s * ps];
+      l[s] = lrow[s * ps];
+      o[s] = orow_s[s * (ps / 4)];
     }
+    if (status != 0) {
+      *orow = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    // splits holding rows: all of them, or those covering a shortened list
+    const int len = min(max(len_in, 1), p.k);
+    const int nused = min(nsplit, (len * p.tpe + p.split_rows - 1) / p.split_rows);
     float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) mx = fmaxf(mx, m[s]);
+    for (int s = 0; s < NS; ++s) mx = s < nused ? fmaxf(mx, m[s]) : mx;
     float lsum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const float wgt = s < nused ? __builtin_amdgcn_exp2f(m[s] - mx) : 0.f;
-      lsum = fmaf(l[s], wgt, lsum);
-      acc.x = fmaf(o[s].x, wgt, acc.x);
-      acc.y = fmaf(o[s].y, wgt, acc.y);
-      acc.z = fmaf(o[s].z, wgt, acc.z);
-      acc.w = fmaf(o[s].w, wgt, acc.w);
+      if (s < nused) {
+        const float wgt = __builtin_amdgcn_exp2f(m[s] - mx);
+        lsum = fmaf(l[s], wgt, lsum);
+        acc.x = fmaf(o[s].x, wgt, acc.x);
+        acc.y = fmaf(o[s].y, wgt, acc.y);
+        acc.z = fmaf(o[s].z, wgt, acc.z);
+        acc.w = fmaf(o[s].w, wgt, acc.w);
+      }
     }
     const float inv = 1.f / lsum;
     *orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   } else {
+    if (p.unit_status[u] != 0) {
+      *orow = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
+    const int nused = min(nsplit, (len * p.tpe + p.split_rows - 1) / p.split_rows);
     float mx = -INFINITY;
     for (int s = 0; s < nused; ++s) mx = fmaxf(mx, mrow[s * ps]);
     float lsum = 0.f;
@@ -114,13 +125,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_latent_kernel(At
   const int uj = (int)(rest / G);
   const int u = uj / p.T, j = uj - u * p.T;
   float4* orow = reinterpret_cast<float4*>(p.out + (((size_t)u * p.T + j) * p.Hq + h) * D) + d4;
-  if (p.unit_status[u] != 0) {
-    *orow = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
   const int nsplit = NS > 0 ? NS : p.nsplit;
-  const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
-  const int nused = min(nsplit, (len + p.split_rows - 1) / p.split_rows);
   const size_t pb = latent_partial_bytes(G, D);
   const uint8_t* base = reinterpret_cast<const uint8_t*>(p.partials) + (size_t)uj * nsplit * pb;
   auto load = [&](int s, float& m, float& l, f16x4& o) {
@@ -140,16 +145,34 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_latent_kernel(At
     acc.w = fmaf((float)o[3], wgt, acc.w);
   };
   if constexpr (NS > 0) {
+    // all splits' partials, the unit's status and its list length in one
+    // memory round trip; splits past a shortened list are dropped by
+    // selection
+    const int status = p.unit_status[u];
+    const int len_in = p.sel_len ? p.sel_len[uj] : p.k;
     float m[NS], l[NS];
     f16x4 o[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) load(min(s, nused - 1), m[s], l[s], o[s]);  // unused: weigh 0
+    for (int s = 0; s < NS; ++s) load(s, m[s], l[s], o[s]);
+    if (status != 0) {
+      *orow = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    const int len = min(max(len_in, 1), p.k);
+    const int nused = min(nsplit, (len + p.split_rows - 1) / p.split_rows);
     float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) mx = fmaxf(mx, m[s]);
+    for (int s = 0; s < NS; ++s) mx = s < nused ? fmaxf(mx, m[s]) : mx;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) add(s < nused ? l[s] * __builtin_amdgcn_exp2f(m[s] - mx) : 0.f, o[s]);
+    for (int s = 0; s < NS; ++s)
+      if (s < nused) add(l[s] * __builtin_amdgcn_exp2f(m[s] - mx), o[s]);
   } else {
+    if (p.unit_status[u] != 0) {
+      *orow = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    const int len = p.sel_len ? min(max(p.sel_len[uj], 1), p.k) : p.k;
+    const int nused = min(nsplit, (len + p.split_rows - 1) / p.split_rows);
     float mx = -INFINITY;
     for (int s = 0; s < nused; ++s) {
       float m, l;

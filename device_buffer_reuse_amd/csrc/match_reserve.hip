@@ -482,6 +482,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     }
   }
   int hit_i[MAXP];
+#pragma unroll
+  for (int q = 0; q < MAXP; ++q) hit_i[q] = -1;
   if (sMisc[0] == 0 && p.match_mode == AVSG_MATCH_MERGE) {
     // comparison baseline: sort the resident (id, slot) pairs by id (bitonic,
     // in LDS), then one lane walks the sorted union and the sorted residents
@@ -688,6 +690,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     }
     if (bad) atomicOr(&sMisc[0], kFlagState);
   }
+  {  // hits of this wave, summed into sMisc[2]: with every entry of U a hit
+     // there are no misses to rank
+    int nh = 0;
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) nh += __popcll(__ballot(hit_i[q] >= 0));
+    if (lane == 0 && nh) atomicAdd(&sMisc[2], nh);
+  }
   __syncthreads();
 
   // a data error: the unit keeps its state (nothing has been written to it)
@@ -743,7 +752,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // ---- 6. misses of U in ascending id order (two consecutive entries per
   //         thread, ranked by two ballots)
   int m = 0;
-  for (int c0 = 0; c0 < nu; c0 += 2 * kMRThreads) {
+  const bool all_hit = sMisc[2] == nu;  // the same in every wave
+  for (int c0 = 0; c0 < (all_hit ? 0 : nu); c0 += 2 * kMRThreads) {
     const int i0 = c0 + 2 * tid;
     const int v0 = sUslot[min(i0, nu - 1)], v1 = sUslot[min(i0 + 1, nu - 1)];
     const bool m0 = i0 < nu && v0 < 0;
