@@ -408,9 +408,18 @@ def ablations(a):
         ms, kern = b.one_pass(a.fill, a.fill + n, profile=True)
         match[name] = {"match_reserve_us": round(kern[0] / n * 1e3, 2),
                        "ms_per_step": round(ms / n, 4)}
+        if mode == 1:
+            # the baseline's two phases, from the kernel's own clock
+            sort_ms, walk_ms = b.ctx.profile_match_phases()
+            match[name]["sort_us"] = round(sort_ms / n * 1e3, 2)
+            match[name]["walk_us"] = round(walk_ms / n * 1e3, 2)
     b.ctx.set_match_mode(0)
-    match["speedup"] = round(match["dual_pointer"]["match_reserve_us"] /
-                             match["hash"]["match_reserve_us"], 2)
+    dp = match["dual_pointer"]
+    match["speedup"] = round(dp["match_reserve_us"] / match["hash"]["match_reserve_us"], 2)
+    # as if the residents were kept sorted across steps: the baseline's
+    # kernel time without its per-step sort
+    match["speedup_without_sort"] = round(
+        (dp["match_reserve_us"] - dp["sort_us"]) / match["hash"]["match_reserve_us"], 2)
     out["matching"] = match
     assert b.ctx.last_error() == 0
     b.close()

@@ -33,7 +33,7 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
             "avsg_rebuild_index", "avsg_step_varlen", "avsg_set_capacity",
             "avsg_plan_capacity", "avsg_step_static", "avsg_set_host_directory",
-            "avsg_set_gather_workgroups"]
+            "avsg_set_gather_workgroups", "avsg_profile_match_phases"]
 STATIC_SCRATCH_BYTES = 64 << 20   # AVSG_STATIC_SCRATCH_BYTES
 
 
@@ -105,6 +105,8 @@ def load():
         "avsg_set_gather_workgroups": ([p, ctypes.c_int32], i32),
         "avsg_set_match_mode": ([p, ctypes.c_int32], i32),
         "avsg_profile_end": ([p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)], i32),
+        "avsg_profile_match_phases": ([p, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -235,6 +237,13 @@ def avsg_profile_end(ctx: int):
     n = ctypes.c_int32()
     st = load().avsg_profile_end(ctx, ms, ctypes.byref(n))
     return st, [ms[0], ms[1], ms[2], ms[3]], n.value
+
+
+def avsg_profile_match_phases(ctx: int):
+    """Returns (status, sort ms, walk ms) of the dual-pointer baseline."""
+    a, b = ctypes.c_double(), ctypes.c_double()
+    st = load().avsg_profile_match_phases(ctx, ctypes.byref(a), ctypes.byref(b))
+    return st, a.value, b.value
 
 
 def avsg_host_alloc(nbytes: int, flags: int = 0):
@@ -441,6 +450,13 @@ class Context:
         if st != OK:
             raise AvsgError(st, "avsg_profile_end")
         return ms, n
+
+    def profile_match_phases(self):
+        """(sort ms, walk ms) of the dual-pointer baseline in the last profile"""
+        st, a, b = avsg_profile_match_phases(self.handle)
+        if st != OK:
+            raise AvsgError(st, "avsg_profile_match_phases")
+        return a, b
 
     @property
     def attn_splits(self) -> int:

@@ -27,6 +27,7 @@ struct avsg_ctx {
   int lds_max;
   hipEvent_t* prof_events;       // kProfMarks per profiled step, or null
   int32_t prof_max, prof_used;
+  double prof_sort_ms, prof_walk_ms;  // merge baseline's phases in the last profile
 };
 
 namespace avsg {
@@ -100,6 +101,7 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->fetch = off;       off = align256(off + (size_t)d->units * tk);
   ws->host_row = off;    off = align256(off + 4 * (size_t)d->units * tk);
   ws->err_word = off;    off = align256(off + 8);
+  ws->phase_clk = off;   off = align256(off + 3 * 8);
   ws->partials = off;
   const size_t part_bytes = c.kv_layout == AVSG_KV_LATENT
                                 ? latent_partial_bytes(c.n_q_heads, c.head_dim_v)
@@ -277,6 +279,7 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->cap = nullptr;
   c->prof_events = nullptr;
   c->prof_max = c->prof_used = 0;
+  c->prof_sort_ms = c->prof_walk_ms = 0.0;
   c->transfer_mode = AVSG_TRANSFER_FUSED;
   c->match_mode = AVSG_MATCH_HASH;
   c->lds_max = lds_max;
@@ -329,11 +332,19 @@ avsg_status avsg_profile_begin(avsg_ctx* ctx, int32_t max_steps) {
   if (!ctx->prof_events) return AVSG_ERR_INVALID_ARG;
   ctx->prof_max = max_steps;
   ctx->prof_used = 0;
+  ctx->prof_sort_ms = ctx->prof_walk_ms = 0.0;
   for (int32_t i = 0; i < kProfMarks * max_steps; ++i)
     if (hipEventCreate(&ctx->prof_events[i]) != hipSuccess) {
       destroy_prof_events(ctx);
       return AVSG_ERR_HIP;
     }
+  // the merge baseline's phase clocks start from zero (a fill kernel, in
+  // stream order with the steps)
+  if (launch_fill_i32((int32_t*)(ctx->workspace + ctx->ws.phase_clk), 0, 6, ctx->stream) !=
+      hipSuccess) {
+    destroy_prof_events(ctx);
+    return AVSG_ERR_HIP;
+  }
   return AVSG_OK;
 }
 
@@ -352,9 +363,26 @@ avsg_status avsg_profile_end(avsg_ctx* ctx, double* ms, int32_t* steps) {
       }
       ms[k] += x;
     }
+  unsigned long long clk[3] = {0, 0, 0};
+  if (st == AVSG_OK &&
+      hipMemcpy(clk, ctx->workspace + ctx->ws.phase_clk, sizeof(clk), hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    st = AVSG_ERR_HIP;
+  // per step: the mean over units of each phase (units run concurrently);
+  // the clock counts at 100 MHz
+  const double per_unit_step = clk[2] > 0 ? (double)ctx->prof_used / (double)clk[2] : 0.0;
+  ctx->prof_sort_ms = (double)clk[0] * 1e-5 * per_unit_step;
+  ctx->prof_walk_ms = (double)clk[1] * 1e-5 * per_unit_step;
   *steps = ctx->prof_used;
   destroy_prof_events(ctx);
   return st;
+}
+
+avsg_status avsg_profile_match_phases(const avsg_ctx* ctx, double* sort_ms, double* walk_ms) {
+  if (!ctx || !sort_ms || !walk_ms) return AVSG_ERR_INVALID_ARG;
+  *sort_ms = ctx->prof_sort_ms;
+  *walk_ms = ctx->prof_walk_ms;
+  return AVSG_OK;
 }
 
 static inline void prof_mark(avsg_ctx* ctx, int k) {
@@ -479,6 +507,9 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   mp.direct_words = ctx->match_mode == AVSG_MATCH_HASH ? ctx->d.direct_words : 0;
   mp.dir = ctx->dir;
   mp.host_row = (int32_t*)(ws + ctx->ws.host_row);
+  mp.phase_clk = (merge && ctx->prof_events && ctx->prof_used < ctx->prof_max)
+                     ? (unsigned long long*)(ws + ctx->ws.phase_clk)
+                     : nullptr;
   prof_mark(ctx, 0);
   const size_t mr_lds = merge ? ctx->d.mr_lds_merge : ctx->d.mr_lds;
   if (launch_match_reserve(mp, ctx->d.units, mr_lds, ctx->stream) != hipSuccess)

@@ -17,7 +17,7 @@ constexpr int kGatherThreads = 256;
 
 // Layout of the caller's workspace (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t unit_status, miss_count, misses, fetch, host_row, err_word, partials, total;
+  size_t unit_status, miss_count, misses, fetch, host_row, err_word, phase_clk, partials, total;
   int32_t ucap;       // union capacity per unit = min(T*k, S)
   int32_t table_cap;  // hash table cells, power of two >= 2*ucap
   int32_t nsplit;     // attention splits per (unit, token)
@@ -82,6 +82,9 @@ struct MatchReserveParams {
   // host KV through a two-level directory (null dir_top: flat [units][N][row])
   HostDir dir;
   int32_t* host_row;      // workspace [units][T][k]: pool row of each fetched entry (directory)
+  // merge baseline under profiling: summed 100 MHz clocks of its sort and
+  // of its walk over all units, and the units counted (null: not recorded)
+  unsigned long long* phase_clk;
 };
 
 struct GatherParams {

@@ -509,6 +509,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     int2* sPair = reinterpret_cast<int2*>(
         (reinterpret_cast<uintptr_t>(sDup + (T > 1 ? k + 1 : 0)) + 7) & ~(uintptr_t)7);
     int32_t* sSlotU = reinterpret_cast<int32_t*>(sPair + P2);              // [S]
+    // under profiling, thread 0 stamps the sort and the walk (100 MHz clock)
+    const uint64_t c_sort0 = p.phase_clk ? __builtin_amdgcn_s_memrealtime() : 0;
     for (int i = tid; i < P2; i += kMRThreads) {
       const int32_t x = i < cap ? slot_table[i] : -1;
       sPair[i] = make_int2((x >= 0 && x < N) ? x : INT_MAX, i);
@@ -531,6 +533,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         }
         __syncthreads();
       }
+    const uint64_t c_sort1 = p.phase_clk ? __builtin_amdgcn_s_memrealtime() : 0;
     if (tid == 0) {
       int a = 0, b = 0, dup = 0;
       while (a < nu && b < P2 && sPair[b].x != INT_MAX) {
@@ -550,6 +553,12 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       if (dup) atomicOr(&sMisc[0], kFlagState);
     }
     __syncthreads();
+    if (p.phase_clk && tid == 0) {
+      const uint64_t c_walk1 = __builtin_amdgcn_s_memrealtime();
+      atomicAdd(&p.phase_clk[0], (unsigned long long)(c_sort1 - c_sort0));
+      atomicAdd(&p.phase_clk[1], (unsigned long long)(c_walk1 - c_sort1));
+      atomicAdd(&p.phase_clk[2], 1ull);
+    }
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) {
       if (bin[q] == kInvalid || tok[q] < 0) continue;

@@ -397,6 +397,19 @@ avsg_status avsg_set_gather_workgroups(avsg_ctx* ctx, int32_t n);
 avsg_status avsg_profile_begin(avsg_ctx* ctx, int32_t max_steps);
 avsg_status avsg_profile_end(avsg_ctx* ctx, double* ms, int32_t* steps);
 
+/* The two phases of the scalar dual-pointer baseline (AVSG_MATCH_MERGE; the
+ * AVSG abstract compares its vectorised matching against scalar
+ * dual-pointer matching) in the last profiling session that
+ * avsg_profile_end closed: *sort_ms is the summed time of ordering the
+ * resident ids (loading them and sorting (id, slot) pairs by id), *walk_ms
+ * that of the one-lane walk over the sorted union and the sorted residents,
+ * each the mean over units per profiled step (units run concurrently), from
+ * the GPU's constant 100 MHz clock.  Both are 0 when no profiled step ran in
+ * that mode.  The rest of the match kernel's time (validation, policy,
+ * victims, reservation) is common to both modes.  Returns
+ * AVSG_ERR_INVALID_ARG on a null argument. */
+avsg_status avsg_profile_match_phases(const avsg_ctx* ctx, double* sort_ms, double* walk_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -215,6 +215,38 @@ def test_profile_events_per_stage():
     a.close()
 
 
+def test_profile_merge_baseline_phases():
+    """The dual-pointer baseline reports the time of its sort and of its walk
+    under profiling (both positive, walk and sort within the match stage);
+    the hash modes report none; profiling it does not change its results."""
+    say("[behaviour] profile merge phases")
+    sel = tg.selections(W)
+    a, oa, _ = _run(W, sel, stop=3)
+    run = Runner(W, host=a.host, track_buf=False)
+    run.ctx.set_match_mode(avsg_match_merge())
+    run.ctx.profile_begin(3)
+    for t in range(3):
+        run.gpu_step(sel[t], tg.queries(W, t))
+    ms, n = run.ctx.profile_end()
+    sort_ms, walk_ms = run.ctx.profile_match_phases()
+    assert n == 3 and sort_ms > 0 and walk_ms > 0
+    assert sort_ms + walk_ms < ms[0]
+    assert np.array_equal(run.st.out.cpu().numpy(), oa[2])
+    run.ctx.set_match_mode(0)
+    run.ctx.profile_begin(1)
+    run.gpu_step(sel[3], tg.queries(W, 3))
+    run.ctx.profile_end()
+    assert run.ctx.profile_match_phases() == (0.0, 0.0)
+    assert run.ctx.last_error() == 0
+    run.close()
+    a.close()
+
+
+def avsg_match_merge():
+    from device_buffer_reuse_amd import avsg
+    return avsg.MATCH_MERGE
+
+
 def test_new_entry_points_reject_bad_arguments():
     """Argument errors of the append, the variable-length step and the
     capacity call are reported synchronously and enqueue nothing."""
