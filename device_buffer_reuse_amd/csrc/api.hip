@@ -116,9 +116,9 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   // and slot -> union index
   WsLayout wm = *ws;
   wm.table_cap = next_pow2(2 * (int64_t)ws->ucap);
-  d->table_cap_merge = wm.table_cap;
-  d->log_table_cap_merge = 0;
-  while ((1 << d->log_table_cap_merge) < wm.table_cap) ++d->log_table_cap_merge;
+  d->table_cap_half = wm.table_cap;
+  d->log_table_cap_half = 0;
+  while ((1 << d->log_table_cap_half) < wm.table_cap) ++d->log_table_cap_half;
   d->mr_lds_merge = mr_lds_bytes(c, wm, *d) + 4 + 8 * (size_t)d->merge_pow2 + 4 * (size_t)c.n_slots;
   return true;
 }
@@ -495,8 +495,11 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   mp.k = c.k;
   mp.ucap = ctx->ws.ucap;
   const bool merge = ctx->match_mode == AVSG_MATCH_MERGE;
-  mp.table_cap = merge ? ctx->d.table_cap_merge : ctx->ws.table_cap;
-  mp.log_table_cap = merge ? ctx->d.log_table_cap_merge : ctx->d.log_table_cap;
+  // the table-only mode runs at load factor <= 1/2 (the setting the batch
+  // workload states), in the LDS sized for the default mode's larger table
+  const bool half = merge || ctx->match_mode == AVSG_MATCH_HASH_TABLE;
+  mp.table_cap = half ? ctx->d.table_cap_half : ctx->ws.table_cap;
+  mp.log_table_cap = half ? ctx->d.log_table_cap_half : ctx->d.log_table_cap;
   mp.ubits = ctx->d.ubits;
   mp.policy = c.policy;
   mp.L = c.lifetime_L;

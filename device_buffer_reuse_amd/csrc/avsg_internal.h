@@ -29,7 +29,9 @@ struct Derived {
   size_t mr_lds;        // dynamic LDS bytes of match_reserve
   size_t mr_lds_merge;  // the same with the merge baseline's sort buffers
   int32_t merge_pow2;
-  int32_t table_cap_merge, log_table_cap_merge;  // hash table of the merge baseline
+  // hash table at load factor <= 1/2 (2|U| cells, rounded up to a power of
+  // two): the table-only matching mode and the merge baseline
+  int32_t table_cap_half, log_table_cap_half;
   int32_t direct_words;  // membership words of the direct-address match (0: hash table)
 };
 

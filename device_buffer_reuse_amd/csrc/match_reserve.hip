@@ -14,9 +14,10 @@
 //  * The union U of the iteration's sorted selections is built in LDS (for
 //    two tokens by a rank formula: each element's position in U is found by
 //    binary search in the other list minus the duplicates before it).
-//  * U is hashed into an LDS open-addressing table (load factor <= 1/4 where
-//    LDS allows, else <= 1/2; multiplicative hash) of 4-cell buckets.  A cell packs (id << ubits |
-//    union index) in 32 bits.  Insertion takes a position in the home bucket
+//  * U is hashed into an LDS open-addressing table of 4-cell buckets
+//    (multiplicative hash; load factor <= 1/4 where LDS allows, else <= 1/2,
+//    and <= 1/2 in the table-only matching mode).  A cell packs (id << ubits
+//    | union index) in 32 bits.  Insertion takes a position in the home bucket
 //    from a per-bucket attempt counter (one LDS atomic; a full bucket sends
 //    the entry on along its double-hashing sequence), so a counter of at
 //    most 4 proves that an id absent from its home bucket is absent from the
@@ -24,7 +25,7 @@
 //    of the buffer then probes its resident id, one slot per lane, 64 lanes
 //    at a time: one 16-byte read fetches the home bucket, a second its
 //    counter, and only the rare probe of an overflowed bucket reads on.
-//    Hashing U rather than the slots keeps the table at 4|U| cells and turns
+//    Hashing U rather than the slots keeps the table at 2-4|U| cells and turns
 //    "is this slot a candidate" into the same probe.
 //  * Victim selection is a stable counting selection: each candidate slot gets
 //    a bin (empty first, then lifetime 0..L, or LRU bucket oldest-first).  A

@@ -367,7 +367,9 @@ avsg_status avsg_set_transfer_mode(avsg_ctx* ctx, int32_t mode);
  *    one lane walks both sorted lists.  Kept for comparison; needs more LDS
  *    (AVSG_ERR_UNSUPPORTED if the device has too little).
  *  AVSG_MATCH_HASH_TABLE: AVSG_MATCH_HASH always in its open-addressing
- *    form (kept for comparison and tests).
+ *    form, at load factor <= 1/2 (2|U| cells rounded up to a power of two,
+ *    U the union of the step's lists; the default mode's table, used where
+ *    direct addressing does not fit, takes 4|U| cells where LDS allows).
  * Results are identical in every mode. */
 typedef enum avsg_match_mode {
   AVSG_MATCH_HASH = 0,

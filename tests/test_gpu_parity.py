@@ -162,7 +162,7 @@ def test_parity_full_size(cid):
     """Full workload shapes, every step: all state bit-exact, attention of a
     sample of units against the oracle, buffer bytes at the end."""
     w = tg.WORKLOADS[cid]
-    steps = w.steps if cid != 4 else 64
+    steps = w.steps
     say("[parity-full] %s units=%d steps=%d" % (w.name, w.units, steps))
     sel = tg.selections(w, steps=steps)
     rng = np.random.default_rng(cid)
@@ -171,6 +171,31 @@ def test_parity_full_size(cid):
     try:
         for t in range(steps):
             run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=(t % 4 == 0 or t == steps - 1))
+        got = run.st.buf_kv.cpu().numpy().view(np.uint16)
+        occ = run.ob.slot_tok >= 0
+        assert np.array_equal(got[occ], run.ob.buf[occ])
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
+def test_parity_full_size_hash_table():
+    """The batch workload at full size, every step, matched by the
+    open-addressing table at load factor 1/2 (its stated setting; the
+    default mode direct-addresses this context): state bit-exact, attention
+    of sampled units, buffer bytes at the end."""
+    from gpu_harness import ensure_lib
+    avsg = ensure_lib()
+    w = tg.WORKLOADS[2]
+    say("[parity-full] %s hash table, units=%d steps=%d" % (w.name, w.units, w.steps))
+    sel = tg.selections(w)
+    rng = np.random.default_rng(22)
+    sample = sorted(rng.choice(w.units, size=6, replace=False).tolist())
+    run = Runner(w, attn_units=sample)
+    run.ctx.set_match_mode(avsg.MATCH_HASH_TABLE)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=(t % 8 == 0))
         got = run.st.buf_kv.cpu().numpy().view(np.uint16)
         occ = run.ob.slot_tok >= 0
         assert np.array_equal(got[occ], run.ob.buf[occ])
