@@ -287,7 +287,8 @@ KERNEL_SOURCES = {"attention": {2: "attn_split_kernel<4, false>", 3: "attn_split
                   "match_reserve": {2: "match_reserve_kernel<8>", 3: "match_reserve_kernel<8>",
                                     4: "match_reserve_kernel<1>", 5: "match_reserve_kernel<8>"}}
 KERNEL_FILES = {"attn_split_kernel": "attn_split.hip", "attn_latent_kernel": "attn_latent.hip",
-                "match_reserve_kernel": "match_reserve.hip", "attn_combine_kernel": "attn_combine.hip"}
+                "match_reserve_kernel": "match_reserve.hip", "attn_combine_kernel": "attn_combine.hip",
+                "attn_combine_latent_kernel": "attn_combine.hip"}
 
 
 def kernel_source_hash(name, root=None):
