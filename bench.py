@@ -615,8 +615,9 @@ def cpu_baseline(w, host_kv, t_start, seconds, threads=1):
     except (OSError, StopIteration):
         pass
     return {"value": done * w.entries_per_step / el, "unit": "entries/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "steps_per_s": done / el,
             "state_only_value": done * w.entries_per_step / t_state,
+            "state_only_steps_per_s": done / t_state,
             "cpu_model": cpu,
             "sample": "%d decode steps (t=%d..%d) of the %s workload, all %d units: C state "
                       "machine + C float64 attention, %s" % (
