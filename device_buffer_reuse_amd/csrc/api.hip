@@ -365,14 +365,16 @@ avsg_status avsg_profile_end(avsg_ctx* ctx, double* ms, int32_t* steps) {
     }
   unsigned long long clk[3] = {0, 0, 0};
   if (st == AVSG_OK &&
-      hipMemcpy(clk, ctx->workspace + ctx->ws.phase_clk, sizeof(clk), hipMemcpyDeviceToHost) !=
-          hipSuccess)
+      (hipMemcpyAsync(clk, ctx->workspace + ctx->ws.phase_clk, sizeof(clk), hipMemcpyDeviceToHost,
+                      ctx->stream) != hipSuccess ||
+       hipStreamSynchronize(ctx->stream) != hipSuccess))
     st = AVSG_ERR_HIP;
-  // per step: the mean over units of each phase (units run concurrently);
-  // the clock counts at 100 MHz
-  const double per_unit_step = clk[2] > 0 ? (double)ctx->prof_used / (double)clk[2] : 0.0;
-  ctx->prof_sort_ms = (double)clk[0] * 1e-5 * per_unit_step;
-  ctx->prof_walk_ms = (double)clk[1] * 1e-5 * per_unit_step;
+  // the clocks are summed over units and steps (100 MHz); divided by the
+  // number of units they give, summed over the profiled steps in that mode,
+  // each step's mean over units (the units run concurrently)
+  const double units = (double)ctx->d.units;
+  ctx->prof_sort_ms = st == AVSG_OK ? (double)clk[0] * 1e-5 / units : 0.0;
+  ctx->prof_walk_ms = st == AVSG_OK ? (double)clk[1] * 1e-5 / units : 0.0;
   *steps = ctx->prof_used;
   destroy_prof_events(ctx);
   return st;
