@@ -255,3 +255,60 @@ def test_directory_full_size_long_context():
         ctx.close()
         host.free()
         segs.free()
+
+
+COMBINED = {
+    "token": (tg.WORKLOADS[2].replace(batch=3, n_kv_heads=2, n_q_heads=8, n_entries=3001, k=300,
+                                      n_slots=900, steps=10), 64),
+    "mtp_lru": (tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=3001, k=200,
+                                        n_slots=700, steps=8, policy="lru", n_buckets=5), 16),
+    "latent": (tg.WORKLOADS[5].replace(batch=2, n_entries=3001, k=600, n_slots=1500, steps=6), 256),
+}
+
+
+@pytest.mark.parametrize("name", list(COMBINED))
+def test_lengths_sizes_and_directory_together(name):
+    """Variable-length lists, a buffer size per unit that shrinks and grows
+    between steps, and host rows reached through the directory, all in one
+    trace: state, flags, slots, buffer bytes and attention against the
+    oracle given the same lengths, sizes and flat rows."""
+    w, seg = COMBINED[name]
+    say("[directory] lengths + sizes + directory: %s" % name)
+    rng = np.random.default_rng(97 + len(name))
+    sel_full = tg.selections(w)
+    sel, lens = tg.shorten(sel_full, seed=31 + len(name), lo=max(1, w.k // 8))
+    lens = lens.reshape(w.steps, w.units, w.n_q_tokens)
+    run = DirRun(w, seg, rng)
+    torch = run.torch
+    try:
+        for t in range(w.steps):
+            # sizes at least the union of this step's lists in use
+            need = np.array([len(np.unique(np.concatenate(
+                [sel[t, u, j, :lens[t, u, j]] for j in range(w.n_q_tokens)])))
+                for u in range(w.units)], np.int32)
+            caps = np.minimum(w.n_slots, need + rng.integers(0, w.n_slots // 2, size=w.units)).astype(np.int32)
+            cap_dev = torch.from_numpy(caps).cuda()
+            run.ctx.set_capacity(cap_dev)
+            q = tg.queries(w, t)
+            s = run.st
+            ln_dev = torch.from_numpy(np.ascontiguousarray(lens[t].reshape(-1))).cuda()
+            run.ctx.step(torch.from_numpy(np.ascontiguousarray(sel[t])).cuda(),
+                         torch.from_numpy(q.view(np.int16)).cuda(), run.pool, s.buf_kv,
+                         s.slot_table, s.lifetimes, s.out, s.stats, sel_len=ln_dev)
+            torch.cuda.synchronize()
+            r = run.ob.step(sel[t], run.flat, lengths=lens[t], caps=caps, mapped=run.mapped)
+            what = "%s t=%d" % (name, t)
+            assert (r["status"] == 0).all(), what
+            assert np.array_equal(s.slot_table.cpu().numpy(), run.ob.slot_tok), what
+            assert np.array_equal(s.lifetimes.cpu().numpy(), run.ob.life), what
+            assert np.array_equal(s.stats.sel_slot.cpu().numpy(), r["sel_slot"]), what
+            assert np.array_equal(s.stats.hit_flag.cpu().numpy(), r["hit_flag"]), what
+            assert np.array_equal(s.stats.n_miss.cpu().numpy(), r["n_miss"]), what
+            assert np.array_equal(s.stats.n_evict.cpu().numpy(), r["n_evict"]), what
+            occ = run.ob.slot_tok >= 0
+            assert np.array_equal(s.buf_kv.cpu().numpy().view(np.uint16)[occ], run.ob.buf[occ]), what
+            ref = oatt.attend(w, q, run.flat, sel[t], r["status"], lengths=lens[t])
+            check_attention(s.out.cpu().numpy(), ref, what)
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
