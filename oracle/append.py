@@ -20,12 +20,30 @@ bytes, so the buffer keeps exact copies of host rows (the AVSG abstract's
 reuse is only valid for exact copies).  Slots, lifetimes and stamps do not
 change: an append is not a selection.  A position outside [0, N P) is a range
 error: that request writes nothing.
+
+append_insert adds the optional second half of Offload: the token's entry is
+also made resident in every unit of the request, between steps, so that the
+next step finds it in the buffer.  The pages fix no rule for it; the reading
+taken follows the step's own eviction order without ageing anyone:
+
+  * the slots in use are [0, cap) (the unit's buffer size); slots past it are
+    emptied, as the next step would empty them;
+  * if a slot in use holds the entry it is written through and its keep-state
+    refreshed (lifetime L; for bucketed LRU the stamp t - 1, i.e. bucket 0 at
+    the coming step t);
+  * otherwise the first slot in the order (occupied?, lifetime or minus
+    bucket at step t, slot index) takes the entry, receives its whole host
+    row with the token already written, and the fresh keep-state;
+  * a unit whose slots in use are not a valid state (an id outside [-1, N),
+    a lifetime outside [0, L] or stamp outside [0, t), the entry in two slots)
+    writes nothing and reports a state error; a bad position or capacity, or
+    an entry without a host row, is a range error of the unit.
 """
 from __future__ import annotations
 
 import numpy as np
 
-OK, ERR_RANGE = 0, 17
+OK, ERR_RANGE, ERR_STATE = 0, 17, 19
 
 
 def token_slices(latent: bool, tokens_per_entry: int, d_qk: int, d_v: int, r: int):
@@ -64,4 +82,69 @@ def append(w, host_kv: np.ndarray, new_kv: np.ndarray, pos: np.ndarray,
                 row[ks] = new_kv[u, :d_qk]
                 if vs is not None:
                     row[vs] = new_kv[u, d_qk:d_qk + d_v]
+    return status
+
+
+def _write_token(row, new_tok, latent, P, d_qk, d_v, r):
+    ks, vs = token_slices(latent, P, d_qk, d_v, r)
+    row[ks] = new_tok[:d_qk]
+    if vs is not None:
+        row[vs] = new_tok[d_qk:d_qk + d_v]
+
+
+def append_insert(w, host_kv: np.ndarray, new_kv: np.ndarray, pos: np.ndarray,
+                  slot_tok: np.ndarray, life: np.ndarray, buf: np.ndarray, t: int,
+                  caps: np.ndarray | None = None, mapped: np.ndarray | None = None) -> np.ndarray:
+    """append() plus insertion of the token's entry into each unit's buffer
+    (slot_tok, life [units][S] int32 and buf [units][S][row] updated in
+    place) before step t.  caps [units]: slots in use (None: all S);
+    mapped [units][N] bool: entries with a host row (None: all).  Returns
+    the per-unit status (0, 17 or 19)."""
+    P, N, S = w.tokens_per_entry, w.n_entries, w.n_slots
+    d_qk, d_v = w.head_dim_qk, w.head_dim_v
+    lru = w.policy == "lru"
+    L, B = w.lifetime_L, w.n_buckets
+    assert not (lru and t < 1), "a bucketed-LRU stamp needs a step before it"
+    fresh = t - 1 if lru else L
+    empty_life = -1 if lru else 0
+    status = np.zeros(w.units, dtype=np.int32)
+    for u in range(w.units):
+        b = u // w.n_kv_heads
+        p = int(pos[b])
+        cap = S if caps is None else int(caps[u])
+        if p < 0 or p >= N * P or not 1 <= cap <= S:
+            status[u] = ERR_RANGE
+            continue
+        e, r = divmod(p, P)
+        if mapped is not None and not mapped[u, e]:
+            status[u] = ERR_RANGE
+            continue
+        ids, lv = slot_tok[u, :cap], life[u, :cap]
+        occ = ids >= 0
+        bad = ((ids < -1) | (ids >= N)).any()
+        if lru:
+            bad |= (occ & ((lv < 0) | (lv >= t))).any()
+        else:
+            bad |= (occ & ((lv < 0) | (lv > L))).any()
+        bad |= np.count_nonzero(ids == e) > 1
+        if bad:
+            status[u] = ERR_STATE
+            continue
+        _write_token(host_kv[u, e], new_kv[u], w.latent, P, d_qk, d_v, r)
+        slot_tok[u, cap:] = -1
+        life[u, cap:] = empty_life
+        held = np.nonzero(ids == e)[0]
+        if held.size:
+            s = int(held[0])
+            _write_token(buf[u, s], new_kv[u], w.latent, P, d_qk, d_v, r)
+        else:
+            def order(s):
+                if slot_tok[u, s] < 0:
+                    return (0, 0, s)
+                key = int(life[u, s]) if not lru else -min(t - int(life[u, s]) - 1, B - 1)
+                return (1, key, s)
+            s = min(range(cap), key=order)
+            slot_tok[u, s] = e
+            buf[u, s] = host_kv[u, e]
+        life[u, s] = fresh
     return status
