@@ -503,6 +503,36 @@ def extras(b, a):
     out["append"] = {"us": round(e0.elapsed_time(e1) / na * 1e3, 2),
                      "host_write_bytes": w.units * tok_elems * 2,
                      "slot_table_bytes_read": w.units * w.n_slots * 4}
+    # append with insertion: (a) into the resident entries above (write
+    # through, keep-state refreshed); (b) into entries no slot holds
+    for _ in range(4):
+        b.ctx.append_insert(newkv, pos, b.host, st.buf_kv, st.slot_table, st.lifetimes)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(na):
+        b.ctx.append_insert(newkv, pos, b.host, st.buf_kv, st.slot_table, st.lifetimes)
+    e1.record()
+    torch.cuda.synchronize()
+    us_res = e0.elapsed_time(e1) / na * 1e3
+    # (b) from an emptied buffer at step 1: call i puts entry i of every unit
+    # into slot i (empty slots go first), each unit copying the whole row
+    b.reset()
+    b.ctx.t = 1
+    pos_miss = [torch.full((w.batch,), i * w.tokens_per_entry, dtype=torch.int32, device="cuda")
+                for i in range(na)]
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(na):
+        b.ctx.append_insert(newkv, pos_miss[i], b.host, st.buf_kv, st.slot_table, st.lifetimes)
+    e1.record()
+    torch.cuda.synchronize()
+    assert (st.slot_table[:, :na].cpu().numpy() == np.arange(na)).all()
+    us_miss = e0.elapsed_time(e1) / na * 1e3
+    assert b.ctx.last_error() == 0
+    out["append_insert"] = {
+        "resident_us": round(us_res, 2), "insert_us": round(us_miss, 2),
+        "insert_host_read_bytes": w.units * (w.row_bytes - tok_elems * 2),
+        "insert_host_GB/s": round(w.units * (w.row_bytes - tok_elems * 2) / (us_miss * 1e-6) / 1e9, 2)}
     # pinned hipMemcpy host->device peak, for context
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8).pin_memory()

@@ -30,7 +30,7 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_destroy", "avsg_reset", "avsg_step", "avsg_last_error", "avsg_validate_state",
             "avsg_get_step", "avsg_set_step", "avsg_host_alloc", "avsg_host_free",
             "avsg_status_string", "avsg_attn_splits", "avsg_profile_begin", "avsg_profile_end",
-            "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append",
+            "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append", "avsg_append_insert",
             "avsg_rebuild_index", "avsg_step_varlen", "avsg_set_capacity",
             "avsg_plan_capacity", "avsg_step_static", "avsg_set_host_directory",
             "avsg_set_gather_workgroups", "avsg_profile_match_phases"]
@@ -89,6 +89,7 @@ def load():
         "avsg_step_static": ([cfgp, i64, p] + [p] * 7 + [ctypes.POINTER(avsg_hit_stats)], i32),
         "avsg_last_error": ([p], i32),
         "avsg_append": ([p] * 6, i32),
+        "avsg_append_insert": ([p] * 7, i32),
         "avsg_validate_state": ([p, p, p], i32),
         "avsg_rebuild_index": ([p, p], i32),
         "avsg_set_capacity": ([p, p], i32),
@@ -170,6 +171,11 @@ def avsg_step_static(cfg: avsg_config, t: int, stream: int, sel_idx: int, q: int
 def avsg_append(ctx: int, new_kv: int, pos: int, host_kv: int, buf_kv: int,
                 slot_table: int) -> int:
     return load().avsg_append(ctx, new_kv, pos, host_kv, buf_kv, slot_table)
+
+
+def avsg_append_insert(ctx: int, new_kv: int, pos: int, host_kv: int, buf_kv: int,
+                       slot_table: int, lifetimes: int) -> int:
+    return load().avsg_append_insert(ctx, new_kv, pos, host_kv, buf_kv, slot_table, lifetimes)
 
 
 def avsg_last_error(ctx: int) -> int:
@@ -386,6 +392,15 @@ class Context:
                          slot_table.data_ptr())
         if st != OK:
             raise AvsgError(st, "avsg_append")
+
+    def append_insert(self, new_kv, pos, host_kv, buf_kv, slot_table, lifetimes):
+        """append() that also makes the token's entry resident in each unit's
+        buffer before the coming step (slot_table, lifetimes in/out)."""
+        hptr = host_kv.ptr if isinstance(host_kv, HostBuffer) else int(host_kv)
+        st = avsg_append_insert(self.handle, new_kv.data_ptr(), pos.data_ptr(), hptr,
+                                buf_kv.data_ptr(), slot_table.data_ptr(), lifetimes.data_ptr())
+        if st != OK:
+            raise AvsgError(st, "avsg_append_insert")
 
     def last_error(self) -> int:
         return avsg_last_error(self.handle)

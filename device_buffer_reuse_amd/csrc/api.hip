@@ -720,24 +720,32 @@ avsg_status avsg_plan_capacity(int32_t units, const int32_t* demand, const int32
   return AVSG_OK;
 }
 
-avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
-                        uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table) {
-  RoctxRange range("avsg_append");
+static avsg_status enqueue_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
+                                  uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table,
+                                  int32_t* lifetimes, bool insert) {
   if (!ctx || !new_kv || !pos || !host_kv || !buf_kv || !slot_table) return AVSG_ERR_INVALID_ARG;
+  if (insert && !lifetimes) return AVSG_ERR_INVALID_ARG;
   if (((uintptr_t)new_kv | (uintptr_t)host_kv | (uintptr_t)buf_kv) & 15)
     return AVSG_ERR_INVALID_ARG;
+  const avsg_config& c = ctx->cfg;
+  const bool lru = c.policy == AVSG_POLICY_BUCKET_LRU;
+  // a bucketed-LRU stamp of the step before the coming one needs a step
+  // before it; the counter is the host's, so this is checked here
+  if (insert && lru && ctx->t < 1) return AVSG_ERR_INVALID_ARG;
   const void* host_dev = nullptr;
   avsg_status st = device_view_of_pinned(host_kv, &host_dev);
   if (st != AVSG_OK) return st;
-  const avsg_config& c = ctx->cfg;
   AppendParams ap;
   ap.new_kv = new_kv;
   ap.pos = pos;
   ap.host_kv = (uint16_t*)host_dev;
   ap.buf_kv = buf_kv;
-  ap.slot_table = slot_table;
+  ap.slot_table = const_cast<int32_t*>(slot_table);  // written only when inserting
+  ap.lifetimes = insert ? lifetimes : nullptr;
+  ap.cap = insert ? ctx->cap : nullptr;
   ap.err_word = (uint32_t*)(ctx->workspace + ctx->ws.err_word);
   ap.dir = ctx->dir;
+  ap.t = ctx->t;
   ap.Hkv = c.n_kv_heads;
   ap.N = c.n_entries;
   ap.S = c.n_slots;
@@ -747,7 +755,24 @@ avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* po
   ap.dqk = c.head_dim_qk;
   ap.dv = c.head_dim_v;
   ap.tok_elems = ap.latent ? c.head_dim_qk : c.head_dim_qk + c.head_dim_v;
+  ap.insert = insert ? 1 : 0;
+  ap.lru = lru ? 1 : 0;
+  ap.L = c.lifetime_L;
+  ap.B = c.n_buckets;
   return launch_append(ap, ctx->d.units, ctx->stream) == hipSuccess ? AVSG_OK : AVSG_ERR_HIP;
+}
+
+avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
+                        uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table) {
+  RoctxRange range("avsg_append");
+  return enqueue_append(ctx, new_kv, pos, host_kv, buf_kv, slot_table, nullptr, false);
+}
+
+avsg_status avsg_append_insert(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
+                               uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
+                               int32_t* lifetimes) {
+  RoctxRange range("avsg_append_insert");
+  return enqueue_append(ctx, new_kv, pos, host_kv, buf_kv, slot_table, lifetimes, true);
 }
 
 avsg_status avsg_host_alloc(size_t bytes, unsigned flags, void** host_ptr) {

@@ -128,10 +128,14 @@ struct AppendParams {
   const int32_t* pos;         // [batch]: token position of each request
   uint16_t* host_kv;          // device-visible address of the pinned host rows [units][N][row]
   uint16_t* buf_kv;           // [units][S][row]
-  const int32_t* slot_table;  // [units][S]
+  int32_t* slot_table;        // [units][S] (written only when inserting)
+  int32_t* lifetimes;         // [units][S] (inserting only)
+  const int32_t* cap;         // [units] slots in use, or null: all S (inserting only)
   uint32_t* err_word;
   HostDir dir;                // null dir.top: flat host KV
+  int64_t t;                  // the coming step (inserting only)
   int32_t Hkv, N, S, tpe, row_elems, tok_elems, dqk, dv, latent;
+  int32_t insert, lru, L, B;  // insert: make the entry resident as well
 };
 
 hipError_t launch_match_reserve(const MatchReserveParams& p, int units, size_t lds, hipStream_t s);

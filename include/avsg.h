@@ -299,6 +299,35 @@ avsg_status avsg_plan_capacity(int32_t units, const int32_t* demand, const int32
 avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
                         uint16_t* host_kv, uint16_t* buf_kv, const int32_t* slot_table);
 
+/* Offload with insertion (Spin summary, section 2A: Offload places KV data
+ * into memory; the rule for placing the entry in the buffer is this
+ * library's, the step's own eviction order without ageing).  Does what
+ * avsg_append does and also makes the token's entry resident, before the
+ * coming step t (avsg_get_step), in every unit of the request:
+ *   - the unit's slots in use are [0, cap) (avsg_set_capacity; all S by
+ *     default); slots past it are emptied, as the coming step would do;
+ *   - a slot in use holding the entry is written through and gets the fresh
+ *     keep-state: lifetime L, or (bucketed LRU) stamp t - 1, which is bucket
+ *     0 at step t;
+ *   - otherwise the first slot in the order (empty first, then the lowest
+ *     lifetime or the oldest bucket at step t, then the lowest index) takes
+ *     the entry: slot_table and the keep-state as above, and buf_kv the
+ *     entry's whole host row with the token written.
+ * No other slot changes; the step counter does not advance.
+ *   slot_table device, int32 [units][S].                            in/out
+ *   lifetimes  device, int32 [units][S].                            in/out
+ *   the rest   as avsg_append.
+ * Per unit, a bad position, a capacity outside [1, S] or an entry without a
+ * host row is AVSG_ERR_RANGE, and slots in use that are not a valid state
+ * (an id outside [-1, N), a lifetime outside [0, L] or stamp outside [0, t)
+ * on an occupied slot, the entry in two slots) are AVSG_ERR_STATE: that unit
+ * writes nothing (avsg_last_error reports it).  Returns AVSG_ERR_INVALID_ARG
+ * for a null lifetimes or, under bucketed LRU, before the first step (t = 0:
+ * no stamp in [0, t) exists), else as avsg_append. */
+avsg_status avsg_append_insert(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
+                               uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
+                               int32_t* lifetimes);
+
 /* Syncs the stream and returns the highest-precedence data error raised by
  * the steps and appends since the last call (RANGE, then UNSORTED, CAPACITY, STATE), or
  * AVSG_OK; then clears it. */

@@ -145,3 +145,194 @@ def test_append_full_size(cid):
     finally:
         run.close()
         run.host.free()
+
+
+# ---------------------------------------------------------------------------
+# Append with insertion (avsg_append_insert): the token's entry is also made
+# resident before the coming step.  After each insertion the host rows, the
+# buffer, the slot table and the lifetimes must equal the oracle's bit for
+# bit; the steps after it (which hit or evict the inserted entries) must still
+# match the oracle in state and attention.
+
+INSERT_CASES = dict(CASES, lifetime_pages=tg.WORKLOADS[4].replace(
+    batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001, k=37, n_slots=60, steps=8,
+    policy="lifetime", lifetime_L=3))
+
+
+def _insert_and_compare(run, w, new, pos, what):
+    torch = run.torch
+    ref_host = run.host.array.copy()
+    status = oapp.append_insert(w, ref_host, new, pos, run.ob.slot_tok, run.ob.life, run.ob.buf,
+                                run.ob.t, caps=getattr(run, "caps", None))
+    run.ctx.append_insert(torch.from_numpy(new.view(np.int16)).cuda(), torch.from_numpy(pos).cuda(),
+                          run.host, run.st.buf_kv, run.st.slot_table, run.st.lifetimes)
+    torch.cuda.synchronize()
+    assert np.array_equal(run.host.array, ref_host), "host_kv after insert " + what
+    assert np.array_equal(run.st.slot_table.cpu().numpy(), run.ob.slot_tok), "slot_table " + what
+    assert np.array_equal(run.st.lifetimes.cpu().numpy(), run.ob.life), "lifetimes " + what
+    assert np.array_equal(run.st.buf_kv.cpu().numpy().view(np.uint16), run.ob.buf), \
+        "buf_kv after insert " + what
+    return status
+
+
+def _insert_positions(w, sel_t, rng, t):
+    """Even steps: an entry of the current selection (resident: written
+    through and refreshed); odd steps: an entry outside every unit's
+    selection (not resident unless kept from earlier: takes a victim)."""
+    P = w.tokens_per_entry
+    pos = np.empty(w.batch, np.int32)
+    for b in range(w.batch):
+        units = range(b * w.n_kv_heads, (b + 1) * w.n_kv_heads)
+        if t % 2 == 0:
+            e = int(rng.choice(sel_t[b * w.n_kv_heads, 0]))
+        else:
+            taken = set(int(x) for u in units for x in sel_t[u].ravel())
+            e = int(rng.choice(sorted(set(range(w.n_entries)) - taken)))
+        pos[b] = e * P + int(rng.integers(0, P))
+    return pos
+
+
+@pytest.mark.parametrize("name", list(INSERT_CASES))
+def test_append_insert_parity(name):
+    from device_buffer_reuse_amd import avsg
+    w = INSERT_CASES[name]
+    say("[append-insert] %s units=%d tpe=%d policy=%s" % (name, w.units, w.tokens_per_entry,
+                                                          w.policy))
+    sel = tg.selections(w)
+    rng = np.random.default_rng(100 + len(name))
+    run = Runner(w)
+    inserted = 0
+    try:
+        for t in range(w.steps):
+            r, _ = run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+            pos = _insert_positions(w, sel[t], rng, t)
+            before = run.ob.slot_tok.copy()
+            st = _insert_and_compare(run, w, _new_tokens(w, rng), pos, "t=%d" % t)
+            assert (st == 0).all()
+            inserted += int((run.ob.slot_tok != before).any(axis=1).sum())
+        assert inserted > 0
+        assert run.ctx.last_error() == avsg.OK
+    finally:
+        run.close()
+        run.host.free()
+
+
+def test_append_insert_with_capacity_and_errors():
+    """Buffer sizes shrink between steps: an insertion empties the slots past
+    each unit's size and places the entry inside it.  Then a unit with a
+    corrupted state (its entry in two slots) and a request with a position
+    out of range write nothing, and the others insert as usual."""
+    from device_buffer_reuse_amd import avsg
+    w = INSERT_CASES["token"]
+    say("[append-insert] capacity and errors")
+    sel = tg.selections(w)
+    rng = np.random.default_rng(7)
+    run = Runner(w)
+    try:
+        for t in range(3):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+        u_sizes = np.sort(run.ob.slot_tok >= 0, axis=1).sum(axis=1)
+        caps = np.array([max(w.k + 50, int(n) - 150 * (u % 3)) for u, n in enumerate(u_sizes)],
+                        np.int32)
+        run.set_caps(caps)
+        pos = _insert_positions(w, sel[2], rng, 1)
+        st = _insert_and_compare(run, w, _new_tokens(w, rng), pos, "capacity")
+        assert (st == 0).all()
+        for u in range(w.units):
+            assert (run.ob.slot_tok[u, caps[u]:] == -1).all()
+        for t in range(3, 6):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+        # unit 1: its entry in two slots inside its size (written to both
+        # sides' state); request 2: position out of range
+        pos = _insert_positions(w, sel[5], rng, 0)
+        e1 = pos[0] // w.tokens_per_entry
+        s_held = int(np.nonzero(run.ob.slot_tok[1] == e1)[0][0]) if (run.ob.slot_tok[1] == e1).any() \
+            else 0
+        s_dup = (s_held + 1) % int(caps[1])
+        for s in (s_held, s_dup):
+            run.ob.slot_tok[1, s] = e1
+        run.st.slot_table[1, s_held] = int(e1)
+        run.st.slot_table[1, s_dup] = int(e1)
+        pos[2] = w.n_entries * w.tokens_per_entry
+        st = _insert_and_compare(run, w, _new_tokens(w, rng), pos, "errors")
+        assert st.tolist() == [0, oapp.ERR_STATE, 0, 0, oapp.ERR_RANGE, oapp.ERR_RANGE]
+        assert run.ctx.last_error() == avsg.ERR_RANGE
+        assert run.ctx.last_error() == avsg.OK
+    finally:
+        run.close()
+        run.host.free()
+
+
+def test_append_insert_lru_before_first_step_is_rejected():
+    from device_buffer_reuse_amd import avsg
+    w = CASES["page16"]
+    assert w.policy == "lru"
+    run = Runner(w)
+    try:
+        pos = np.zeros(w.batch, np.int32)
+        new = _new_tokens(w, np.random.default_rng(0))
+        with pytest.raises(avsg.AvsgError) as ei:
+            run.ctx.append_insert(run.torch.from_numpy(new.view(np.int16)).cuda(),
+                                  run.torch.from_numpy(pos).cuda(), run.host, run.st.buf_kv,
+                                  run.st.slot_table, run.st.lifetimes)
+        assert ei.value.status == avsg.ERR_INVALID_ARG
+        run.torch.cuda.synchronize()
+        assert (run.st.slot_table.cpu().numpy() == -1).all()
+    finally:
+        run.close()
+        run.host.free()
+
+
+class _TouchedRows:
+    """Host rows by (unit, entry), copied on first use from the full host
+    store: the oracle's insertion at full size touches one row per unit."""
+
+    def __init__(self, host):
+        self.host, self.rows = host, {}
+
+    def __getitem__(self, key):
+        u, e = int(key[0]), int(key[1])
+        if (u, e) not in self.rows:
+            self.rows[(u, e)] = self.host[u, e].copy()
+        return self.rows[(u, e)]
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_append_insert_full_size(cid):
+    """Full workload shapes, in the launch configuration of the steps: after
+    a few steps every unit inserts an entry outside its selection; the slot
+    state is compared whole, the written host rows and slots one by one, and
+    one more step is checked against the oracle."""
+    from device_buffer_reuse_amd import avsg
+    w = tg.WORKLOADS[cid]
+    steps = 4
+    say("[append-insert-full] %s units=%d" % (w.name, w.units))
+    sel = tg.selections(w, steps=steps + 1)
+    run = Runner(w, attn_units=[0, w.units - 1])
+    rng = np.random.default_rng(cid)
+    try:
+        for t in range(steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=False)
+        pos = _insert_positions(w, sel[steps - 1], rng, 1)
+        new = _new_tokens(w, rng)
+        rows = _TouchedRows(run.host.array)
+        before = run.ob.slot_tok.copy()
+        st = oapp.append_insert(w, rows, new, pos, run.ob.slot_tok, run.ob.life, run.ob.buf, run.ob.t)
+        assert (st == 0).all()
+        run.ctx.append_insert(run.torch.from_numpy(new.view(np.int16)).cuda(),
+                              run.torch.from_numpy(pos).cuda(), run.host, run.st.buf_kv,
+                              run.st.slot_table, run.st.lifetimes)
+        run.torch.cuda.synchronize()
+        assert np.array_equal(run.st.slot_table.cpu().numpy(), run.ob.slot_tok)
+        assert np.array_equal(run.st.lifetimes.cpu().numpy(), run.ob.life)
+        for (u, e), row in rows.rows.items():
+            assert np.array_equal(run.host.array[u, e], row), (u, e)
+        us, ss = np.nonzero(run.ob.slot_tok != before)
+        assert len(us) > 0
+        got = run.st.buf_kv[run.torch.from_numpy(us).cuda(), run.torch.from_numpy(ss).cuda()]
+        assert np.array_equal(got.cpu().numpy().view(np.uint16), run.ob.buf[us, ss])
+        run.step_and_compare(steps, sel[steps], tg.queries(w, steps))
+        assert run.ctx.last_error() == avsg.OK
+    finally:
+        run.close()
+        run.host.free()

@@ -186,6 +186,61 @@ def test_append_through_the_directory():
         run.close()
 
 
+def test_append_insert_through_the_directory():
+    """Insertion reads the entry's whole row from its pool row; a unit whose
+    entry has no row writes nothing (a range error of that unit alone)."""
+    import torch
+    avsg = ensure_lib()
+    w, seg = CASES["lru_pages"]
+    say("[directory] append with insertion")
+    sel = tg.selections(w)
+    hole = (w.units - 1, 599)
+    run = DirRun(w, seg, np.random.default_rng(92), mapping_filter=lambda u, e: (u, e) != hole)
+    rng = np.random.default_rng(4)
+    try:
+        for t in range(5):
+            run.step(t, sel[t])
+            # even steps: the first selected entry; odd: an unselected one
+            ent = [int(sel[t, b * w.n_kv_heads, 0, 0]) if t % 2 == 0 else 590 + b
+                   for b in range(w.batch)]
+            pos = np.array([e * w.tokens_per_entry + t for e in ent], np.int32)
+            x = rng.standard_normal((w.units, w.head_dim_qk + w.head_dim_v)).astype(np.float32)
+            new = (x.view(np.uint32) >> 16).astype(np.uint16)
+            st = oapp.append_insert(w, run.flat, new, pos, run.ob.slot_tok, run.ob.life, run.ob.buf,
+                                    run.ob.t, mapped=run.mapped)
+            assert (st == 0).all()
+            run.ctx.append_insert(torch.from_numpy(new.view(np.int16)).cuda(),
+                                  torch.from_numpy(pos).cuda(), run.pool, run.st.buf_kv,
+                                  run.st.slot_table, run.st.lifetimes)
+            torch.cuda.synchronize()
+            for (u, e), row in run.mapping.items():
+                assert np.array_equal(run.pool.array[row], run.flat[u, e]), (u, e)
+            assert np.array_equal(run.st.slot_table.cpu().numpy(), run.ob.slot_tok)
+            assert np.array_equal(run.st.lifetimes.cpu().numpy(), run.ob.life)
+            assert np.array_equal(run.st.buf_kv.cpu().numpy().view(np.uint16), run.ob.buf)
+        assert run.ctx.last_error() == 0
+        # the last request inserts entry 599: its last unit has no row for it
+        pos = np.full(w.batch, 3 * w.tokens_per_entry, np.int32)
+        pos[-1] = 599 * w.tokens_per_entry
+        new = np.ones((w.units, w.head_dim_qk + w.head_dim_v), np.uint16)
+        st = oapp.append_insert(w, run.flat, new, pos, run.ob.slot_tok, run.ob.life, run.ob.buf,
+                                run.ob.t, mapped=run.mapped)
+        assert st.tolist() == [0] * (w.units - 1) + [oapp.ERR_RANGE]
+        run.ctx.append_insert(torch.from_numpy(new.view(np.int16)).cuda(),
+                              torch.from_numpy(pos).cuda(), run.pool, run.st.buf_kv,
+                              run.st.slot_table, run.st.lifetimes)
+        torch.cuda.synchronize()
+        assert run.ctx.last_error() == avsg.ERR_RANGE
+        for (u, e), row in run.mapping.items():
+            assert np.array_equal(run.pool.array[row], run.flat[u, e]), (u, e)
+        assert np.array_equal(run.st.slot_table.cpu().numpy(), run.ob.slot_tok)
+        assert np.array_equal(run.st.lifetimes.cpu().numpy(), run.ob.life)
+        assert np.array_equal(run.st.buf_kv.cpu().numpy().view(np.uint16), run.ob.buf)
+        run.step(5, sel[5])
+    finally:
+        run.close()
+
+
 def test_directory_bad_arguments():
     import torch
     avsg = ensure_lib()
