@@ -67,13 +67,13 @@ def _load():
             lib = ctypes.CDLL(_LIB_PATH)
             p = ctypes.c_void_p
             lib.oracle_unit_step.argtypes = ([ctypes.POINTER(_Cfg), ctypes.c_int64, p, p,
-                                              ctypes.c_int32] + [p] * 8)
+                                              ctypes.c_int32] + [p] * 8 + [ctypes.c_int32])
             lib.oracle_unit_step.restype = ctypes.c_int
-            lib.oracle_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, ctypes.c_int64] + [p] * 12
+            lib.oracle_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int64, ctypes.c_int64] + [p] * 13
             lib.oracle_step.restype = None
             lib.oracle_set_threads.argtypes = [ctypes.c_int]
             lib.oracle_set_threads.restype = None
-            lib.oracle_attend.argtypes = [ctypes.POINTER(AttnCfg)] + [p] * 6
+            lib.oracle_attend.argtypes = [ctypes.POINTER(AttnCfg)] + [p] * 7
             lib.oracle_attend.restype = None
             _lib = lib
     return _lib
@@ -123,14 +123,19 @@ class OracleBuffer:
 
     def step(self, sel: np.ndarray, host_kv: np.ndarray | None = None,
              lengths: np.ndarray | None = None, caps: np.ndarray | None = None,
-             mapped: np.ndarray | None = None) -> dict:
+             mapped: np.ndarray | None = None, ctx_len: np.ndarray | None = None,
+             tokens_per_entry: int = 1) -> dict:
         """Advance one step with selections sel [units][T][k], of which the
         first lengths[u][j] entries of each list are in use (all k when
         lengths is None), unit u using slots [0, caps[u]) (all S when caps
         is None; slots past it are emptied).  mapped [units][N] (bool):
         entries that have a host row (all when None); a miss without one is
-        a range error of its unit.  When the buffer is tracked, reserved
-        slots receive host_kv[u][id] byte for byte."""
+        a range error of its unit.  ctx_len [batch]: context length of each
+        request in tokens (None: every entry is in the context); entry e
+        holds positions [e P, (e + 1) P), P = tokens_per_entry, and an id in
+        use whose first position is at or past the length is a range error,
+        as is a length outside [1, N P].  When the buffer is tracked,
+        reserved slots receive host_kv[u][id] byte for byte."""
         c = self.cfg
         sel = np.ascontiguousarray(sel, dtype=np.int32)
         assert sel.shape == (self.units, c.n_tokens, c.k)
@@ -150,12 +155,17 @@ class OracleBuffer:
             caps = np.ascontiguousarray(caps, dtype=np.int32).reshape(self.units)
         if mapped is not None:
             mapped = np.ascontiguousarray(mapped, dtype=np.uint8).reshape(self.units, c.n_entries)
+        n_ctx = None
+        if ctx_len is not None:
+            n_ctx = context_entries(ctx_len, tokens_per_entry, c.n_entries)
+            n_ctx = np.ascontiguousarray(np.repeat(n_ctx, self.units // len(n_ctx)), dtype=np.int32)
         _load().oracle_step(ctypes.byref(c), self.units, self.t, _p(sel),
                             None if lengths is None else _p(lengths),
                             None if caps is None else _p(caps), _p(self.slot_tok),
                             _p(self.life), _p(res["hit_flag"]), _p(res["sel_slot"]),
                             _p(res["fill_slot"]), _p(res["fill_id"]), _p(res["counts"]),
-                            _p(res["status"]), None if mapped is None else _p(mapped))
+                            _p(res["status"]), None if mapped is None else _p(mapped),
+                            None if n_ctx is None else _p(n_ctx))
         res["n_hit"] = res["counts"][:, 0].copy()
         res["n_miss"] = res["counts"][:, 1].copy()
         res["n_evict"] = res["counts"][:, 2].copy()
@@ -179,13 +189,24 @@ class OracleBuffer:
         self.buf = None if bf is None else bf.copy()
 
 
+def context_entries(ctx_len, tokens_per_entry: int, n_entries: int) -> np.ndarray:
+    """Entries holding tokens of each context: entry e holds positions
+    [e P, (e + 1) P) and is in a context of length n when e P < n, so there
+    are ceil(n / P) of them; 0 for a length outside [1, N P] (a range
+    error)."""
+    n = np.asarray(ctx_len, dtype=np.int64).reshape(-1)
+    P = int(tokens_per_entry)
+    ok = (n >= 1) & (n <= n_entries * P)
+    return np.where(ok, (n + P - 1) // P, 0).astype(np.int32)
+
+
 def unit_step(n_slots, n_entries, k, policy, lifetime_L, n_buckets, t, sel, slot_tok, life,
-              lengths=None, cap=None, mapped=None):
+              lengths=None, cap=None, mapped=None, n_ctx=None):
     """Single-unit call for small hand-built cases: returns (status, result
     dict) and updates slot_tok / life (int32 arrays) in place.  lengths: the
     entries in use of each token's list (default: all k); cap: slots in use
     (default: all n_slots); mapped: [N] bool, entries with a host row
-    (default: all)."""
+    (default: all); n_ctx: entries in the request's context (default: N)."""
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     if sel.ndim == 1:
         sel = sel[None, :]
@@ -202,7 +223,8 @@ def unit_step(n_slots, n_entries, k, policy, lifetime_L, n_buckets, t, sel, slot
     mp = None if mapped is None else np.ascontiguousarray(mapped, dtype=np.uint8).reshape(n_entries)
     st = _load().oracle_unit_step(ctypes.byref(cfg), t, _p(sel), None if ln is None else _p(ln),
                                   n_slots if cap is None else int(cap), _p(slot_tok), _p(life), _p(hit),
-                                  _p(ss), _p(fs), _p(fi), _p(cnt), None if mp is None else _p(mp))
+                                  _p(ss), _p(fs), _p(fi), _p(cnt), None if mp is None else _p(mp),
+                                  n_entries if n_ctx is None else int(n_ctx))
     m = int(cnt[1])
     return st, dict(hit_flag=hit, sel_slot=ss, fill_slot=fs[:m].copy(), fill_id=fi[:m].copy(),
                     n_hit=int(cnt[0]), n_miss=m, n_evict=int(cnt[2]), n_union=int(cnt[3]))

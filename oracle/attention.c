@@ -16,9 +16,13 @@
  * Row layouts (Spin summary, section 2B, head-wise pages): a split-layout
  * entry is K[tpe][dqk] followed by V[tpe][dv] and contributes all of its tpe
  * token rows; a latent entry is one vector whose dqk values are the key and
- * whose first dv values are the value.  A unit whose step failed (nonzero
- * status) produces zeros.  The work is independent per (unit, token, head)
- * and shared over OpenMP threads on that index, nothing else.
+ * whose first dv values are the value.  With context lengths, token row t of
+ * entry e is position e * tpe + t of its request, and rows at or past the
+ * request's length are not attended (the last page of a context may be only
+ * partly written; what its other rows hold never matters).  A unit whose
+ * step failed (nonzero status) produces zeros.  The work is independent per
+ * (unit, token, head) and shared over OpenMP threads on that index, nothing
+ * else.
  */
 #include <math.h>
 #include <stdint.h>
@@ -48,10 +52,13 @@ static double bf16_value(uint16_t bits) {
  *   len      [units][T] entries in use of each list (its first len ids), or
  *            NULL for k
  *   status   [units] or NULL (all 0)
+ *   ctx_len  [B] context length of each request in tokens, or NULL (every
+ *            row of a selected entry is attended)
  *   out      [B][T][Hq][dv] doubles, every element written
  */
 void oracle_attend(const oracle_attn_cfg* c, const uint16_t* q, const uint16_t* host_kv,
-                   const int32_t* sel, const int32_t* len, const int32_t* status, double* out) {
+                   const int32_t* sel, const int32_t* len, const int32_t* status,
+                   const int32_t* ctx_len, double* out) {
   const int64_t Hkv = c->n_kv_heads, Hq = c->n_q_heads, T = c->n_tokens, k = c->k;
   const int64_t dqk = c->head_dim_qk, dv = c->head_dim_v, G = Hq / Hkv;
   const int64_t tpe = c->latent ? 1 : c->tokens_per_entry;
@@ -73,31 +80,41 @@ void oracle_attend(const oracle_attn_cfg* c, const uint16_t* q, const uint16_t* 
     const uint16_t* qrow = q + ((b * T + j) * Hq + h) * dqk;
     for (int64_t d = 0; d < dqk; ++d) qd[d] = bf16_value(qrow[d]);
     const int32_t* ids = sel + (u * T + j) * k;
+    /* token row t of entry e is attended iff its position is in the context */
+    const int64_t lim = ctx_len ? ctx_len[b] : INT64_MAX;
+#define IN_CONTEXT(e, t) ((int64_t)ids[e] * tpe + (t) < lim)
     /* scores, token rows in selection order (the tokens of a page in order) */
+    int have = 0;
+    double mx = 0.0;
     for (int64_t e = 0; e < n_sel; ++e) {
       const uint16_t* r = host_kv + (u * (int64_t)c->n_entries + ids[e]) * row;
       for (int64_t t = 0; t < tpe; ++t) {
+        if (!IN_CONTEXT(e, t)) continue;
         const uint16_t* key = r + t * dqk;
         double acc = 0.0;
         for (int64_t d = 0; d < dqk; ++d) acc += qd[d] * bf16_value(key[d]);
         s[e * tpe + t] = c->scale * acc;
+        if (!have || s[e * tpe + t] > mx) mx = s[e * tpe + t];
+        have = 1;
       }
     }
-    double mx = s[0];
-    for (int64_t i = 1; i < n; ++i) mx = s[i] > mx ? s[i] : mx;
     double sum = 0.0;
-    for (int64_t i = 0; i < n; ++i) {
-      s[i] = exp(s[i] - mx);
-      sum += s[i];
-    }
+    for (int64_t e = 0; e < n_sel; ++e)
+      for (int64_t t = 0; t < tpe; ++t) {
+        if (!IN_CONTEXT(e, t)) continue;
+        s[e * tpe + t] = exp(s[e * tpe + t] - mx);
+        sum += s[e * tpe + t];
+      }
     for (int64_t e = 0; e < n_sel; ++e) {
       const uint16_t* r = host_kv + (u * (int64_t)c->n_entries + ids[e]) * row;
       for (int64_t t = 0; t < tpe; ++t) {
+        if (!IN_CONTEXT(e, t)) continue;
         const uint16_t* val = c->latent ? r : r + tpe * dqk + t * dv;
         const double p = s[e * tpe + t] / sum;
         for (int64_t d = 0; d < dv; ++d) o[d] += p * bf16_value(val[d]);
       }
     }
+#undef IN_CONTEXT
     free(qd);
     free(s);
   }

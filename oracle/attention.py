@@ -10,7 +10,10 @@ the host KV, not from any buffer.
 
 Readings where the pages are silent:
   - query head h uses KV head h // (Hq / Hkv) (consecutive groups);
-  - a selected page contributes all of its tokens (no intra-page mask);
+  - a selected page contributes all of its tokens, unless a context length
+    is given: token row t of entry e is position e P + t of its request, and
+    rows at or past the length are not attended (the context's last page may
+    be only partly written);
   - a latent row serves as the key (all head_dim_qk values) and its first
     head_dim_v values serve as the value;
   - a unit whose step failed validation produces zeros.
@@ -46,10 +49,19 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float)
     return p @ V                                                 # [G][dv]
 
 
+def in_context(w, ids, ctx_len) -> np.ndarray:
+    """Mask over the token rows of the entries `ids` (in unit_kv's order):
+    row t of entry e is position e P + t, kept when below ctx_len."""
+    P = 1 if w.latent else w.tokens_per_entry
+    pos = np.asarray(ids, dtype=np.int64)[:, None] * P + np.arange(P)[None, :]
+    return (pos < ctx_len).reshape(-1)
+
+
 def attend_unit(w, q_bits: np.ndarray, host_kv_unit: np.ndarray, sel_unit: np.ndarray, unit: int,
-                token: int, heads=None) -> np.ndarray:
+                token: int, heads=None, ctx_len=None) -> np.ndarray:
     """Output rows [G'][dv] of unit `unit`, query token `token`, for the query
-    heads `heads` (default: all heads mapped to this unit's KV head)."""
+    heads `heads` (default: all heads mapped to this unit's KV head), over
+    the rows of the request's context when ctx_len (its length) is given."""
     G = w.n_q_heads // w.n_kv_heads
     b, g = divmod(unit, w.n_kv_heads)
     if heads is None:
@@ -57,15 +69,19 @@ def attend_unit(w, q_bits: np.ndarray, host_kv_unit: np.ndarray, sel_unit: np.nd
     heads = list(heads)
     q = bf16_to_f64(q_bits[b, token, heads, :])                  # [G'][dqk]
     K, V = unit_kv(w, host_kv_unit, sel_unit[token])
+    if ctx_len is not None:
+        keep = in_context(w, sel_unit[token], ctx_len)
+        K, V = K[keep], V[keep]
     return softmax_attention(q, K, V, w.softmax_scale)
 
 
 def attend(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=None,
-           units=None, lengths=None) -> np.ndarray:
+           units=None, lengths=None, ctx_len=None) -> np.ndarray:
     """float64 out [B][T][Hq][dv] for one step.  host_kv is [units][N][row]
     (uint16 bf16 bits), sel is [units][T][k], of which the first
-    lengths[u][j] entries are in use (all when lengths is None).  Units not
-    in `units` are NaN; units with a nonzero status are zero."""
+    lengths[u][j] entries are in use (all when lengths is None); ctx_len
+    [B]: context lengths in tokens (None: whole entries).  Units not in
+    `units` are NaN; units with a nonzero status are zero."""
     out = np.full((w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_v), np.nan)
     G = w.n_q_heads // w.n_kv_heads
     for u in (range(w.units) if units is None else units):
@@ -76,12 +92,14 @@ def attend(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=N
             else:
                 su = sel[u] if lengths is None else [sel[u][jj][:lengths[u][jj]]
                                                      for jj in range(w.n_q_tokens)]
-                out[b, j, g * G:(g + 1) * G] = attend_unit(w, q_bits, host_kv[u], su, u, j)
+                out[b, j, g * G:(g + 1) * G] = attend_unit(
+                    w, q_bits, host_kv[u], su, u, j,
+                    ctx_len=None if ctx_len is None else int(ctx_len[b]))
     return out
 
 
 def attend_native(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, status=None,
-                  lengths=None, threads=None) -> np.ndarray:
+                  lengths=None, threads=None, ctx_len=None) -> np.ndarray:
     """The same attention as `attend`, computed by the oracle library's C
     loops in double precision (attention.c), with OpenMP over (unit, token,
     head); every unit is computed.  threads: OpenMP threads (None: leave the
@@ -100,11 +118,12 @@ def attend_native(w, q_bits: np.ndarray, host_kv: np.ndarray, sel: np.ndarray, s
     ln = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32).reshape(
         w.units, w.n_q_tokens)
     stt = None if status is None else np.ascontiguousarray(status, dtype=np.int32).reshape(w.units)
+    cl = None if ctx_len is None else np.ascontiguousarray(ctx_len, dtype=np.int32).reshape(w.batch)
     out = np.empty((w.batch, w.n_q_tokens, w.n_q_heads, w.head_dim_v), np.float64)
     cfg = AttnCfg(w.batch, w.n_kv_heads, w.n_q_heads, w.n_q_tokens, w.head_dim_qk, w.head_dim_v,
                   1 if w.latent else 0, w.tokens_per_entry, w.n_entries, w.k,
                   float(w.softmax_scale))
     lib.oracle_attend(ctypes.byref(cfg), q_bits.ctypes.data, host_kv.ctypes.data, sel.ctypes.data,
                       None if ln is None else ln.ctypes.data, None if stt is None else stt.ctypes.data,
-                      out.ctypes.data)
+                      None if cl is None else cl.ctypes.data, out.ctypes.data)
     return out

@@ -113,12 +113,18 @@ static int32_t find_sorted(const int32_t* a, int32_t n, int32_t x) {
  *                      2C), or NULL: every entry has one.  A miss without a
  *                      row cannot be transferred: a range error, found
  *                      after every other check.
+ *   n_ctx              entries that hold tokens of the request's context
+ *                      (page e holds positions [e P, (e + 1) P); it is in
+ *                      the context when e P < the context length): an id in
+ *                      use at or past n_ctx is out of range like one past N.
+ *                      n_ctx < 1 (a context length outside [1, N P]) is a
+ *                      range error.
  * Returns a status; on error the state is unchanged, flags are 0, slots -1.
  */
 int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const int32_t* len,
                      int32_t cap, int32_t* slot_tok, int32_t* life, uint8_t* hit_flag,
                      int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts,
-                     const uint8_t* mapped) {
+                     const uint8_t* mapped, int32_t n_ctx) {
   const int32_t S_all = c->n_slots, N = c->n_entries, T = c->n_tokens, k = c->k;
   /* the slots in use: [0, S) */
   const int32_t S = cap;
@@ -136,12 +142,12 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
     if (nj < 1 || nj > k) { range_bad = 1; continue; }
     for (int32_t i = 0; i < nj; ++i) {
       int32_t x = sel[j * k + i];
-      if (x < 0 || x >= N) range_bad = 1;
+      if (x < 0 || x >= N || x >= n_ctx) range_bad = 1;
       if (i > 0 && x <= sel[j * k + i - 1]) order_bad = 1;
     }
     n_used += nj;
   }
-  if (cap < 1 || cap > S_all) range_bad = 1;
+  if (cap < 1 || cap > S_all || n_ctx < 1) range_bad = 1;
   if (range_bad) return OR_ERR_RANGE;
   if (order_bad) return OR_ERR_UNSORTED;
   int32_t* U = (int32_t*)malloc(sizeof(int32_t) * (size_t)(tk > 0 ? tk : 1));
@@ -278,11 +284,12 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
 
 /* All units of one step (units are independent; OpenMP over units).  len is
  * [units][T] or NULL, cap [units] or NULL (every unit uses all S slots),
- * mapped [units][N] or NULL (every entry has a host row). */
+ * mapped [units][N] or NULL (every entry has a host row), n_ctx [units] or
+ * NULL (every entry is in the context). */
 void oracle_step(const oracle_cfg* c, int64_t units, int64_t t, const int32_t* sel,
                  const int32_t* len, const int32_t* cap, int32_t* slot_tok, int32_t* life,
                  uint8_t* hit_flag, int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id,
-                 int32_t* counts, int32_t* status, const uint8_t* mapped) {
+                 int32_t* counts, int32_t* status, const uint8_t* mapped, const int32_t* n_ctx) {
   const int64_t tk = (int64_t)c->n_tokens * c->k, S = c->n_slots;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t u = 0; u < units; ++u)
@@ -290,7 +297,8 @@ void oracle_step(const oracle_cfg* c, int64_t units, int64_t t, const int32_t* s
                                  cap ? cap[u] : c->n_slots,
                                  slot_tok + u * S, life + u * S, hit_flag + u * tk,
                                  sel_slot + u * tk, fill_slot + u * S, fill_id + u * S,
-                                 counts + u * 4, mapped ? mapped + u * c->n_entries : NULL);
+                                 counts + u * 4, mapped ? mapped + u * c->n_entries : NULL,
+                                 n_ctx ? n_ctx[u] : c->n_entries);
 }
 
 /* Threads used by oracle_step's loop over units. */

@@ -37,9 +37,10 @@ typedef struct {
 int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const int32_t* len,
                      int32_t cap, int32_t* slot_tok, int32_t* life, uint8_t* hit_flag,
                      int32_t* sel_slot, int32_t* fill_slot, int32_t* fill_id, int32_t* counts,
-                     const uint8_t* mapped);
+                     const uint8_t* mapped, int32_t n_ctx);
 void oracle_attend(const oracle_attn_cfg* c, const uint16_t* q, const uint16_t* host_kv,
-                   const int32_t* sel, const int32_t* len, const int32_t* status, double* out);
+                   const int32_t* sel, const int32_t* len, const int32_t* status,
+                   const int32_t* ctx_len, double* out);
 
 static long long rd(void) {
   long long v;
@@ -84,7 +85,7 @@ static int run_state(void) {
     const int32_t cap = (int32_t)rd();
     for (int64_t e = 0; e < tk; ++e) sel[e] = (int32_t)rd();
     const int st = oracle_unit_step(&c, t, sel, NULL, cap < 0 ? c.n_slots : cap, tok, life, flags,
-                                    slots, fs, fi, counts, NULL);
+                                    slots, fs, fi, counts, NULL, c.n_entries);
     printf("%d %d %d %d %d\n", st, counts[0], counts[1], counts[2], counts[3]);
     for (int64_t e = 0; e < tk; ++e) fl[e] = flags[e];
     print_i32(fl, tk);
@@ -126,7 +127,7 @@ static int run_attn(void) {
   for (int64_t i = 0; i < nh; ++i) host[i] = (uint16_t)rd();
   for (int64_t i = 0; i < ns; ++i) sel[i] = (int32_t)rd();
   for (int64_t i = 0; i < units; ++i) status[i] = (int32_t)rd();
-  oracle_attend(&c, q, host, sel, NULL, status, out);
+  oracle_attend(&c, q, host, sel, NULL, status, NULL, out);
   for (int64_t i = 0; i < no; ++i) printf(i ? " %.17g" : "%.17g", out[i]);
   printf("\n");
   free(q); free(host); free(sel); free(status); free(out);
