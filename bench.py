@@ -476,6 +476,28 @@ def extras(b, a):
         "ms_per_step": round(statistics.median(per_pass), 4),
         "hit_rate": round(ch / max(ch + cm, 1), 5),
         "host_bytes_per_step": int(cm / K * w.row_bytes)}
+    # context lengths ending inside each request's last page, which every
+    # list selects (its last id becomes N - 1, the largest): the attention
+    # masks that page's rows past the length
+    if w.tokens_per_entry > 1:
+        b.load_trace("natural", t0 + K)
+        b.sel_np[..., -1] = w.n_entries - 1
+        b.sel_dev = torch.from_numpy(b.sel_np).cuda()
+        P = w.tokens_per_entry
+        cl = torch.tensor([(w.n_entries - 1) * P + 1 + (r % (P - 1)) for r in range(w.batch)],
+                          dtype=torch.int32, device="cuda")
+        b.ctx.set_context_lengths(cl)
+        ms_c, _, kc = b.passes(t0, t0 + K, 1, a.passes)
+        b.ctx.set_context_lengths(None)
+        ms_f, _, kf = b.passes(t0, t0 + K, 1, a.passes)
+        assert b.ctx.last_error() == 0
+        out["context_lengths"] = {
+            "steps": K, "lists": "natural trace, last id of every list replaced by N - 1",
+            "lengths": "(N - 1) P + 1 + (b mod (P - 1)) per request b: 1 to P - 1 rows of the "
+                       "last page attended",
+            "ms_per_step": round(ms_c, 4), "attention_us": round(kc["attention"], 2),
+            "whole_pages_ms_per_step": round(ms_f, 4),
+            "whole_pages_attention_us": round(kf["attention"], 2)}
     # the host KV reached through the two-level directory (256-entry
     # segments in pinned host memory, the top level in HBM), over the same
     # rows: entry e of unit u at pool row u * N + e

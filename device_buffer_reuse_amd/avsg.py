@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes
 import dataclasses
 import os
+import sys
 
 import numpy as np
 
@@ -33,7 +34,8 @@ EXPORTED = ["avsg_check_config", "avsg_workspace_bytes", "avsg_create", "avsg_se
             "avsg_set_transfer_mode", "avsg_set_match_mode", "avsg_append", "avsg_append_insert",
             "avsg_rebuild_index", "avsg_step_varlen", "avsg_set_capacity",
             "avsg_plan_capacity", "avsg_step_static", "avsg_set_host_directory",
-            "avsg_set_gather_workgroups", "avsg_profile_match_phases"]
+            "avsg_set_gather_workgroups", "avsg_profile_match_phases",
+            "avsg_set_context_lengths"]
 STATIC_SCRATCH_BYTES = 64 << 20   # AVSG_STATIC_SCRATCH_BYTES
 
 
@@ -93,6 +95,7 @@ def load():
         "avsg_validate_state": ([p, p, p], i32),
         "avsg_rebuild_index": ([p, p], i32),
         "avsg_set_capacity": ([p, p], i32),
+        "avsg_set_context_lengths": ([p, p], i32),
         "avsg_set_host_directory": ([p, p, p, ctypes.c_int32, ctypes.c_int32, i64], i32),
         "avsg_plan_capacity": ([ctypes.c_int32, p, p, i64, ctypes.c_int32, p], i32),
         "avsg_get_step": ([p], i64),
@@ -194,6 +197,10 @@ def avsg_set_capacity(ctx: int, cap: int | None) -> int:
     return load().avsg_set_capacity(ctx, cap)
 
 
+def avsg_set_context_lengths(ctx: int, ctx_len: int | None) -> int:
+    return load().avsg_set_context_lengths(ctx, ctx_len)
+
+
 def avsg_set_host_directory(ctx: int, top: int | None, segments: int | None, seg_entries: int,
                             n_segments: int, pool_rows: int) -> int:
     return load().avsg_set_host_directory(ctx, top, segments, seg_entries, n_segments, pool_rows)
@@ -280,6 +287,24 @@ def config_from_workload(w, attn_split_rows: int = 0) -> avsg_config:
                   w.lifetime_L, w.n_buckets, w.softmax_scale, attn_split_rows)
 
 
+# (address, ctypes buffer) of freed HostBuffers whose memory numpy arrays may
+# still view: every array made from the buffer holds a reference to it
+_pending_host_frees = []
+
+
+def _release_host_memory():
+    keep = []
+    while _pending_host_frees:
+        ptr, raw = _pending_host_frees.pop()
+        # references: `raw` and getrefcount's argument
+        if sys.getrefcount(raw) <= 2:
+            avsg_host_free(ptr)
+        else:
+            keep.append((ptr, raw))
+        del raw
+    _pending_host_frees.extend(keep)
+
+
 class HostBuffer:
     """Pinned, device-readable host memory from avsg_host_alloc, viewed as a
     numpy array (bf16 bit patterns as uint16 by default)."""
@@ -292,14 +317,18 @@ class HostBuffer:
         if st != OK:
             raise AvsgError(st, "avsg_host_alloc(%d bytes)" % self.nbytes)
         self.ptr = ptr
-        raw = (ctypes.c_char * self.nbytes).from_address(ptr)
-        self.array = np.frombuffer(raw, dtype=self.dtype).reshape(self.shape)
+        self._raw = (ctypes.c_char * self.nbytes).from_address(ptr)
+        self.array = np.frombuffer(self._raw, dtype=self.dtype).reshape(self.shape)
 
     def free(self):
+        """Returns the memory once no numpy view of it is left (a view kept
+        elsewhere, e.g. by a traceback, would otherwise read freed memory);
+        until then the release is retried by later calls."""
         if self.ptr:
             self.array = None
-            avsg_host_free(self.ptr)
-            self.ptr = None
+            _pending_host_frees.append((self.ptr, self._raw))
+            self.ptr, self._raw = None, None
+        _release_host_memory()
 
     def __del__(self):
         try:
@@ -414,6 +443,14 @@ class Context:
         st = avsg_set_capacity(self.handle, None if cap is None else cap.data_ptr())
         if st != OK:
             raise AvsgError(st, "avsg_set_capacity")
+
+    def set_context_lengths(self, ctx_len):
+        """ctx_len: device int32 tensor [batch] of context lengths in tokens
+        (kept alive by the caller), or None: whole entries."""
+        self._ctx_len = ctx_len
+        st = avsg_set_context_lengths(self.handle, None if ctx_len is None else ctx_len.data_ptr())
+        if st != OK:
+            raise AvsgError(st, "avsg_set_context_lengths")
 
     def set_host_directory(self, top, segments, seg_entries: int, n_segments: int, pool_rows: int):
         """top: device int32 tensor [units][n_seg] (kept alive by the caller),

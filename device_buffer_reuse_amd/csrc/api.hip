@@ -23,6 +23,7 @@ struct avsg_ctx {
   int32_t transfer_mode;         // avsg_transfer_mode
   int32_t match_mode;            // avsg_match_mode
   const int32_t* cap;            // device [units] buffer size of each unit, or null (S)
+  const int32_t* ctx_len;        // device [batch] context length in tokens, or null (N * tpe)
   avsg::HostDir dir;             // two-level host directory (null top: flat host KV)
   int lds_max;
   hipEvent_t* prof_events;       // kProfMarks per profiled step, or null
@@ -477,6 +478,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   mp.sel = sel_idx;
   mp.sel_len = sel_len;
   mp.cap = ctx->cap;
+  mp.ctx_len = ctx->ctx_len;
   mp.slot_table = slot_table;
   mp.lifetimes = lifetimes;
   mp.hit_flag = hs->hit_flag;
@@ -507,6 +509,8 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   mp.L = c.lifetime_L;
   mp.B = c.n_buckets;
   mp.nbins = ctx->d.nbins;
+  mp.Hkv = c.n_kv_heads;
+  mp.tpe = c.tokens_per_entry;
   mp.match_mode = ctx->match_mode;
   mp.merge_pow2 = ctx->d.merge_pow2;
   mp.direct_words = ctx->match_mode == AVSG_MATCH_HASH ? ctx->d.direct_words : 0;
@@ -542,6 +546,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   ap.sel_slot = hs->sel_slot;
   ap.sel_len = sel_len;
   ap.sel = sel_idx;
+  ap.ctx_len = ctx->ctx_len;
   ap.fetch = fused ? (const uint8_t*)(ws + ctx->ws.fetch) : nullptr;
   ap.host_row = ctx->dir.top ? (const int32_t*)(ws + ctx->ws.host_row) : nullptr;
   ap.host_kv = (const uint16_t*)host_dev;
@@ -673,6 +678,12 @@ avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const 
 avsg_status avsg_set_capacity(avsg_ctx* ctx, const int32_t* cap) {
   if (!ctx) return AVSG_ERR_INVALID_ARG;
   ctx->cap = cap;
+  return AVSG_OK;
+}
+
+avsg_status avsg_set_context_lengths(avsg_ctx* ctx, const int32_t* ctx_len) {
+  if (!ctx) return AVSG_ERR_INVALID_ARG;
+  ctx->ctx_len = ctx_len;
   return AVSG_OK;
 }
 

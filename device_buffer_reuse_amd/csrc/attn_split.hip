@@ -183,6 +183,14 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
   // (zero past the unit's G heads), dims 32 ks + 8 gq .. +8
   constexpr int kEnt = kSplitRows / kThreads;
   const int ustat = __builtin_nontemporal_load(p.unit_status + u);
+  // with context lengths: the list's last id and the request's length (the
+  // last entry may hold the context's end)
+  const bool has_ctx = p.ctx_len != nullptr && tpe > 1;
+  int ctx_last = 0, ctx_n = 0;
+  if (has_ctx && wave == 0) {
+    ctx_last = p.sel[(size_t)uj * p.k + len - 1];
+    ctx_n = p.ctx_len[b];
+  }
   int slot_v[kEnt], id_v[kEnt], fl_v[kEnt];
   // without fetch flags (rows already gathered) the flag loads read the
   // slot array instead and are ignored
@@ -213,6 +221,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
   for (int k = 0; k < kEnt; ++k) asm volatile("" ::"v"(slot_v[k]), "v"(id_v[k]), "v"(fl_v[k]));
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" ::"v"(qf[ks]));
+  asm volatile("" ::"v"(ctx_last), "v"(ctx_n));
   if (__builtin_amdgcn_readfirstlane(ustat) != 0) {  // the same in both waves
     if (nsplit == 1 && wave == 0)
       for (int idx = lane; idx < G * kD; idx += kThreads) orow[idx] = 0.f;
@@ -242,6 +251,19 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
   // the queries are in registers before any copy is issued
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
+
+  // rows attended: [r0, rv1).  The list is ascending, so only its last entry
+  // can hold the end of the request's context; that entry's rows at or past
+  // the context length are masked like rows past the split (and a split
+  // that lies wholly past it contributes nothing).  Those rows are still
+  // staged, so that a row fetched from host memory reaches its slot whole.
+  int rv1 = r1;
+  if (has_ctx) {
+    const int64_t in_ctx = (int64_t)__builtin_amdgcn_readfirstlane(ctx_n) -
+                           (int64_t)__builtin_amdgcn_readfirstlane(ctx_last) * tpe;  // its rows inside
+    const int keep = (int)max((int64_t)1, min((int64_t)tpe, in_ctx));
+    rv1 = min(r1, (len - 1) * tpe + keep);
+  }
 
   uint16_t* ubase = p.buf_kv + (size_t)u * p.S * p.row_elems;
   const uint16_t* hbase = p.host_kv + (p.host_row ? 0 : (size_t)u * p.N * p.row_elems);
@@ -449,8 +471,23 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
     // for them
     write_back(t, buf, f_now);
 
-    // S^T = K Q^T for rows 0..15 and 16..31 of the tile
     const uint32_t tb = tile_lds + buf * kTileBytes;
+    // rows of the tile at or past rv1 (when the context ends inside the
+    // split) may hold anything, NaN included: their V halves are zeroed, so
+    // that their zero probabilities give exact zeros in the MFMA (0 * NaN
+    // would not); their masked scores never read K.  After write_back's LDS
+    // reads, before the V reads below.
+    const int z0 = rv1 - (r0 + t * kChunk);
+    if (rv1 < r1 && z0 < kChunk) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const int zr = max(z0, 0);
+      for (int i = lane; i < (kChunk - zr) * 16; i += kThreads) {
+        const uint32_t a = tb + 512 * (zr + (i >> 4)) + 256 + 16 * (i & 15);
+        asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(zero) : "memory");
+      }
+    }
+
+    // S^T = K Q^T for rows 0..15 and 16..31 of the tile
     u32x4 kf0[kKSteps], kf1[kKSteps];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
@@ -480,8 +517,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ra = r0 + t * kChunk + 4 * gq + i, rb = ra + 16;
-      sv[i] = ra < r1 ? s0[i] * p.scale_log2e : -INFINITY;
-      sv[4 + i] = rb < r1 ? s1[i] * p.scale_log2e : -INFINITY;
+      sv[i] = ra < rv1 ? s0[i] * p.scale_log2e : -INFINITY;
+      sv[4 + i] = rb < rv1 ? s1[i] * p.scale_log2e : -INFINITY;
     }
     float cm = sv[0];
 #pragma unroll
@@ -541,6 +578,13 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
 
   // lane holds O[head li][d = 16 t + 4 gq + i] (heads li < G are real)
   if (li >= G) return;
+  if (rv1 <= r0) {
+    // every row of the split is past the context: an empty partial
+    // (maximum -inf, sum 0), which the merge weighs by zero
+#pragma unroll
+    for (int t = 0; t < kDTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+  }
   if (nsplit == 1) {
     const float inv = 1.f / l_run;
 #pragma unroll

@@ -62,6 +62,7 @@ struct MatchReserveParams {
   const int32_t* sel;     // [units][T][k]
   const int32_t* sel_len; // [units][T] entries in use of each token's list, or null: k
   const int32_t* cap;     // [units] slots in use of each unit's buffer, or null: S
+  const int32_t* ctx_len; // [batch] context length in tokens, or null: every entry holds tokens
   int32_t* slot_table;    // [units][S]
   int32_t* lifetimes;     // [units][S]
   uint8_t* hit_flag;      // [units][T][k]
@@ -77,6 +78,7 @@ struct MatchReserveParams {
   uint32_t* err_word;
   int64_t t;
   int32_t S, N, T, k, ucap, table_cap, log_table_cap, ubits, policy, L, B, nbins;
+  int32_t Hkv, tpe;       // KV heads per request, tokens per entry (context lengths)
   int32_t match_mode;     // avsg_match_mode
   int32_t merge_pow2;     // power of two >= S (sort size of the merge baseline)
   int32_t direct_words;   // > 0: match through N-bit membership words and rank bases
@@ -104,6 +106,7 @@ struct AttnParams {
   const int32_t* sel_slot;    // [units][T][k]
   const int32_t* sel_len;     // [units][T] entries in use of each list, or null: k
   const int32_t* sel;         // [units][T][k] selected ids
+  const int32_t* ctx_len;     // [batch] context length in tokens, or null: whole entries
   const uint8_t* fetch;       // [units][T][k] or null: rows to read from host and store
   const int32_t* host_row;    // [units][T][k] pool row of each fetched entry, or null: flat
                               // host KV, row u * N + sel

@@ -197,6 +197,12 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // emptied by this step); a capacity outside [1, S] is a range error
   const int cap_in = p.cap ? p.cap[u] : S;
   const bool cap_bad = cap_in < 1 || cap_in > S;
+  // entries of the request's context (entry e holds positions [e tpe,
+  // (e + 1) tpe)): selected ids at or past them are out of range like ids
+  // past N; a context length outside [1, N tpe] is a range error
+  const int64_t ctx_in = p.ctx_len ? p.ctx_len[u / p.Hkv] : 1;
+  const bool ctx_bad = ctx_in < 1 || ctx_in > (int64_t)N * p.tpe;
+  const int lim = (p.ctx_len && !ctx_bad) ? (int)((ctx_in + p.tpe - 1) / p.tpe) : N;
   const int cap = cap_bad ? S : cap_in;
   const int nbins = p.nbins, tk = T == 1 ? ka : tks;
   // entry i of the [T][k] array is in use: one token, i < tk; two tokens,
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       for (int r = 0; r < kSelRegs; ++r) {
         const int i = tid + r * kMRThreads;
         const int32_t x = selr[r];
-        if (i < tk && x >= 0 && x < N) {
+        if (i < tk && x >= 0 && x < lim) {
           atomicOr(&sBits[x >> 5], 1u << (x & 31));
           if (i == 0 || (prv[r] >> 5) != (x >> 5)) sBase[x >> 5] = i;
         }
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       for (int r = 0; r < kSelRegs; ++r) {
         const int i = tid + r * kMRThreads;
         const int32_t x = selr[r];
-        if (i < tk && in_use_at(i, k, live_end0, live_end1) && x >= 0 && x < N)
+        if (i < tk && in_use_at(i, k, live_end0, live_end1) && x >= 0 && x < lim)
           atomicOr(&(i < k ? sBitsA : sBits)[x >> 5], 1u << (x & 31));
       }
     } else if (T == 1) {
@@ -311,13 +317,13 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         const int i = tid + r * kMRThreads;
         const int32_t x = selr[r];
         hb[r] = hash_id(x, log_cap) >> 2;
-        pos[r] = atomicAdd((i < tk && x >= 0 && x < N) ? &sBcnt[hb[r]] : &sSink[lane], 1);
+        pos[r] = atomicAdd((i < tk && x >= 0 && x < lim) ? &sBcnt[hb[r]] : &sSink[lane], 1);
       }
 #pragma unroll
       for (int r = 0; r < kSelRegs; ++r) {
         const int i = tid + r * kMRThreads;
         const int32_t x = selr[r];
-        if (i < tk && x >= 0 && x < N) {
+        if (i < tk && x >= 0 && x < lim) {
           const int32_t v = (x << ubits) | i;
           if (pos[r] < 4)
             sHash[hb[r] * 4 + pos[r]] = v;
@@ -331,18 +337,18 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     for (int r = 0; r < kSelRegs; ++r) {
       const int i = tid + r * kMRThreads;
       const int32_t x = selr[r];
-      const bool in_use = i < tk && in_use_at(i, k, live_end0, live_end1), in_range = x >= 0 && x < N;
+      const bool in_use = i < tk && in_use_at(i, k, live_end0, live_end1), in_range = x >= 0 && x < lim;
       // a token's list starts at 0 and, for the second token, at k (T <= 2)
       bad |= (in_use && !in_range) ? kFlagRange : 0;
       bad |= (in_use && i != 0 && i != k && x <= prv[r]) ? kFlagUnsorted : 0;
     }
-    if ((len_bad || cap_bad) && tid == 0) bad |= kFlagRange;
+    if ((len_bad || cap_bad || ctx_bad) && tid == 0) bad |= kFlagRange;
     // one token: U is the list itself
     if (T == 1 && tk > cap && tid == 0) bad |= kFlagCapacity;
     for (int i = tid + kSelRegs * kMRThreads; i < tk; i += kMRThreads) {
       if (!in_use_at(i, k, live_end0, live_end1)) continue;
       const int32_t x = stage[i];
-      const bool in_range = x >= 0 && x < N;
+      const bool in_range = x >= 0 && x < lim;
       if (!in_range) bad |= kFlagRange;
       const int32_t xp = stage[i - 1];
       if (i != k && x <= xp) bad |= kFlagUnsorted;

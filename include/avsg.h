@@ -226,6 +226,21 @@ avsg_status avsg_step_static(const avsg_config* cfg, int64_t t, void* stream,
  * The pointer is kept by the context; the caller owns the array. */
 avsg_status avsg_set_capacity(avsg_ctx* ctx, const int32_t* cap);
 
+/* Context length of each request, in tokens (page-based KV of the Spin
+ * summary, sections 2A and 2B: decoded tokens are appended into the current
+ * page, so the last page of a context may be only partly written).  Entry e
+ * holds positions [e P, (e + 1) P), P = tokens_per_entry.  `ctx_len` is a
+ * device int32 array [batch] read by every later step when it runs (update
+ * it between steps, stream-ordered, e.g. after each avsg_append), or NULL:
+ * every entry holds P tokens.  A step then attends, of each selected entry,
+ * only the rows at positions below the length (what the other rows of the
+ * last page hold never matters, NaN included); transfers still copy whole
+ * rows, so the buffer keeps exact copies.  A selected id whose first position
+ * is at or past the length is a range error of its unit, as is a length
+ * outside [1, N P].  avsg_step_static takes no lengths.  The pointer is kept
+ * by the context; the caller owns the array. */
+avsg_status avsg_set_context_lengths(avsg_ctx* ctx, const int32_t* ctx_len);
+
 /* Host KV through a two-level directory (Spin summary, section 2C:
  * hierarchical metadata; a small top-level directory on the GPU points to
  * second-level segments allocated on demand in CPU memory, so metadata

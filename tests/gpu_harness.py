@@ -42,13 +42,13 @@ def check_attention(got, ref, what=""):
 class Runner:
     """GPU state + oracle state for one workload."""
 
-    def __init__(self, w, host=None, track_buf=True, attn_units=None, mode=None):
+    def __init__(self, w, host=None, track_buf=True, attn_units=None, mode=None, split_rows=0):
         import torch
         self.torch = torch
         avsg = ensure_lib()
         self.avsg = avsg
         self.w = w
-        self.cfg = avsg.config_from_workload(w)
+        self.cfg = avsg.config_from_workload(w, split_rows)
         self.ctx = avsg.Context(self.cfg)
         if mode is not None:
             self.ctx.set_transfer_mode(mode)
@@ -76,14 +76,23 @@ class Runner:
         self.cap_dev = None if caps is None else self.torch.from_numpy(self.caps).cuda()
         self.ctx.set_capacity(self.cap_dev)
 
+    def set_ctx_len(self, ctx_len):
+        """Context lengths in tokens per request for the following steps
+        (None: whole entries)."""
+        self.ctx_len = None if ctx_len is None else np.asarray(ctx_len, np.int32).copy()
+        self.ctx_dev = None if ctx_len is None else self.torch.from_numpy(self.ctx_len).cuda()
+        self.ctx.set_context_lengths(self.ctx_dev)
+
     def step_and_compare(self, t, sel_t, q_t, check_attn=True, check_buf=False, lengths=None):
         """lengths: optional list lengths, [units] or [units][T]."""
         self.gpu_step(sel_t, q_t, lengths)
         self.torch.cuda.synchronize()
         ln = None if lengths is None else np.asarray(lengths, np.int32).reshape(
             self.w.units, self.w.n_q_tokens)
+        ctx_len = getattr(self, "ctx_len", None)
         r = self.ob.step(sel_t, self.host.array if self.ob.track_buf else None, lengths=ln,
-                         caps=getattr(self, "caps", None))
+                         caps=getattr(self, "caps", None), ctx_len=ctx_len,
+                         tokens_per_entry=self.w.tokens_per_entry)
         s = self.st
         assert np.array_equal(s.slot_table.cpu().numpy(), self.ob.slot_tok), "slot_table t=%d" % t
         assert np.array_equal(s.lifetimes.cpu().numpy(), self.ob.life), "lifetimes t=%d" % t
@@ -98,7 +107,7 @@ class Runner:
         err = None
         if check_attn:
             ref = oatt.attend(self.w, q_t, self.host.array, sel_t, r["status"], units=self.attn_units,
-                              lengths=ln)
+                              lengths=ln, ctx_len=ctx_len)
             err = check_attention(s.out.cpu().numpy(), ref, "out t=%d" % t)
         return r, err
 
