@@ -16,6 +16,7 @@ from oracle import attention as oatt
 from oracle import append as oapp
 from gpu_harness import check_attention, ensure_lib, say
 from directory_inputs import build_directory, permuted_pool
+from context_inputs import clip_to_context, nan_past_context, start_lengths
 
 pytestmark = pytest.mark.gpu
 
@@ -34,11 +35,13 @@ class DirRun:
     """GPU context reading a permuted pool through a directory, beside the
     oracle reading the flat rows."""
 
-    def __init__(self, w, seg, rng, mapping_filter=None, mode=None):
+    def __init__(self, w, seg, rng, mapping_filter=None, mode=None, split_rows=0, prepare=None):
         import torch
         avsg = ensure_lib()
         self.avsg, self.torch, self.w, self.seg = avsg, torch, w, seg
         self.flat = tg.fill_kv(w)
+        if prepare is not None:      # changes the rows before the pool is laid out
+            prepare(self.flat)
         pool, mapping = permuted_pool(self.flat, rng, extra_rows=w.units * 3)
         if mapping_filter is not None:
             mapping = {key: r for key, r in mapping.items() if mapping_filter(*key)}
@@ -52,7 +55,7 @@ class DirRun:
         self.segs = avsg.HostBuffer(segs.shape, dtype=np.int32)
         self.segs.array[...] = segs
         self.top = torch.from_numpy(top).cuda()
-        self.cfg = avsg.config_from_workload(w)
+        self.cfg = avsg.config_from_workload(w, split_rows)
         self.ctx = avsg.Context(self.cfg)
         if mode is not None:
             self.ctx.set_transfer_mode(mode)
@@ -364,6 +367,88 @@ def test_lengths_sizes_and_directory_together(name):
             assert np.array_equal(s.buf_kv.cpu().numpy().view(np.uint16)[occ], run.ob.buf[occ]), what
             ref = oatt.attend(w, q, run.flat, sel[t], r["status"], lengths=lens[t])
             check_attention(s.out.cpu().numpy(), ref, what)
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
+EVERYTHING = {
+    "pages16_lru": (tg.WORKLOADS[4].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=301, k=37,
+                                            n_slots=100, steps=12, n_buckets=5), 16, 0),
+    "pages3_lifetime": (tg.WORKLOADS[4].replace(batch=3, n_kv_heads=2, n_q_heads=8, n_entries=400,
+                                                tokens_per_entry=3, k=11, n_slots=40, steps=10,
+                                                policy="lifetime", lifetime_L=4), 8, 32),
+}
+
+
+@pytest.mark.parametrize("name", list(EVERYTHING))
+def test_every_option_together(name):
+    """Context lengths with a partly written last page (rows past each
+    context hold NaN), list lengths whose last entry in use is that page,
+    buffer sizes that change every step, host rows through the directory,
+    and an insertion of each new token's entry after every step: state,
+    flags, buffer bytes, host rows and attention against the oracle."""
+    w, seg, split_rows = EVERYTHING[name]
+    P = w.tokens_per_entry
+    say("[everything] %s" % name)
+    rng = np.random.default_rng(5 + len(name))
+    ctx_len = start_lengths(w)
+    run = DirRun(w, seg, rng, split_rows=split_rows,
+                 prepare=lambda flat: nan_past_context(flat, w, ctx_len))
+    torch = run.torch
+    sel_full = tg.selections(w)
+    _, lens = tg.shorten(sel_full, seed=7, lo=max(2, w.k // 4))
+    lens = lens.reshape(w.steps, w.units, w.n_q_tokens)
+    ob = run.ob
+    try:
+        for t in range(w.steps):
+            sel_t = clip_to_context(sel_full[t], w, ctx_len)
+            for u in range(w.units):           # the page with the context's end is in use
+                last = (int(ctx_len[u // w.n_kv_heads]) - 1) // P
+                for j in range(w.n_q_tokens):
+                    sel_t[u, j, lens[t, u, j] - 1] = last
+            need = np.array([len(np.unique(np.concatenate(
+                [sel_t[u, j, :lens[t, u, j]] for j in range(w.n_q_tokens)])))
+                for u in range(w.units)], np.int32)
+            caps = np.minimum(w.n_slots, need + rng.integers(0, w.n_slots // 2, size=w.units))
+            caps = caps.astype(np.int32)
+            cap_dev = torch.from_numpy(caps).cuda()
+            ctx_dev = torch.from_numpy(ctx_len).cuda()
+            run.ctx.set_capacity(cap_dev)
+            run.ctx.set_context_lengths(ctx_dev)
+            q = tg.queries(w, t)
+            s = run.st
+            ln_dev = torch.from_numpy(np.ascontiguousarray(lens[t].reshape(-1))).cuda()
+            run.ctx.step(torch.from_numpy(np.ascontiguousarray(sel_t)).cuda(),
+                         torch.from_numpy(q.view(np.int16)).cuda(), run.pool, s.buf_kv,
+                         s.slot_table, s.lifetimes, s.out, s.stats, sel_len=ln_dev)
+            torch.cuda.synchronize()
+            r = ob.step(sel_t, run.flat, lengths=lens[t], caps=caps, mapped=run.mapped,
+                        ctx_len=ctx_len, tokens_per_entry=P)
+            what = "%s t=%d" % (name, t)
+            assert (r["status"] == 0).all(), what
+            assert np.array_equal(s.slot_table.cpu().numpy(), ob.slot_tok), what
+            assert np.array_equal(s.lifetimes.cpu().numpy(), ob.life), what
+            assert np.array_equal(s.stats.sel_slot.cpu().numpy(), r["sel_slot"]), what
+            assert np.array_equal(s.stats.hit_flag.cpu().numpy(), r["hit_flag"]), what
+            assert np.array_equal(s.buf_kv.cpu().numpy().view(np.uint16), ob.buf), what
+            ref = oatt.attend(w, q, run.flat, sel_t, r["status"], lengths=lens[t], ctx_len=ctx_len)
+            check_attention(s.out.cpu().numpy(), ref, what)
+            # the new token at position ctx_len, its entry made resident
+            x = rng.standard_normal((w.units, w.head_dim_qk + w.head_dim_v)).astype(np.float32)
+            new = (x.view(np.uint32) >> 16).astype(np.uint16)
+            st = oapp.append_insert(w, run.flat, new, ctx_len, ob.slot_tok, ob.life, ob.buf, ob.t,
+                                    caps=caps, mapped=run.mapped)
+            assert (st == 0).all(), what
+            run.ctx.append_insert(torch.from_numpy(new.view(np.int16)).cuda(), ctx_dev, run.pool,
+                                  s.buf_kv, s.slot_table, s.lifetimes)
+            torch.cuda.synchronize()
+            for (u, e), row in run.mapping.items():
+                assert np.array_equal(run.pool.array[row], run.flat[u, e]), (what, u, e)
+            assert np.array_equal(s.slot_table.cpu().numpy(), ob.slot_tok), what
+            assert np.array_equal(s.lifetimes.cpu().numpy(), ob.life), what
+            assert np.array_equal(s.buf_kv.cpu().numpy().view(np.uint16), ob.buf), what
+            ctx_len = ctx_len + 1
         assert run.ctx.last_error() == 0
     finally:
         run.close()
