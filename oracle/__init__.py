@@ -50,7 +50,8 @@ def build(force: bool = False) -> str:
 
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("n_slots", "n_entries", "n_tokens", "k", "policy", "lifetime_L", "n_buckets")]
+                ("n_slots", "n_entries", "n_tokens", "k", "policy", "lifetime_L", "n_buckets",
+                 "bucket_width")]
 
 
 class AttnCfg(ctypes.Structure):
@@ -100,9 +101,10 @@ class OracleBuffer:
     """
 
     def __init__(self, n_slots, n_entries, n_tokens, k, policy, lifetime_L, n_buckets, units,
-                 row_elems=0, track_buf=False):
+                 row_elems=0, track_buf=False, bucket_width=1):
         self.cfg = _Cfg(n_slots, n_entries, n_tokens, k,
-                        LRU if policy in ("lru", LRU) else LIFETIME, lifetime_L, n_buckets)
+                        LRU if policy in ("lru", LRU) else LIFETIME, lifetime_L, n_buckets,
+                        bucket_width)
         self.units = units
         self.row_elems = row_elems
         self.track_buf = track_buf
@@ -111,7 +113,7 @@ class OracleBuffer:
     @classmethod
     def for_workload(cls, w, track_buf=False, units=None):
         return cls(w.n_slots, w.n_entries, w.n_q_tokens, w.k, w.policy, w.lifetime_L, w.n_buckets,
-                   w.units if units is None else units, w.row_elems, track_buf)
+                   w.units if units is None else units, w.row_elems, track_buf, w.bucket_width)
 
     def reset(self):
         S = self.cfg.n_slots
@@ -201,18 +203,19 @@ def context_entries(ctx_len, tokens_per_entry: int, n_entries: int) -> np.ndarra
 
 
 def unit_step(n_slots, n_entries, k, policy, lifetime_L, n_buckets, t, sel, slot_tok, life,
-              lengths=None, cap=None, mapped=None, n_ctx=None):
+              lengths=None, cap=None, mapped=None, n_ctx=None, bucket_width=1):
     """Single-unit call for small hand-built cases: returns (status, result
     dict) and updates slot_tok / life (int32 arrays) in place.  lengths: the
     entries in use of each token's list (default: all k); cap: slots in use
     (default: all n_slots); mapped: [N] bool, entries with a host row
-    (default: all); n_ctx: entries in the request's context (default: N)."""
+    (default: all); n_ctx: entries in the request's context (default: N);
+    bucket_width: steps per LRU bucket."""
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     if sel.ndim == 1:
         sel = sel[None, :]
     T = sel.shape[0]
     cfg = _Cfg(n_slots, n_entries, T, k, LRU if policy in ("lru", LRU) else LIFETIME, lifetime_L,
-               n_buckets)
+               n_buckets, bucket_width)
     assert slot_tok.dtype == np.int32 and life.dtype == np.int32
     hit = np.zeros((T, k), np.uint8)
     ss = np.zeros((T, k), np.int32)

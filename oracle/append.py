@@ -103,7 +103,7 @@ def append_insert(w, host_kv: np.ndarray, new_kv: np.ndarray, pos: np.ndarray,
     P, N, S = w.tokens_per_entry, w.n_entries, w.n_slots
     d_qk, d_v = w.head_dim_qk, w.head_dim_v
     lru = w.policy == "lru"
-    L, B = w.lifetime_L, w.n_buckets
+    L, B, W = w.lifetime_L, w.n_buckets, w.bucket_width
     assert not (lru and t < 1), "a bucketed-LRU stamp needs a step before it"
     fresh = t - 1 if lru else L
     empty_life = -1 if lru else 0
@@ -141,7 +141,7 @@ def append_insert(w, host_kv: np.ndarray, new_kv: np.ndarray, pos: np.ndarray,
             def order(s):
                 if slot_tok[u, s] < 0:
                     return (0, 0, s)
-                key = int(life[u, s]) if not lru else -min(t - int(life[u, s]) - 1, B - 1)
+                key = int(life[u, s]) if not lru else -min((t - int(life[u, s]) - 1) // W, B - 1)
                 return (1, key, s)
             s = min(range(cap), key=order)
             slot_tok[u, s] = e

@@ -24,7 +24,8 @@
  *    occupied slot loses one (never below 0); a slot at 0 is still resident
  *    and can still hit;
  *  - LRU policy: a slot's stamp is the step it was last selected; its bucket
- *    is min(t - stamp - 1, B - 1), larger buckets are older;
+ *    is min(floor((t - stamp - 1) / W), B - 1) for buckets W steps wide (1
+ *    unless configured), larger buckets are older;
  *  - victims are the m slots not holding an entry of U that come first in
  *    the order (occupied?, lifetime or minus bucket, slot index): empty slots
  *    first, then the least-recently/least-often kept, then the lowest index;
@@ -55,6 +56,7 @@ typedef struct {
   int32_t policy;      /* OR_LIFETIME or OR_LRU */
   int32_t lifetime_L;
   int32_t n_buckets;   /* B */
+  int32_t bucket_width; /* W: steps per LRU bucket */
 } oracle_cfg;
 
 static int cmp_i32(const void* a, const void* b) {
@@ -242,7 +244,7 @@ int oracle_unit_step(const oracle_cfg* c, int64_t t, const int32_t* sel, const i
     if (!cand[nc].occupied) cand[nc].key = 0;
     else if (c->policy == OR_LIFETIME) cand[nc].key = life[s];
     else {
-      int64_t bucket = t - (int64_t)life[s] - 1;
+      int64_t bucket = (t - (int64_t)life[s] - 1) / c->bucket_width;
       if (bucket > B - 1) bucket = B - 1;
       cand[nc].key = -(int32_t)bucket;
     }

@@ -26,7 +26,7 @@
 #include <string.h>
 
 typedef struct {
-  int32_t n_slots, n_entries, n_tokens, k, policy, lifetime_L, n_buckets;
+  int32_t n_slots, n_entries, n_tokens, k, policy, lifetime_L, n_buckets, bucket_width;
 } oracle_cfg;
 typedef struct {
   int32_t batch, n_kv_heads, n_q_heads, n_tokens, head_dim_qk, head_dim_v, latent,
@@ -65,6 +65,7 @@ static int run_state(void) {
   c.policy = (int32_t)rd();
   c.lifetime_L = (int32_t)rd();
   c.n_buckets = (int32_t)rd();
+  c.bucket_width = 1;
   const int64_t steps = rd();
   const int64_t S = c.n_slots, tk = (int64_t)c.n_tokens * c.k;
   int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);

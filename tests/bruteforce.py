@@ -6,7 +6,8 @@ from those two numbers:
   - lifetime after step t of a slot last selected at step t' is
     max(L - (t - t'), 0) (reset to L on selection, minus one per later step,
     floored at 0);
-  - LRU bucket at step t is min(t - t' - 1, B - 1).
+  - LRU bucket at step t is min(floor((t - t' - 1) / W), B - 1), W steps per
+    bucket.
 Matching is an O(|U| * S) scan and each victim is found by a full-scan argmin
 over the remaining candidates, one miss at a time.
 """
@@ -14,8 +15,8 @@ from __future__ import annotations
 
 
 class BruteBuffer:
-    def __init__(self, S, N, L, B, policy):
-        self.S, self.N, self.L, self.B, self.policy = S, N, L, B, policy
+    def __init__(self, S, N, L, B, policy, W=1):
+        self.S, self.N, self.L, self.B, self.policy, self.W = S, N, L, B, policy, W
         self.tok = [-1] * S
         self.last = [None] * S
         self.t = 0
@@ -38,7 +39,7 @@ class BruteBuffer:
             return (0, 0, s)
         age = t - self.last[s]
         if self.policy == "lru":
-            return (1, -min(age - 1, self.B - 1), s)
+            return (1, -min((age - 1) // self.W, self.B - 1), s)
         return (1, max(self.L - age, 0), s)
 
     def step(self, lists):

@@ -350,3 +350,12 @@ def test_insert_keeps_every_unit_separate():
     assert st.tolist() == [0, 0, 0, 0]
     assert slot_tok.tolist() == [[1, 2, 9, -1], [3, 9, 4, -1], [5, 6, 11, 8], [9, 10, 11, 0]]
     assert lf.tolist() == [[5, 5, 5, 0], [1, 5, 2, 0], [3, 2, 5, 4], [1, 1, 5, 1]]
+
+
+def test_insert_lru_bucket_width():
+    # t = 10, W = 3, B = 3: stamps 9, 7, 6, 3 are buckets 0, 0, 1, 2: slot 3
+    w, host, rng = _one_unit(policy="lru", S=4, B=3)
+    w = w.replace(bucket_width=3)
+    slot_tok, lf, buf = _state(w, host, [4, 6, 8, 10], [9, 7, 6, 3])
+    st, _, _ = _insert(w, host, rng, slot_tok, lf, buf, e=2, t=10)
+    assert st == 0 and slot_tok[0].tolist() == [4, 6, 8, 2] and lf[0].tolist() == [9, 7, 6, 9]

@@ -110,8 +110,8 @@ def _random_trace(rng, S, N, k, T, steps, overlap):
 @settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(seed=st.integers(0, 2**31 - 1), S=st.integers(4, 32), N=st.integers(8, 256),
        T=st.integers(1, 2), policy=st.sampled_from(["lifetime", "lru"]),
-       L=st.integers(1, 6), B=st.integers(1, 6))
-def test_oracle_matches_bruteforce(seed, S, N, T, policy, L, B):
+       L=st.integers(1, 6), B=st.integers(1, 6), W=st.integers(1, 4))
+def test_oracle_matches_bruteforce(seed, S, N, T, policy, L, B, W):
     rng = np.random.default_rng(seed)
     k = int(rng.integers(1, max(2, min(S // T, N // 2)) + 1))
     k = max(1, min(k, S // T, N // 2))
@@ -119,9 +119,9 @@ def test_oracle_matches_bruteforce(seed, S, N, T, policy, L, B):
     trace = _random_trace(rng, S, N, k, T, steps, overlap=0.6)
     tok = np.full(S, -1, np.int32)
     life = np.full(S, -1 if policy == "lru" else 0, np.int32)
-    bb = BruteBuffer(S, N, L, B, policy)
+    bb = BruteBuffer(S, N, L, B, policy, W)
     for t, sel in enumerate(trace):
-        st_, r = oracle.unit_step(S, N, k, policy, L, B, t, sel, tok, life)
+        st_, r = oracle.unit_step(S, N, k, policy, L, B, t, sel, tok, life, bucket_width=W)
         assert st_ == oracle.OK
         flags, slots, cnt = bb.step([list(map(int, l)) for l in sel])
         assert r["hit_flag"].astype(bool).tolist() == flags
@@ -439,3 +439,21 @@ def test_plan_capacity_worked_example_and_invariants():
             assert cap is None
             continue
         assert (cap >= d).all() and (cap <= S).all() and cap.sum() <= b
+
+
+def test_lru_bucket_width_worked_by_hand():
+    """Buckets W = 3 steps wide, B = 3, at step t = 10: stamps 9, 7, 6, 3, 0
+    are ages 0, 2, 3, 6, 9 past the last step, buckets 0, 0, 1, 2, 2 (9 // 3
+    = 3 capped).  Slots 3 and 4 share the oldest bucket: slot 3 goes.  With
+    one-step buckets (W = 1) slots 1..4 would all be in bucket 2 and slot 1
+    would go."""
+    sel = np.array([[11]], np.int32)
+    for W, victim in ((3, 3), (1, 1)):
+        tok = np.array([20, 21, 22, 23, 24], np.int32)
+        life = np.array([9, 7, 6, 3, 0], np.int32)
+        st_, r = oracle.unit_step(5, 30, 1, "lru", 4, 3, 10, sel, tok, life, bucket_width=W)
+        assert st_ == oracle.OK and r["n_evict"] == 1
+        assert r["sel_slot"][0, 0] == victim
+        want = [20, 21, 22, 23, 24]
+        want[victim] = 11
+        assert tok.tolist() == want and life[victim] == 10

@@ -89,6 +89,7 @@ class Workload:
     overlap_shared: float  # MTP: fraction of token 0's selection in token j's
     zipf_s: float
     seed: int
+    bucket_width: int = 1  # steps per LRU bucket
 
     @property
     def units(self) -> int:
