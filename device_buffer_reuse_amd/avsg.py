@@ -53,7 +53,8 @@ class avsg_config(ctypes.Structure):
                 ("tokens_per_entry", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("n_slots", ctypes.c_int32), ("policy", ctypes.c_int32),
                 ("lifetime_L", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("attn_split_rows", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("attn_split_rows", ctypes.c_int32),
+                ("bucket_width", ctypes.c_int32)]
 
 
 class avsg_hit_stats(ctypes.Structure):
@@ -273,10 +274,10 @@ def avsg_host_free(ptr: int) -> int:
 
 def config(batch, n_kv_heads, n_q_heads, n_q_tokens, head_dim_qk, head_dim_v, kv_layout,
            n_entries, tokens_per_entry, k, n_slots, policy, lifetime_L, n_buckets,
-           softmax_scale, attn_split_rows=0) -> avsg_config:
+           softmax_scale, attn_split_rows=0, bucket_width=1) -> avsg_config:
     return avsg_config(batch, n_kv_heads, n_q_heads, n_q_tokens, head_dim_qk, head_dim_v,
                        kv_layout, n_entries, tokens_per_entry, k, n_slots, policy, lifetime_L,
-                       n_buckets, softmax_scale, attn_split_rows)
+                       n_buckets, softmax_scale, attn_split_rows, bucket_width)
 
 
 def config_from_workload(w, attn_split_rows: int = 0) -> avsg_config:
@@ -284,7 +285,7 @@ def config_from_workload(w, attn_split_rows: int = 0) -> avsg_config:
     return config(w.batch, w.n_kv_heads, w.n_q_heads, w.n_q_tokens, w.head_dim_qk, w.head_dim_v,
                   KV_LATENT if w.latent else KV_SPLIT, w.n_entries, w.tokens_per_entry, w.k,
                   w.n_slots, POLICY_BUCKET_LRU if w.policy == "lru" else POLICY_LIFETIME,
-                  w.lifetime_L, w.n_buckets, w.softmax_scale, attn_split_rows)
+                  w.lifetime_L, w.n_buckets, w.softmax_scale, attn_split_rows, w.bucket_width)
 
 
 # (address, ctypes buffer) of freed HostBuffers whose memory numpy arrays may

@@ -195,6 +195,7 @@ static avsg_status check_config_impl(const avsg_config* c) {
   if (c->policy == AVSG_POLICY_LIFETIME && c->lifetime_L > 126) return AVSG_ERR_UNSUPPORTED;
   if (c->policy == AVSG_POLICY_BUCKET_LRU && c->n_buckets > 127) return AVSG_ERR_UNSUPPORTED;
   if (c->kv_layout != AVSG_KV_SPLIT && c->kv_layout != AVSG_KV_LATENT) return AVSG_ERR_INVALID_ARG;
+  if (c->bucket_width < 0 || c->bucket_width > (1 << 30)) return AVSG_ERR_INVALID_ARG;
   if (c->attn_split_rows != 0 &&
       (c->attn_split_rows < 32 || c->attn_split_rows % 32 != 0 ||
        c->attn_split_rows > (c->kv_layout == AVSG_KV_LATENT ? 512 : 256)))
@@ -511,6 +512,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   mp.nbins = ctx->d.nbins;
   mp.Hkv = c.n_kv_heads;
   mp.tpe = c.tokens_per_entry;
+  mp.W = c.bucket_width > 1 ? c.bucket_width : 1;
   mp.match_mode = ctx->match_mode;
   mp.merge_pow2 = ctx->d.merge_pow2;
   mp.direct_words = ctx->match_mode == AVSG_MATCH_HASH ? ctx->d.direct_words : 0;
@@ -770,6 +772,7 @@ static avsg_status enqueue_append(avsg_ctx* ctx, const uint16_t* new_kv, const i
   ap.lru = lru ? 1 : 0;
   ap.L = c.lifetime_L;
   ap.B = c.n_buckets;
+  ap.W = c.bucket_width > 1 ? c.bucket_width : 1;
   return launch_append(ap, ctx->d.units, ctx->stream) == hipSuccess ? AVSG_OK : AVSG_ERR_HIP;
 }
 

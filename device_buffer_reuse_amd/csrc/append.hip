@@ -35,7 +35,7 @@ __device__ inline uint64_t insert_key(int32_t id, int32_t lv, int s, const Appen
   if (id < 0) return (uint64_t)s;
   int64_t key = lv;
   if (p.lru) {
-    int64_t bucket = p.t - (int64_t)lv - 1;
+    int64_t bucket = (p.t - (int64_t)lv - 1) / p.W;
     bucket = bucket < 0 ? 0 : (bucket > p.B - 1 ? p.B - 1 : bucket);
     key = -bucket;
   }

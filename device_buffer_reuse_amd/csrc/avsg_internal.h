@@ -79,6 +79,7 @@ struct MatchReserveParams {
   int64_t t;
   int32_t S, N, T, k, ucap, table_cap, log_table_cap, ubits, policy, L, B, nbins;
   int32_t Hkv, tpe;       // KV heads per request, tokens per entry (context lengths)
+  int32_t W;              // steps per LRU bucket (>= 1)
   int32_t match_mode;     // avsg_match_mode
   int32_t merge_pow2;     // power of two >= S (sort size of the merge baseline)
   int32_t direct_words;   // > 0: match through N-bit membership words and rank bases
@@ -138,7 +139,8 @@ struct AppendParams {
   HostDir dir;                // null dir.top: flat host KV
   int64_t t;                  // the coming step (inserting only)
   int32_t Hkv, N, S, tpe, row_elems, tok_elems, dqk, dv, latent;
-  int32_t insert, lru, L, B;  // insert: make the entry resident as well
+  int32_t insert, lru, L, B, W;  // insert: make the entry resident as well; W: steps per
+                                 // LRU bucket
 };
 
 hipError_t launch_match_reserve(const MatchReserveParams& p, int units, size_t lds, hipStream_t s);

@@ -742,7 +742,8 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   // ---- 5. policy update and eviction bins (registers, branch-free):
   //         hits take L (or the stamp t); other occupied slots decrement
   //         (lifetime) and get bin 1 + lifetime, or bin 1 + (B - 1 - bucket)
-  //         (LRU, bucket = min(t - 1 - stamp, B - 1)); empty slots keep bin 0
+  //         (LRU, bucket = min((t - 1 - stamp) / W, B - 1)); empty slots keep
+  //         bin 0
   if (!lru) {
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) {
@@ -754,12 +755,16 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     }
   } else {
     const int32_t t32 = (int32_t)p.t;  // stamps are int32 and below t
+    const uint32_t W = (uint32_t)p.W;
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) {
       const int x = tok[q], l = lf[q];
       const bool hit = bin[q] == -1, occ = x >= 0;
-      const int64_t age = p.t - 1 - (int64_t)l;
-      const int bucket = age < (int64_t)(p.B - 1) ? (int)age : p.B - 1;
+      // steps since the last selection: in [0, 2^31) for a valid stamp (an
+      // empty or padding slot's value is not used)
+      uint32_t age = (uint32_t)t32 - 1u - (uint32_t)l;
+      if (W > 1) age /= W;
+      const int bucket = age < (uint32_t)(p.B - 1) ? (int)age : p.B - 1;
       lf[q] = hit ? t32 : l;
       bin[q] = (x == kInvalid || hit) ? bin[q] : (occ ? p.B - bucket : 0);
     }

@@ -72,7 +72,8 @@ typedef enum avsg_policy {
   AVSG_POLICY_LIFETIME = 0,
   /* Bucketed LRU (Spin summary, section 2B): lifetimes[] holds the step of
    * last selection; the bucket of a slot is min(t - stamp - 1, n_buckets - 1)
-   * and older buckets are evicted first. */
+   * with one-step buckets (bucket_width widens them) and older buckets are
+   * evicted first. */
   AVSG_POLICY_BUCKET_LRU = 1
 } avsg_policy;
 
@@ -97,6 +98,11 @@ typedef struct avsg_config {
    * of 32 in [32, 256] (split layout) or [32, 512] (latent layout).  Results
    * other than the attention output's rounding do not depend on it. */
   int32_t attn_split_rows;
+  /* steps per bucket of the bucketed LRU (Spin summary, section 2B gives
+   * recency buckets but not their width): the bucket of a slot is
+   * min(floor((t - stamp - 1) / W), n_buckets - 1).  0 or 1: one step per
+   * bucket; else W in [2, 2^30]. */
+  int32_t bucket_width;
 } avsg_config;
 
 /* Per-step outputs besides the attention result; all device pointers. */

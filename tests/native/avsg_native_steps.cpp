@@ -59,6 +59,7 @@ int main(int argc, char** argv) {
   cfg.n_buckets = 64;
   cfg.softmax_scale = 1.0f / 11.313708498984761f;
   cfg.attn_split_rows = 0;  // the library's choice
+  cfg.bucket_width = 1;
   CHECK(avsg_check_config(&cfg) == AVSG_OK);
   const int units = B * Hkv, row = 2 * D, Hq = Hkv * G;
 

@@ -180,3 +180,13 @@ def test_split_rows_out_of_range_are_refused():
     a = avsg.avsg_workspace_bytes(avsg.config_from_workload(tg.WORKLOADS[2], 0))
     b = avsg.avsg_workspace_bytes(avsg.config_from_workload(tg.WORKLOADS[2], 64))
     assert b > a
+
+
+def test_bucket_width_range_is_checked():
+    """avsg_config.bucket_width: 0 or 1 (one step per bucket) up to 2^30;
+    host-only check."""
+    avsg = _lib()
+    w = tg.WORKLOADS[4]
+    for W, want in ((0, avsg.OK), (1, avsg.OK), (7, avsg.OK), (1 << 30, avsg.OK),
+                    (-1, avsg.ERR_INVALID_ARG), ((1 << 30) + 1, avsg.ERR_INVALID_ARG)):
+        assert avsg.avsg_check_config(avsg.config_from_workload(w.replace(bucket_width=W))) == want, W

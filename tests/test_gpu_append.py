@@ -156,7 +156,9 @@ def test_append_full_size(cid):
 
 INSERT_CASES = dict(CASES, lifetime_pages=tg.WORKLOADS[4].replace(
     batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001, k=37, n_slots=60, steps=8,
-    policy="lifetime", lifetime_L=3))
+    policy="lifetime", lifetime_L=3), lru_wide_buckets=tg.WORKLOADS[4].replace(
+    batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001, k=37, n_slots=60, steps=10,
+    n_buckets=3, bucket_width=2))
 
 
 def _insert_and_compare(run, w, new, pos, what):

@@ -74,6 +74,18 @@ EDGE = {
     "mtp_lru_b7": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003,
                                           k=300, n_slots=700, policy="lru", n_buckets=7,
                                           steps=12),
+    # LRU buckets several steps wide: 3 steps (5 buckets, so ages past 14
+    # share the oldest), 2 steps with two-token reservations, and 4-step
+    # buckets of 16-token pages
+    "lru_w3": tg.WORKLOADS[4].replace(batch=1, n_kv_heads=2, n_q_heads=4, n_entries=700,
+                                      tokens_per_entry=1, k=50, n_slots=90, n_buckets=5,
+                                      bucket_width=3, steps=30),
+    "mtp_lru_w2": tg.WORKLOADS[3].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=5003,
+                                          k=300, n_slots=700, policy="lru", n_buckets=7,
+                                          bucket_width=2, steps=12),
+    "pages_lru_w4": tg.WORKLOADS[4].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1001,
+                                            k=37, n_slots=100, n_buckets=3, bucket_width=4,
+                                            steps=40),
 }
 
 
@@ -171,6 +183,27 @@ def test_parity_full_size(cid):
     try:
         for t in range(steps):
             run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=(t % 4 == 0 or t == steps - 1))
+        got = run.st.buf_kv.cpu().numpy().view(np.uint16)
+        occ = run.ob.slot_tok >= 0
+        assert np.array_equal(got[occ], run.ob.buf[occ])
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
+def test_parity_full_size_wide_buckets():
+    """The long-context workload at full size with LRU buckets 4 steps wide
+    (64 of them), 64 steps: state bit-exact every step, attention of sampled
+    units, buffer bytes at the end."""
+    w = tg.WORKLOADS[4].replace(bucket_width=4, steps=64)
+    say("[parity-full] %s buckets of 4 steps, units=%d steps=%d" % (w.name, w.units, w.steps))
+    sel = tg.selections(w)
+    rng = np.random.default_rng(44)
+    sample = sorted(rng.choice(w.units, size=4, replace=False).tolist())
+    run = Runner(w, attn_units=sample)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=(t % 16 == 0))
         got = run.st.buf_kv.cpu().numpy().view(np.uint16)
         occ = run.ob.slot_tok >= 0
         assert np.array_equal(got[occ], run.ob.buf[occ])
