@@ -19,7 +19,9 @@ struct avsg_ctx {
   int num_cus;
   int gather_grid;
   char* workspace;
-  int64_t t;
+  int64_t t;                     // the step of a caller-counted call (host_step)
+  bool host_step;                // the caller passes the step (avsg_step_static); else the
+                                 // counter lives in the workspace
   int32_t transfer_mode;         // avsg_transfer_mode
   int32_t match_mode;            // avsg_match_mode
   const int32_t* cap;            // device [units] buffer size of each unit, or null (S)
@@ -102,6 +104,7 @@ bool layout_for(const avsg_config& c, WsLayout* ws, Derived* d) {
   ws->fetch = off;       off = align256(off + (size_t)d->units * tk);
   ws->host_row = off;    off = align256(off + 4 * (size_t)d->units * tk);
   ws->err_word = off;    off = align256(off + 8);
+  ws->step = off;        off = align256(off + 8);
   ws->phase_clk = off;   off = align256(off + 3 * 8);
   ws->partials = off;
   const size_t part_bytes = c.kv_layout == AVSG_KV_LATENT
@@ -278,6 +281,7 @@ avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, s
   c->stream = (hipStream_t)stream;
   c->workspace = (char*)workspace;
   c->t = 0;
+  c->host_step = false;
   c->cap = nullptr;
   c->prof_events = nullptr;
   c->prof_max = c->prof_used = 0;
@@ -400,12 +404,23 @@ avsg_status avsg_destroy(avsg_ctx* ctx) {
   return AVSG_OK;
 }
 
-int64_t avsg_get_step(const avsg_ctx* ctx) { return ctx ? ctx->t : -1; }
+int64_t avsg_get_step(const avsg_ctx* ctx) {
+  if (!ctx) return -1;
+  int64_t t = -1;
+  if (hipMemcpyAsync(&t, ctx->workspace + ctx->ws.step, sizeof(t), hipMemcpyDeviceToHost,
+                     ctx->stream) != hipSuccess ||
+      hipStreamSynchronize(ctx->stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return t;
+}
 
 avsg_status avsg_set_step(avsg_ctx* ctx, int64_t t) {
   if (!ctx || t < 0 || t > INT32_MAX) return AVSG_ERR_INVALID_ARG;
-  ctx->t = t;
-  return AVSG_OK;
+  return launch_set_step((int64_t*)(ctx->workspace + ctx->ws.step), t, ctx->stream) == hipSuccess
+             ? AVSG_OK
+             : AVSG_ERR_HIP;
 }
 
 int32_t avsg_attn_splits(const avsg_ctx* ctx) { return ctx ? ctx->ws.nsplit : 0; }
@@ -422,9 +437,9 @@ avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes) {
   const int32_t life0 = ctx->cfg.policy == AVSG_POLICY_BUCKET_LRU ? -1 : 0;
   if (launch_fill_i32(slot_table, -1, n, ctx->stream) != hipSuccess ||
       launch_fill_i32(lifetimes, life0, n, ctx->stream) != hipSuccess ||
-      launch_fill_i32((int32_t*)(ctx->workspace + ctx->ws.err_word), 0, 2, ctx->stream) != hipSuccess)
+      launch_fill_i32((int32_t*)(ctx->workspace + ctx->ws.err_word), 0, 2, ctx->stream) != hipSuccess ||
+      launch_fill_i32((int32_t*)(ctx->workspace + ctx->ws.step), 0, 2, ctx->stream) != hipSuccess)
     return AVSG_ERR_HIP;
-  ctx->t = 0;
   return AVSG_OK;
 }
 
@@ -493,6 +508,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   mp.misses = misses;
   mp.fetch = (uint8_t*)(ws + ctx->ws.fetch);
   mp.err_word = (uint32_t*)(ws + ctx->ws.err_word);
+  mp.step = ctx->host_step ? nullptr : (int64_t*)(ws + ctx->ws.step);
   mp.t = ctx->t;
   mp.S = c.n_slots;
   mp.N = c.n_entries;
@@ -549,6 +565,7 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   ap.sel_len = sel_len;
   ap.sel = sel_idx;
   ap.ctx_len = ctx->ctx_len;
+  ap.step = ctx->host_step ? nullptr : (int64_t*)(ws + ctx->ws.step);
   ap.fetch = fused ? (const uint8_t*)(ws + ctx->ws.fetch) : nullptr;
   ap.host_row = ctx->dir.top ? (const int32_t*)(ws + ctx->ws.host_row) : nullptr;
   ap.host_kv = (const uint16_t*)host_dev;
@@ -584,7 +601,6 @@ static avsg_status step_impl(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
   }
   prof_mark(ctx, 4);
   if (ctx->prof_events && ctx->prof_used < ctx->prof_max) ctx->prof_used += 1;
-  ctx->t += 1;
   return AVSG_OK;
 }
 
@@ -624,6 +640,7 @@ avsg_status avsg_step_static(const avsg_config* cfg, int64_t t, void* stream,
   c.stream = (hipStream_t)stream;
   c.workspace = (char*)di.scratch_ptr;
   c.t = t;
+  c.host_step = true;
   c.transfer_mode = AVSG_TRANSFER_FUSED;
   c.match_mode = AVSG_MATCH_HASH;
   // the step's words that accumulate (the error bits) start at zero: the
@@ -658,8 +675,11 @@ static avsg_status check_state(avsg_ctx* ctx, const int32_t* slot_table, const i
   uint32_t* word = (uint32_t*)(ctx->workspace + ctx->ws.err_word) + 1;
   if (launch_fill_i32((int32_t*)word, 0, 1, ctx->stream) != hipSuccess) return AVSG_ERR_HIP;
   const avsg_config& c = ctx->cfg;
+  // the step the stamps must precede (a syncing call: read from the workspace)
+  const int64_t t = lifetimes ? avsg_get_step(ctx) : 0;
+  if (t < 0) return AVSG_ERR_HIP;
   if (launch_validate(slot_table, lifetimes, ctx->d.units, c.n_slots, c.n_entries, c.policy,
-                      c.lifetime_L, ctx->t, word, ctx->stream) != hipSuccess)
+                      c.lifetime_L, t, word, ctx->stream) != hipSuccess)
     return AVSG_ERR_HIP;
   uint32_t bits = 0;
   if (hipMemcpyAsync(&bits, word, 4, hipMemcpyDeviceToHost, ctx->stream) != hipSuccess ||
@@ -742,9 +762,6 @@ static avsg_status enqueue_append(avsg_ctx* ctx, const uint16_t* new_kv, const i
     return AVSG_ERR_INVALID_ARG;
   const avsg_config& c = ctx->cfg;
   const bool lru = c.policy == AVSG_POLICY_BUCKET_LRU;
-  // a bucketed-LRU stamp of the step before the coming one needs a step
-  // before it; the counter is the host's, so this is checked here
-  if (insert && lru && ctx->t < 1) return AVSG_ERR_INVALID_ARG;
   const void* host_dev = nullptr;
   avsg_status st = device_view_of_pinned(host_kv, &host_dev);
   if (st != AVSG_OK) return st;
@@ -758,7 +775,7 @@ static avsg_status enqueue_append(avsg_ctx* ctx, const uint16_t* new_kv, const i
   ap.cap = insert ? ctx->cap : nullptr;
   ap.err_word = (uint32_t*)(ctx->workspace + ctx->ws.err_word);
   ap.dir = ctx->dir;
-  ap.t = ctx->t;
+  ap.step = (const int64_t*)(ctx->workspace + ctx->ws.step);
   ap.Hkv = c.n_kv_heads;
   ap.N = c.n_entries;
   ap.S = c.n_slots;
@@ -815,6 +832,13 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
+}
+
+__global__ void set_step_kernel(int64_t* step, int64_t t) { step[0] = t; }
+
+hipError_t launch_set_step(int64_t* step, int64_t t, hipStream_t s) {
+  hipLaunchKernelGGL(set_step_kernel, dim3(1), dim3(1), 0, s, step, t);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {

@@ -31,11 +31,12 @@ constexpr int kMaxHolders = 32;  // slots recorded per entry (1 in a valid state
 // Eviction key of slot s for an insertion before step t, smaller = evicted
 // first: (occupied, lifetime or minus bucket, slot index) packed into 64 bits
 // (the key is biased by 256: lifetimes are at most 126, buckets at most 127).
-__device__ inline uint64_t insert_key(int32_t id, int32_t lv, int s, const AppendParams& p) {
+__device__ inline uint64_t insert_key(int32_t id, int32_t lv, int s, int64_t t,
+                                      const AppendParams& p) {
   if (id < 0) return (uint64_t)s;
   int64_t key = lv;
   if (p.lru) {
-    int64_t bucket = (p.t - (int64_t)lv - 1) / p.W;
+    int64_t bucket = (t - (int64_t)lv - 1) / p.W;
     bucket = bucket < 0 ? 0 : (bucket > p.B - 1 ? p.B - 1 : bucket);
     key = -bucket;
   }
@@ -59,6 +60,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
   }
   const int e = (int)(pos / p.tpe);
   const int r = (int)(pos - (int64_t)e * p.tpe);
+  // the coming step (inserting): the context's counter in the workspace
+  const int64_t t = p.insert ? p.step[0] : 0;
   if (tid == 0) {
     sCount = 0;
     sBad = 0;
@@ -80,6 +83,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
       cap = p.cap[u];
       if (cap < 1 || cap > p.S) hrow = -1;
     }
+    // a bucketed-LRU stamp of the step before the coming one needs a step
+    // before it: an insertion before the first step is a range error
+    if (p.insert && p.lru && t < 1) hrow = -1;
     sCap = cap;
     sHostRow = hrow;
   }
@@ -107,9 +113,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
       int32_t lv = 0;
       if (id >= 0) {
         lv = lf[s];
-        if (lv < 0 || (p.lru ? (int64_t)lv >= p.t : lv > p.L)) bad = 1;
+        if (lv < 0 || (p.lru ? (int64_t)lv >= t : lv > p.L)) bad = 1;
       }
-      const uint64_t key = insert_key(id, lv, s, p);
+      const uint64_t key = insert_key(id, lv, s, t, p);
       best = key < best ? key : best;
     }
   }
@@ -161,11 +167,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
     }
     if (tid == 0) {
       st[v] = e;
-      lf[v] = p.lru ? (int32_t)(p.t - 1) : p.L;
+      lf[v] = p.lru ? (int32_t)(t - 1) : p.L;
     }
     return;
   }
-  if (p.insert && tid == 0) lf[sHolder[0]] = p.lru ? (int32_t)(p.t - 1) : p.L;
+  if (p.insert && tid == 0) lf[sHolder[0]] = p.lru ? (int32_t)(t - 1) : p.L;
   if (tid >= kp + vp) return;
   const int64_t off = tid < kp ? kbase + 8 * tid : vbase + 8 * (tid - kp);
   const u32x4 v = *reinterpret_cast<const u32x4*>(tok + 8 * tid);

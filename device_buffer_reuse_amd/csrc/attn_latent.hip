@@ -139,6 +139,10 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnParams p) {
   constexpr int kInstr = (kTileInstr + NW - 1) / NW;     // copies per chunk, first waves
   constexpr int kFull = kTileInstr - (kInstr - 1) * NW;  // waves issuing kInstr copies
 
+  // the context's step counter advances once per step, here: the match
+  // kernel that read it has finished (a non-returning atomic: no wait)
+  if (p.step && p.token == 0 && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_add(p.step, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int nsplit = p.nsplit;
   // workgroups are dealt to the 8 XCDs in turn; when the grid divides by 8,
   // XCD x takes the x-th eighth of the (request, split) range, so a

@@ -150,6 +150,10 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
   __shared__ int32_t sGathered;          // gather-first: wave 1 has stored every missed entry
   __shared__ int32_t sNHost;             // gather-first: entries to fetch
 
+  // the context's step counter advances once per step, here: the match
+  // kernel that read it has finished (a non-returning atomic: no wait)
+  if (p.step && p.token == 0 && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_add(p.step, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int nsplit = p.nsplit;
   // workgroups are dealt to the 8 XCDs in turn (workgroup i on XCD i mod 8);
   // when the grid divides by 8, XCD x takes the x-th eighth of the (unit,

@@ -17,7 +17,8 @@ constexpr int kGatherThreads = 256;
 
 // Layout of the caller's workspace (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t unit_status, miss_count, misses, fetch, host_row, err_word, phase_clk, partials, total;
+  size_t unit_status, miss_count, misses, fetch, host_row, err_word, step, phase_clk, partials,
+      total;
   int32_t ucap;       // union capacity per unit = min(T*k, S)
   int32_t table_cap;  // hash table cells, power of two >= 2*ucap
   int32_t nsplit;     // attention splits per (unit, token)
@@ -76,6 +77,8 @@ struct MatchReserveParams {
   int2* misses;           // workspace [units][ucap]: (slot, id) in miss order
   uint8_t* fetch;         // workspace [units][T][k]: row to transfer with this token
   uint32_t* err_word;
+  // the decode step: the context's counter in the workspace; null: the value t
+  const int64_t* step;
   int64_t t;
   int32_t S, N, T, k, ucap, table_cap, log_table_cap, ubits, policy, L, B, nbins;
   int32_t Hkv, tpe;       // KV heads per request, tokens per entry (context lengths)
@@ -108,6 +111,8 @@ struct AttnParams {
   const int32_t* sel_len;     // [units][T] entries in use of each list, or null: k
   const int32_t* sel;         // [units][T][k] selected ids
   const int32_t* ctx_len;     // [batch] context length in tokens, or null: whole entries
+  int64_t* step;              // the context's step counter: advanced once by the step's first
+                              // launch (token 0, workgroup 0); null: not counted here
   const uint8_t* fetch;       // [units][T][k] or null: rows to read from host and store
   const int32_t* host_row;    // [units][T][k] pool row of each fetched entry, or null: flat
                               // host KV, row u * N + sel
@@ -137,7 +142,7 @@ struct AppendParams {
   const int32_t* cap;         // [units] slots in use, or null: all S (inserting only)
   uint32_t* err_word;
   HostDir dir;                // null dir.top: flat host KV
-  int64_t t;                  // the coming step (inserting only)
+  const int64_t* step;        // the coming step, in the workspace (inserting only)
   int32_t Hkv, N, S, tpe, row_elems, tok_elems, dqk, dv, latent;
   int32_t insert, lru, L, B, W;  // insert: make the entry resident as well; W: steps per
                                  // LRU bucket
@@ -153,6 +158,7 @@ hipError_t launch_append(const AppendParams& p, int units, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_validate(const int32_t* slot_table, const int32_t* lifetimes, int units, int S,
                            int N, int policy, int L, int64_t t, uint32_t* err, hipStream_t s);
+hipError_t launch_set_step(int64_t* step, int64_t t, hipStream_t s);
 hipError_t match_reserve_set_lds(size_t lds);
 
 }  // namespace avsg

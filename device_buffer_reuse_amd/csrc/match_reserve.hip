@@ -183,6 +183,10 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
   const int u = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S, N = p.N, T = p.T, k = p.k, ucap = p.ucap, C = p.table_cap;
+  // the decode step: the context's counter in the workspace (the step's
+  // first attention launch advances it once this kernel has finished), or
+  // the caller's value
+  const int64_t step_t = p.step ? p.step[0] : p.t;
   // tks: stride of a unit's lists.  With a length array token j uses the
   // first sel_len[u][j] entries of its list (ka for token 0, kb for token 1;
   // a length outside [1, k] is a range error); tk: one token, the entries
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       } else if (x >= 0) {
         const int32_t l = lf[q];
         if (!lru && (l < 0 || l > p.L)) bad = 1;
-        if (lru && (l < 0 || (int64_t)l >= p.t)) bad = 1;
+        if (lru && (l < 0 || (int64_t)l >= step_t)) bad = 1;
       }
     }
     const int P2 = p.merge_pow2;
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         const int32_t x = tok[q], l = lf[q];
         const bool valid = x != kInvalid;
         const bool resident = x >= 0 && x < N;
-        const bool bad_l = lru ? (l < 0 || (int64_t)l >= p.t) : (l < 0 || l > p.L);
+        const bool bad_l = lru ? (l < 0 || (int64_t)l >= step_t) : (l < 0 || l > p.L);
         bad |= (valid && (x < -1 || x >= N)) | (resident && bad_l);
         bin[q] = valid ? 0 : kInvalid;
         const int wi = resident ? (x >> 5) : 0;
@@ -643,7 +647,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         const int32_t x = tok[q], l = lf[q];
         const bool valid = x != kInvalid;
         const bool resident = x >= 0 && x < N;
-        const bool bad_l = lru ? (l < 0 || (int64_t)l >= p.t) : (l < 0 || l > p.L);
+        const bool bad_l = lru ? (l < 0 || (int64_t)l >= step_t) : (l < 0 || l > p.L);
         bad |= (valid && (x < -1 || x >= N)) | (resident && bad_l);
         bin[q] = valid ? 0 : kInvalid;
         hit_i[q] = -1;
@@ -754,7 +758,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       bin[q] = (x == kInvalid || hit) ? bin[q] : (occ ? 1 + dec : 0);
     }
   } else {
-    const int32_t t32 = (int32_t)p.t;  // stamps are int32 and below t
+    const int32_t t32 = (int32_t)step_t;  // stamps are int32 and below t
     const uint32_t W = (uint32_t)p.W;
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) {
@@ -996,7 +1000,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
           const int s = s0 + q * 64 + lane;
           if (tok[q] >= 0) ++ev;
           tok[q] = idv[qq];
-          lf[q] = lru ? (int32_t)p.t : p.L;
+          lf[q] = lru ? (int32_t)step_t : p.L;
           changed[q] = true;
           sUslot[mi[qq]] = s | kMissFlag;
           if (dir) sURow[mi[qq]] = rowv[qq];

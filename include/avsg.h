@@ -130,7 +130,9 @@ size_t avsg_workspace_bytes(const avsg_config* cfg);
  * (NULL = the null stream).  `workspace` is device memory of at least
  * avsg_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the caller and
  * kept alive and untouched until avsg_destroy.  Initialising it is enqueued
- * on the stream.  The step counter starts at 0. */
+ * on the stream.  The workspace holds the step counter (starting at 0), so a
+ * step needs no host state: steps may be captured in a HIP graph and
+ * replayed. */
 avsg_status avsg_create(const avsg_config* cfg, void* stream, void* workspace, size_t ws_bytes,
                         avsg_ctx** out);
 
@@ -145,7 +147,8 @@ avsg_status avsg_destroy(avsg_ctx* ctx);
  * Device pointers; enqueued on the stream. */
 avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes);
 
-/* One decode step t (the context's counter; it then advances by one).
+/* One decode step t (the context's counter in the workspace; the step's
+ * kernels advance it by one on the GPU).
  *   sel_idx    device, int32 [batch][n_kv_heads][T][k]: each token's selected
  *              entry ids, strictly ascending, in [0, N).          read only
  *   q          device, bf16 [batch][T][n_q_heads][head_dim_qk]     read only
@@ -338,13 +341,13 @@ avsg_status avsg_append(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* po
  *   slot_table device, int32 [units][S].                            in/out
  *   lifetimes  device, int32 [units][S].                            in/out
  *   the rest   as avsg_append.
- * Per unit, a bad position, a capacity outside [1, S] or an entry without a
- * host row is AVSG_ERR_RANGE, and slots in use that are not a valid state
- * (an id outside [-1, N), a lifetime outside [0, L] or stamp outside [0, t)
- * on an occupied slot, the entry in two slots) are AVSG_ERR_STATE: that unit
- * writes nothing (avsg_last_error reports it).  Returns AVSG_ERR_INVALID_ARG
- * for a null lifetimes or, under bucketed LRU, before the first step (t = 0:
- * no stamp in [0, t) exists), else as avsg_append. */
+ * Per unit, a bad position, a capacity outside [1, S], an entry without a
+ * host row or, under bucketed LRU, a call before the first step (t = 0: no
+ * stamp t - 1 exists) is AVSG_ERR_RANGE, and slots in use that are not a
+ * valid state (an id outside [-1, N), a lifetime outside [0, L] or stamp
+ * outside [0, t) on an occupied slot, the entry in two slots) are
+ * AVSG_ERR_STATE: that unit writes nothing (avsg_last_error reports it).
+ * Returns AVSG_ERR_INVALID_ARG for a null lifetimes, else as avsg_append. */
 avsg_status avsg_append_insert(avsg_ctx* ctx, const uint16_t* new_kv, const int32_t* pos,
                                uint16_t* host_kv, uint16_t* buf_kv, int32_t* slot_table,
                                int32_t* lifetimes);
@@ -367,7 +370,11 @@ avsg_status avsg_validate_state(avsg_ctx* ctx, const int32_t* slot_table, const 
  * Returns AVSG_OK or AVSG_ERR_STATE. */
 avsg_status avsg_rebuild_index(avsg_ctx* ctx, const int32_t* slot_table);
 
-/* Step counter (decode step of the next avsg_step), for checkpoint/resume. */
+/* Step counter (decode step of the next avsg_step), for checkpoint/resume.
+ * The counter lives in the workspace and every step advances it on the GPU,
+ * so steps captured in a HIP graph and replayed keep counting.
+ * avsg_get_step syncs the stream and returns it (-1 on error); avsg_set_step
+ * sets it, stream-ordered, t in [0, 2^31). */
 int64_t avsg_get_step(const avsg_ctx* ctx);
 avsg_status avsg_set_step(avsg_ctx* ctx, int64_t t);
 

@@ -36,8 +36,9 @@ taken follows the step's own eviction order without ageing anyone:
     row with the token already written, and the fresh keep-state;
   * a unit whose slots in use are not a valid state (an id outside [-1, N),
     a lifetime outside [0, L] or stamp outside [0, t), the entry in two slots)
-    writes nothing and reports a state error; a bad position or capacity, or
-    an entry without a host row, is a range error of the unit.
+    writes nothing and reports a state error; a bad position or capacity, an
+    entry without a host row, or (bucketed LRU) an insertion before the
+    first step, when no stamp t - 1 exists, is a range error of the unit.
 """
 from __future__ import annotations
 
@@ -104,7 +105,6 @@ def append_insert(w, host_kv: np.ndarray, new_kv: np.ndarray, pos: np.ndarray,
     d_qk, d_v = w.head_dim_qk, w.head_dim_v
     lru = w.policy == "lru"
     L, B, W = w.lifetime_L, w.n_buckets, w.bucket_width
-    assert not (lru and t < 1), "a bucketed-LRU stamp needs a step before it"
     fresh = t - 1 if lru else L
     empty_life = -1 if lru else 0
     status = np.zeros(w.units, dtype=np.int32)
@@ -112,7 +112,7 @@ def append_insert(w, host_kv: np.ndarray, new_kv: np.ndarray, pos: np.ndarray,
         b = u // w.n_kv_heads
         p = int(pos[b])
         cap = S if caps is None else int(caps[u])
-        if p < 0 or p >= N * P or not 1 <= cap <= S:
+        if p < 0 or p >= N * P or not 1 <= cap <= S or (lru and t < 1):
             status[u] = ERR_RANGE
             continue
         e, r = divmod(p, P)

@@ -276,6 +276,18 @@ def test_insert_errors_write_nothing(ids, life, caps, pos_entry, status):
         assert np.array_equal(a, b)
 
 
+def test_insert_before_the_first_lru_step_is_a_range_error():
+    # no stamp t - 1 exists at t = 0: every unit writes nothing
+    w, host, rng = _one_unit(policy="lru", S=4)
+    slot_tok, lf, buf = _state(w, host, [-1] * 4, [-1] * 4)
+    st, _, (h0, s0, l0, b0) = _insert(w, host, rng, slot_tok, lf, buf, e=3, t=0)
+    assert st == oapp.ERR_RANGE
+    for a, b in zip((host, slot_tok, lf, buf), (h0, s0, l0, b0)):
+        assert np.array_equal(a, b)
+    st, _, _ = _insert(w, host, rng, slot_tok, lf, buf, e=3, t=1)
+    assert st == 0 and slot_tok[0].tolist() == [3, -1, -1, -1] and lf[0].tolist() == [0, -1, -1, -1]
+
+
 def test_insert_of_an_unmapped_entry_is_a_range_error():
     w, host, rng = _one_unit()
     slot_tok, lf, buf = _state(w, host, [-1] * 5, [0] * 5)
