@@ -479,8 +479,9 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_split_kernel(AttnParams p) 
     // rows of the tile at or past rv1 (when the context ends inside the
     // split) may hold anything, NaN included: their V halves are zeroed, so
     // that their zero probabilities give exact zeros in the MFMA (0 * NaN
-    // would not); their masked scores never read K.  After write_back's LDS
-    // reads, before the V reads below.
+    // would not); their scores, whatever K gives, are replaced by -inf
+    // before the softmax.  After write_back's LDS reads, before the V reads
+    // below.
     const int z0 = rv1 - (r0 + t * kChunk);
     if (rv1 < r1 && z0 < kChunk) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
