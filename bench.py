@@ -741,6 +741,7 @@ def config_of(w, a):
             "tokens_per_entry": w.tokens_per_entry,
             "context_tokens": w.n_entries * w.tokens_per_entry, "k": w.k, "slots": w.n_slots,
             "policy": w.policy, "lifetime_L": w.lifetime_L, "buckets": w.n_buckets,
+            "bucket_width_steps": w.bucket_width,
             "trace": ("natural: %.0f%% overlap + Zipf(%.1f) tail" % (100 * w.overlap, w.zipf_s)
                       if a.trace == "natural" else a.trace),
             "transfer": ["fused", "balanced", "per-unit", "fused-gather-first"][a.transfer],
