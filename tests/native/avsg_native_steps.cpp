@@ -1,7 +1,11 @@
 // A native caller of libavsg: plain C ABI, HIP runtime memory, no Python or
-// torch.  Runs a few decode steps of a small workload whose inputs follow
-// simple closed formulas (so that a test can rebuild them exactly) and writes
-// the slot table, lifetimes, hit counts and outputs of every step to a file.
+// torch.  Runs a few decode steps of a small workload (bucketed LRU) whose
+// inputs follow simple closed formulas (so that a test can rebuild them
+// exactly) and writes the slot table, stamps, hit counts and outputs of every
+// step to a file.  The first steps run directly; one step is then captured
+// in a HIP graph and the graph is replayed for the remaining steps, with the
+// next step's inputs copied into the same device buffers before each replay
+// (the step counter lives in the workspace, so the replays count on).
 //
 //   avsg_native_steps <out_file>
 //
@@ -54,9 +58,9 @@ int main(int argc, char** argv) {
   cfg.tokens_per_entry = 1;
   cfg.k = k;
   cfg.n_slots = S;
-  cfg.policy = AVSG_POLICY_LIFETIME;
+  cfg.policy = AVSG_POLICY_BUCKET_LRU;
   cfg.lifetime_L = 3;
-  cfg.n_buckets = 64;
+  cfg.n_buckets = 8;
   cfg.softmax_scale = 1.0f / 11.313708498984761f;
   cfg.attn_split_rows = 0;  // the library's choice
   cfg.bucket_width = 1;
@@ -87,8 +91,10 @@ int main(int argc, char** argv) {
       for (int i = 0; i < row; ++i)
         hk[((size_t)u * N + e) * row + i] = bf16_of(((u * 7 + e * 3 + i) % 17 - 8) / 8.0f);
 
+  hipStream_t stream = nullptr;
+  CHECK(hipStreamCreate(&stream) == hipSuccess);
   avsg_ctx* ctx = nullptr;
-  CHECK(avsg_create(&cfg, nullptr, ws, ws_bytes, &ctx) == AVSG_OK);
+  CHECK(avsg_create(&cfg, stream, ws, ws_bytes, &ctx) == AVSG_OK);
   CHECK(avsg_reset(ctx, (int32_t*)slots, (int32_t*)life) == AVSG_OK);
   avsg_hit_stats hs = {(uint8_t*)hit, (int32_t*)ss, (int32_t*)nh, (int32_t*)nm, (int32_t*)ne,
                        (int32_t*)us};
@@ -97,6 +103,9 @@ int main(int argc, char** argv) {
   std::vector<int32_t> sel(units * k), st(units * S), lf(units * S), cnt(units);
   std::vector<uint16_t> q((size_t)B * Hq * D);
   std::vector<float> out((size_t)B * Hq * D);
+  const int eager_steps = 3;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
   for (int t = 0; t < steps; ++t) {
     for (int u = 0; u < units; ++u) {
       for (int j = 0; j < k; ++j) sel[u * k + j] = (j * 3 + t * 5 + u) % N;
@@ -106,11 +115,27 @@ int main(int argc, char** argv) {
       for (int h = 0; h < Hq; ++h)
         for (int i = 0; i < D; ++i)
           q[((size_t)b * Hq + h) * D + i] = bf16_of(((b * 5 + h * 11 + i + t) % 13 - 6) / 8.0f);
-    CHECK(hipMemcpy(sel_d, sel.data(), sel.size() * 4, hipMemcpyHostToDevice) == hipSuccess);
-    CHECK(hipMemcpy(q_d, q.data(), q.size() * 2, hipMemcpyHostToDevice) == hipSuccess);
-    CHECK(avsg_step(ctx, (int32_t*)sel_d, (uint16_t*)q_d, hk, (uint16_t*)buf, (int32_t*)slots,
-                    (int32_t*)life, (float*)out_d, &hs) == AVSG_OK);
-    CHECK(hipDeviceSynchronize() == hipSuccess);
+    CHECK(hipMemcpyAsync(sel_d, sel.data(), sel.size() * 4, hipMemcpyHostToDevice, stream) ==
+          hipSuccess);
+    CHECK(hipMemcpyAsync(q_d, q.data(), q.size() * 2, hipMemcpyHostToDevice, stream) ==
+          hipSuccess);
+    CHECK(hipStreamSynchronize(stream) == hipSuccess);
+    if (t < eager_steps) {
+      CHECK(avsg_step(ctx, (int32_t*)sel_d, (uint16_t*)q_d, hk, (uint16_t*)buf, (int32_t*)slots,
+                      (int32_t*)life, (float*)out_d, &hs) == AVSG_OK);
+    } else {
+      if (!exec) {  // recorded once, not run while recording
+        CHECK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal) == hipSuccess);
+        CHECK(avsg_step(ctx, (int32_t*)sel_d, (uint16_t*)q_d, hk, (uint16_t*)buf,
+                        (int32_t*)slots, (int32_t*)life, (float*)out_d, &hs) == AVSG_OK);
+        CHECK(hipStreamEndCapture(stream, &graph) == hipSuccess);
+        CHECK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess);
+        CHECK(avsg_get_step(ctx) == eager_steps);
+      }
+      CHECK(hipGraphLaunch(exec, stream) == hipSuccess);
+    }
+    CHECK(hipStreamSynchronize(stream) == hipSuccess);
+    CHECK(avsg_get_step(ctx) == t + 1);
     CHECK(hipMemcpy(st.data(), slots, st.size() * 4, hipMemcpyDeviceToHost) == hipSuccess);
     CHECK(hipMemcpy(lf.data(), life, lf.size() * 4, hipMemcpyDeviceToHost) == hipSuccess);
     CHECK(hipMemcpy(cnt.data(), nh, cnt.size() * 4, hipMemcpyDeviceToHost) == hipSuccess);
@@ -122,10 +147,14 @@ int main(int argc, char** argv) {
   }
   fclose(f);
   CHECK(avsg_last_error(ctx) == AVSG_OK);
+  CHECK(hipGraphExecDestroy(exec) == hipSuccess);
+  CHECK(hipGraphDestroy(graph) == hipSuccess);
   CHECK(avsg_destroy(ctx) == AVSG_OK);
+  CHECK(hipStreamDestroy(stream) == hipSuccess);
   CHECK(avsg_host_free(host) == AVSG_OK);
   for (void* p : {ws, buf, slots, life, sel_d, q_d, out_d, hit, ss, nh, nm, ne, us})
     CHECK(hipFree(p) == hipSuccess);
-  printf("native caller: %d steps\n", steps);
+  printf("native caller: %d steps, %d of them replayed from a graph\n", steps,
+         steps - eager_steps);
   return 0;
 }

@@ -1,5 +1,7 @@
 """libavsg driven by a native program through its C ABI alone (HIP runtime
-memory, plain pointers, no Python binding or torch), against the oracle.
+memory, plain pointers, HIP graph calls, no Python binding or torch), against
+the oracle: bucketed LRU, three direct steps, then one step captured in a
+graph and replayed for the rest.
 
 tests/native/avsg_native_steps.cpp builds its inputs from closed formulas;
 this test rebuilds the same inputs, runs the oracle on them and compares the
@@ -22,7 +24,7 @@ pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 BIN = os.path.join(HERE, "native", "avsg_native_steps")
 W = tg.WORKLOADS[2].replace(batch=2, n_kv_heads=2, n_q_heads=8, n_entries=1000, k=100,
-                            n_slots=300, lifetime_L=3, steps=6)
+                            n_slots=300, lifetime_L=3, policy="lru", n_buckets=8, steps=6)
 
 
 def _bf16(x):
