@@ -52,7 +52,7 @@ typedef enum avsg_status {
   AVSG_ERR_UNSUPPORTED = 4,  /* config valid but outside the library's kernels */
   /* data errors, found on the GPU and reported by avsg_last_error */
   AVSG_ERR_UNSORTED = 16,    /* a token's selection is not strictly ascending */
-  AVSG_ERR_RANGE = 17,       /* a selected id is outside [0, n_entries) */
+  AVSG_ERR_RANGE = 17,       /* an id, length, size, position or context length out of range */
   AVSG_ERR_CAPACITY = 18,    /* the union of an iteration's selections exceeds n_slots */
   AVSG_ERR_STATE = 19        /* slot_table / lifetimes are not a valid buffer state */
 } avsg_status;
@@ -148,9 +148,13 @@ avsg_status avsg_destroy(avsg_ctx* ctx);
 avsg_status avsg_reset(avsg_ctx* ctx, int32_t* slot_table, int32_t* lifetimes);
 
 /* One decode step t (the context's counter in the workspace; the step's
- * kernels advance it by one on the GPU).
+ * kernels advance it by one on the GPU).  The context's settings apply:
+ * buffer sizes (avsg_set_capacity), context lengths
+ * (avsg_set_context_lengths), the host directory (avsg_set_host_directory),
+ * the transfer and match modes.
  *   sel_idx    device, int32 [batch][n_kv_heads][T][k]: each token's selected
- *              entry ids, strictly ascending, in [0, N).          read only
+ *              entry ids, strictly ascending, in [0, N) (and inside the
+ *              request's context when context lengths are set).  read only
  *   q          device, bf16 [batch][T][n_q_heads][head_dim_qk]     read only
  *   host_kv    host, pinned, bf16 [units][N][row]: the full KV cache, row as
  *              given by kv_layout.                                  read only
@@ -203,8 +207,10 @@ avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
  *              emptied buffer, then +1 per call), in [0, 2^31)
  *   stream     hipStream_t to enqueue on (NULL = the null stream), of the
  *              current device
- *   the rest   exactly as avsg_step, with the fused transfer and the hash
- *              match; hit_stats->unit_status is required (it is where data
+ *   the rest   exactly as avsg_step, with the fused transfer, the hash
+ *              match, all S slots, whole entries and a flat host KV (the
+ *              context settings do not exist here); hit_stats->unit_status
+ *              is required (it is where data
  *              errors are reported, per unit: there is no context to hold an
  *              error word for avsg_last_error).
  * Returns AVSG_ERR_UNSUPPORTED if the configuration's scratch exceeds
