@@ -210,9 +210,9 @@ avsg_status avsg_step_varlen(avsg_ctx* ctx, const int32_t* sel_idx, const int32_
  *   the rest   exactly as avsg_step, with the fused transfer, the hash
  *              match, all S slots, whole entries and a flat host KV (the
  *              context settings do not exist here); hit_stats->unit_status
- *              is required (it is where data
- *              errors are reported, per unit: there is no context to hold an
- *              error word for avsg_last_error).
+ *              is required (it is where data errors are reported, per unit:
+ *              there is no context to hold an error word for
+ *              avsg_last_error).
  * Returns AVSG_ERR_UNSUPPORTED if the configuration's scratch exceeds
  * AVSG_STATIC_SCRATCH_BYTES (see avsg_workspace_bytes) and otherwise the
  * codes of avsg_check_config and avsg_step.  Results are bit-identical to
