@@ -554,7 +554,11 @@ def extras(b, a):
     # its own selections and queries) and replayed per pass, after the reset
     # and the fill steps run eagerly; the step counter lives in the
     # workspace, so the replayed steps stamp the right step numbers
-    out["graph_replay"] = graph_replay(b, a, t0, K)
+    try:
+        out["graph_replay"] = graph_replay(b, a, t0, K)
+    except Exception as e:  # reported in the line; the other figures stand
+        out["graph_replay"] = {"error": "%s: %s" % (type(e).__name__, e)}
+        torch.cuda.synchronize()
     # the host KV reached through the two-level directory (256-entry
     # segments in pinned host memory, the top level in HBM), over the same
     # rows: entry e of unit u at pool row u * N + e
