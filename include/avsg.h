@@ -379,8 +379,9 @@ avsg_status avsg_rebuild_index(avsg_ctx* ctx, const int32_t* slot_table);
 /* Step counter (decode step of the next avsg_step), for checkpoint/resume.
  * The counter lives in the workspace and every step advances it on the GPU,
  * so steps captured in a HIP graph and replayed keep counting.
- * avsg_get_step syncs the stream and returns it (-1 on error); avsg_set_step
- * sets it, stream-ordered, t in [0, 2^31). */
+ * avsg_get_step syncs the stream and returns it (-1 on error), so it cannot
+ * be called while the stream is being captured; avsg_set_step sets it,
+ * stream-ordered (capturable), t in [0, 2^31). */
 int64_t avsg_get_step(const avsg_ctx* ctx);
 avsg_status avsg_set_step(avsg_ctx* ctx, int64_t t);
 
