@@ -73,6 +73,8 @@ def parse(argv=None):
                          "dual-pointer matching (batch workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--buffer-sweep", default="",
+                    help="comma-separated slot counts: the headline trace at each buffer size")
     return ap.parse_args(argv)
 
 
@@ -98,6 +100,17 @@ class Bench:
     def close(self):
         self.ctx.close()
         self.host.free()
+
+    def resize(self, n_slots):
+        """A new context and device state with n_slots slots per unit, over
+        the same host KV and queries (the selection trace does not depend on
+        the buffer size)."""
+        self.ctx.close()
+        self.w = self.w.replace(n_slots=n_slots)
+        self.cfg = self.avsg.config_from_workload(self.w)
+        self.ctx = self.avsg.Context(self.cfg)
+        self.st = self.avsg.State(self.cfg)
+        self.hs = self.st.stats.struct()
 
     def load_trace(self, mode, steps):
         self.len_np = self.len_dev = None
@@ -376,6 +389,23 @@ def brief(r):
     keep = ("ms_per_step", "steps_per_s", "entries_per_s", "hit_rate", "host_bytes_per_step",
             "step_hbm_frac", "step_host_link_frac", "roofline", "kernels")
     return {k: r[k] for k in keep}
+
+
+def buffer_sweep(b, a, sizes):
+    """The headline workload's natural trace with the buffer at each size
+    (slots per unit): hit rate, host bytes and time per step.  Each size gets
+    its own fill phase before the timed window."""
+    out = {}
+    for S in sizes:
+        b.resize(S)
+        r = measure(b, "natural", a.fill + a.warmup, a.steps, a.warmup_passes, a.passes, True)
+        out[str(S)] = {"hbm_buffer_bytes": b.w.units * S * b.w.row_bytes,
+                       "ms_per_step": r["ms_per_step"], "hit_rate": r["hit_rate"],
+                       "host_bytes_per_step": r["host_bytes_per_step"],
+                       "entries_per_s": r["entries_per_s"],
+                       "attention_us": r["kernels"]["attention"]["us"],
+                       "match_reserve_us": r["kernels"]["match_reserve"]["us"]}
+    return out
 
 
 def ablations(a):
@@ -804,6 +834,8 @@ def main(argv=None):
             line["all_hit"] = brief(rest["allhit"])
             line["all_miss"] = brief(rest["allmiss"])
         line.update(extras(b, a))
+    if a.buffer_sweep:
+        line["buffer_sweep"] = buffer_sweep(b, a, [int(x) for x in a.buffer_sweep.split(",")])
     if a.ablations:
         line["ablations"] = ablations(a)
     if a.calibrate_copy:
