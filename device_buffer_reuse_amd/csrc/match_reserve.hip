@@ -894,6 +894,7 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     int bstar = nbins;
     int off[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // fast: this wave's first rank in bins 0..7
     uint32_t nz = ~0u;  // fast: bins 0..7 in which this wave has candidates (bit b)
+    uint64_t nz_lo = 0, nz_hi = 0;  // general: bins 0..63, 64..127 holding this wave's candidates
     if (fast) {
       const uint64_t r0 = __ballot((lane & 15) == 15 && inc0 >= m);
       const uint64_t r1 = __ballot((lane & 15) == 15 && inc1 >= m);
@@ -907,17 +908,18 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
       }
       nz = (uint32_t)__ballot(lane < 8 && c8 != 0) | ~0xFFu;
     } else {
-      // general: histogram of all bins (per wave, in LDS), the bin totals,
-      // their exclusive starts, b* and each wave's first rank per bin; lane
-      // l covers bins l and l + 64 (nbins <= 128)
-      for (int b = 0; b < nbins; ++b) {
-        int cnt = 0;
+      // general: histogram of all bins (per wave, in LDS: the wave clears
+      // its row, then one LDS add per candidate, in the wave's issue order),
+      // the bin totals, their exclusive starts, b* and each wave's first
+      // rank per bin; lane l covers bins l and l + 64 (nbins <= 128)
+      int32_t* cnt_w = sCnt + w * nbins;
+      if (lane < nbins) cnt_w[lane] = 0;
+      if (lane + 64 < nbins) cnt_w[lane + 64] = 0;
 #pragma unroll
-        for (int q = 0; q < MAXP; ++q) cnt += __popcll(__ballot(bin[q] == b));
-        if (lane == 0) sCnt[w * nbins + b] = cnt;
-      }
+      for (int q = 0; q < MAXP; ++q)
+        if (bin[q] >= 0) atomicAdd(&cnt_w[bin[q]], 1);
       __syncthreads();
-      int tot0 = 0, tot1 = 0, bef0 = 0, bef1 = 0;
+      int tot0 = 0, tot1 = 0, bef0 = 0, bef1 = 0, own0 = 0, own1 = 0;
       const int b0 = lane, b1 = lane + 64;
 #pragma unroll
       for (int v = 0; v < kMRWaves; ++v) {
@@ -927,7 +929,11 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
         tot1 += c1v;
         bef0 += v < w ? c0v : 0;
         bef1 += v < w ? c1v : 0;
+        own0 = v == w ? c0v : own0;
+        own1 = v == w ? c1v : own1;
       }
+      nz_lo = __ballot(own0 != 0);
+      nz_hi = __ballot(own1 != 0);
       const int inc0 = wave_incl_scan(tot0);
       const int sum0 = __builtin_amdgcn_readlane(inc0, 63);
       const int inc1 = wave_incl_scan(tot1) + sum0;
@@ -942,14 +948,30 @@ __global__ __launch_bounds__(kMRThreads) void match_reserve_kernel(MatchReserveP
     // the same bin, in slot order (slot groups in order, lanes in order)
 #pragma unroll
     for (int q = 0; q < MAXP; ++q) rank[q] = 0;
-    for (int b = 0; b <= bstar; ++b) {
-      if (b < 8 && !((nz >> b) & 1)) continue;  // the wave has no candidate in bin b
+    auto rank_in_bin = [&](int b) {
       int run = 0;
 #pragma unroll
       for (int q = 0; q < MAXP; ++q) {
         const uint64_t grp = __ballot(bin[q] == b);
         if (bin[q] == b) rank[q] = run + mbcnt64(grp);
         run += __popcll(grp);
+      }
+    };
+    if (fast) {
+      for (int b = 0; b <= bstar; ++b)
+        if ((nz >> b) & 1) rank_in_bin(b);  // bins where the wave has candidates
+    } else {
+      // only the bins <= b* that hold candidates of this wave: with m
+      // victims there are at most m of them besides b* itself
+      uint64_t lo = nz_lo & (bstar >= 63 ? ~0ull : (2ull << bstar) - 1);
+      uint64_t hi = bstar < 64 ? 0ull : nz_hi & (bstar >= 127 ? ~0ull : (2ull << (bstar - 64)) - 1);
+      while (lo) {
+        rank_in_bin(__builtin_ctzll(lo));
+        lo &= lo - 1;
+      }
+      while (hi) {
+        rank_in_bin(64 + __builtin_ctzll(hi));
+        hi &= hi - 1;
       }
     }
     // rank[q] becomes the candidate's rank r among all candidates (m for

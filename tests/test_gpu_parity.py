@@ -212,6 +212,28 @@ def test_parity_full_size_wide_buckets():
         run.close()
 
 
+def test_parity_full_size_small_buffer():
+    """The long-context workload at full size with 384 slots per unit: the
+    slots outside each union are few and young, so victims come from LRU
+    buckets past the first eight bins (the general histogram and ranking);
+    state bit-exact every step, attention of sampled units, buffer bytes."""
+    w = tg.WORKLOADS[4].replace(n_slots=384, steps=48)
+    say("[parity-full] %s 384 slots, units=%d steps=%d" % (w.name, w.units, w.steps))
+    sel = tg.selections(w)
+    rng = np.random.default_rng(45)
+    sample = sorted(rng.choice(w.units, size=4, replace=False).tolist())
+    run = Runner(w, attn_units=sample)
+    try:
+        for t in range(w.steps):
+            run.step_and_compare(t, sel[t], tg.queries(w, t), check_attn=(t % 16 == 0))
+        got = run.st.buf_kv.cpu().numpy().view(np.uint16)
+        occ = run.ob.slot_tok >= 0
+        assert np.array_equal(got[occ], run.ob.buf[occ])
+        assert run.ctx.last_error() == 0
+    finally:
+        run.close()
+
+
 def test_parity_full_size_hash_table():
     """The batch workload at full size, every step, matched by the
     open-addressing table at load factor 1/2 (its stated setting; the
