@@ -87,6 +87,11 @@ class Runner:
         """lengths: optional list lengths, [units] or [units][T]."""
         self.gpu_step(sel_t, q_t, lengths)
         self.torch.cuda.synchronize()
+        return self.compare(t, sel_t, q_t, check_attn, check_buf, lengths)
+
+    def compare(self, t, sel_t, q_t, check_attn=True, check_buf=False, lengths=None):
+        """Steps the oracle and compares it with the GPU state and outputs of
+        a step that has run (the device synchronized)."""
         ln = None if lengths is None else np.asarray(lengths, np.int32).reshape(
             self.w.units, self.w.n_q_tokens)
         ctx_len = getattr(self, "ctx_len", None)
