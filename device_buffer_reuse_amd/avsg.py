@@ -477,6 +477,13 @@ class Context:
         if st != OK:
             raise AvsgError(st, "avsg_set_step")
 
+    def set_stream(self, stream):
+        """Later calls enqueue on `stream` (a torch.cuda.Stream)."""
+        st = avsg_set_stream(self.handle, stream.cuda_stream)
+        if st != OK:
+            raise AvsgError(st, "avsg_set_stream")
+        self.stream = stream
+
     def set_transfer_mode(self, mode: int):
         st = avsg_set_transfer_mode(self.handle, mode)
         if st != OK:

@@ -61,3 +61,30 @@ def test_contexts_on_two_streams():
     assert a.ctx.last_error() == 0 and b.ctx.last_error() == 0
     a.close()
     b.close()
+
+
+def test_context_moves_to_another_stream():
+    """A context's later calls go to the stream avsg_set_stream names: steps
+    continue there, with the step counter kept in the workspace."""
+    import torch
+    say("[concurrent] set_stream")
+    w = PAGED_LRU
+    run = Runner(w)
+    sel = tg.selections(w)
+    half = w.steps // 2
+    for t in range(half):
+        run.step_and_compare(t, sel[t], tg.queries(w, t), check_buf=True)
+    s2 = torch.cuda.Stream()
+    run.ctx.set_stream(s2)
+    for t in range(half, w.steps):
+        q = tg.queries(w, t)
+        sel_d = torch.from_numpy(np.ascontiguousarray(sel[t])).cuda()
+        q_d = torch.from_numpy(q.view(np.int16)).cuda()
+        torch.cuda.synchronize()   # inputs in place before s2's kernels read them
+        run.ctx.step(sel_d, q_d, run.host, run.st.buf_kv, run.st.slot_table, run.st.lifetimes,
+                     run.st.out, run.st.stats)
+        s2.synchronize()
+        run.compare(t, sel[t], q, check_buf=True)
+    assert run.ctx.t == w.steps
+    assert run.ctx.last_error() == 0
+    run.close()
