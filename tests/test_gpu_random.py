@@ -19,7 +19,7 @@ from context_inputs import clip_to_context
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(128))
+SEEDS = list(range(256))
 
 
 def draw(seed):
