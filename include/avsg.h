@@ -73,7 +73,9 @@ typedef enum avsg_policy {
   /* Bucketed LRU (Spin summary, section 2B): lifetimes[] holds the step of
    * last selection; the bucket of a slot is min(t - stamp - 1, n_buckets - 1)
    * with one-step buckets (bucket_width widens them) and older buckets are
-   * evicted first. */
+   * evicted first.  Stamps are int32, so a context takes at most 2^31 steps
+   * under this policy before avsg_reset (a later step's stamps fail
+   * validation: AVSG_ERR_STATE). */
   AVSG_POLICY_BUCKET_LRU = 1
 } avsg_policy;
 
